@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed form
+worked by hand, a textbook or library routine the step reduces to in a special
+case, an invariant the pages state, or brute force on tiny inputs.  The
+citations name the page and section the pinned property comes from.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dflash2 as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def to_bf16_bits(x):
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- number plumbing
+
+def test_widen_bf16_known_patterns():
+    # IEEE bf16: 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25, 0x0000 = 0
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x0000], dtype=np.uint16)
+    assert O.widen_bf16(bits).tolist() == [1.0, -2.0, 0.25, 0.0]
+
+
+def test_round_to_bf16_matches_torch():
+    x = np.random.default_rng(0).standard_normal(10000) * 37.0
+    ref = torch.as_tensor(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to_bf16(x), ref)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rms_norm_hand_example():
+    # x = [3, 4]: mean square 12.5; y = x / sqrt(12.5) * gamma
+    y = O.rms_norm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.0)
+    assert np.allclose(y, [3 / math.sqrt(12.5), 8 / math.sqrt(12.5)], rtol=1e-15)
+
+
+def test_rms_norm_scale_invariance_and_unit_rms(rng):
+    x = rng.standard_normal((5, 64))
+    g = np.ones(64)
+    y = O.rms_norm(x, g, 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-14)
+    assert np.allclose(O.rms_norm(7.5 * x, g, 0.0), y, rtol=1e-13)
+
+
+def test_rms_norm_eps_limits_tiny_rows():
+    # a zero row stays zero (eps keeps the division finite)
+    assert np.all(O.rms_norm(np.zeros((1, 8)), np.ones(8), 1e-6) == 0.0)
+
+
+# ---------------------------------------------------------------- RoPE (neox)
+
+def test_rope_position_zero_is_identity(rng):
+    x = rng.standard_normal((3, 2, 16))
+    assert np.array_equal(O.rope_neox(x, np.zeros(3), 1e7), x)
+
+
+def test_rope_hand_example_pair_rotation():
+    # D = 4, theta = 100: inv_freq = [1, 0.1]; pos 1 rotates pair (x0, x2) by 1 rad
+    # and pair (x1, x3) by 0.1 rad, each a textbook 2-D rotation.
+    x = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    y = O.rope_neox(x, np.array([1]), 100.0)[0, 0]
+    c1, s1, c2, s2 = math.cos(1), math.sin(1), math.cos(0.1), math.sin(0.1)
+    want = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    assert np.allclose(y, want, rtol=1e-14)
+
+
+def test_rope_is_complex_multiplication(rng):
+    D, theta = 32, 1e7
+    x = rng.standard_normal((4, 1, D))
+    pos = np.array([0, 5, 77, 8191])
+    y = O.rope_neox(x, pos, theta)
+    zc = x[..., : D // 2] + 1j * x[..., D // 2:]
+    ang = pos[:, None, None] * theta ** (-np.arange(D // 2) * 2.0 / D)
+    w = zc * np.exp(1j * ang)
+    assert np.allclose(y[..., : D // 2], w.real, atol=1e-12)
+    assert np.allclose(y[..., D // 2:], w.imag, atol=1e-12)
+
+
+def test_rope_relative_position(rng):
+    D = 64
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    dots = []
+    for m, n in [(10, 3), (107, 100), (7, 0)]:
+        qm = O.rope_neox(q, np.array([m]), 1e7)
+        kn = O.rope_neox(k, np.array([n]), 1e7)
+        dots.append(float(np.sum(qm * kn)))
+    assert np.allclose(dots, dots[0], rtol=1e-11)
+
+
+def test_rope_keeps_pair_norms(rng):
+    D = 128
+    x = rng.standard_normal((6, 3, D))
+    y = O.rope_neox(x, np.arange(6) * 1000, 1e7)
+    nx = x[..., :64] ** 2 + x[..., 64:] ** 2
+    ny = y[..., :64] ** 2 + y[..., 64:] ** 2
+    assert np.allclose(nx, ny, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- grouped dynamic conv
+
+def _conv_case(rng, T=12, H=8, G=4, grp=2):
+    ng = H // grp
+    x = rng.standard_normal((T, H))
+    w_kp = rng.standard_normal((4 * ng, H)) * 0.3
+    base = rng.standard_normal((2, 2, H)) * 0.1 + 0.5
+    return x, w_kp, base, G, grp
+
+
+def test_conv_zero_delta_is_textbook_depthwise_conv(rng):
+    # [P2 header, P3 DFlash2GroupedConv]: with kernel_projection = 0 the conv is a fixed
+    # two-tap depthwise conv1d per block with a zero left pad: np.convolve per channel.
+    x, w_kp, base, G, grp = _conv_case(rng)
+    w_kp[:] = 0
+    a, d1 = O.conv_prepare(x, w_kp, base, G, grp)
+    T, H = x.shape
+    for blk in range(T // G):
+        for c in range(H):
+            col = x[blk * G:(blk + 1) * G, c]
+            want = np.convolve(col, [base[0, 0, c], base[0, 1, c]])[:G]
+            assert np.allclose(a[blk * G:(blk + 1) * G, c], want, rtol=1e-14)
+    assert np.all(d1 == 0)
+    f = O.conv_finish(x, d1, base, G, grp)
+    want = torch.nn.functional.conv1d(
+        torch.as_tensor(x.reshape(T // G, G, H).transpose(0, 2, 1)),
+        torch.as_tensor(base[1][::-1].T.copy()[:, None, :]), padding=1, groups=H)[..., :G]
+    assert np.allclose(f, want.numpy().transpose(0, 2, 1).reshape(T, H), rtol=1e-13)
+
+
+def test_conv_block_locality(rng):
+    # [P3 DFlash2GroupedConv]: never reads across a block boundary.
+    x, w_kp, base, G, grp = _conv_case(rng)
+    a, d1 = O.conv_prepare(x, w_kp, base, G, grp)
+    x2 = x.copy()
+    x2[G - 1] += 5.0                                   # last row of block 0
+    a2, d12 = O.conv_prepare(x2, w_kp, base, G, grp)
+    assert np.array_equal(a2[G:], a[G:])
+    assert np.array_equal(d12[G:], d1[G:])
+    x3 = x.copy()
+    x3[G + 1] -= 3.0                                   # row 1 of block 1 leaves row 0 alone
+    a3, _ = O.conv_prepare(x3, w_kp, base, G, grp)
+    assert np.array_equal(a3[G], a[G])
+
+
+def test_conv_finish_is_linear(rng):
+    x, w_kp, base, G, grp = _conv_case(rng)
+    _, d1 = O.conv_prepare(x, w_kp, base, G, grp)
+    y1, y2 = rng.standard_normal(x.shape), rng.standard_normal(x.shape)
+    lhs = O.conv_finish(2.0 * y1 - 0.5 * y2, d1, base, G, grp)
+    rhs = 2.0 * O.conv_finish(y1, d1, base, G, grp) - 0.5 * O.conv_finish(y2, d1, base, G, grp)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_hand_example():
+    # tests/golden/conv_hand.json is worked by hand from the conv equation of the
+    # dflash2.ts header: out[t,c] = sum_tap (base[side,tap,c] + D[t,side,tap,c//grp]) y[t-tap,c].
+    with open(os.path.join(GOLDEN, "conv_hand.json")) as f:
+        case = json.load(f)
+    x = np.array(case["x"], dtype=float)
+    a, d1 = O.conv_prepare(x, np.array(case["w_kp"], dtype=float), np.array(case["base"], dtype=float),
+                           case["block"], case["group"])
+    assert np.allclose(a, case["prepare_out"], rtol=1e-15)
+    assert np.allclose(d1, case["side1_deltas"], rtol=1e-15)
+    f_ = O.conv_finish(np.array(case["y"], dtype=float), d1, np.array(case["base"], dtype=float),
+                       case["block"], case["group"])
+    assert np.allclose(f_, case["finish_out"], rtol=1e-15)
+
+
+def test_conv_group_broadcast_and_column_order(rng):
+    # kernel_projection columns read as [side][tap][group] (dflash2.ts header: "[stage, tap, group]");
+    # one-hot rows make D[t, s, tap, g] = x[t, src(s, tap, g)], so every coefficient is traceable.
+    T, H, G, grp = 4, 8, 4, 4
+    ng = H // grp
+    x = rng.standard_normal((T, H))
+    src = np.arange(4 * ng) % H
+    w_kp = np.zeros((4 * ng, H))
+    w_kp[np.arange(4 * ng), src] = 1.0
+    base = np.zeros((2, 2, H))
+    a, d1 = O.conv_prepare(x, w_kp, base, G, grp)
+    for t in range(T):
+        for c in range(H):
+            g = c // grp
+            d00 = x[t, src[(0 * 2 + 0) * ng + g]]
+            d01 = x[t, src[(0 * 2 + 1) * ng + g]]
+            prev = x[t - 1, c] if t % G else 0.0
+            assert math.isclose(a[t, c], d00 * x[t, c] + d01 * prev, rel_tol=1e-14, abs_tol=1e-15)
+        for tap in range(2):
+            for g in range(ng):
+                assert d1[t, tap, g] == x[t, src[(1 * 2 + tap) * ng + g]]
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_reference(q, kc, vc, kb, vb, ctx_len):
+    """torch's scaled_dot_product_attention (CPU, float64) with GQA heads repeated."""
+    B, G, NH, D = q.shape
+    rep = NH // kb.shape[2]
+    out = np.zeros_like(q)
+    for b in range(B):
+        L = int(ctx_len[b])
+        keys = torch.as_tensor(np.concatenate([kc[b, :L], kb[b]], 0)).permute(1, 0, 2)
+        vals = torch.as_tensor(np.concatenate([vc[b, :L], vb[b]], 0)).permute(1, 0, 2)
+        keys = keys.repeat_interleave(rep, 0)
+        vals = vals.repeat_interleave(rep, 0)
+        qq = torch.as_tensor(q[b]).permute(1, 0, 2)
+        o = torch.nn.functional.scaled_dot_product_attention(qq, keys, vals)
+        out[b] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+def test_attention_matches_library_sdpa(rng):
+    B, G, NH, NKV, D, Lcap = 3, 5, 4, 2, 16, 9
+    q = rng.standard_normal((B, G, NH, D))
+    kc, vc = rng.standard_normal((B, Lcap, NKV, D)), rng.standard_normal((B, Lcap, NKV, D))
+    kb, vb = rng.standard_normal((B, G, NKV, D)), rng.standard_normal((B, G, NKV, D))
+    ctx_len = np.array([9, 0, 4])                      # ragged, including an empty context
+    got = O.attention(q, kc, vc, kb, vb, ctx_len)
+    assert np.allclose(got, _sdpa_reference(q, kc, vc, kb, vb, ctx_len), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases(rng):
+    B, G, NH, NKV, D = 1, 3, 2, 1, 8
+    q = rng.standard_normal((B, G, NH, D))
+    # identical keys: softmax is uniform, the output is the mean of the values
+    k_same = np.broadcast_to(rng.standard_normal(D), (B, 4, NKV, D)).copy()
+    kb_same = np.broadcast_to(k_same[0, 0], (B, G, NKV, D)).copy()
+    vc, vb = rng.standard_normal((B, 4, NKV, D)), rng.standard_normal((B, G, NKV, D))
+    out = O.attention(q, k_same, vc, kb_same, vb, np.array([4]))
+    mean_v = np.concatenate([vc[0], vb[0]], 0)[:, 0].mean(0)
+    assert np.allclose(out[0, :, 0], mean_v, rtol=1e-12)
+    # a single key (no context, one block row): the output is that value
+    q1 = rng.standard_normal((1, 1, 2, D))
+    kb1, vb1 = rng.standard_normal((1, 1, 1, D)), rng.standard_normal((1, 1, 1, D))
+    out1 = O.attention(q1, np.zeros((1, 0, 1, D)), np.zeros((1, 0, 1, D)), kb1, vb1, np.array([0]))
+    assert np.allclose(out1[0, 0, 0], vb1[0, 0, 0]) and np.allclose(out1[0, 0, 1], vb1[0, 0, 0])
+
+
+def test_attention_brute_force_loops(rng):
+    B, G, NH, NKV, D, L = 1, 2, 2, 1, 4, 3
+    q = rng.standard_normal((B, G, NH, D))
+    kc, vc = rng.standard_normal((B, L, NKV, D)), rng.standard_normal((B, L, NKV, D))
+    kb, vb = rng.standard_normal((B, G, NKV, D)), rng.standard_normal((B, G, NKV, D))
+    got = O.attention(q, kc, vc, kb, vb, np.array([L]))
+    keys = [kc[0, j, 0] for j in range(L)] + [kb[0, j, 0] for j in range(G)]
+    vals = [vc[0, j, 0] for j in range(L)] + [vb[0, j, 0] for j in range(G)]
+    for t in range(G):
+        for h in range(NH):
+            logits = [sum(q[0, t, h, d] * kk[d] for d in range(D)) / math.sqrt(D) for kk in keys]
+            w = [math.exp(s) for s in logits]
+            z = sum(w)
+            want = [sum(w[j] * vals[j][d] for j in range(len(keys))) / z for d in range(D)]
+            assert np.allclose(got[0, t, h], want, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- MLP
+
+def test_swiglu_matches_torch(rng):
+    i = rng.standard_normal((3, 8))
+    wg, wu, wd = rng.standard_normal((6, 8)), rng.standard_normal((6, 8)), rng.standard_normal((8, 6))
+    t = torch.as_tensor
+    ref = (torch.nn.functional.silu(t(i) @ t(wg).T) * (t(i) @ t(wu).T)) @ t(wd).T
+    assert np.allclose(O.mlp(i, wg, wu, wd), ref.numpy(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- top-k candidates
+
+def test_topk_brute_force_with_ties(rng):
+    V, K = 40, 6
+    vals = rng.integers(-3, 4, size=(5, V)).astype(np.float32)   # many ties
+    ids, unary = O.compute_candidates(vals, K)
+    for r in range(5):
+        want = sorted(range(V), key=lambda i: (-vals[r, i], i))[:K]
+        assert ids[r].tolist() == want
+        assert unary[r].tolist() == [vals[r, i] for i in want]
+
+
+def test_topk_constant_row_takes_lowest_ids():
+    ids, _ = O.compute_candidates(np.full((2, 100), 0.5, np.float32), 4)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2
+
+
+# ---------------------------------------------------------------- score_edges / select_path
+
+def _selector_case(rng, B=2, S=4, K=3, R=5, V=11):
+    logits = rng.standard_normal((B, S, V)).astype(np.float32)
+    cand, unary = O.compute_candidates(logits, K)
+    z = rng.standard_normal((B, S, R))
+    pred, succ = rng.standard_normal((V, R)), rng.standard_normal((V, R))
+    anchors = rng.integers(0, V, size=B)
+    return logits, cand, unary, z, pred, succ, anchors
+
+
+def test_score_edges_brute_force(rng):
+    _, cand, unary, z, pred, succ, anchors = _selector_case(rng)
+    S_ = O.score_edges(cand, unary, z, anchors, pred, succ)
+    B, S, K = cand.shape
+    for b, l, p, c in itertools.product(range(B), range(S), range(K), range(K)):
+        prev = anchors[b] if l == 0 else cand[b, l - 1, p]
+        want = unary[b, l, c] + sum(pred[prev, r] * z[b, l, r] * succ[cand[b, l, c], r]
+                                    for r in range(z.shape[-1]))
+        assert math.isclose(S_[b, l, p, c], want, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_score_edges_slot0_is_anchor_broadcast(rng):
+    # [P3 DFlash2CandidateSelector]: at slot 0 every predecessor row is the anchor's.
+    _, cand, unary, z, pred, succ, anchors = _selector_case(rng)
+    S_ = O.score_edges(cand, unary, z, anchors, pred, succ)
+    assert np.all(S_[:, 0, :, :] == S_[:, 0, :1, :])
+
+
+def test_score_edges_zero_codebooks_give_unary(rng):
+    _, cand, unary, z, pred, succ, anchors = _selector_case(rng)
+    S_ = O.score_edges(cand, unary, z, anchors, np.zeros_like(pred), succ)
+    assert np.array_equal(S_, np.broadcast_to(unary[:, :, None, :], S_.shape))
+
+
+def test_select_path_seed_index_independent(rng):
+    # [P3 select_path]: seeding the walk at index 0 selects the same row as any other index.
+    _, cand, unary, z, pred, succ, anchors = _selector_case(rng, K=5)
+    S_ = O.score_edges(cand, unary, z, anchors, pred, succ)
+    first = O.select_path(S_, cand, 0)
+    for p0 in range(1, 5):
+        assert np.array_equal(O.select_path(S_, cand, p0), first)
+
+
+def test_select_path_zero_codebooks_is_argmax_decoding(rng):
+    logits, cand, unary, z, pred, succ, anchors = _selector_case(rng, V=50)
+    S_ = O.score_edges(cand, unary, z, anchors, np.zeros_like(pred), np.zeros_like(succ))
+    tokens = O.select_path(S_, cand)
+    assert np.array_equal(tokens, np.argmax(logits, axis=-1))
+
+
+def test_select_path_matches_sequential_gather_walk(rng):
+    # The dflash2.ts `#select` form: at each position gather pred[previous token] and
+    # succ[candidates] and take the argmax of unary + edge; the previous token starts at
+    # the anchor.  It must agree with score_edges + select_path.
+    for _ in range(5):
+        _, cand, unary, z, pred, succ, anchors = _selector_case(rng, K=4)
+        S_ = O.score_edges(cand, unary, z, anchors, pred, succ)
+        tokens = O.select_path(S_.astype(np.float32), cand)
+        B, S, K = cand.shape
+        for b in range(B):
+            prev = anchors[b]
+            for l in range(S):
+                tot = [np.float32(unary[b, l, c] + np.dot(succ[cand[b, l, c]], pred[prev] * z[b, l]))
+                       for c in range(K)]
+                best = max(range(K), key=lambda c: (tot[c], -c))
+                prev = cand[b, l, best]
+                assert tokens[b, l] == prev
+
+
+def test_select_path_greedy_property(rng):
+    _, cand, unary, z, pred, succ, anchors = _selector_case(rng, K=6, S=5)
+    S_ = O.score_edges(cand, unary, z, anchors, pred, succ).astype(np.float32)
+    tokens = O.select_path(S_, cand)
+    B, S, K = cand.shape
+    for b in range(B):
+        j = 0
+        for l in range(S):
+            c = list(cand[b, l]).index(tokens[b, l])
+            assert S_[b, l, j, c] == S_[b, l, j].max()
+            assert all(S_[b, l, j, c2] < S_[b, l, j, c] for c2 in range(c))   # lowest slot on ties
+            j = c
+
+
+def test_select_path_ties_take_lowest_slot():
+    scores = np.zeros((1, 2, 3, 3), np.float32)
+    cand = np.array([[[7, 8, 9], [4, 5, 6]]], np.int32)
+    assert O.select_path(scores, cand).tolist() == [[7, 4]]
