@@ -1,0 +1,298 @@
+"""ctypes binding of libdflash2.so with the C ABI's names.
+
+Argument marshalling only: tensors become device pointers, the stream is torch's current
+HIP stream, and a non-zero status raises DflError with dfl_last_error().  Every step of
+the path runs in the library's kernels; there is no fallback.  PyTorch only allocates the
+device memory the calls read and write.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdflash2.so")
+
+DFL_OK, DFL_E_INVALID, DFL_E_SHAPE, DFL_E_UNSUPPORTED = 0, -1, -2, -3
+DFL_E_WORKSPACE, DFL_E_NOMEM, DFL_E_DEVICE = -4, -5, -6
+
+KERNEL_CLASSES = ["gemm_head", "gemm_gateup", "gemm_down", "gemm_qkv", "gemm_o", "gemm_kproj",
+                  "gemm_selproj", "gemm_context", "attention", "conv_prepare", "conv_finish",
+                  "rmsnorm", "rope", "topk", "score_edges", "select_path"]
+
+
+class DflError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dflash2 error {code}: {msg}")
+        self.code = code
+
+
+class dfl_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in
+                ("hidden", "layers", "heads", "kv_heads", "head_dim", "intermediate", "n_taps",
+                 "block_size", "conv_taps", "conv_group", "top_k", "rank", "vocab")] + \
+               [("rms_eps", C.c_float), ("rope_theta", C.c_float),
+                ("tap_layer_ids", C.POINTER(C.c_int32))]
+
+
+LAYER_FIELDS = ("input_norm", "post_norm", "q_proj", "k_proj", "v_proj", "o_proj", "q_norm",
+                "k_norm", "gate_proj", "up_proj", "down_proj", "attn_base", "attn_kproj",
+                "mlp_base", "mlp_kproj")
+
+
+class dfl_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in LAYER_FIELDS]
+
+
+class dfl_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("fc", "hidden_norm", "norm", "sel_proj", "pred", "succ")] + \
+               [("layers", C.POINTER(dfl_layer_weights))]
+
+
+_P, _I, _F, _Z = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+_SIGS = {
+    "dfl_last_error": (C.c_char_p, []),
+    "dfl_drafter_load": (_I, [C.POINTER(dfl_config), C.POINTER(dfl_weights), _P, C.POINTER(_P)]),
+    "dfl_drafter_free": (None, [_P]),
+    "dfl_context_workspace_bytes": (_Z, [_P, _I, _I]),
+    "dfl_context_materialize": (_I, [_P, _P, _I, _I, _I, _I, C.POINTER(_P), C.POINTER(_P), _P, _Z, _P]),
+    "dfl_draft_workspace_bytes": (_Z, [_P, _I, _I, _I]),
+    "dfl_draft_block": (_I, [_P, _P, _P, _I, _I, C.POINTER(_P), C.POINTER(_P), _I, _I, _P, _P, _P,
+                             _P, _P, _P, _Z, _P]),
+    "dfl_rms_norm": (_I, [_P, _I, _I, _I, _P, _F, _P, _I, _P]),
+    "dfl_linear_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dfl_linear": (_I, [_P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
+    "dfl_head_norm_rope": (_I, [_P, _I, _I, _I, _I, _P, _F, _F, _P, _I, _P]),
+    "dfl_attention_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "dfl_block_attention": (_I, [_P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _I,
+                                 _P, _Z, _P]),
+    "dfl_conv_prepare_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dfl_conv_prepare": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "dfl_conv_finish": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "dfl_candidates_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dfl_compute_candidates": (_I, [_P, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "dfl_selector_project_workspace_bytes": (_Z, [_I, _I, _I]),
+    "dfl_selector_project": (_I, [_P, _I, _I, _P, _I, _P, _P, _Z, _P]),
+    "dfl_score_edges": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dfl_set_timed_kernel": (_I, [_P, _I]),
+    "dfl_read_kernel_time": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64),
+                                  C.POINTER(C.c_double)]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libdflash2.so (built in-tree by the package's build step); fail loudly if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> list[str]:
+    return list(_SIGS)
+
+
+def _check(code: int) -> None:
+    if code != DFL_OK:
+        raise DflError(code, lib().dfl_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None, dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _bf(t):
+    return _ptr(t, torch.bfloat16)
+
+
+def _f32(t):
+    return _ptr(t, torch.float32)
+
+
+def _i32(t):
+    return _ptr(t, torch.int32)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr_array(ts) -> C.Array:
+    arr = (C.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _bf(t)
+    return arr
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """Device workspace of at least nbytes (256-byte aligned by the caching allocator)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- config/load
+
+def make_config(dims, tap_layer_ids=None) -> tuple[dfl_config, object]:
+    ids = None
+    if tap_layer_ids is not None:
+        ids = (C.c_int32 * len(tap_layer_ids))(*tap_layer_ids)
+    cfg = dfl_config(dims.hidden, dims.layers, dims.heads, dims.kv_heads, dims.head_dim,
+                     dims.intermediate, dims.n_taps, dims.block_size, dims.conv_taps,
+                     dims.conv_group, dims.top_k, dims.rank, dims.vocab, dims.rms_eps,
+                     dims.rope_theta, C.cast(ids, C.POINTER(C.c_int32)) if ids is not None else None)
+    return cfg, ids
+
+
+def dfl_drafter_load(dims, weights: dict, tap_layer_ids=None, stream=None) -> int:
+    """weights: checkpoint name -> bf16 device tensor (the drafter's checkpoint names)."""
+    cfg, keep = make_config(dims, tap_layer_ids)
+    layers = (dfl_layer_weights * dims.layers)()
+    names = {"input_norm": "input_layernorm.weight", "post_norm": "post_attention_layernorm.weight",
+             "q_proj": "self_attn.q_proj.weight", "k_proj": "self_attn.k_proj.weight",
+             "v_proj": "self_attn.v_proj.weight", "o_proj": "self_attn.o_proj.weight",
+             "q_norm": "self_attn.q_norm.weight", "k_norm": "self_attn.k_norm.weight",
+             "gate_proj": "mlp.gate_proj.weight", "up_proj": "mlp.up_proj.weight",
+             "down_proj": "mlp.down_proj.weight", "attn_base": "attention_conv.base_kernel",
+             "attn_kproj": "attention_conv.kernel_projection.weight",
+             "mlp_base": "mlp_conv.base_kernel", "mlp_kproj": "mlp_conv.kernel_projection.weight"}
+    for i in range(dims.layers):
+        for f, n in names.items():
+            setattr(layers[i], f, _bf(weights[f"layers.{i}.{n}"]))
+    w = dfl_weights(_bf(weights["fc.weight"]), _bf(weights["hidden_norm.weight"]),
+                    _bf(weights["norm.weight"]),
+                    _bf(weights["candidate_selector.hidden_projection.weight"]),
+                    _bf(weights["candidate_selector.predecessor_codebook"]),
+                    _bf(weights["candidate_selector.successor_codebook"]),
+                    C.cast(layers, C.POINTER(dfl_layer_weights)))
+    h = C.c_void_p()
+    _check(lib().dfl_drafter_load(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
+    del keep
+    return h.value
+
+
+def dfl_drafter_free(handle: int) -> None:
+    if handle:
+        lib().dfl_drafter_free(handle)
+
+
+def dfl_context_workspace_bytes(handle, B, L) -> int:
+    return lib().dfl_context_workspace_bytes(handle, B, L)
+
+
+def dfl_context_materialize(handle, taps, B, L, row_offset, Lcap, K: list, V: list, ws, stream=None):
+    _check(lib().dfl_context_materialize(handle, _bf(taps), B, L, row_offset, Lcap, _ptr_array(K),
+                                         _ptr_array(V), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_draft_workspace_bytes(handle, B, G, Lmax) -> int:
+    return lib().dfl_draft_workspace_bytes(handle, B, G, Lmax)
+
+
+def dfl_draft_block(handle, embeds, anchors, B, G, K: list, V: list, Lcap, Lmax, ctx_len, pos0,
+                    lm_head, tokens, logits_out, ws, stream=None):
+    kp = _ptr_array(K) if K else None
+    vp = _ptr_array(V) if V else None
+    _check(lib().dfl_draft_block(handle, _bf(embeds), _i32(anchors), B, G, kp, vp, Lcap, Lmax,
+                                 _i32(ctx_len), _i32(pos0), _bf(lm_head), _i32(tokens),
+                                 _f32(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_rms_norm(x, rows, H, ldx, gamma, eps, y, ldy, stream=None):
+    _check(lib().dfl_rms_norm(_bf(x), rows, H, ldx, _bf(gamma), eps, _bf(y), ldy, _stream(stream)))
+
+
+def dfl_linear_workspace_bytes(M, N, K) -> int:
+    return lib().dfl_linear_workspace_bytes(M, N, K)
+
+
+def dfl_linear(x, M, K, ldx, W, N, y, ldy, out_f32, ws, stream=None):
+    _check(lib().dfl_linear(_bf(x), M, K, ldx, _bf(W), N, _ptr(y, torch.float32 if out_f32 else torch.bfloat16),
+                            ldy, int(out_f32), _ptr(ws) if ws is not None else None,
+                            ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def dfl_head_norm_rope(x, rows, heads, D, ldx, gamma, eps, theta, pos0, rows_per_req, stream=None):
+    _check(lib().dfl_head_norm_rope(_bf(x), rows, heads, D, ldx, _bf(gamma), eps, theta, _i32(pos0),
+                                    rows_per_req, _stream(stream)))
+
+
+def dfl_attention_workspace_bytes(B, G, NH, NKV, D, Lmax) -> int:
+    return lib().dfl_attention_workspace_bytes(B, G, NH, NKV, D, Lmax)
+
+
+def dfl_block_attention(q, ldq, kb, vb, ldkv, K, V, Lcap, Lmax, ctx_len, B, G, NH, NKV, D, out, ldo, ws,
+                        stream=None):
+    _check(lib().dfl_block_attention(_bf(q), ldq, _bf(kb), _bf(vb), ldkv, _bf(K), _bf(V), Lcap, Lmax,
+                                     _i32(ctx_len), B, G, NH, NKV, D, _bf(out), ldo, _ptr(ws), ws.numel(),
+                                     _stream(stream)))
+
+
+def dfl_conv_prepare_workspace_bytes(T, H, grp) -> int:
+    return lib().dfl_conv_prepare_workspace_bytes(T, H, grp)
+
+
+def dfl_conv_prepare(x, T, H, G, grp, kproj, base, out, coef1, ws, stream=None):
+    _check(lib().dfl_conv_prepare(_bf(x), T, H, G, grp, _bf(kproj), _bf(base), _bf(out), _f32(coef1),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_conv_finish(y, coef1, base, T, H, G, grp, residual, out, stream=None):
+    _check(lib().dfl_conv_finish(_bf(y), _f32(coef1), _bf(base), T, H, G, grp, _bf(residual), _bf(out),
+                                 _stream(stream)))
+
+
+def dfl_candidates_workspace_bytes(N, V, K) -> int:
+    return lib().dfl_candidates_workspace_bytes(N, V, K)
+
+
+def dfl_compute_candidates(logits, N, V, K, ids, unary, ws, stream=None):
+    _check(lib().dfl_compute_candidates(_f32(logits), N, V, K, _i32(ids), _f32(unary), _ptr(ws), ws.numel(),
+                                        _stream(stream)))
+
+
+def dfl_selector_project_workspace_bytes(N, H, R) -> int:
+    return lib().dfl_selector_project_workspace_bytes(N, H, R)
+
+
+def dfl_selector_project(h, N, H, proj, R, z, ws, stream=None):
+    _check(lib().dfl_selector_project(_bf(h), N, H, _bf(proj), R, _f32(z), _ptr(ws) if ws is not None else None,
+                                      ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def dfl_score_edges(cand, unary, z, anchors, B, S, K, R, pred, succ, V, scores, stream=None):
+    _check(lib().dfl_score_edges(_i32(cand), _f32(unary), _f32(z), _i32(anchors), B, S, K, R, _bf(pred),
+                                 _bf(succ), V, _f32(scores), _stream(stream)))
+
+
+def dfl_select_path(scores, cand, B, S, K, tokens, stream=None):
+    _check(lib().dfl_select_path(_f32(scores), _i32(cand), B, S, K, _i32(tokens), _stream(stream)))
+
+
+def dfl_set_timed_kernel(handle, kclass: int | str):
+    k = KERNEL_CLASSES.index(kclass) if isinstance(kclass, str) else kclass
+    _check(lib().dfl_set_timed_kernel(handle, k))
+
+
+def dfl_read_kernel_time(handle) -> tuple[float, int, float]:
+    ms, n, by = C.c_double(), C.c_int64(), C.c_double()
+    _check(lib().dfl_read_kernel_time(handle, C.byref(ms), C.byref(n), C.byref(by)))
+    return ms.value, n.value, by.value

@@ -1,0 +1,742 @@
+// C ABI of the drafter (include/dflash2.h): argument validation, owned weight repacking,
+// workspace carving and the launch sequence of a draft block.  Nothing here synchronises
+// the caller's stream except dfl_drafter_load and dfl_read_kernel_time.
+#include "dflash2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define DFL_REQUIRE(cond, code, ...) \
+  do {                               \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define DFL_HIP(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(DFL_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carve of a caller workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct LayerBuf {
+  uint16_t *in_norm, *post_norm, *q_norm, *k_norm;
+  uint16_t *qkv, *o, *gateup, *down;
+  uint16_t *attn_base, *attn_kproj, *mlp_base, *mlp_kproj;
+  uint16_t* kv_ctx;  // [k | v] rows for the context path
+};
+
+struct TimedLaunch {
+  hipEvent_t start, stop;
+  double bytes;
+};
+
+}  // namespace
+
+struct dfl_drafter {
+  dfl_config cfg;
+  void* arena = nullptr;
+  uint16_t *fc, *hidden_norm, *norm, *sel_proj, *pred, *succ;
+  std::vector<LayerBuf> layers;
+  int timed_class = DFL_K_NONE;
+  std::vector<TimedLaunch> timed;
+  std::vector<hipEvent_t> pool;
+};
+
+namespace {
+
+hipEvent_t pooled_event(dfl_drafter* d) {
+  if (!d->pool.empty()) {
+    hipEvent_t e = d->pool.back();
+    d->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `f` (which enqueues the launches of kernel class k), bracketed by events when k is
+// the class being timed.
+template <class F>
+int timed(dfl_drafter* d, int k, double bytes, hipStream_t s, F&& f) {
+  const bool on = d && d->timed_class == k;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (on) {
+    a = pooled_event(d);
+    b = pooled_event(d);
+    if (!a || !b) return fail(DFL_E_DEVICE, "hipEventCreate failed");
+    DFL_HIP(hipEventRecord(a, s));
+  }
+  hipError_t e = f();
+  if (e != hipSuccess) return fail(DFL_E_DEVICE, "kernel launch (class %d): %s", k, hipGetErrorString(e));
+  if (on) {
+    DFL_HIP(hipEventRecord(b, s));
+    d->timed.push_back({a, b, bytes});
+  }
+  return DFL_OK;
+}
+
+#define DFL_TRY(expr)          \
+  do {                         \
+    int rc_ = (expr);          \
+    if (rc_ != DFL_OK) return rc_; \
+  } while (0)
+
+double gemm_bytes(int M, int N, int K, int epi) {
+  const double out = epi == dfl::EPI_F32 ? 4.0 * M * N : (epi == dfl::EPI_SILU_MUL ? 1.0 * M * N : 2.0 * M * N);
+  return 2.0 * M * K + 2.0 * N * K + out;
+}
+
+int check_config(const dfl_config* c) {
+  DFL_REQUIRE(c, DFL_E_INVALID, "config is NULL");
+  DFL_REQUIRE(c->hidden > 0 && c->layers > 0 && c->heads > 0 && c->kv_heads > 0 && c->head_dim > 0 &&
+                  c->intermediate > 0 && c->n_taps > 0 && c->block_size > 0 && c->conv_group > 0 &&
+                  c->top_k > 0 && c->rank > 0 && c->vocab > 0,
+              DFL_E_INVALID, "config sizes must be positive");
+  DFL_REQUIRE(c->conv_taps == 2, DFL_E_UNSUPPORTED, "conv_taps %d not supported (two-tap only)", c->conv_taps);
+  DFL_REQUIRE(c->block_size >= 2, DFL_E_UNSUPPORTED, "block_size %d < 2: zero draft rows are not supported",
+              c->block_size);
+  DFL_REQUIRE(c->heads % c->kv_heads == 0, DFL_E_SHAPE, "heads %d not a multiple of kv_heads %d", c->heads,
+              c->kv_heads);
+  DFL_REQUIRE(c->head_dim == 64 || c->head_dim == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128",
+              c->head_dim);
+  DFL_REQUIRE(c->hidden % 64 == 0 && c->hidden <= 8192, DFL_E_UNSUPPORTED,
+              "hidden %d must be a multiple of 64 and <= 8192", c->hidden);
+  DFL_REQUIRE(c->intermediate % 64 == 0, DFL_E_UNSUPPORTED, "intermediate %d must be a multiple of 64",
+              c->intermediate);
+  DFL_REQUIRE(c->conv_group % 8 == 0 && c->hidden % c->conv_group == 0, DFL_E_UNSUPPORTED,
+              "conv_group %d must be a multiple of 8 dividing hidden", c->conv_group);
+  DFL_REQUIRE(c->top_k <= 32 && c->top_k <= c->vocab, DFL_E_UNSUPPORTED, "top_k %d must be <= 32 and <= vocab",
+              c->top_k);
+  DFL_REQUIRE(c->rank <= 128, DFL_E_UNSUPPORTED, "rank %d must be <= 128", c->rank);
+  DFL_REQUIRE(c->block_size * (c->heads / c->kv_heads) <= 64, DFL_E_UNSUPPORTED,
+              "block_size x heads/kv_heads = %d query rows per KV head exceeds 64",
+              c->block_size * (c->heads / c->kv_heads));
+  DFL_REQUIRE(c->rms_eps >= 0.f && c->rope_theta > 0.f, DFL_E_INVALID, "rms_eps must be >= 0, rope_theta > 0");
+  if (c->tap_layer_ids) {
+    std::set<int> seen;
+    for (int i = 0; i < c->n_taps; ++i)
+      DFL_REQUIRE(seen.insert(c->tap_layer_ids[i]).second, DFL_E_UNSUPPORTED,
+                  "tap layer id %d repeats", c->tap_layer_ids[i]);
+  }
+  return DFL_OK;
+}
+
+struct DraftLayout {
+  size_t x, n, a, d0, d1, qkv, ao, u, p, h, logits, z, cand, unary, scores, attn, topk, partial;
+  size_t total;
+};
+
+DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
+  const int H = c.hidden, ng = c.hidden / c.conv_group, T = B * G, S = G - 1, N = B * S;
+  const int qkvw = (c.heads + 2 * c.kv_heads) * c.head_dim;
+  const int F = c.intermediate;
+  DraftLayout L;
+  Carver cv(nullptr);
+  L.x = cv.off; cv.take<uint16_t>((size_t)T * H);
+  L.n = cv.off; cv.take<uint16_t>((size_t)T * H);
+  L.a = cv.off; cv.take<uint16_t>((size_t)T * H);
+  L.d0 = cv.off; cv.take<float>((size_t)T * 2 * ng);
+  L.d1 = cv.off; cv.take<float>((size_t)T * 2 * ng);
+  L.qkv = cv.off; cv.take<uint16_t>((size_t)T * qkvw);
+  L.ao = cv.off; cv.take<uint16_t>((size_t)T * c.heads * c.head_dim);
+  L.u = cv.off; cv.take<uint16_t>((size_t)T * H);
+  L.p = cv.off; cv.take<uint16_t>((size_t)T * F);
+  L.h = cv.off; cv.take<uint16_t>((size_t)N * H);
+  L.logits = cv.off; cv.take<float>((size_t)N * c.vocab);
+  L.z = cv.off; cv.take<float>((size_t)N * c.rank);
+  L.cand = cv.off; cv.take<int32_t>((size_t)N * c.top_k);
+  L.unary = cv.off; cv.take<float>((size_t)N * c.top_k);
+  L.scores = cv.off; cv.take<float>((size_t)N * c.top_k * c.top_k);
+  L.attn = cv.off; cv.take<char>(dfl::plan_attention(B, G, c.heads, c.kv_heads, c.head_dim, Lmax).ws_bytes);
+  L.topk = cv.off; cv.take<char>(dfl::plan_topk(N, c.vocab, c.top_k).ws_bytes);
+  size_t part = 0;
+  const int shapes[][3] = {{T, 4 * ng, H},    {T, qkvw, H},     {T, H, c.heads * c.head_dim},
+                           {T, 2 * F, H},     {T, H, F},        {N, c.vocab, H},
+                           {N, c.rank, H}};
+  for (auto& s : shapes) part = std::max(part, dfl::plan_gemm(s[0], s[1], s[2]).partial_bytes);
+  L.partial = cv.off; cv.take<char>(part);
+  L.total = cv.off;
+  return L;
+}
+
+struct CtxLayout {
+  size_t craw, c, kv, partial, total;
+};
+
+CtxLayout ctx_layout(const dfl_config& c, int B, int L) {
+  const size_t M = (size_t)B * L;
+  const int H = c.hidden, kvw = 2 * c.kv_heads * c.head_dim;
+  CtxLayout o;
+  Carver cv(nullptr);
+  o.craw = cv.off; cv.take<uint16_t>(M * H);
+  o.c = cv.off; cv.take<uint16_t>(M * H);
+  o.kv = cv.off; cv.take<uint16_t>(M * kvw);
+  const size_t p1 = dfl::plan_gemm((int)M, H, c.n_taps * H).partial_bytes;
+  const size_t p2 = dfl::plan_gemm((int)M, kvw, H).partial_bytes;
+  o.partial = cv.off; cv.take<char>(std::max(p1, p2));
+  o.total = cv.off;
+  return o;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dfl_last_error(void) { return g_err.c_str(); }
+
+int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t stream,
+                     dfl_drafter** out) {
+  DFL_REQUIRE(out, DFL_E_INVALID, "out is NULL");
+  *out = nullptr;
+  DFL_TRY(check_config(cfg));
+  DFL_REQUIRE(w && w->fc && w->hidden_norm && w->norm && w->sel_proj && w->pred && w->succ && w->layers,
+              DFL_E_INVALID, "a drafter weight pointer is NULL");
+  const dfl_config& c = *cfg;
+  for (int i = 0; i < c.layers; ++i) {
+    const dfl_layer_weights& L = w->layers[i];
+    DFL_REQUIRE(L.input_norm && L.post_norm && L.q_proj && L.k_proj && L.v_proj && L.o_proj && L.q_norm &&
+                    L.k_norm && L.gate_proj && L.up_proj && L.down_proj && L.attn_base && L.attn_kproj &&
+                    L.mlp_base && L.mlp_kproj,
+                DFL_E_INVALID, "layer %d has a NULL weight pointer", i);
+  }
+  const size_t H = c.hidden, D = c.head_dim, NH = c.heads, NKV = c.kv_heads, F = c.intermediate;
+  const size_t ng = H / c.conv_group, V = c.vocab, R = c.rank;
+  const size_t qkvw = (NH + 2 * NKV) * D;
+  // owned arena
+  Carver cv(nullptr);
+  auto sz_fc = cv.off; cv.take<uint16_t>(H * c.n_taps * H);
+  auto sz_hn = cv.off; cv.take<uint16_t>(H);
+  auto sz_nm = cv.off; cv.take<uint16_t>(H);
+  auto sz_sp = cv.off; cv.take<uint16_t>(R * H);
+  auto sz_pr = cv.off; cv.take<uint16_t>(V * R);
+  auto sz_sc = cv.off; cv.take<uint16_t>(V * R);
+  const size_t layer0 = cv.off;
+  size_t off_in = 0, off_post, off_qn, off_kn, off_qkv, off_o, off_gu, off_dn, off_ab, off_ak, off_mb, off_mk, off_kv;
+  {
+    Carver lc(nullptr);
+    off_in = lc.off; lc.take<uint16_t>(H);
+    off_post = lc.off; lc.take<uint16_t>(H);
+    off_qn = lc.off; lc.take<uint16_t>(D);
+    off_kn = lc.off; lc.take<uint16_t>(D);
+    off_qkv = lc.off; lc.take<uint16_t>(qkvw * H);
+    off_o = lc.off; lc.take<uint16_t>(H * NH * D);
+    off_gu = lc.off; lc.take<uint16_t>(2 * F * H);
+    off_dn = lc.off; lc.take<uint16_t>(H * F);
+    off_ab = lc.off; lc.take<uint16_t>(4 * H);
+    off_ak = lc.off; lc.take<uint16_t>(4 * ng * H);
+    off_mb = lc.off; lc.take<uint16_t>(4 * H);
+    off_mk = lc.off; lc.take<uint16_t>(4 * ng * H);
+    off_kv = lc.off; lc.take<uint16_t>(2 * NKV * D * H);
+    cv.off += lc.off * c.layers;
+  }
+  const size_t per_layer = (cv.off - layer0) / c.layers;
+  dfl_drafter* d = new (std::nothrow) dfl_drafter();
+  DFL_REQUIRE(d, DFL_E_NOMEM, "host allocation failed");
+  d->cfg = c;
+  d->cfg.tap_layer_ids = nullptr;
+  if (hipMalloc(&d->arena, cv.off) != hipSuccess) {
+    delete d;
+    return fail(DFL_E_NOMEM, "hipMalloc of %zu bytes for the drafter weights failed", cv.off);
+  }
+  char* A = static_cast<char*>(d->arena);
+  auto at = [&](size_t off) { return reinterpret_cast<uint16_t*>(A + off); };
+  d->fc = at(sz_fc);
+  d->hidden_norm = at(sz_hn);
+  d->norm = at(sz_nm);
+  d->sel_proj = at(sz_sp);
+  d->pred = at(sz_pr);
+  d->succ = at(sz_sc);
+  int rc = DFL_OK;
+  auto cp = [&](void* dst, const void* src, size_t n) {
+    if (rc == DFL_OK) {
+      hipError_t e = hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    }
+  };
+  auto cp2d = [&](void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height) {
+    if (rc == DFL_OK) {
+      hipError_t e = hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, stream);
+      if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "hipMemcpy2DAsync: %s", hipGetErrorString(e));
+    }
+  };
+  cp(d->fc, w->fc, H * c.n_taps * H * 2);
+  cp(d->hidden_norm, w->hidden_norm, H * 2);
+  cp(d->norm, w->norm, H * 2);
+  cp(d->sel_proj, w->sel_proj, R * H * 2);
+  cp(d->pred, w->pred, V * R * 2);
+  cp(d->succ, w->succ, V * R * 2);
+  d->layers.resize(c.layers);
+  for (int i = 0; i < c.layers; ++i) {
+    const dfl_layer_weights& s = w->layers[i];
+    const size_t lb = layer0 + per_layer * i;
+    LayerBuf& L = d->layers[i];
+    L.in_norm = at(lb + off_in);
+    L.post_norm = at(lb + off_post);
+    L.q_norm = at(lb + off_qn);
+    L.k_norm = at(lb + off_kn);
+    L.qkv = at(lb + off_qkv);
+    L.o = at(lb + off_o);
+    L.gateup = at(lb + off_gu);
+    L.down = at(lb + off_dn);
+    L.attn_base = at(lb + off_ab);
+    L.attn_kproj = at(lb + off_ak);
+    L.mlp_base = at(lb + off_mb);
+    L.mlp_kproj = at(lb + off_mk);
+    L.kv_ctx = at(lb + off_kv);
+    cp(L.in_norm, s.input_norm, H * 2);
+    cp(L.post_norm, s.post_norm, H * 2);
+    cp(L.q_norm, s.q_norm, D * 2);
+    cp(L.k_norm, s.k_norm, D * 2);
+    cp(L.qkv, s.q_proj, NH * D * H * 2);
+    cp(L.qkv + NH * D * H, s.k_proj, NKV * D * H * 2);
+    cp(L.qkv + (NH + NKV) * D * H, s.v_proj, NKV * D * H * 2);
+    cp(L.o, s.o_proj, H * NH * D * 2);
+    // gate/up interleaved per 16 rows: [gate 16 | up 16] ...
+    cp2d(L.gateup, 32 * H * 2, s.gate_proj, 16 * H * 2, 16 * H * 2, F / 16);
+    cp2d(L.gateup + 16 * H, 32 * H * 2, s.up_proj, 16 * H * 2, 16 * H * 2, F / 16);
+    cp(L.down, s.down_proj, H * F * 2);
+    cp(L.attn_base, s.attn_base, 4 * H * 2);
+    cp(L.attn_kproj, s.attn_kproj, 4 * ng * H * 2);
+    cp(L.mlp_base, s.mlp_base, 4 * H * 2);
+    cp(L.mlp_kproj, s.mlp_kproj, 4 * ng * H * 2);
+    cp(L.kv_ctx, s.k_proj, NKV * D * H * 2);
+    cp(L.kv_ctx + NKV * D * H, s.v_proj, NKV * D * H * 2);
+  }
+  if (rc == DFL_OK) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  }
+  if (rc != DFL_OK) {
+    (void)hipFree(d->arena);
+    delete d;
+    return rc;
+  }
+  *out = d;
+  return DFL_OK;
+}
+
+void dfl_drafter_free(dfl_drafter* d) {
+  if (!d) return;
+  for (auto& t : d->timed) {
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  for (auto e : d->pool) (void)hipEventDestroy(e);
+  if (d->arena) (void)hipFree(d->arena);
+  delete d;
+}
+
+size_t dfl_context_workspace_bytes(const dfl_drafter* d, int B, int L) {
+  if (!d || B <= 0 || L <= 0) return 0;
+  return ctx_layout(d->cfg, B, L).total;
+}
+
+int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, int row_offset,
+                            int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  DFL_REQUIRE(d && taps && K && V && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(B > 0 && L > 0 && row_offset >= 0 && Lcap > 0, DFL_E_INVALID, "B, L, Lcap must be positive");
+  DFL_REQUIRE((int64_t)row_offset + L <= Lcap, DFL_E_SHAPE, "row_offset %d + L %d exceeds Lcap %d", row_offset, L,
+              Lcap);
+  DFL_REQUIRE((int64_t)B * L <= (1 << 30), DFL_E_SHAPE, "B*L too large");
+  const dfl_config& c = d->cfg;
+  for (int i = 0; i < c.layers; ++i) DFL_REQUIRE(K[i] && V[i], DFL_E_INVALID, "K/V pointer of layer %d is NULL", i);
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const CtxLayout lay = ctx_layout(c, B, L);
+  DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
+  char* W = static_cast<char*>(ws);
+  uint16_t* craw = reinterpret_cast<uint16_t*>(W + lay.craw);
+  uint16_t* cc = reinterpret_cast<uint16_t*>(W + lay.c);
+  uint16_t* kv = reinterpret_cast<uint16_t*>(W + lay.kv);
+  float* part = reinterpret_cast<float*>(W + lay.partial);
+  const int M = B * L, H = c.hidden, kvw = 2 * c.kv_heads * c.head_dim;
+  const dfl::GemmPlan pfc = dfl::plan_gemm(M, H, c.n_taps * H);
+  DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, H, c.n_taps * H, dfl::EPI_BF16), stream, [&] {
+    return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
+                            0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * M * H, stream, [&] {
+    return dfl::launch_rms_norm(craw, H, M, H, d->hidden_norm, c.rms_eps, cc, H, 1, 1, 0, stream);
+  }));
+  const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
+  for (int i = 0; i < c.layers; ++i) {
+    const LayerBuf& Lb = d->layers[i];
+    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16), stream, [&] {
+      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
+                              stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
+      return dfl::launch_context_kv_store(kv, B, L, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,
+                                          row_offset, Lcap, K[i], V[i], stream);
+    }));
+  }
+  return DFL_OK;
+}
+
+size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax) {
+  if (!d || B <= 0 || G < 2 || Lmax < 0) return 0;
+  return draft_layout(d->cfg, B, G, Lmax).total;
+}
+
+int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
+                    const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,
+                    const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
+                    int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  DFL_REQUIRE(d && embeds && anchors && ctx_len && pos0 && lm_head && tokens && ws, DFL_E_INVALID,
+              "NULL argument");
+  const dfl_config& c = d->cfg;
+  DFL_REQUIRE(B > 0, DFL_E_INVALID, "B must be positive");
+  DFL_REQUIRE(G >= 2 && G <= c.block_size, DFL_E_UNSUPPORTED, "G=%d outside [2, block_size=%d]", G, c.block_size);
+  DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax %d must be in [0, Lcap=%d]", Lmax, Lcap);
+  DFL_REQUIRE((int64_t)B * G * std::max(c.vocab, c.intermediate * 2) < (1ll << 31), DFL_E_SHAPE, "B*G too large");
+  if (Lmax > 0) {
+    DFL_REQUIRE(K && V, DFL_E_INVALID, "K/V arrays are NULL");
+    for (int i = 0; i < c.layers; ++i) DFL_REQUIRE(K[i] && V[i], DFL_E_INVALID, "K/V of layer %d is NULL", i);
+  }
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const DraftLayout lay = draft_layout(c, B, G, Lmax);
+  DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
+
+  const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
+  const int ng = H / c.conv_group, T = B * G, S = G - 1, N = B * S;
+  const int qkvw = (NH + 2 * NKV) * D, V_ = c.vocab, R = c.rank, Kc = c.top_k;
+  char* W = static_cast<char*>(ws);
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
+  uint16_t *x = u16(lay.x), *n = u16(lay.n), *a = u16(lay.a), *qkv = u16(lay.qkv), *ao = u16(lay.ao);
+  uint16_t *u = u16(lay.u), *p = u16(lay.p), *h = u16(lay.h);
+  float *d0 = f32(lay.d0), *d1 = f32(lay.d1), *z = f32(lay.z), *unary = f32(lay.unary), *scores = f32(lay.scores);
+  float* logits = logits_out ? logits_out : f32(lay.logits);
+  int32_t* cand = reinterpret_cast<int32_t*>(W + lay.cand);
+  float* part = f32(lay.partial);
+  const dfl::AttnPlan apl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
+  const dfl::TopkPlan tpl = dfl::plan_topk(N, V_, Kc);
+  const dfl::GemmPlan p_kp = dfl::plan_gemm(T, 4 * ng, H), p_qkv = dfl::plan_gemm(T, qkvw, H),
+                      p_o = dfl::plan_gemm(T, H, NH * D), p_gu = dfl::plan_gemm(T, 2 * F, H),
+                      p_dn = dfl::plan_gemm(T, H, F), p_head = dfl::plan_gemm(N, V_, H),
+                      p_sel = dfl::plan_gemm(N, R, H);
+  const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
+  const double norm_bytes = 4.0 * T * H;
+
+  const uint16_t* xin = embeds;
+  for (int li = 0; li < c.layers; ++li) {
+    const LayerBuf& L = d->layers[li];
+    const uint16_t* Kl = Lmax > 0 ? K[li] : nullptr;
+    const uint16_t* Vl = Lmax > 0 ? V[li] : nullptr;
+    // attention half
+    DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
+      return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
+      return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
+                              2 * ng, part, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
+      return dfl::launch_conv(n, d0, 2 * ng, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_BF16), stream, [&] {
+      return dfl::launch_gemm(p_qkv, a, H, L.qkv, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
+                              stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
+      hipError_t e = dfl::launch_head_norm_rope(qkv, qkvw, T, NH, D, L.q_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
+                                                stream);
+      if (e != hipSuccess) return e;
+      return dfl::launch_head_norm_rope(qkv + NH * D, qkvw, T, NKV, D, L.k_norm, c.rms_eps, c.rope_theta, pos0, G,
+                                        0, stream);
+    }));
+    const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
+    DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
+      return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
+                                   B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
+      return dfl::launch_gemm(p_o, ao, NH * D, L.o, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
+      return dfl::launch_conv(u, d1, 2 * ng, L.attn_base, 1, T, H, G, c.conv_group, xin, x, stream);
+    }));
+    // MLP half
+    DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
+      return dfl::launch_rms_norm(x, H, T, H, L.post_norm, c.rms_eps, n, H, 1, 1, 0, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
+      return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
+                              part, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
+      return dfl::launch_conv(n, d0, 2 * ng, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
+      return dfl::launch_gemm(p_gu, a, H, L.gateup, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
+                              stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
+      return dfl::launch_gemm(p_dn, p, F, L.down, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
+      return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
+    }));
+    xin = x;
+  }
+  // rows 1..G-1 of every block -> final norm -> head, selector
+  DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * N * H, stream, [&] {
+    return dfl::launch_rms_norm(xin, H, N, H, d->norm, c.rms_eps, h, H, S, G, 1, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, V_, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm(p_head, h, H, lm_head, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm(p_sel, h, H, d->sel_proj, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_TOPK, 4.0 * N * V_, stream, [&] {
+    return dfl::launch_topk(tpl, logits, N, V_, Kc, cand, unary, W + lay.topk, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (R + Kc + 2), stream, [&] {
+    return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, V_, scores, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_SELECT_PATH, 4.0 * N * Kc, stream, [&] {
+    return dfl::launch_select_path(scores, cand, B, S, Kc, tokens, stream);
+  }));
+  return DFL_OK;
+}
+
+// ---------------------------------------------------------------- single steps
+
+int dfl_rms_norm(const dfl_bf16* x, int rows, int H, int ldx, const dfl_bf16* gamma, float eps, dfl_bf16* y,
+                 int ldy, hipStream_t stream) {
+  DFL_REQUIRE(x && gamma && y, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(rows >= 0 && H > 0 && ldx >= H && ldy >= H, DFL_E_INVALID, "bad sizes");
+  DFL_REQUIRE(H % 8 == 0 && H <= 8192 && ldx % 8 == 0 && ldy % 8 == 0, DFL_E_UNSUPPORTED,
+              "H and leading dimensions must be multiples of 8, H <= 8192");
+  DFL_REQUIRE(eps >= 0.f, DFL_E_INVALID, "eps < 0");
+  hipError_t e = dfl::launch_rms_norm(x, ldx, rows, H, gamma, eps, y, ldy, 1, 1, 0, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+size_t dfl_linear_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 64) return 0;
+  return dfl::plan_gemm(M, N, K).partial_bytes;
+}
+
+int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int N, void* y, int ldy, int out_f32,
+               void* ws, size_t ws_bytes, hipStream_t stream) {
+  DFL_REQUIRE(x && W && y, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(M > 0 && N > 0 && K > 0 && ldx >= K && ldy >= N, DFL_E_INVALID, "bad sizes");
+  DFL_REQUIRE(K % 64 == 0 && ldx % 8 == 0, DFL_E_UNSUPPORTED, "K must be a multiple of 64 and ldx of 8");
+  const dfl::GemmPlan pl = dfl::plan_gemm(M, N, K);
+  DFL_REQUIRE(ws_bytes >= pl.partial_bytes && (pl.partial_bytes == 0 || ws), DFL_E_WORKSPACE,
+              "workspace %zu < %zu bytes", ws_bytes, pl.partial_bytes);
+  DFL_REQUIRE(pl.partial_bytes == 0 || aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  hipError_t e = dfl::launch_gemm(pl, x, ldx, W, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy, nullptr,
+                                  0, 0, static_cast<float*>(ws), stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const dfl_bf16* gamma, float eps,
+                       float theta, const int32_t* pos0, int rows_per_req, hipStream_t stream) {
+  DFL_REQUIRE(x && gamma && pos0, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(rows >= 0 && heads > 0 && rows_per_req > 0 && ldx >= heads * D, DFL_E_INVALID, "bad sizes");
+  DFL_REQUIRE(D == 64 || D == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128", D);
+  DFL_REQUIRE(eps >= 0.f && theta > 0.f, DFL_E_INVALID, "eps < 0 or theta <= 0");
+  hipError_t e = dfl::launch_head_norm_rope(x, ldx, rows, heads, D, gamma, eps, theta, pos0, rows_per_req, 0, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+size_t dfl_attention_workspace_bytes(int B, int G, int NH, int NKV, int D, int Lmax) {
+  if (B <= 0 || G <= 0 || NH <= 0 || NKV <= 0 || NH % NKV || Lmax < 0) return 0;
+  return dfl::plan_attention(B, G, NH, NKV, D, Lmax).ws_bytes;
+}
+
+int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const dfl_bf16* vb, int ldkv,
+                        const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax, const int32_t* ctx_len, int B,
+                        int G, int NH, int NKV, int D, dfl_bf16* out, int ldo, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  DFL_REQUIRE(q && kb && vb && ctx_len && out && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(B > 0 && G > 0 && NH > 0 && NKV > 0 && NH % NKV == 0, DFL_E_INVALID, "bad head counts");
+  DFL_REQUIRE(D == 64 || D == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128", D);
+  DFL_REQUIRE(G * (NH / NKV) <= 64, DFL_E_UNSUPPORTED, "more than 64 query rows per KV head");
+  DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax outside [0, Lcap]");
+  DFL_REQUIRE(Lmax == 0 || (K && V), DFL_E_INVALID, "K/V NULL with Lmax > 0");
+  DFL_REQUIRE(ldq >= NH * D && ldkv >= NKV * D && ldo >= NH * D && ldq % 8 == 0 && ldkv % 8 == 0, DFL_E_SHAPE,
+              "leading dimensions too small or not multiples of 8");
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const dfl::AttnPlan pl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
+  DFL_REQUIRE(ws_bytes >= pl.ws_bytes, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.ws_bytes);
+  hipError_t e = dfl::launch_attention(pl, q, ldq, kb, vb, ldkv, K, V, Lcap, ctx_len, B, G, NH, NKV, D, Lmax, out,
+                                       ldo, ws, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+size_t dfl_conv_prepare_workspace_bytes(int T, int H, int grp) {
+  if (T <= 0 || H <= 0 || grp <= 0 || H % grp || H % 64) return 0;
+  const int ng = H / grp;
+  return align_up((size_t)T * 2 * ng * sizeof(float)) + dfl::plan_gemm(T, 4 * ng, H).partial_bytes;
+}
+
+static int check_conv(int T, int H, int G, int grp) {
+  DFL_REQUIRE(T > 0 && H > 0 && G > 0 && grp > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(T % G == 0, DFL_E_SHAPE, "T=%d is not a whole number of %d-row blocks", T, G);
+  DFL_REQUIRE(grp % 8 == 0 && H % grp == 0, DFL_E_UNSUPPORTED, "group %d must be a multiple of 8 dividing H", grp);
+  return DFL_OK;
+}
+
+int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_bf16* kproj, const dfl_bf16* base,
+                     dfl_bf16* out, float* coef1, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DFL_REQUIRE(x && kproj && base && out && coef1 && ws, DFL_E_INVALID, "NULL argument");
+  DFL_TRY(check_conv(T, H, G, grp));
+  DFL_REQUIRE(H % 64 == 0, DFL_E_UNSUPPORTED, "H must be a multiple of 64");
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const size_t need = dfl_conv_prepare_workspace_bytes(T, H, grp);
+  DFL_REQUIRE(ws_bytes >= need, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const int ng = H / grp;
+  float* d0 = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)T * 2 * ng * sizeof(float)));
+  const dfl::GemmPlan pl = dfl::plan_gemm(T, 4 * ng, H);
+  hipError_t e = dfl::launch_gemm(pl, x, H, kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, coef1, 2 * ng, 2 * ng,
+                                  part, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  e = dfl::launch_conv(x, d0, 2 * ng, base, 0, T, H, G, grp, nullptr, out, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base, int T, int H, int G, int grp,
+                    const dfl_bf16* residual, dfl_bf16* out, hipStream_t stream) {
+  DFL_REQUIRE(y && coef1 && base && out, DFL_E_INVALID, "NULL argument");
+  DFL_TRY(check_conv(T, H, G, grp));
+  DFL_REQUIRE(y != out, DFL_E_INVALID, "y must not alias out");
+  hipError_t e = dfl::launch_conv(y, coef1, 2 * (H / grp), base, 1, T, H, G, grp, residual, out, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+size_t dfl_candidates_workspace_bytes(int N, int V, int K) {
+  if (N <= 0 || V <= 0 || K <= 0) return 0;
+  return dfl::plan_topk(N, V, K).ws_bytes;
+}
+
+int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* ids, float* unary, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  DFL_REQUIRE(logits && ids && unary && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(N > 0 && V > 0 && K > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= 32 && K <= V, DFL_E_UNSUPPORTED, "K=%d must be <= 32 and <= V", K);
+  const dfl::TopkPlan pl = dfl::plan_topk(N, V, K);
+  DFL_REQUIRE(ws_bytes >= pl.ws_bytes, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.ws_bytes);
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  hipError_t e = dfl::launch_topk(pl, logits, N, V, K, ids, unary, ws, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+size_t dfl_selector_project_workspace_bytes(int N, int H, int R) {
+  if (N <= 0 || H <= 0 || R <= 0 || H % 64) return 0;
+  return dfl::plan_gemm(N, R, H).partial_bytes;
+}
+
+int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  return dfl_linear(h, N, H, H, proj, R, z, R, 1, ws, ws_bytes, stream);
+}
+
+int dfl_score_edges(const int32_t* cand, const float* unary, const float* z, const int32_t* anchors, int B, int S,
+                    int K, int R, const dfl_bf16* pred, const dfl_bf16* succ, int V, float* scores,
+                    hipStream_t stream) {
+  DFL_REQUIRE(cand && unary && z && anchors && pred && succ && scores, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(B > 0 && S > 0 && K > 0 && R > 0 && V > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= 32 && R <= 128, DFL_E_UNSUPPORTED, "K <= 32 and R <= 128 required");
+  hipError_t e = dfl::launch_score_edges(cand, unary, z, anchors, B, S, K, R, pred, succ, V, scores, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_select_path(const float* scores, const int32_t* cand, int B, int S, int K, int32_t* tokens,
+                    hipStream_t stream) {
+  DFL_REQUIRE(scores && cand && tokens, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(B > 0 && S > 0 && K > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= 64, DFL_E_UNSUPPORTED, "K must be <= 64");
+  hipError_t e = dfl::launch_select_path(scores, cand, B, S, K, tokens, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+// ---------------------------------------------------------------- timing
+
+int dfl_set_timed_kernel(dfl_drafter* d, int k) {
+  DFL_REQUIRE(d, DFL_E_INVALID, "NULL drafter");
+  DFL_REQUIRE(k >= DFL_K_NONE && k < DFL_K_COUNT, DFL_E_INVALID, "unknown kernel class %d", k);
+  d->timed_class = k;
+  return DFL_OK;
+}
+
+int dfl_read_kernel_time(dfl_drafter* d, double* total_ms, int64_t* launches, double* bytes) {
+  DFL_REQUIRE(d && total_ms && launches, DFL_E_INVALID, "NULL argument");
+  double ms = 0.0, by = 0.0;
+  int rc = DFL_OK;
+  for (auto& t : d->timed) {
+    if (rc == DFL_OK) {
+      float e = 0.f;
+      hipError_t s = hipEventSynchronize(t.stop);
+      if (s == hipSuccess) s = hipEventElapsedTime(&e, t.start, t.stop);
+      if (s != hipSuccess) rc = fail(DFL_E_DEVICE, "event timing: %s", hipGetErrorString(s));
+      ms += e;
+      by += t.bytes;
+    }
+    d->pool.push_back(t.start);
+    d->pool.push_back(t.stop);
+  }
+  *total_ms = ms;
+  *launches = static_cast<int64_t>(d->timed.size());
+  if (bytes) *bytes = by;
+  d->timed.clear();
+  return rc;
+}
+
+}  // extern "C"

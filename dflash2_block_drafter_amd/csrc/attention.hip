@@ -1,0 +1,293 @@
+// Bidirectional block attention over a context K/V prefix (dflash2.ts diff: header, "no
+// sliding window", and `#block`, which hands the block's own k/v to `context.attend` with
+// scale 1/sqrt(D)).  Every query row of a request attends to all ctx_len[b] context rows
+// and all G block rows; query head h reads KV head h / (NH/NKV).
+//
+// Work split: one workgroup per (request b, KV head g, key chunk).  The Q tile is the
+// G x NH/NKV query rows that share KV head g (<= 64 rows, 16 per wavefront), so every
+// K/V row read from HBM serves all of them.  Chunks 0..nchunks-2 cover context rows,
+// the last chunk the block's own G keys; each writes (max, sum, unnormalised O) in fp32
+// and a combine kernel merges the chunks with their log-sum-exp weights.
+//
+// Per 64-key tile a wavefront computes S^T = K . Q^T (keys on rows, its 16 queries on
+// columns) with v_mfma_f32_16x16x32_bf16, so each lane holds one query's scores and the
+// softmax row statistics need only two cross-lane steps; then O^T += V^T . P^T, where
+// P^T comes straight from the S^T accumulators and V is staged transposed in LDS with
+// the same key order per lane.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dfl {
+
+namespace {
+
+constexpr int KT = 64;  // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kb;
+  const uint16_t* vb;
+  const uint16_t* K;
+  const uint16_t* V;
+  const int32_t* ctx_len;
+  float* part_o;   // [B, NKV, nchunks, QR, D]
+  float* part_ml;  // [B, NKV, nchunks, QR, 2]
+  int ldq, ldkv, Lcap, Lmax, G, NH, NKV, chunk, nchunks, qrows;
+  float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
+  constexpr int KS = D + 8;   // K tile row stride (bf16)
+  constexpr int VS = KT + 8;  // V^T tile row stride (bf16)
+  constexpr int DT = D / 16;  // output d tiles
+  constexpr int DK = D / 32;  // MFMA k steps over D
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+
+  const int chunk = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hpg = a.NH / a.NKV;
+  const int lg = lane >> 4;  // lane group
+
+  // key range of this chunk
+  const bool block_chunk = chunk == a.nchunks - 1;
+  const int ctx = min(max(a.ctx_len[b], 0), a.Lmax);  // never past the rows the plan covers
+  int kbeg, kend;
+  const uint16_t *ksrc, *vsrc;
+  size_t kstride;
+  if (block_chunk) {
+    kbeg = 0;
+    kend = a.G;
+    ksrc = a.kb + (size_t)b * a.G * a.ldkv + g * D;
+    vsrc = a.vb + (size_t)b * a.G * a.ldkv + g * D;
+    kstride = a.ldkv;
+  } else {
+    kbeg = chunk * a.chunk;
+    kend = min(ctx, kbeg + a.chunk);
+    ksrc = a.K + ((size_t)b * a.Lcap * a.NKV + g) * D;
+    vsrc = a.V + ((size_t)b * a.Lcap * a.NKV + g) * D;
+    kstride = (size_t)a.NKV * D;
+  }
+
+  // this wavefront's 16 queries as MFMA B operands (column = query, k = d)
+  const int qi = wave * 16 + (lane & 15);
+  const bool qvalid = qi < a.qrows;
+  bf16x8_t qf[DK];
+  {
+    const int t = qi / hpg;
+    const int h = g * hpg + qi % hpg;
+    const uint16_t* qrow = a.q + ((size_t)b * a.G + t) * a.ldq + h * D;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4_t*>(qrow + ks * 32 + lg * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  float m = -INFINITY, l = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int CPR = D / 8;             // 16-byte chunks per key row
+  constexpr int PER = KT * CPR / 256;    // chunks per thread per tile
+  for (int j0 = kbeg; j0 < kend; j0 += KT) {
+    const int nvalid = min(KT, kend - j0);
+    // stage K rows and V^T into LDS
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / CPR;
+      const int dc = (c % CPR) * 8;
+      u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (r < nvalid) {
+        kv = *reinterpret_cast<const u32x4_t*>(ksrc + (size_t)(j0 + r) * kstride + dc);
+        vv = *reinterpret_cast<const u32x4_t*>(vsrc + (size_t)(j0 + r) * kstride + dc);
+      }
+      *reinterpret_cast<u32x4_t*>(&Ks[r * KS + dc]) = kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(dc + 2 * e) * VS + r] = static_cast<uint16_t>(vv[e] & 0xFFFFu);
+        Vt[(dc + 2 * e + 1) * VS + r] = static_cast<uint16_t>(vv[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T tiles: s[kt] holds keys kt*16 + 4*lg + e for query (lane & 15)
+    f32x4_t s[KT / 16];
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt) {
+      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8_t kf =
+            *reinterpret_cast<const bf16x8_t*>(&Ks[(kt * 16 + (lane & 15)) * KS + ks * 32 + lg * 8]);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kt], 0, 0, 0);
+      }
+    }
+    // online softmax in the log2 domain
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kt * 16 + lg * 4 + e;
+        const float v = key < nvalid ? s[kt][e] * a.scale_log2 : -INFINITY;
+        s[kt][e] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = exp2f(m - mnew);  // m = -inf on the first tile: alpha = 0
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = exp2f(s[kt][e] - mnew);
+        s[kt][e] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l = l * alpha + psum;
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[i] *= alpha;
+
+    // O^T += V^T . P^T over two 32-key steps.  Lane slots 0..3 are keys 32*ks + 4*lg + e,
+    // slots 4..7 keys 32*ks + 16 + 4*lg + e: the same order for both operands.
+#pragma unroll
+    for (int ks = 0; ks < KT / 32; ++ks) {
+      u32x4_t pw;
+      pw[0] = pack_bf16x2(s[2 * ks][0], s[2 * ks][1]);
+      pw[1] = pack_bf16x2(s[2 * ks][2], s[2 * ks][3]);
+      pw[2] = pack_bf16x2(s[2 * ks + 1][0], s[2 * ks + 1][1]);
+      pw[3] = pack_bf16x2(s[2 * ks + 1][2], s[2 * ks + 1][3]);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vrow = &Vt[(dt * 16 + (lane & 15)) * VS + ks * 32 + lg * 4];
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+        const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
+                                                        o[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!qvalid) return;
+  const size_t slot = (((size_t)b * a.NKV + g) * a.nchunks + chunk) * a.qrows + qi;
+  if (lg == 0) {
+    a.part_ml[slot * 2 + 0] = m;
+    a.part_ml[slot * 2 + 1] = l;
+  }
+  float* po = a.part_o + slot * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4_t*>(po + dt * 16 + lg * 4) = o[dt];
+}
+
+// Merge the chunks of one query row: weights 2^(m_c - max m) and the summed denominators.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t* out, int ldo) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // over NKV * qrows of request b
+  const int b = blockIdx.y;
+  if (row >= a.NKV * a.qrows) return;
+  const int qi = row % a.qrows;
+  const int g = row / a.qrows;
+  const size_t base = ((size_t)b * a.NKV + g) * a.nchunks;
+  float mx = -INFINITY;
+  for (int c = 0; c < a.nchunks; ++c) mx = fmaxf(mx, a.part_ml[((base + c) * a.qrows + qi) * 2]);
+  constexpr int PL = D / 64;  // values per lane
+  float acc[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) acc[i] = 0.f;
+  float den = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const size_t slot = (base + c) * a.qrows + qi;
+    const float mc = a.part_ml[slot * 2];
+    if (mc == -INFINITY) continue;
+    const float w = exp2f(mc - mx);
+    den += w * a.part_ml[slot * 2 + 1];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) acc[i] += w * a.part_o[slot * D + lane + 64 * i];
+  }
+  const float inv = 1.f / den;
+  const int hpg = a.NH / a.NKV;
+  const int t = qi / hpg;
+  const int h = g * hpg + qi % hpg;
+  uint16_t* orow = out + ((size_t)b * a.G + t) * ldo + h * D;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) orow[lane + 64 * i] = f32_to_bf16(acc[i] * inv);
+}
+
+}  // namespace
+
+AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax) {
+  AttnPlan pl;
+  pl.qrows = G * (NH / NKV);
+  const int pairs = B * NKV;
+  const int want = (2048 + pairs - 1) / pairs;  // chunks per (b, g) to fill the chip
+  int chunk = (Lmax + want - 1) / want;
+  chunk = ((chunk + KT - 1) / KT) * KT;
+  if (chunk < 256) chunk = 256;
+  pl.chunk = chunk;
+  const int ctx_chunks = Lmax > 0 ? (Lmax + chunk - 1) / chunk : 0;
+  pl.nchunks = ctx_chunks + 1;
+  const size_t slots = (size_t)B * NKV * pl.nchunks * pl.qrows;
+  pl.ws_bytes = slots * D * sizeof(float) + slots * 2 * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, const uint16_t* kb,
+                            const uint16_t* vb, int ldkv, const uint16_t* K, const uint16_t* V,
+                            int Lcap, const int32_t* ctx_len, int B, int G, int NH, int NKV,
+                            int D, int Lmax, uint16_t* out, int ldo, void* ws,
+                            hipStream_t stream) {
+  AttnArgs a;
+  a.q = q;
+  a.kb = kb;
+  a.vb = vb;
+  a.K = K;
+  a.V = V;
+  a.ctx_len = ctx_len;
+  const size_t slots = (size_t)B * NKV * pl.nchunks * pl.qrows;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = a.part_o + slots * D;
+  a.ldq = ldq;
+  a.ldkv = ldkv;
+  a.Lcap = Lcap;
+  a.Lmax = Lmax;
+  a.G = G;
+  a.NH = NH;
+  a.NKV = NKV;
+  a.chunk = pl.chunk;
+  a.nchunks = pl.nchunks;
+  a.qrows = pl.qrows;
+  a.scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+  dim3 grid(pl.nchunks, NKV, B);
+  const int rows = NKV * pl.qrows;  // per request
+  dim3 cgrid((rows + 3) / 4, B);
+  if (D == 128) {
+    attn_chunk_kernel<128><<<grid, 256, 0, stream>>>(a);
+    attn_combine_kernel<128><<<cgrid, 256, 0, stream>>>(a, out, ldo);
+  } else {
+    attn_chunk_kernel<64><<<grid, 256, 0, stream>>>(a);
+    attn_combine_kernel<64><<<cgrid, 256, 0, stream>>>(a, out, ldo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dfl

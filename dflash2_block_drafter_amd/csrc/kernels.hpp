@@ -1,0 +1,81 @@
+// Host-side launchers of the gfx950 kernels.  Each enqueues on `stream`, assumes its
+// arguments were validated by the C ABI layer, and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfl {
+
+enum Epilogue { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU_MUL = 2 };
+
+struct GemmPlan {
+  int bm = 0, bn = 0;
+  int splits = 1;
+  int k_per_split = 0;
+  size_t partial_bytes = 0;  // split-K scratch (fp32 [splits, M, N])
+};
+
+GemmPlan plan_gemm(int M, int N, int K);
+// y = A . W^T.  A [M, K] (lda), W [N, K].  EPI_BF16: out0 bf16 (ld0).  EPI_F32: columns
+// < nsplit to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL:
+// W rows interleaved per 16 as [gate|up]; out0 bf16 [M, N/2] = silu(gate) * up.
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, int M,
+                       int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
+                       float* partial, hipStream_t stream);
+
+// RMSNorm of `rows` rows.  Input row r is row in_row(r) = (r / out_per_grp) * in_per_grp +
+// skip + r % out_per_grp, so the final norm can drop the anchor row of every block.
+hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const uint16_t* gamma,
+                           float eps, uint16_t* y, int ldy, int out_per_grp, int in_per_grp,
+                           int skip, hipStream_t stream);
+
+// Per-head RMSNorm + neox RoPE in place on `heads` heads of each row.
+hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int D,
+                                 const uint16_t* gamma, float eps, float theta,
+                                 const int32_t* pos0, int rows_per_req, int pos_offset,
+                                 hipStream_t stream);
+
+// Context K/V store: kv [B*L, 2*NKV*D] (k then v) -> K/V caches [B, Lcap, NKV, D] at rows
+// row_offset + j with k_norm and RoPE at position row_offset + j.
+hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, int D,
+                                   const uint16_t* k_norm, float eps, float theta,
+                                   int row_offset, int Lcap, uint16_t* K, uint16_t* V,
+                                   hipStream_t stream);
+
+// Grouped dynamic conv.  coef: fp32 deltas [T, 2 (tap), ng] at row stride ldc.
+// side selects base[side]; residual may be null.
+hipError_t launch_conv(const uint16_t* y, const float* coef, int ldc, const uint16_t* base,
+                       int side, int T, int H, int G, int grp, const uint16_t* residual,
+                       uint16_t* out, hipStream_t stream);
+
+struct AttnPlan {
+  int chunk = 0;     // context rows per chunk (multiple of 64)
+  int nchunks = 0;   // context chunks + 1 block chunk
+  int qrows = 0;     // G * NH / NKV
+  size_t ws_bytes = 0;
+};
+AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax);
+hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, const uint16_t* kb,
+                            const uint16_t* vb, int ldkv, const uint16_t* K, const uint16_t* V,
+                            int Lcap, const int32_t* ctx_len, int B, int G, int NH, int NKV,
+                            int D, int Lmax, uint16_t* out, int ldo, void* ws,
+                            hipStream_t stream);
+
+struct TopkPlan {
+  int chunk = 0;    // elements per stage-1 wave
+  int nchunks = 0;  // chunks per row
+  size_t ws_bytes = 0;
+};
+TopkPlan plan_topk(int N, int V, int K);
+hipError_t launch_topk(const TopkPlan& pl, const float* logits, int N, int V, int K,
+                       int32_t* ids, float* vals, void* ws, hipStream_t stream);
+
+hipError_t launch_score_edges(const int32_t* cand, const float* unary, const float* z,
+                              const int32_t* anchors, int B, int S, int K, int R,
+                              const uint16_t* pred, const uint16_t* succ, int V, float* scores,
+                              hipStream_t stream);
+hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
+                              int32_t* tokens, hipStream_t stream);
+
+}  // namespace dfl

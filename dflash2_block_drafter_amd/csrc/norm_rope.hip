@@ -1,0 +1,163 @@
+// RMSNorm (one wavefront per row), per-head RMSNorm + neox RoPE, and the context K/V
+// store.  All are HBM/latency-bound; loads are 16-byte vectors where rows allow.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dfl {
+
+namespace {
+
+constexpr int kMaxChunks = 16;  // 16-byte chunks per lane: H <= 64 * 16 * 8 = 8192
+
+// RMSNorm with a direct gain (dflash2.ts diff, `#rms`): y = x * rsqrt(mean(x^2) + eps) * g,
+// reduced in fp32, rounded once to bf16.
+__global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restrict__ x, int ldx,
+                                                       int rows, int H,
+                                                       const uint16_t* __restrict__ gamma,
+                                                       float eps, uint16_t* __restrict__ y,
+                                                       int ldy, int out_per_grp, int in_per_grp,
+                                                       int skip) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int rin = (r / out_per_grp) * in_per_grp + skip + r % out_per_grp;
+  const uint16_t* xr = x + (size_t)rin * ldx;
+  const int chunks = H >> 3;
+  u32x4_t v[kMaxChunks];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * 64;
+    if (c < chunks) {
+      v[i] = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
+      float f[8];
+      unpack8(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / static_cast<float>(H) + eps);
+  uint16_t* yr = y + (size_t)r * ldy;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * 64;
+    if (c < chunks) {
+      float f[8], g[8];
+      unpack8(v[i], f);
+      unpack8(*reinterpret_cast<const u32x4_t*>(gamma + c * 8), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] * inv * g[e];
+      *reinterpret_cast<u32x4_t*>(yr + c * 8) = pack8(f);
+    }
+  }
+}
+
+// cos/sin of position `pos` for rotary pair i of a D-wide head, angle in fp64:
+// inv_freq_i = theta^(-2i/D) (neox RoPE, mirror-sd listing's RoPE docstring).
+__device__ __forceinline__ void rope_cs(int pos, int i, int D, double log_theta, float* c,
+                                        float* s) {
+  const double inv_freq = exp(-(2.0 * i / D) * log_theta);
+  const double ang = static_cast<double>(pos) * inv_freq;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+// In-place per-head RMSNorm then RoPE of one D-wide head held by one wavefront:
+// lane i < D/2 holds the neox pair (x[i], x[i + D/2]).
+__device__ __forceinline__ void norm_rope_head(const uint16_t* src, uint16_t* dst, int D,
+                                               const uint16_t* gamma, float eps, float c,
+                                               float s, int lane) {
+  const int half = D >> 1;
+  float a = 0.f, b = 0.f;
+  if (lane < half) {
+    a = bf16_to_f32(src[lane]);
+    b = bf16_to_f32(src[lane + half]);
+  }
+  const float ss = wave_sum(a * a + b * b);
+  const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
+  if (lane < half) {
+    a = a * inv * bf16_to_f32(gamma[lane]);
+    b = b * inv * bf16_to_f32(gamma[lane + half]);
+    // rotate_half(x) = cat(-x2, x1): out1 = x1 c - x2 s, out2 = x2 c + x1 s
+    dst[lane] = f32_to_bf16(a * c - b * s);
+    dst[lane + half] = f32_to_bf16(b * c + a * s);
+  }
+}
+
+__global__ __launch_bounds__(256) void head_norm_rope_kernel(uint16_t* x, int ldx, int rows,
+                                                             int heads, int D,
+                                                             const uint16_t* __restrict__ gamma,
+                                                             float eps, double log_theta,
+                                                             const int32_t* __restrict__ pos0,
+                                                             int rows_per_req, int pos_offset) {
+  const int r = blockIdx.x;
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int pos = pos0[r / rows_per_req] + r % rows_per_req + pos_offset;
+  float c = 1.f, s = 0.f;
+  if (lane < (D >> 1)) rope_cs(pos, lane, D, log_theta, &c, &s);
+  uint16_t* row = x + (size_t)r * ldx;
+  for (int h = wave; h < heads; h += 4) norm_rope_head(row + h * D, row + h * D, D, gamma, eps, c, s, lane);
+}
+
+// Context K/V (dflash2.ts diff, `#contextKV`): kv row (b, j) holds [k | v] for all KV heads;
+// K[b, row_offset + j] = RoPE(k_norm(k)) at position row_offset + j, V = v.
+__global__ __launch_bounds__(256) void context_kv_store_kernel(
+    const uint16_t* __restrict__ kv, int L, int NKV, int D, const uint16_t* __restrict__ k_norm,
+    float eps, double log_theta, int row_offset, int Lcap, uint16_t* __restrict__ K,
+    uint16_t* __restrict__ V) {
+  const int j = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int pos = row_offset + j;
+  const uint16_t* src = kv + ((size_t)b * L + j) * (2 * NKV * D);
+  const size_t dst_row = ((size_t)b * Lcap + pos) * NKV * D;
+  float c = 1.f, s = 0.f;
+  if (lane < (D >> 1)) rope_cs(pos, lane, D, log_theta, &c, &s);
+  for (int h = wave; h < NKV; h += 4)
+    norm_rope_head(src + h * D, K + dst_row + h * D, D, k_norm, eps, c, s, lane);
+  const int vchunks = NKV * D / 8;
+  for (int i = threadIdx.x; i < vchunks; i += 256)
+    *reinterpret_cast<u32x4_t*>(V + dst_row + i * 8) =
+        *reinterpret_cast<const u32x4_t*>(src + NKV * D + i * 8);
+}
+
+}  // namespace
+
+hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const uint16_t* gamma,
+                           float eps, uint16_t* y, int ldy, int out_per_grp, int in_per_grp,
+                           int skip, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  rms_norm_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, ldx, rows, H, gamma, eps, y, ldy,
+                                                      out_per_grp, in_per_grp, skip);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int D,
+                                 const uint16_t* gamma, float eps, float theta,
+                                 const int32_t* pos0, int rows_per_req, int pos_offset,
+                                 hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  head_norm_rope_kernel<<<rows, 256, 0, stream>>>(x, ldx, rows, heads, D, gamma, eps,
+                                                  log(static_cast<double>(theta)), pos0,
+                                                  rows_per_req, pos_offset);
+  return hipGetLastError();
+}
+
+hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, int D,
+                                   const uint16_t* k_norm, float eps, float theta,
+                                   int row_offset, int Lcap, uint16_t* K, uint16_t* V,
+                                   hipStream_t stream) {
+  if (B <= 0 || L <= 0) return hipSuccess;
+  context_kv_store_kernel<<<dim3(L, B), 256, 0, stream>>>(kv, L, NKV, D, k_norm, eps,
+                                                          log(static_cast<double>(theta)),
+                                                          row_offset, Lcap, K, V);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

@@ -1,0 +1,57 @@
+"""Convenience wrapper over the C ABI: allocates the caller-owned buffers (workspaces,
+context K/V caches, outputs) with PyTorch and forwards to the binding."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B_
+
+
+class Drafter:
+    def __init__(self, dims, weights: dict, tap_layer_ids=None):
+        self.dims = dims
+        self.handle = B_.dfl_drafter_load(dims, weights, tap_layer_ids)
+        self._ws = None
+
+    def close(self):
+        if self.handle:
+            B_.dfl_drafter_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc_kv(self, B: int, Lcap: int, device="cuda"):
+        d = self.dims
+        shape = (B, Lcap, d.kv_heads, d.head_dim)
+        K = [torch.zeros(shape, dtype=torch.bfloat16, device=device) for _ in range(d.layers)]
+        V = [torch.zeros(shape, dtype=torch.bfloat16, device=device) for _ in range(d.layers)]
+        return K, V
+
+    def materialize(self, taps: torch.Tensor, K: list, V: list, row_offset: int = 0):
+        Bq, L = taps.shape[0], taps.shape[1]
+        ws = B_.workspace(B_.dfl_context_workspace_bytes(self.handle, Bq, L))
+        B_.dfl_context_materialize(self.handle, taps, Bq, L, row_offset, K[0].shape[1], K, V, ws)
+        return ws
+
+    def workspace(self, B: int, G: int, Lmax: int) -> torch.Tensor:
+        need = B_.dfl_draft_workspace_bytes(self.handle, B, G, Lmax)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = B_.workspace(need)
+        return self._ws
+
+    def draft(self, embeds, anchors, K, V, Lmax, ctx_len, pos0, lm_head, *, want_logits=False,
+              tokens=None, logits=None, ws=None):
+        Bq, G = embeds.shape[0], embeds.shape[1]
+        Lcap = K[0].shape[1] if K else 0
+        if tokens is None:
+            tokens = torch.empty((Bq, G - 1), dtype=torch.int32, device=embeds.device)
+        if want_logits and logits is None:
+            logits = torch.empty((Bq, G - 1, self.dims.vocab), dtype=torch.float32, device=embeds.device)
+        ws = ws if ws is not None else self.workspace(Bq, G, Lmax)
+        B_.dfl_draft_block(self.handle, embeds, anchors, Bq, G, K, V, Lcap, Lmax, ctx_len, pos0, lm_head,
+                           tokens, logits, ws)
+        return (tokens, logits) if want_logits else tokens

@@ -1,0 +1,246 @@
+/*
+ * dflash2.h - C ABI of the DFlash2 block-drafter hot path for MI355X (gfx950).
+ *
+ * Sources cited by page title and section:
+ *   [P2] @mlx-bun/inference diff, dflash2.ts (header comment, `#rms`, `#coefficients`,
+ *        `#conv`, `#rope`, `projectContext`, `#contextKV`, `#block`, `#select`, `dispose`).
+ *   [P3] MAX Python API, max.pipelines.architectures.dflash2_qwen3_5
+ *        (`DFlash2GroupedConv.prepare/finish`, `DFlash2CandidateSelector.score_edges/
+ *        select_path`, `DFlash2Qwen3_5.compute_candidates/forward_block/materialize`,
+ *        `supports_zero_draft_rows`).
+ *   [P1] codehub.bot listing of mirror-sd functions (neox RoPE, per-head RMSNorm docstrings).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are HIP device pointers into row-major, contiguous memory unless a
+ *     leading dimension is passed.  bf16 tensors are raw bit patterns (uint16_t).
+ *   - Inputs are borrowed until the enqueued work completes; outputs are caller-owned.
+ *   - Every call only enqueues work on `stream` and never synchronises it, except
+ *     dfl_drafter_load (one synchronisation after repacking) and dfl_read_kernel_time.
+ *   - Arguments are validated in full before anything is enqueued.  On error nothing
+ *     is written, a negative status is returned and dfl_last_error() describes it; the
+ *     drafter handle stays usable.  No C++ exception crosses this boundary.
+ *   - Workspaces (`ws`, `ws_bytes`) are caller-allocated device memory, 256-byte
+ *     aligned, sized by the matching *_workspace_bytes call.  Concurrent calls need
+ *     separate workspaces.
+ *   - Floating-point inputs must be finite; results for NaN/Inf inputs are undefined.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dfl_bf16; /* bf16 bit pattern, round-to-nearest-even by the producer */
+typedef struct dfl_drafter dfl_drafter; /* opaque; immutable after load except timing state */
+
+enum dfl_status {
+  DFL_OK = 0,
+  DFL_E_INVALID = -1,     /* null pointer, non-positive size, misaligned workspace */
+  DFL_E_SHAPE = -2,       /* sizes inconsistent with each other or with the config */
+  DFL_E_UNSUPPORTED = -3, /* conv taps != 2, G < 2 or G > block_size, repeated tap ids,
+                             top_k > 32 or > vocab, head_dim not 64/128, ... */
+  DFL_E_WORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes figure */
+  DFL_E_NOMEM = -5,       /* device allocation failed (load only) */
+  DFL_E_DEVICE = -6       /* a HIP call failed; the message carries hipGetErrorString */
+};
+
+/* Drafter dimensions ([P2] `Dflash2Config`/`readConfig`; [P3] `DFlash2Qwen3_5`). */
+typedef struct {
+  int32_t hidden;       /* H */
+  int32_t layers;
+  int32_t heads;        /* NH */
+  int32_t kv_heads;     /* NKV, divides NH */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t intermediate; /* F, multiple of 16 */
+  int32_t n_taps;       /* target taps concatenated into fc */
+  int32_t block_size;   /* G max: anchor + mask rows */
+  int32_t conv_taps;    /* must be 2 ([P2] `readConfig` accepts only two taps) */
+  int32_t conv_group;   /* channels per dynamic coefficient; multiple of 8, divides H */
+  int32_t top_k;        /* K, 1..32 */
+  int32_t rank;         /* R, multiple of 16, <= 128 */
+  int32_t vocab;        /* V */
+  float rms_eps;
+  float rope_theta;
+  const int32_t* tap_layer_ids; /* host array of n_taps target layer ids; must be distinct
+                                   ([P3] `build_module` rejects repeated tap ids); may be NULL */
+} dfl_config;
+
+/* One layer's tensors under the checkpoint layout ([P2] `Layer`: weights are [out, in]). */
+typedef struct {
+  const dfl_bf16* input_norm;  /* [H] */
+  const dfl_bf16* post_norm;   /* [H] */
+  const dfl_bf16* q_proj;      /* [NH*D, H] */
+  const dfl_bf16* k_proj;      /* [NKV*D, H] */
+  const dfl_bf16* v_proj;      /* [NKV*D, H] */
+  const dfl_bf16* o_proj;      /* [H, NH*D] */
+  const dfl_bf16* q_norm;      /* [D] */
+  const dfl_bf16* k_norm;      /* [D] */
+  const dfl_bf16* gate_proj;   /* [F, H] */
+  const dfl_bf16* up_proj;     /* [F, H] */
+  const dfl_bf16* down_proj;   /* [H, F] */
+  const dfl_bf16* attn_base;   /* [2 side, 2 tap, H] */
+  const dfl_bf16* attn_kproj;  /* [2*2*H/grp, H], output columns [side][tap][group] */
+  const dfl_bf16* mlp_base;    /* [2, 2, H] */
+  const dfl_bf16* mlp_kproj;   /* [2*2*H/grp, H] */
+} dfl_layer_weights;
+
+typedef struct {
+  const dfl_bf16* fc;          /* [H, n_taps*H] */
+  const dfl_bf16* hidden_norm; /* [H] */
+  const dfl_bf16* norm;        /* [H] final norm */
+  const dfl_bf16* sel_proj;    /* candidate_selector.hidden_projection [R, H] */
+  const dfl_bf16* pred;        /* predecessor codebook [V, R] */
+  const dfl_bf16* succ;        /* successor codebook [V, R] */
+  const dfl_layer_weights* layers; /* host array of `layers` entries */
+} dfl_weights;
+
+/* Copy and repack every drafter weight into buffers the handle owns ([P2] constructor
+ * and `#releaseCheckpoint`: the drafter owns its tensors; `dispose` frees them): fused
+ * q|k|v, gate/up interleaved per 16 rows, fused context k|v.  Synchronises `stream`
+ * once; the caller may free the source tensors afterwards.  The target's embedding and
+ * lm_head are not part of the drafter ([P2] header) and are passed per call. */
+int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t stream,
+                     dfl_drafter** out);
+void dfl_drafter_free(dfl_drafter* d);
+
+/* Workspace of dfl_context_materialize for B requests of L new rows. */
+size_t dfl_context_workspace_bytes(const dfl_drafter* d, int B, int L);
+
+/* Context K/V of every layer from the target taps ([P2] `projectContext`: c =
+ * RMSNorm(fc(concat taps), hidden_norm); `#contextKV`: K = RoPE(k_norm(k_proj c)) at the
+ * row's absolute position, V = v_proj c; [P3] `materialize`: no input norm, no conv).
+ *   taps:   [B, L, n_taps*H] bf16, taps concatenated on the feature axis.
+ *   K, V:   host arrays of `layers` device pointers, each [B, Lcap, NKV, D] bf16.
+ *   Rows row_offset .. row_offset+L-1 of every request are written, at absolute positions
+ *   row_offset + j, so committed rows can be appended incrementally.
+ *   Requires row_offset + L <= Lcap. */
+int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, int row_offset,
+                            int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Workspace of dfl_draft_block for B requests of G rows whose context holds at most
+ * Lmax rows. */
+size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
+
+/* One draft block per request ([P2] `#block` then `#select`; [P3] `forward_block`,
+ * `compute_candidates`, `score_edges`, `select_path`):
+ *   embeds:   [B, G, H] bf16, the target's embedding of [anchor, MASK x (G-1)]
+ *             ([P3] `mask_embeddings`: the drafter has no embedding of its own).
+ *   anchors:  [B] int32 device, id of each request's last verified token.
+ *   K, V:     host arrays of `layers` device pointers, [B, Lcap, NKV, D] bf16 each.
+ *   ctx_len:  [B] int32 device, context rows attended per request (0..Lmax, Lmax <= Lcap).
+ *   pos0:     [B] int32 device, absolute position of block row 0 of each request.
+ *   lm_head:  [V, H] bf16, the target's head, borrowed.
+ *   tokens:   [B, G-1] int32 device output ([P2] returns the proposals on the device).
+ *   logits_out: NULL or [B, G-1, V] float32 device output of the head.
+ *   G must satisfy 2 <= G <= block_size ([P3] `supports_zero_draft_rows` is false). */
+int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
+                    const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,
+                    const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
+                    int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* ---- the steps of the path, one call each ---- */
+
+/* RMSNorm over rows ([P2] `#rms`): y = x / sqrt(mean(x^2) + eps) * gamma, fp32 reduction.
+ * x [rows, H] bf16 with leading dimension ldx; y [rows, H] bf16 (ldy); gamma [H] bf16. */
+int dfl_rms_norm(const dfl_bf16* x, int rows, int H, int ldx, const dfl_bf16* gamma, float eps,
+                 dfl_bf16* y, int ldy, hipStream_t stream);
+
+/* Dense projection y = x . W^T ([P2] `Bf16Projection`), bf16 in, fp32 accumulate.
+ * x [M, K] (ldx >= K), W [N, K]; out_f32 != 0: y fp32 [M, N] (ldy); else bf16.
+ * K must be a multiple of 64.  ws/ws_bytes: split-K partials (dfl_linear_workspace_bytes). */
+size_t dfl_linear_workspace_bytes(int M, int N, int K);
+int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int N, void* y,
+               int ldy, int out_f32, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-head RMSNorm then neox RoPE, in place ([P2] `#block`: q/k norm before RoPE;
+ * [P1] per-head RMSNorm and split-half RoPE docstrings).  x holds rows of `heads`
+ * heads of D values at leading dimension ldx; row r sits at position
+ * pos0[r / rows_per_req] + r % rows_per_req (pos0 device int32). gamma [D] bf16. */
+int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const dfl_bf16* gamma,
+                       float eps, float theta, const int32_t* pos0, int rows_per_req,
+                       hipStream_t stream);
+
+/* Bidirectional block attention over each request's context prefix plus the block's own
+ * rows ([P2] header and `#block`: no mask, no window, scale 1/sqrt(D); GQA kv head =
+ * h / (NH/NKV)).  q [B*G, NH*D] (ldq), kb/vb [B*G, NKV*D] (ldkv), K/V [B, Lcap, NKV, D],
+ * ctx_len [B] device; out [B*G, NH*D] bf16 (ldo).  ws: dfl_attention_workspace_bytes. */
+size_t dfl_attention_workspace_bytes(int B, int G, int NH, int NKV, int D, int Lmax);
+int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const dfl_bf16* vb,
+                        int ldkv, const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax,
+                        const int32_t* ctx_len, int B, int G, int NH, int NKV, int D,
+                        dfl_bf16* out, int ldo, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouped dynamic conv, side 0 ([P3] `DFlash2GroupedConv.prepare`; [P2] `#coefficients`
+ * and `#conv`): D = x . kproj^T read as [side][tap][group]; out[t,c] = sum_tap
+ * (base[0,tap,c] + D[t,0,tap,c/grp]) * x[t-tap,c] with x[-1] = 0 at every block start.
+ * x, out [T, H] bf16; T a multiple of G; base [2,2,H] bf16; kproj [4*H/grp, H] bf16.
+ * coef1: [T, 2, H/grp] fp32 output, the side-1 deltas finish() reuses (base excluded). */
+size_t dfl_conv_prepare_workspace_bytes(int T, int H, int grp);
+int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_bf16* kproj,
+                     const dfl_bf16* base, dfl_bf16* out, float* coef1, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Grouped dynamic conv, side 1 ([P3] `DFlash2GroupedConv.finish`): out[t,c] =
+ * residual[t,c] + sum_tap (base[1,tap,c] + coef1[t,tap,c/grp]) * y[t-tap,c], y[-1] = 0 per
+ * block, summed in fp32 and rounded once to bf16 ([P2] `#block` adds the residual in fp32).
+ * residual may be NULL (then no residual) and may alias out. */
+int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base, int T, int H,
+                    int G, int grp, const dfl_bf16* residual, dfl_bf16* out, hipStream_t stream);
+
+/* Top-k of each row of fp32 logits ([P3] `compute_candidates`; [P2] `#select`), listed by
+ * value descending then id ascending.  logits [N, V]; ids int32 [N, K]; unary fp32 [N, K]. */
+size_t dfl_candidates_workspace_bytes(int N, int V, int K);
+int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* ids, float* unary,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Selector projection z = h . proj^T kept in fp32 ([P2] `#block`: z = hidden_projection(h)).
+ * h [N, H] bf16, proj [R, H] bf16, z [N, R] fp32. */
+size_t dfl_selector_project_workspace_bytes(int N, int H, int R);
+int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* score_edges ([P3] `DFlash2CandidateSelector.score_edges`):
+ * S[b,l,p,c] = unary[b,l,c] + sum_r pred[pid(b,l,p),r] * z[b,l,r] * succ[cand[b,l,c],r],
+ * pid(b,0,p) = anchors[b], pid(b,l,p) = cand[b,l-1,p].  cand int32 [B,S,K], unary fp32
+ * [B,S,K], z fp32 [B,S,R], anchors int32 [B], pred/succ bf16 [V,R]; scores fp32 [B,S,K,K].
+ * Ids outside [0, V) are clamped to that range. */
+int dfl_score_edges(const int32_t* cand, const float* unary, const float* z,
+                    const int32_t* anchors, int B, int S, int K, int R, const dfl_bf16* pred,
+                    const dfl_bf16* succ, int V, float* scores, hipStream_t stream);
+
+/* Greedy walk ([P3] `select_path`): j_0 = argmax_c S[b,0,0,c], j_l = argmax_c
+ * S[b,l,j_{l-1},c], tokens[b,l] = cand[b,l,j_l]; ties go to the lowest c. */
+int dfl_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
+                    int32_t* tokens, hipStream_t stream);
+
+/* ---- measurement ---- */
+
+/* Kernel classes whose launches can be bracketed with HIP events. */
+enum dfl_kernel_class {
+  DFL_K_NONE = -1,
+  DFL_K_GEMM_HEAD = 0, DFL_K_GEMM_GATEUP, DFL_K_GEMM_DOWN, DFL_K_GEMM_QKV, DFL_K_GEMM_O,
+  DFL_K_GEMM_KPROJ, DFL_K_GEMM_SELPROJ, DFL_K_GEMM_CONTEXT, DFL_K_ATTENTION, DFL_K_CONV_PREPARE,
+  DFL_K_CONV_FINISH, DFL_K_RMSNORM, DFL_K_ROPE, DFL_K_TOPK, DFL_K_SCORE_EDGES,
+  DFL_K_SELECT_PATH, DFL_K_COUNT
+};
+
+/* Bracket every later launch of class `k` made through `d` with a pair of HIP events on
+ * the launch's own stream (DFL_K_NONE stops).  dfl_read_kernel_time synchronises those
+ * events, returns the summed duration and launch count since the last read, and resets. */
+int dfl_set_timed_kernel(dfl_drafter* d, int k);
+int dfl_read_kernel_time(dfl_drafter* d, double* total_ms, int64_t* launches, double* bytes);
+
+/* Last error message of the calling thread ("" if none). */
+const char* dfl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH2_H */

@@ -1,0 +1,80 @@
+"""Comparison helpers shared by the parity tests."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# bf16-in / fp32-accumulate tensors: |g - o| <= ABS + REL * |o|
+BF16_ABS, BF16_REL = 2e-3, 2e-2
+# fp32 paths: |g - o| <= 1e-5 * (|o| + rms(o))
+F32_REL = 1e-5
+
+
+def to_host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_bf16_close(got, want, what=""):
+    g = to_host_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    err = np.abs(g - w)
+    bound = BF16_ABS + BF16_REL * np.abs(w)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside bf16 tolerance; worst at {i}: "
+                             f"got {g[i]!r} want {w[i]!r}")
+
+
+def assert_f32_close(got, want, what="", rel=F32_REL):
+    g = to_host_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    bound = rel * (np.abs(w) + rms)
+    err = np.abs(g - w)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside fp32 tolerance; worst at {i}: "
+                             f"got {g[i]!r} want {w[i]!r}")
+
+
+def band(v):
+    return BF16_ABS + BF16_REL * abs(float(v))
+
+
+def compare_tokens(gpu_tokens, oracle, cand_gpu=None):
+    """Compare drafted tokens slot by slot until the first mismatch.
+
+    A mismatch at slot l is accepted only when the oracle itself is within the bf16
+    tolerance band of a tie there: either for set membership (the K-th and (K+1)-th
+    logits of the slot) or for the walk (the top two scores on the predecessor row the
+    oracle's walk used).  Later slots of that request are not compared.  Returns the
+    number of slots compared equal.
+    """
+    tok = np.asarray(gpu_tokens)
+    want = oracle["tokens"]
+    logits = oracle["logits"]
+    scores = oracle["scores"]
+    cand = oracle["cand"]
+    B, S = want.shape
+    K = cand.shape[-1]
+    equal = 0
+    for b in range(B):
+        j = 0
+        for l in range(S):
+            if tok[b, l] == want[b, l]:
+                equal += 1
+                j = int(np.where(cand[b, l] == want[b, l])[0][0])
+                continue
+            row = np.sort(logits[b, l].astype(np.float64))[::-1]
+            member_margin = row[K - 1] - row[K]
+            sr = np.sort(scores[b, l, j].astype(np.float64))[::-1]
+            walk_margin = sr[0] - sr[1]
+            ok = member_margin <= 2 * band(row[K - 1]) or walk_margin <= 2 * band(sr[0])
+            assert ok, (f"request {b} slot {l}: GPU token {tok[b, l]} vs oracle {want[b, l]} with no "
+                        f"near-tie (membership margin {member_margin:.3g}, walk margin {walk_margin:.3g})")
+            break
+    return equal

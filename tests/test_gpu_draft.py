@@ -1,0 +1,78 @@
+"""End-to-end parity of the draft path (context materialisation and draft_block) on the GPU
+against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from dflash2_block_drafter_amd import configs, synth
+from dflash2_block_drafter_amd.drafter import Drafter
+from oracle import dflash2 as O
+from tests.helpers import assert_bf16_close, compare_tokens
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(d):
+    return {k: synth.host(v) for k, v in d.items()}
+
+
+def _run_tiny(w):
+    d = w.dims
+    weights_cpu = synth.drafter_weights(w)
+    tgt_cpu = synth.target_inputs(w)
+    weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
+    tgt = {k: v.to(DEV) for k, v in tgt_cpu.items()}
+    dr = Drafter(d, weights, tap_layer_ids=list(range(d.n_taps)))
+    K, V = dr.alloc_kv(w.batch, w.ctx_len + 3)
+    dr.materialize(tgt["taps"], K, V)
+    tokens, logits = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
+                              tgt["lm_head"], want_logits=True)
+    torch.cuda.synchronize()
+    return dr, _host(weights_cpu), _host(tgt_cpu), K, V, tokens, logits
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_tiny_drafter_end_to_end(batch):
+    w = configs.with_batch(configs.TINY, batch)
+    d = w.dims
+    dr, wh, th, K, V, tokens, logits = _run_tiny(w)
+    ks, vs = O.materialize_context(th["taps"], wh, d)
+    for i in range(d.layers):
+        assert_bf16_close(K[i][:, :w.ctx_len], ks[i], f"context K layer {i}")
+        assert_bf16_close(V[i][:, :w.ctx_len], vs[i], f"context V layer {i}")
+    ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
+                        return_all=True)
+    assert_bf16_close(logits, ref["logits"], "head logits")
+    n_eq = compare_tokens(tokens.cpu().numpy(), ref)
+    assert n_eq >= 1
+    dr.close()
+
+
+def test_tiny_context_append_matches_one_shot():
+    # appending committed rows at their absolute positions gives the same cache as one call
+    w = configs.TINY
+    d = w.dims
+    weights = {k: v.to(DEV) for k, v in synth.drafter_weights(w).items()}
+    taps = synth.target_inputs(w)["taps"].to(DEV)
+    dr = Drafter(d, weights)
+    K1, V1 = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(taps, K1, V1)
+    K2, V2 = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(taps[:, :20].contiguous(), K2, V2, row_offset=0)
+    dr.materialize(taps[:, 20:].contiguous(), K2, V2, row_offset=20)
+    torch.cuda.synchronize()
+    for i in range(d.layers):
+        assert torch.equal(K1[i], K2[i]) and torch.equal(V1[i], V2[i])
+    dr.close()
+
+
+def test_tiny_draft_is_deterministic():
+    w = configs.TINY
+    dr, _, _, K, V, tokens, logits = _run_tiny(w)
+    tgt = {k: v.to(DEV) for k, v in synth.target_inputs(w).items()}
+    t2, l2 = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
+                      tgt["lm_head"], want_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(tokens, t2) and torch.equal(logits, l2)
+    dr.close()
