@@ -199,36 +199,44 @@ def attention(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, k_blk: np.nda
 
 def mlp(i: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, bf16_points=False):
     """SwiGLU: down(silu(gate(i)) * up(i)) ([P2] `#block` MLP half; [P4] SwiGLU
-    as silu(g) * u)."""
-    g = linear(i, w_gate)
-    u = linear(i, w_up)
-    prod = _maybe_round(silu(g) * u, bf16_points)
+    as silu(g) * u).  With `bf16_points`, g, u, silu(g) and the product are each
+    rounded to bf16, as the bf16 ops of [P2] `#block` return them."""
+    rnd = lambda a: _maybe_round(a, bf16_points)
+    g = rnd(linear(i, w_gate))
+    u = rnd(linear(i, w_up))
+    prod = rnd(rnd(silu(g)) * u)
     return linear(prod, w_down)
 
 
 # ----------------------------------------------------------------------------
 # context and block
 
-def project_context(taps: np.ndarray, w_fc: np.ndarray, hidden_norm: np.ndarray, eps: float):
+def project_context(taps: np.ndarray, w_fc: np.ndarray, hidden_norm: np.ndarray, eps: float,
+                    bf16_points=False):
     """c = RMSNorm(fc(concat of the target taps)) ([P2] header "context c =
-    hidden_norm(fc(concat(target layers)))" and `projectContext`).
+    hidden_norm(fc(concat(target layers)))" and `projectContext`, whose bf16 fc
+    output and norm output are what `bf16_points` rounds).
 
     taps: [B, L, n_taps*H] with the taps concatenated on the feature axis.
     """
-    return rms_norm(linear(taps, w_fc), hidden_norm, eps)
+    rnd = lambda a: _maybe_round(a, bf16_points)
+    return rnd(rms_norm(rnd(linear(taps, w_fc)), hidden_norm, eps))
 
 
 def context_kv(c: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, k_norm: np.ndarray,
-               kv_heads: int, head_dim: int, eps: float, theta: float, positions=None):
+               kv_heads: int, head_dim: int, eps: float, theta: float, positions=None,
+               bf16_points=False):
     """One layer's context K/V: K = RoPE(k_norm(k_proj c)) at each row's absolute
     position, V = v_proj c; no input norm and no conv ([P2] `#contextKV`;
-    [P3] `materialize`).  c: [B, L, H] -> K, V: [B, L, NKV, D]."""
+    [P3] `materialize`).  c: [B, L, H] -> K, V: [B, L, NKV, D].  `bf16_points`
+    rounds the projection, norm and RoPE outputs, which [P2] holds in bf16."""
+    rnd = lambda a: _maybe_round(a, bf16_points)
     B, L, _ = c.shape
-    k = linear(c, w_k).reshape(B, L, kv_heads, head_dim)
-    v = linear(c, w_v).reshape(B, L, kv_heads, head_dim)
-    k = rms_norm(k, k_norm, eps)
+    k = rnd(linear(c, w_k)).reshape(B, L, kv_heads, head_dim)
+    v = rnd(linear(c, w_v)).reshape(B, L, kv_heads, head_dim)
+    k = rnd(rms_norm(k, k_norm, eps))
     pos = np.arange(L) if positions is None else np.asarray(positions)
-    kr = np.stack([rope_neox(k[b], pos, theta) for b in range(B)], axis=0)
+    kr = np.stack([rnd(rope_neox(k[b], pos, theta)) for b in range(B)], axis=0)
     return kr, v
 
 
@@ -279,16 +287,17 @@ def layer_weights(weights: dict, i: int) -> dict:
     return {k[len(p):]: v for k, v in weights.items() if k.startswith(p)}
 
 
-def materialize_context(taps, weights: dict, dims, positions=None):
+def materialize_context(taps, weights: dict, dims, positions=None, bf16_points=False):
     """Context K/V of every layer from the target taps ([P2] `projectContext` then
     `#contextKV`).  Returns lists K[layer], V[layer], each [B, L, NKV, D]."""
-    c = project_context(taps, weights["fc.weight"], weights["hidden_norm.weight"], dims.rms_eps)
+    c = project_context(taps, weights["fc.weight"], weights["hidden_norm.weight"], dims.rms_eps,
+                        bf16_points)
     ks, vs = [], []
     for i in range(dims.layers):
         lw = layer_weights(weights, i)
         k, v = context_kv(c, lw["self_attn.k_proj.weight"], lw["self_attn.v_proj.weight"],
                           lw["self_attn.k_norm.weight"], dims.kv_heads, dims.head_dim,
-                          dims.rms_eps, dims.rope_theta, positions)
+                          dims.rms_eps, dims.rope_theta, positions, bf16_points)
         ks.append(k)
         vs.append(v)
     return ks, vs

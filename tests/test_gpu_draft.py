@@ -37,12 +37,12 @@ def test_tiny_drafter_end_to_end(batch):
     w = configs.with_batch(configs.TINY, batch)
     d = w.dims
     dr, wh, th, K, V, tokens, logits = _run_tiny(w)
-    ks, vs = O.materialize_context(th["taps"], wh, d)
+    ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
     for i in range(d.layers):
         assert_bf16_close(K[i][:, :w.ctx_len], ks[i], f"context K layer {i}")
         assert_bf16_close(V[i][:, :w.ctx_len], vs[i], f"context V layer {i}")
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
-                        return_all=True)
+                        bf16_points=True, return_all=True)
     assert_bf16_close(logits, ref["logits"], "head logits")
     n_eq = compare_tokens(tokens.cpu().numpy(), ref)
     assert n_eq >= 1
