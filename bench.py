@@ -1,0 +1,216 @@
+"""Benchmark of the DFlash2 block-drafter hot path on one MI355X.
+
+A step is one draft_block call: the block of G rows of each of B requests through the
+five layers, the head, top-k, score_edges and the greedy walk.  Inputs and weights are
+synthetic and resident in HBM before the timed region; the context K/V is materialised
+once before it (it runs per prefill/commit, not per draft).
+
+Prints one JSON line with the throughput (drafted block tokens/s = B*G / step time), a
+per-kernel-class breakdown, the roofline of the dominant kernel (HIP events around its
+launches on the launch stream during the timed region), the HBM fraction of the grouped
+conv and of the candidate walk, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="full", choices=["full", "long", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-requests", type=int, default=1, help="requests in the oracle's timed sample")
+    return p.parse_args()
+
+
+def pmc_traffic(kernel_class: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
+    on the current kernel sources (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_class}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dflash2_block_drafter_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dflash2_block_drafter_amd import binding as B_
+    from dflash2_block_drafter_amd import configs, synth
+    from dflash2_block_drafter_amd.drafter import Drafter
+
+    w = configs.WORKLOADS[args.workload]
+    d = w.dims
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    weights = synth.drafter_weights(w, device=dev)
+    tgt = synth.target_inputs(w, device=dev, with_taps=not w.kv_given)
+    dr = Drafter(d, weights)
+    Bq, G, L = w.batch, d.block_size, w.ctx_len
+    if w.kv_given:
+        K, V = [], []
+        for i in range(d.layers):
+            k, v = synth.given_kv(w, i, device=dev)
+            K.append(k)
+            V.append(v)
+        ctx_ms = None
+    else:
+        K, V = dr.alloc_kv(Bq, L)
+        dr.materialize(tgt["taps"], K, V)          # compile-free warm call
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dr.materialize(tgt["taps"], K, V)
+        e.record()
+        torch.cuda.synchronize()
+        ctx_ms = s.elapsed_time(e)
+        del tgt["taps"]
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    ws = dr.workspace(Bq, G, L)
+    tokens = torch.empty((Bq, G - 1), dtype=torch.int32, device=dev)
+
+    def step():
+        dr.draft(tgt["embeds"], tgt["anchors"], K, V, L, tgt["ctx_len"], tgt["pos0"], tgt["lm_head"],
+                 tokens=tokens, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel-class breakdown: one step per class with that class bracketed by events
+    breakdown = {}
+    for k in B_.KERNEL_CLASSES:
+        B_.dfl_set_timed_kernel(dr.handle, k)
+        step()
+        torch.cuda.synchronize()
+        ms, n, by = B_.dfl_read_kernel_time(dr.handle)
+        if n:
+            breakdown[k] = {"ms": round(ms, 4), "launches": n, "GBps": round(by / (ms * 1e-3) / 1e9, 1)}
+    B_.dfl_set_timed_kernel(dr.handle, -1)
+    dominant = max(breakdown, key=lambda k: breakdown[k]["ms"])
+    print(f"# breakdown {json.dumps(breakdown)}", file=sys.stderr, flush=True)
+
+    # timed region: the dominant class bracketed on the launch stream
+    B_.dfl_set_timed_kernel(dr.handle, dominant)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_dom, n_dom, by_dom = B_.dfl_read_kernel_time(dr.handle)
+    B_.dfl_set_timed_kernel(dr.handle, -1)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = Bq * G / (elapsed / args.steps)
+
+    launch_ms = ms_dom / n_dom
+    bytes_per_launch = by_dom / n_dom
+    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+
+    def frac(cls):
+        b = breakdown.get(cls)
+        return None if b is None else round(b["GBps"] / HBM_PEAK_GBS, 4)
+
+    walk_cls = ["topk", "score_edges", "select_path"]
+    walk_ms = sum(breakdown[c]["ms"] for c in walk_cls if c in breakdown)
+    N = Bq * (G - 1)
+    walk_bytes = 4.0 * N * d.vocab + 4.0 * N * d.top_k * (d.rank + d.top_k + 2)
+    hbm = {"conv_prepare": frac("conv_prepare"), "conv_finish": frac("conv_finish"),
+           "walk": round(walk_bytes / (walk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if walk_ms else None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, weights, tgt, args.cpu_requests)
+
+    out = {
+        "metric": "drafted block tokens/sec (B×G) on 5-layer DFlash2; conv+walk % HBM peak",
+        "value": round(value, 1),
+        "unit": "block tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/embeddings)",
+        "config": {"workload": f"{w.name}: {d.layers}-layer drafter H={d.hidden} NH/NKV/D="
+                               f"{d.heads}/{d.kv_heads}/{d.head_dim} F={d.intermediate} V={d.vocab}, "
+                               f"B={Bq} G={G} L={L}", "B": Bq, "G": G, "L": L},
+        "roofline": roofline,
+        "hbm_frac": hbm,
+        "breakdown_ms": {k: v["ms"] for k, v in breakdown.items()},
+        "context_materialize_ms": None if ctx_ms is None else round(ctx_ms, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    dr.close()
+
+
+def cpu_baseline(w, weights, tgt, n_req):
+    """The oracle's draft block for the first n_req requests of the same workload, with the
+    context K/V drawn N(0,1) at the workload's shape (its cost does not depend on values)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from dflash2_block_drafter_amd import synth
+    from oracle import dflash2 as O
+
+    d = w.dims
+    wh = {k: synth.host(v) for k, v in weights.items()}
+    th = {k: synth.host(v[:n_req] if k in ("embeds", "anchors", "ctx_len", "pos0") else v)
+          for k, v in tgt.items() if k != "taps"}
+    rng = np.random.default_rng(0)
+    shape = (n_req, w.ctx_len, d.kv_heads, d.head_dim)
+    ks = [rng.standard_normal(shape) for _ in range(d.layers)]
+    vs = [rng.standard_normal(shape) for _ in range(d.layers)]
+    t = time.perf_counter()
+    O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d)
+    dt = time.perf_counter() - t
+    threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                  default=1)
+    return {"value": round(n_req * d.block_size / dt, 3), "unit": "block tok/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"oracle draft_block for {n_req} of {w.batch} requests (G={d.block_size}, "
+                      f"L={w.ctx_len} context K/V drawn N(0,1)), float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

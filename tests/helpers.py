@@ -78,3 +78,27 @@ def compare_tokens(gpu_tokens, oracle, cand_gpu=None):
                         f"near-tie (membership margin {member_margin:.3g}, walk margin {walk_margin:.3g})")
             break
     return equal
+
+
+# Composed outputs (several bf16-rounded steps in a row, e.g. the context K/V after fc,
+# norm, projection, norm and RoPE, or the head logits after five layers): every bf16
+# rounding of a value of scale s moves it by up to 2^-8 s, and a rotation or dot product
+# of such values can cancel to near zero while keeping that absolute error.  The bound
+# therefore scales its absolute term with the rms of the row the element belongs to:
+# |g - o| <= 2e-2 * (|o| + rms_row(o)).
+COMPOSED_REL = 2e-2
+
+
+def assert_composed_close(got, want, what="", rel=COMPOSED_REL):
+    g = to_host_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    rms = np.sqrt(np.mean(w * w, axis=-1, keepdims=True))
+    bound = rel * (np.abs(w) + rms)
+    err = np.abs(g - w)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside the composed-path bound; worst at "
+                             f"{i}: got {g[i]!r} want {w[i]!r} (row rms {float(rms[i[:-1]][0]):.3g})")
+    return float(np.max(err / (np.abs(w) + rms))) if w.size else 0.0

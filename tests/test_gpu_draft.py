@@ -7,7 +7,7 @@ import torch
 from dflash2_block_drafter_amd import configs, synth
 from dflash2_block_drafter_amd.drafter import Drafter
 from oracle import dflash2 as O
-from tests.helpers import assert_bf16_close, compare_tokens
+from tests.helpers import assert_composed_close, compare_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -39,11 +39,11 @@ def test_tiny_drafter_end_to_end(batch):
     dr, wh, th, K, V, tokens, logits = _run_tiny(w)
     ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
     for i in range(d.layers):
-        assert_bf16_close(K[i][:, :w.ctx_len], ks[i], f"context K layer {i}")
-        assert_bf16_close(V[i][:, :w.ctx_len], vs[i], f"context V layer {i}")
+        assert_composed_close(K[i][:, :w.ctx_len], ks[i], f"context K layer {i}")
+        assert_composed_close(V[i][:, :w.ctx_len], vs[i], f"context V layer {i}")
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
-    assert_bf16_close(logits, ref["logits"], "head logits")
+    assert_composed_close(logits, ref["logits"], "head logits")
     n_eq = compare_tokens(tokens.cpu().numpy(), ref)
     assert n_eq >= 1
     dr.close()
