@@ -244,12 +244,13 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
   const size_t H = c.hidden, D = c.head_dim, NH = c.heads, NKV = c.kv_heads, F = c.intermediate;
   const size_t ng = H / c.conv_group, V = c.vocab, R = c.rank;
   const size_t qkvw = (NH + 2 * NKV) * D;
-  // owned arena
+  auto tiled = [](size_t n, size_t k) { return dfl::tiled_weight_elems((int)n, (int)k); };
+  // owned arena: projections in the tile-contiguous layout, everything else as given
   Carver cv(nullptr);
-  auto sz_fc = cv.off; cv.take<uint16_t>(H * c.n_taps * H);
+  auto sz_fc = cv.off; cv.take<uint16_t>(tiled(H, c.n_taps * H));
   auto sz_hn = cv.off; cv.take<uint16_t>(H);
   auto sz_nm = cv.off; cv.take<uint16_t>(H);
-  auto sz_sp = cv.off; cv.take<uint16_t>(R * H);
+  auto sz_sp = cv.off; cv.take<uint16_t>(tiled(R, H));
   auto sz_pr = cv.off; cv.take<uint16_t>(V * R);
   auto sz_sc = cv.off; cv.take<uint16_t>(V * R);
   const size_t layer0 = cv.off;
@@ -260,15 +261,15 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
     off_post = lc.off; lc.take<uint16_t>(H);
     off_qn = lc.off; lc.take<uint16_t>(D);
     off_kn = lc.off; lc.take<uint16_t>(D);
-    off_qkv = lc.off; lc.take<uint16_t>(qkvw * H);
-    off_o = lc.off; lc.take<uint16_t>(H * NH * D);
-    off_gu = lc.off; lc.take<uint16_t>(2 * F * H);
-    off_dn = lc.off; lc.take<uint16_t>(H * F);
+    off_qkv = lc.off; lc.take<uint16_t>(tiled(qkvw, H));
+    off_o = lc.off; lc.take<uint16_t>(tiled(H, NH * D));
+    off_gu = lc.off; lc.take<uint16_t>(tiled(2 * F, H));
+    off_dn = lc.off; lc.take<uint16_t>(tiled(H, F));
     off_ab = lc.off; lc.take<uint16_t>(4 * H);
-    off_ak = lc.off; lc.take<uint16_t>(4 * ng * H);
+    off_ak = lc.off; lc.take<uint16_t>(tiled(4 * ng, H));
     off_mb = lc.off; lc.take<uint16_t>(4 * H);
-    off_mk = lc.off; lc.take<uint16_t>(4 * ng * H);
-    off_kv = lc.off; lc.take<uint16_t>(2 * NKV * D * H);
+    off_mk = lc.off; lc.take<uint16_t>(tiled(4 * ng, H));
+    off_kv = lc.off; lc.take<uint16_t>(tiled(2 * NKV * D, H));
     cv.off += lc.off * c.layers;
   }
   const size_t per_layer = (cv.off - layer0) / c.layers;
@@ -279,6 +280,14 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
   if (hipMalloc(&d->arena, cv.off) != hipSuccess) {
     delete d;
     return fail(DFL_E_NOMEM, "hipMalloc of %zu bytes for the drafter weights failed", cv.off);
+  }
+  // row-major staging for the fused projections (q|k|v, gate/up interleaved, k|v)
+  const size_t stage_elems = std::max({qkvw * H, 2 * F * H, 2 * NKV * D * H});
+  uint16_t* stage = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&stage), stage_elems * 2) != hipSuccess) {
+    (void)hipFree(d->arena);
+    delete d;
+    return fail(DFL_E_NOMEM, "hipMalloc of %zu bytes of load staging failed", stage_elems * 2);
   }
   char* A = static_cast<char*>(d->arena);
   auto at = [&](size_t off) { return reinterpret_cast<uint16_t*>(A + off); };
@@ -301,10 +310,16 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
       if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "hipMemcpy2DAsync: %s", hipGetErrorString(e));
     }
   };
-  cp(d->fc, w->fc, H * c.n_taps * H * 2);
+  auto tile = [&](const uint16_t* src, size_t n, size_t k, uint16_t* dst) {
+    if (rc == DFL_OK) {
+      hipError_t e = dfl::launch_tile_weights(src, (int)n, (int)k, dst, stream);
+      if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "weight tiling: %s", hipGetErrorString(e));
+    }
+  };
+  tile(w->fc, H, c.n_taps * H, d->fc);
   cp(d->hidden_norm, w->hidden_norm, H * 2);
   cp(d->norm, w->norm, H * 2);
-  cp(d->sel_proj, w->sel_proj, R * H * 2);
+  tile(w->sel_proj, R, H, d->sel_proj);
   cp(d->pred, w->pred, V * R * 2);
   cp(d->succ, w->succ, V * R * 2);
   d->layers.resize(c.layers);
@@ -329,25 +344,29 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
     cp(L.post_norm, s.post_norm, H * 2);
     cp(L.q_norm, s.q_norm, D * 2);
     cp(L.k_norm, s.k_norm, D * 2);
-    cp(L.qkv, s.q_proj, NH * D * H * 2);
-    cp(L.qkv + NH * D * H, s.k_proj, NKV * D * H * 2);
-    cp(L.qkv + (NH + NKV) * D * H, s.v_proj, NKV * D * H * 2);
-    cp(L.o, s.o_proj, H * NH * D * 2);
+    cp(stage, s.q_proj, NH * D * H * 2);
+    cp(stage + NH * D * H, s.k_proj, NKV * D * H * 2);
+    cp(stage + (NH + NKV) * D * H, s.v_proj, NKV * D * H * 2);
+    tile(stage, qkvw, H, L.qkv);
+    tile(s.o_proj, H, NH * D, L.o);
     // gate/up interleaved per 16 rows: [gate 16 | up 16] ...
-    cp2d(L.gateup, 32 * H * 2, s.gate_proj, 16 * H * 2, 16 * H * 2, F / 16);
-    cp2d(L.gateup + 16 * H, 32 * H * 2, s.up_proj, 16 * H * 2, 16 * H * 2, F / 16);
-    cp(L.down, s.down_proj, H * F * 2);
+    cp2d(stage, 32 * H * 2, s.gate_proj, 16 * H * 2, 16 * H * 2, F / 16);
+    cp2d(stage + 16 * H, 32 * H * 2, s.up_proj, 16 * H * 2, 16 * H * 2, F / 16);
+    tile(stage, 2 * F, H, L.gateup);
+    tile(s.down_proj, H, F, L.down);
     cp(L.attn_base, s.attn_base, 4 * H * 2);
-    cp(L.attn_kproj, s.attn_kproj, 4 * ng * H * 2);
+    tile(s.attn_kproj, 4 * ng, H, L.attn_kproj);
     cp(L.mlp_base, s.mlp_base, 4 * H * 2);
-    cp(L.mlp_kproj, s.mlp_kproj, 4 * ng * H * 2);
-    cp(L.kv_ctx, s.k_proj, NKV * D * H * 2);
-    cp(L.kv_ctx + NKV * D * H, s.v_proj, NKV * D * H * 2);
+    tile(s.mlp_kproj, 4 * ng, H, L.mlp_kproj);
+    cp(stage, s.k_proj, NKV * D * H * 2);
+    cp(stage + NKV * D * H, s.v_proj, NKV * D * H * 2);
+    tile(stage, 2 * NKV * D, H, L.kv_ctx);
   }
   if (rc == DFL_OK) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "hipStreamSynchronize: %s", hipGetErrorString(e));
   }
+  (void)hipFree(stage);
   if (rc != DFL_OK) {
     (void)hipFree(d->arena);
     delete d;
@@ -394,7 +413,7 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
   const int M = B * L, H = c.hidden, kvw = 2 * c.kv_heads * c.head_dim;
   const dfl::GemmPlan pfc = dfl::plan_gemm(M, H, c.n_taps * H);
   DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, H, c.n_taps * H, dfl::EPI_BF16), stream, [&] {
-    return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
+    return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, true, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
                             0, 0, part, stream);
   }));
   DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * M * H, stream, [&] {
@@ -404,7 +423,7 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
   for (int i = 0; i < c.layers; ++i) {
     const LayerBuf& Lb = d->layers[i];
     DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
+      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, true, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
                               stream);
     }));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
@@ -471,14 +490,14 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
       return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-      return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
+      return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
                               2 * ng, part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
       return dfl::launch_conv(n, d0, 2 * ng, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_qkv, a, H, L.qkv, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
+      return dfl::launch_gemm(p_qkv, a, H, L.qkv, true, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
                               stream);
     }));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
@@ -494,7 +513,7 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
                                    B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_o, ao, NH * D, L.o, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+      return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
       return dfl::launch_conv(u, d1, 2 * ng, L.attn_base, 1, T, H, G, c.conv_group, xin, x, stream);
@@ -504,18 +523,18 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
       return dfl::launch_rms_norm(x, H, T, H, L.post_norm, c.rms_eps, n, H, 1, 1, 0, stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-      return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
+      return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
                               part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
       return dfl::launch_conv(n, d0, 2 * ng, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
-      return dfl::launch_gemm(p_gu, a, H, L.gateup, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
+      return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
                               stream);
     }));
     DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_dn, p, F, L.down, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+      return dfl::launch_gemm(p_dn, p, F, L.down, true, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
       return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
@@ -527,10 +546,10 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
     return dfl::launch_rms_norm(xin, H, N, H, d->norm, c.rms_eps, h, H, S, G, 1, stream);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, V_, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_head, h, H, lm_head, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream);
+    return dfl::launch_gemm(p_head, h, H, lm_head, false, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_sel, h, H, d->sel_proj, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
+    return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
   }));
   DFL_TRY(timed(d, DFL_K_TOPK, 4.0 * N * V_, stream, [&] {
     return dfl::launch_topk(tpl, logits, N, V_, Kc, cand, unary, W + lay.topk, stream);
@@ -572,7 +591,7 @@ int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int 
   DFL_REQUIRE(ws_bytes >= pl.partial_bytes && (pl.partial_bytes == 0 || ws), DFL_E_WORKSPACE,
               "workspace %zu < %zu bytes", ws_bytes, pl.partial_bytes);
   DFL_REQUIRE(pl.partial_bytes == 0 || aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
-  hipError_t e = dfl::launch_gemm(pl, x, ldx, W, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy, nullptr,
+  hipError_t e = dfl::launch_gemm(pl, x, ldx, W, false, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy, nullptr,
                                   0, 0, static_cast<float*>(ws), stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
@@ -640,7 +659,7 @@ int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_
   float* d0 = static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)T * 2 * ng * sizeof(float)));
   const dfl::GemmPlan pl = dfl::plan_gemm(T, 4 * ng, H);
-  hipError_t e = dfl::launch_gemm(pl, x, H, kproj, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, coef1, 2 * ng, 2 * ng,
+  hipError_t e = dfl::launch_gemm(pl, x, H, kproj, false, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, coef1, 2 * ng, 2 * ng,
                                   part, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   e = dfl::launch_conv(x, d0, 2 * ng, base, 0, T, H, G, grp, nullptr, out, stream);

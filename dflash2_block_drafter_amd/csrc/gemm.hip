@@ -3,8 +3,20 @@
 // Every projection of the drafter multiplies activations by a weight stored [out, in]
 // (dflash2.ts diff, `Bf16Projection`), so both operands are K-contiguous: each lane
 // loads 16 contiguous bytes of one row for either MFMA operand and no transpose is
-// needed.  A and W tiles are staged through LDS with double buffering (one barrier per
-// 64-wide K step); global loads of step k+1 are in flight while step k computes.
+// needed.
+//
+// At the drafter's row counts (B*G = 128 block rows, B*(G-1) = 120 head rows) every
+// projection streams its weight once and is bound by HBM, not by the matrix cores
+// (128 flop per weight byte against a ridge near 312).  What decides the speed is the
+// weight bytes in flight per CU and the DRAM pattern of the stream:
+//   * one 128 x 256 tile per workgroup (8 wavefronts of 64 x 64), so a K step moves a
+//     32 KB weight tile and the grid stays within one resident wave of workgroups;
+//   * a register ring of PF stages: the loads of step k+PF are issued before step k is
+//     computed, each step is parked in one of two LDS buffers one iteration before use,
+//     one barrier per 64-wide K step; loads are branch-free (rows past M or N are clamped)
+//     so the compiler waits only on the stage it needs;
+//   * the drafter's own weights are stored tile-contiguous, [N/256][K/64][256][64], so a K
+//     step of a tile is one contiguous 32 KB block; the target's head stays row-major.
 //
 // Split-K: grid.z slices K; slices write fp32 partials and a separate kernel sums them
 // in slice order (deterministic, no float atomics) and applies the epilogue.
@@ -15,8 +27,7 @@ namespace dfl {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // 144-byte rows: 16-byte reads of 16 rows hit distinct banks
+constexpr int BK = 64;  // K step of the library's GEMM plans
 
 struct GemmArgs {
   const uint16_t* A;
@@ -43,17 +54,68 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, float
   }
 }
 
+// Loads one K step of the A tile [BM x BKS] and the W tile [BN x BKS] into registers.
+// TILED: W is stored tile-contiguous, [N/BN][K/BKS][BN][BKS], so one step of one tile is
+// a single contiguous BN*BKS*2-byte block; otherwise W is row-major [N, K].
+template <int BM, int BN, int BKS, int NT, bool TILED>
+struct TileLoader {
+  static constexpr int CPR = BKS / 8;  // 16-byte chunks per tile row
+  static constexpr int A_PER = BM * CPR / NT;
+  static constexpr int B_PER = BN * CPR / NT;
+  static_assert(A_PER * NT == BM * CPR, "A tile must split evenly over threads");
+  static_assert(B_PER * NT == BN * CPR, "B tile must split evenly over threads");
+  u32x4_t a[A_PER];
+  u32x4_t b[B_PER];
+
+  // Rows past M or N are clamped to the last row instead of branching around the load:
+  // their products land only in accumulator rows/columns that are never stored, and a
+  // branch-free body lets the compiler wait on exactly the stage it needs.
+  __device__ __forceinline__ void load(const GemmArgs& p, int m0, int n0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + i * NT;
+      const int gm = min(m0 + c / CPR, p.M - 1);
+      a[i] = *reinterpret_cast<const u32x4_t*>(p.A + (size_t)gm * p.lda + k0 + (c % CPR) * 8);
+    }
+    if (TILED) {
+      const uint16_t* tile = p.W + ((size_t)(n0 / BN) * (p.K / BKS) + k0 / BKS) * (BN * BKS);
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i)
+        b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(tile + (tid + i * NT) * 8));
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) {
+        const int c = tid + i * NT;
+        const int gn = min(n0 + c / CPR, p.N - 1);
+        b[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(p.W + (size_t)gn * p.K + k0 + (c % CPR) * 8));
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* sA, uint16_t* sB, int tid) const {
+    constexpr int LS = BKS + 8;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(&sA[(c / CPR) * LS + (c % CPR) * 8]) = a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(&sB[(c / CPR) * LS + (c % CPR) * 8]) = b[i];
+    }
+  }
+};
+
 // W rows for EPI_SILU_MUL are interleaved per 16: [gate 16 | up 16] ... so output
 // column j pairs accumulator columns (j/16)*32 + j%16 (gate) and +16 (up).
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs p) {
+template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED>
+__global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM / 16;
   constexpr int TN = BN / WN / 16;
-  constexpr int A_PER = BM * BK / 8 / NT;
-  constexpr int B_PER = BN * BK / 8 / NT;
-  static_assert(A_PER * NT * 8 == BM * BK, "A tile must split evenly over threads");
-  static_assert(B_PER * NT * 8 == BN * BK, "B tile must split evenly over threads");
+  constexpr int LDS_STRIDE = BKS + 8;  // +16 bytes: 16-byte reads of 16 rows hit distinct banks
+  using Loader = TileLoader<BM, BN, BKS, NT, TILED>;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
 
@@ -66,58 +128,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs p) {
   const int m0 = blockIdx.y * BM;
   const int kbeg = blockIdx.z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
-  const int nk = (kend - kbeg) / BK;
+  const int nk = (kend - kbeg) / BKS;
 
-  u32x4_t ra[A_PER], rb[B_PER];
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * NT;
-      const int r = c >> 3;
-      const int kc = (c & 7) * 8;
-      const int gm = m0 + r;
-      ra[i] = gm < p.M ? *reinterpret_cast<const u32x4_t*>(p.A + (size_t)gm * p.lda + k0 + kc) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + i * NT;
-      const int r = c >> 3;
-      const int kc = (c & 7) * 8;
-      const int gn = n0 + r;
-      rb[i] = gn < p.N ? *reinterpret_cast<const u32x4_t*>(p.W + (size_t)gn * p.K + k0 + kc) : zero;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&sA[buf][(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int c = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&sB[buf][(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = rb[i];
-    }
-  };
-
+  Loader ring[PF];
   f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    gload(kbeg);
-    sstore(0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kbeg + (kt + 1) * BK);
-    __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
+  for (int s = 0; s < PF; ++s)
+    if (s < nk) ring[s].load(p, m0, n0, kbeg + s * BKS, tid);
+  if (nk > 0) ring[0].store(sA[0], sB[0], tid);
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BKS / 32; ++ks) {
       const int kk = ks * 32 + (lane >> 4) * 8;
       bf16x8_t af[TM], bfr[TN];
 #pragma unroll
@@ -136,7 +163,32 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmArgs p) {
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  // Iteration kt: refill ring slot kt%PF with step kt+PF, compute step kt from LDS buffer
+  // kt%2, then move step kt+1 (ring slot (kt+1)%PF) into LDS buffer (kt+1)%2.  The main
+  // loop runs while every refill is in range and is unrolled PF times so every ring index
+  // is a compile-time constant; the last steps run in a guarded tail without refills.
+  int kt0 = 0;
+  for (; kt0 + 2 * PF <= nk; kt0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int kt = kt0 + s;
+      ring[s].load(p, m0, n0, kbeg + (kt + PF) * BKS, tid);
+      __syncthreads();
+      compute(kt & 1);
+      ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2 * PF; ++s) {
+    const int kt = kt0 + s;
+    if (kt < nk) {
+      if (kt + PF < nk) ring[s % PF].load(p, m0, n0, kbeg + (kt + PF) * BKS, tid);
+      __syncthreads();
+      compute(kt & 1);
+      if (kt + 1 < nk) ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
+    }
   }
 
   // Accumulator layout: lane holds column (lane & 15) and rows 4*(lane >> 4) + e.
@@ -208,29 +260,45 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   store_out(p, m, n, v);
 }
 
-struct TileCfg {
-  int bm, bn;
-};
+constexpr int kBM = 128, kBN = 256, kMaxSplits = 8;
+constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
 
-TileCfg pick_tile(int M) { return M <= 128 ? TileCfg{128, 64} : TileCfg{128, 128}; }
-
-int pick_splits(int M, int N, int K, TileCfg t) {
-  const int tiles = ((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-  const int nk = K / BK;
-  int s = 1;
-  while (tiles * s < 512 && nk / (s * 2) >= 8) s *= 2;
-  return s;
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ src, int N, int K,
+                                                           uint16_t* __restrict__ dst, size_t chunks) {
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  // destination chunk c = ((t * (K/64) + s) * 256 + r) * 8 + q, 8 bf16 each
+  const int q = static_cast<int>(c & 7);
+  const size_t rest = c >> 3;
+  const int r = static_cast<int>(rest % kBN);
+  const size_t ts = rest / kBN;
+  const int steps = K / BK;
+  const int sstep = static_cast<int>(ts % steps);
+  const int t = static_cast<int>(ts / steps);
+  const int n = t * kBN + r;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < N) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)n * K + sstep * BK + q * 8);
+  *reinterpret_cast<u32x4_t*>(dst + c * 8) = v;
 }
 
 }  // namespace
 
+size_t tiled_weight_elems(int N, int K) { return (size_t)((N + kBN - 1) / kBN) * kBN * K; }
+
+hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream) {
+  const size_t chunks = tiled_weight_elems(N, K) / 8;
+  tile_weights_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(src, N, K, dst, chunks);
+  return hipGetLastError();
+}
+
 GemmPlan plan_gemm(int M, int N, int K) {
-  const TileCfg t = pick_tile(M);
   GemmPlan pl;
-  pl.bm = t.bm;
-  pl.bn = t.bn;
-  int s = pick_splits(M, N, K, t);
+  pl.bm = kBM;
+  pl.bn = kBN;
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int nk = K / BK;
+  int s = 1;
+  while (s < kMaxSplits && tiles * (s + 1) <= kTargetWorkgroups && nk / (s + 1) >= 6) ++s;
   int per = (nk + s - 1) / s;
   pl.k_per_split = per * BK;
   pl.splits = (nk + per - 1) / per;
@@ -238,9 +306,9 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return pl;
 }
 
-hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, int M,
-                       int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
-                       int nsplit, float* partial, hipStream_t stream) {
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
+                       int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
+                       float* partial, hipStream_t stream) {
   GemmArgs p;
   p.A = A;
   p.W = W;
@@ -257,12 +325,11 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uin
   p.nsplit = epi == EPI_F32 ? (out1 ? nsplit : N) : N;
   p.partial = partial;
   p.splits = pl.splits;
-  dim3 grid((N + pl.bn - 1) / pl.bn, (M + pl.bm - 1) / pl.bm, pl.splits);
-  if (pl.bm == 128 && pl.bn == 64) {
-    gemm_bf16_kernel<128, 64, 2, 2><<<grid, 256, 0, stream>>>(p);
-  } else {
-    gemm_bf16_kernel<128, 128, 2, 2><<<grid, 256, 0, stream>>>(p);
-  }
+  dim3 grid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM, pl.splits);
+  if (w_tiled)
+    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true><<<grid, 512, 0, stream>>>(p);
+  else
+    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false><<<grid, 512, 0, stream>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int nout = epi == EPI_SILU_MUL ? N / 2 : N;

@@ -17,12 +17,17 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int M, int N, int K);
-// y = A . W^T.  A [M, K] (lda), W [N, K].  EPI_BF16: out0 bf16 (ld0).  EPI_F32: columns
-// < nsplit to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL:
-// W rows interleaved per 16 as [gate|up]; out0 bf16 [M, N/2] = silu(gate) * up.
-hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, int M,
-                       int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
-                       float* partial, hipStream_t stream);
+// y = A . W^T.  A [M, K] (lda).  W: row-major [N, K], or tile-contiguous (w_tiled) as
+// written by launch_tile_weights.  EPI_BF16: out0 bf16 (ld0).  EPI_F32: columns < nsplit
+// to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL: W rows
+// interleaved per 16 as [gate|up]; out0 bf16 [M, N/2] = silu(gate) * up.
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
+                       int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
+                       int nsplit, float* partial, hipStream_t stream);
+// Tile-contiguous copy of a row-major [N, K] weight: [ceil(N/256)][K/64][256][64], rows
+// past N zero.  tiled_weight_elems gives the destination size in bf16 elements.
+size_t tiled_weight_elems(int N, int K);
+hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream);
 
 // RMSNorm of `rows` rows.  Input row r is row in_row(r) = (r / out_per_grp) * in_per_grp +
 // skip + r % out_per_grp, so the final norm can drop the anchor row of every block.
