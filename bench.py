@@ -33,7 +33,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="full", choices=["full", "long", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-requests", type=int, default=1, help="requests in the oracle's timed sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB copy (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -56,6 +57,9 @@ def pmc_traffic(kernel_class: str, workload: str):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
@@ -155,7 +159,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, weights, tgt, args.cpu_requests)
+        print("# cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, weights, tgt)
 
     out = {
         "metric": "drafted block tokens/sec (B×G) on 5-layer DFlash2; conv+walk % HBM peak",
@@ -183,11 +188,13 @@ def main():
     dr.close()
 
 
-def cpu_baseline(w, weights, tgt, n_req):
-    """The oracle's draft block for the first n_req requests of the same workload, with the
-    context K/V drawn N(0,1) at the workload's shape (its cost does not depend on values)."""
+def cpu_baseline(w, weights, tgt, budget_s: float = 10.0):
+    """The CPU oracle as it stands, timed on a bounded sample of the same workload: whole
+    draft blocks of requests 0, 1, ... one at a time (requests are independent), stopping
+    once about `budget_s` seconds of oracle time have been spent or all requests are done.
+    The sampled requests' context K/V is drawn N(0,1) at the workload's shape (the
+    oracle's cost does not depend on the values)."""
     import numpy as np
-    import torch
     from threadpoolctl import threadpool_info
 
     from dflash2_block_drafter_amd import synth
@@ -195,21 +202,39 @@ def cpu_baseline(w, weights, tgt, n_req):
 
     d = w.dims
     wh = {k: synth.host(v) for k, v in weights.items()}
-    th = {k: synth.host(v[:n_req] if k in ("embeds", "anchors", "ctx_len", "pos0") else v)
-          for k, v in tgt.items() if k != "taps"}
+    th = {k: synth.host(v) for k, v in tgt.items() if k != "taps"}
     rng = np.random.default_rng(0)
-    shape = (n_req, w.ctx_len, d.kv_heads, d.head_dim)
-    ks = [rng.standard_normal(shape) for _ in range(d.layers)]
-    vs = [rng.standard_normal(shape) for _ in range(d.layers)]
-    t = time.perf_counter()
-    O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d)
-    dt = time.perf_counter() - t
+    shape = (1, w.ctx_len, d.kv_heads, d.head_dim)
+    spent, done = 0.0, 0
+    while done < w.batch and spent < budget_s:
+        b = done
+        ks = [rng.standard_normal(shape) for _ in range(d.layers)]
+        vs = [rng.standard_normal(shape) for _ in range(d.layers)]
+        t = time.perf_counter()
+        O.draft_block(th["embeds"][b:b + 1], wh, th["lm_head"], th["anchors"][b:b + 1], ks, vs,
+                      th["ctx_len"][b:b + 1], th["pos0"][b:b + 1], d)
+        spent += time.perf_counter() - t
+        done += 1
+        print(f"# oracle block {b}: {spent:.1f} s so far", file=sys.stderr, flush=True)
     threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
                   default=1)
-    return {"value": round(n_req * d.block_size / dt, 3), "unit": "block tok/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"oracle draft_block for {n_req} of {w.batch} requests (G={d.block_size}, "
-                      f"L={w.ctx_len} context K/V drawn N(0,1)), float64 NumPy"}
+    return {"value": round(done * d.block_size / spent, 4), "unit": "block tok/s", "cores": threads,
+            "kind": "oracle", "seconds": round(spent, 2),
+            "sample": f"whole oracle draft blocks of requests 0..{done - 1} of {w.batch} (G={d.block_size}, "
+                      f"all {d.layers} layers, full V={d.vocab} head), one request per call, context K/V "
+                      f"drawn N(0,1) at L={w.ctx_len}; float64 NumPy on the host"}
+
+
+def calibrate_copy():
+    """A plain copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch copy_", "bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
 if __name__ == "__main__":
