@@ -60,6 +60,7 @@ _SIGS = {
     "dfl_draft_workspace_bytes": (_Z, [_P, _I, _I, _I]),
     "dfl_draft_block": (_I, [_P, _P, _P, _I, _I, C.POINTER(_P), C.POINTER(_P), _I, _I, _P, _P, _P,
                              _P, _P, _P, _Z, _P]),
+    "dfl_block_layer": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "dfl_rms_norm": (_I, [_P, _I, _I, _I, _P, _F, _P, _I, _P]),
     "dfl_linear_workspace_bytes": (_Z, [_I, _I, _I]),
     "dfl_linear": (_I, [_P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
@@ -214,6 +215,11 @@ def dfl_draft_block(handle, embeds, anchors, B, G, K: list, V: list, Lcap, Lmax,
     _check(lib().dfl_draft_block(handle, _bf(embeds), _i32(anchors), B, G, kp, vp, Lcap, Lmax,
                                  _i32(ctx_len), _i32(pos0), _bf(lm_head), _i32(tokens),
                                  _f32(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_block_layer(handle, layer, x_in, x_out, B, G, K, V, Lcap, Lmax, ctx_len, pos0, ws, stream=None):
+    _check(lib().dfl_block_layer(handle, layer, _bf(x_in), _bf(x_out), B, G, _bf(K), _bf(V), Lcap, Lmax,
+                                 _i32(ctx_len), _i32(pos0), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def dfl_rms_norm(x, rows, H, ldx, gamma, eps, y, ldy, stream=None):

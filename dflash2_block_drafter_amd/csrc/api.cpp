@@ -220,7 +220,87 @@ CtxLayout ctx_layout(const dfl_config& c, int B, int L) {
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
+// One layer on the block (P3 DFlash2TransformerBlock; P2 #block, the body of the layer loop):
+// x_out = x_in + conv1(attn(conv0(rms x_in))), then the same for the MLP.  x_out may alias
+// x_in (every element is read and written by the same thread of the residual conv).
+int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, int G, const uint16_t* Kl,
+              const uint16_t* Vl, int Lcap, int Lmax, const int32_t* ctx_len, const int32_t* pos0, char* W,
+              const DraftLayout& lay, hipStream_t stream) {
+  const dfl_config& c = d->cfg;
+  const LayerBuf& L = d->layers[li];
+  const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
+  const int ng = H / c.conv_group, T = B * G;
+  const int qkvw = (NH + 2 * NKV) * D;
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
+  uint16_t *n = u16(lay.n), *a = u16(lay.a), *qkv = u16(lay.qkv), *ao = u16(lay.ao);
+  uint16_t *u = u16(lay.u), *p = u16(lay.p);
+  float *d0 = f32(lay.d0), *d1 = f32(lay.d1), *part = f32(lay.partial);
+  const dfl::AttnPlan apl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
+  const dfl::GemmPlan p_kp = dfl::plan_gemm(T, 4 * ng, H), p_qkv = dfl::plan_gemm(T, qkvw, H),
+                      p_o = dfl::plan_gemm(T, H, NH * D), p_gu = dfl::plan_gemm(T, 2 * F, H),
+                      p_dn = dfl::plan_gemm(T, H, F);
+  const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
+  const double norm_bytes = 4.0 * T * H;
+  // attention half
+  DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
+    return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
+                            2 * ng, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
+    return dfl::launch_conv(n, d0, 2 * ng, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_BF16), stream, [&] {
+    return dfl::launch_gemm(p_qkv, a, H, L.qkv, true, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
+                            stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
+    hipError_t e = dfl::launch_head_norm_rope(qkv, qkvw, T, NH, D, L.q_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
+                                              stream);
+    if (e != hipSuccess) return e;
+    return dfl::launch_head_norm_rope(qkv + NH * D, qkvw, T, NKV, D, L.k_norm, c.rms_eps, c.rope_theta, pos0, G,
+                                      0, stream);
+  }));
+  const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
+  DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
+    return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
+                                 B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
+    return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
+    return dfl::launch_conv(u, d1, 2 * ng, L.attn_base, 1, T, H, G, c.conv_group, xin, x, stream);
+  }));
+  // MLP half
+  DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
+    return dfl::launch_rms_norm(x, H, T, H, L.post_norm, c.rms_eps, n, H, 1, 1, 0, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
+                            part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
+    return dfl::launch_conv(n, d0, 2 * ng, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
+    return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
+                            stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
+    return dfl::launch_gemm(p_dn, p, F, L.down, true, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
+    return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
+  }));
+  return DFL_OK;
+}
+
 }  // namespace
+
 
 extern "C" {
 
@@ -459,86 +539,24 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   const DraftLayout lay = draft_layout(c, B, G, Lmax);
   DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
 
-  const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
-  const int ng = H / c.conv_group, T = B * G, S = G - 1, N = B * S;
-  const int qkvw = (NH + 2 * NKV) * D, V_ = c.vocab, R = c.rank, Kc = c.top_k;
+  const int H = c.hidden, S = G - 1, N = B * S;
+  const int V_ = c.vocab, R = c.rank, Kc = c.top_k;
   char* W = static_cast<char*>(ws);
   auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
-  uint16_t *x = u16(lay.x), *n = u16(lay.n), *a = u16(lay.a), *qkv = u16(lay.qkv), *ao = u16(lay.ao);
-  uint16_t *u = u16(lay.u), *p = u16(lay.p), *h = u16(lay.h);
-  float *d0 = f32(lay.d0), *d1 = f32(lay.d1), *z = f32(lay.z), *unary = f32(lay.unary), *scores = f32(lay.scores);
+  uint16_t *x = u16(lay.x), *h = u16(lay.h);
+  float *z = f32(lay.z), *unary = f32(lay.unary), *scores = f32(lay.scores);
   float* logits = logits_out ? logits_out : f32(lay.logits);
   int32_t* cand = reinterpret_cast<int32_t*>(W + lay.cand);
   float* part = f32(lay.partial);
-  const dfl::AttnPlan apl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
   const dfl::TopkPlan tpl = dfl::plan_topk(N, V_, Kc);
-  const dfl::GemmPlan p_kp = dfl::plan_gemm(T, 4 * ng, H), p_qkv = dfl::plan_gemm(T, qkvw, H),
-                      p_o = dfl::plan_gemm(T, H, NH * D), p_gu = dfl::plan_gemm(T, 2 * F, H),
-                      p_dn = dfl::plan_gemm(T, H, F), p_head = dfl::plan_gemm(N, V_, H),
-                      p_sel = dfl::plan_gemm(N, R, H);
-  const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
-  const double norm_bytes = 4.0 * T * H;
+  const dfl::GemmPlan p_head = dfl::plan_gemm(N, V_, H), p_sel = dfl::plan_gemm(N, R, H);
 
   const uint16_t* xin = embeds;
   for (int li = 0; li < c.layers; ++li) {
-    const LayerBuf& L = d->layers[li];
     const uint16_t* Kl = Lmax > 0 ? K[li] : nullptr;
     const uint16_t* Vl = Lmax > 0 ? V[li] : nullptr;
-    // attention half
-    DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
-      return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-      return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
-                              2 * ng, part, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-      return dfl::launch_conv(n, d0, 2 * ng, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_qkv, a, H, L.qkv, true, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
-                              stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
-      hipError_t e = dfl::launch_head_norm_rope(qkv, qkvw, T, NH, D, L.q_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
-                                                stream);
-      if (e != hipSuccess) return e;
-      return dfl::launch_head_norm_rope(qkv + NH * D, qkvw, T, NKV, D, L.k_norm, c.rms_eps, c.rope_theta, pos0, G,
-                                        0, stream);
-    }));
-    const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
-    DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
-      return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
-                                   B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-      return dfl::launch_conv(u, d1, 2 * ng, L.attn_base, 1, T, H, G, c.conv_group, xin, x, stream);
-    }));
-    // MLP half
-    DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
-      return dfl::launch_rms_norm(x, H, T, H, L.post_norm, c.rms_eps, n, H, 1, 1, 0, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-      return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
-                              part, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-      return dfl::launch_conv(n, d0, 2 * ng, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
-      return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
-                              stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(p_dn, p, F, L.down, true, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
-    }));
-    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-      return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
-    }));
+    DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, stream));
     xin = x;
   }
   // rows 1..G-1 of every block -> final norm -> head, selector
@@ -561,6 +579,24 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
     return dfl::launch_select_path(scores, cand, B, S, Kc, tokens, stream);
   }));
   return DFL_OK;
+}
+
+int dfl_block_layer(dfl_drafter* d, int layer, const dfl_bf16* x_in, dfl_bf16* x_out, int B, int G,
+                    const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax, const int32_t* ctx_len,
+                    const int32_t* pos0, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DFL_REQUIRE(d && x_in && x_out && ctx_len && pos0 && ws, DFL_E_INVALID, "NULL argument");
+  const dfl_config& c = d->cfg;
+  DFL_REQUIRE(layer >= 0 && layer < c.layers, DFL_E_INVALID, "layer %d outside [0, %d)", layer, c.layers);
+  DFL_REQUIRE(B > 0, DFL_E_INVALID, "B must be positive");
+  DFL_REQUIRE(G >= 2 && G <= c.block_size, DFL_E_UNSUPPORTED, "G=%d outside [2, block_size=%d]", G, c.block_size);
+  DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax %d must be in [0, Lcap=%d]", Lmax, Lcap);
+  DFL_REQUIRE(Lmax == 0 || (K && V), DFL_E_INVALID, "K/V NULL with Lmax > 0");
+  DFL_REQUIRE((int64_t)B * G * std::max(c.vocab, c.intermediate * 2) < (1ll << 31), DFL_E_SHAPE, "B*G too large");
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const DraftLayout lay = draft_layout(c, B, G, Lmax);
+  DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
+  return run_layer(d, layer, x_in, x_out, B, G, Lmax > 0 ? K : nullptr, Lmax > 0 ? V : nullptr, Lcap, Lmax, ctx_len,
+                   pos0, static_cast<char*>(ws), lay, stream);
 }
 
 // ---------------------------------------------------------------- single steps

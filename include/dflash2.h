@@ -145,6 +145,15 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
                     int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* One drafter layer on a block ([P3] `DFlash2TransformerBlock`: r = x; h = conv.prepare(norm r);
+ * h = attn(h); r += conv.finish(h), then the same for the MLP; [P2] `#block`, the body of the
+ * layer loop).  x_in, x_out: [B*G, H] bf16, block rows of request b at b*G..b*G+G-1; x_out may
+ * alias x_in.  K, V: this layer's context cache [B, Lcap, NKV, D]; ctx_len, pos0 as for
+ * dfl_draft_block.  ws: at least dfl_draft_workspace_bytes(d, B, G, Lmax). */
+int dfl_block_layer(dfl_drafter* d, int layer, const dfl_bf16* x_in, dfl_bf16* x_out, int B, int G,
+                    const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax, const int32_t* ctx_len,
+                    const int32_t* pos0, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- the steps of the path, one call each ---- */
 
 /* RMSNorm over rows ([P2] `#rms`): y = x / sqrt(mean(x^2) + eps) * gamma, fp32 reduction.

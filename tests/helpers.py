@@ -102,3 +102,26 @@ def assert_composed_close(got, want, what="", rel=COMPOSED_REL):
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside the composed-path bound; worst at "
                              f"{i}: got {g[i]!r} want {w[i]!r} (row rms {float(rms[i[:-1]][0]):.3g})")
     return float(np.max(err / (np.abs(w) + rms))) if w.size else 0.0
+
+
+# One whole drafter layer (about ten bf16 roundings in a chain, amplified by the dynamic conv
+# coefficients, whose deltas have std ~1.4 with N(0, 0.02) kernel_projection weights at H=5120):
+# elementwise bars do not survive that chain (two precisions the pages allow, the oracle at
+# P2's bf16 cast points and the same oracle in plain float64, already differ by ~3.8% at the
+# worst element of a full-size layer).  The GPU must be no further from the cast-point
+# oracle than 1.5x that spread, with the relative error e = |x - o| / (|o| + rms_row(o)):
+#   max e(GPU) <= max(2e-2, 1.5 * max e(float64 oracle))
+#   mean e(GPU) <= 1.5 * mean e(float64 oracle) + 1e-3
+def assert_layer_close(got, want, want64, what=""):
+    g = to_host_f64(got) if isinstance(got, torch.Tensor) else np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    w64 = np.asarray(want64, np.float64)
+    assert g.shape == w.shape == w64.shape, (what, g.shape, w.shape, w64.shape)
+    scale = np.abs(w) + np.sqrt(np.mean(w * w, axis=-1, keepdims=True))
+    eg = np.abs(g - w) / scale
+    es = np.abs(w64 - w) / scale
+    assert eg.max() <= max(COMPOSED_REL, 1.5 * es.max()), \
+        f"{what}: max error {eg.max():.3g} above 1.5x the precision spread {es.max():.3g}"
+    assert eg.mean() <= 1.5 * es.mean() + 1e-3, \
+        f"{what}: mean error {eg.mean():.3g} above 1.5x the mean precision spread {es.mean():.3g}"
+    return float(eg.max()), float(es.max())
