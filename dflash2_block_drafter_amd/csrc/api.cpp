@@ -223,9 +223,13 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) =
 // One layer on the block (P3 DFlash2TransformerBlock; P2 #block, the body of the layer loop):
 // x_out = x_in + conv1(attn(conv0(rms x_in))), then the same for the MLP.  x_out may alias
 // x_in (every element is read and written by the same thread of the residual conv).
+//
+// n_ready: the workspace's n already holds RMSNorm(x_in; input_norm) (written by the previous
+// layer's fused finish).  next_gamma: when not NULL, the MLP finish also writes
+// n = RMSNorm(x_out; next_gamma), the next layer's normed input.
 int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, int G, const uint16_t* Kl,
               const uint16_t* Vl, int Lcap, int Lmax, const int32_t* ctx_len, const int32_t* pos0, char* W,
-              const DraftLayout& lay, hipStream_t stream) {
+              const DraftLayout& lay, bool n_ready, const uint16_t* next_gamma, hipStream_t stream) {
   const dfl_config& c = d->cfg;
   const LayerBuf& L = d->layers[li];
   const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
@@ -243,9 +247,11 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
   const double norm_bytes = 4.0 * T * H;
   // attention half
-  DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
-    return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
-  }));
+  if (!n_ready) {
+    DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
+      return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
+    }));
+  }
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
                             2 * ng, part, stream);
@@ -258,11 +264,8 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
                             stream);
   }));
   DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
-    hipError_t e = dfl::launch_head_norm_rope(qkv, qkvw, T, NH, D, L.q_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
-                                              stream);
-    if (e != hipSuccess) return e;
-    return dfl::launch_head_norm_rope(qkv + NH * D, qkvw, T, NKV, D, L.k_norm, c.rms_eps, c.rope_theta, pos0, G,
-                                      0, stream);
+    return dfl::launch_head_norm_rope(qkv, qkvw, T, NH + NKV, NH, D, L.q_norm, L.k_norm, c.rms_eps, c.rope_theta,
+                                      pos0, G, 0, stream);
   }));
   const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
   DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
@@ -272,13 +275,12 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
     return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-    return dfl::launch_conv(u, d1, 2 * ng, L.attn_base, 1, T, H, G, c.conv_group, xin, x, stream);
+  // x = x_in + conv1(u), fused with the MLP half's input norm
+  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
+    return dfl::launch_conv_residual_norm(u, d1, 2 * ng, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
+                                          c.rms_eps, n, stream);
   }));
   // MLP half
-  DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
-    return dfl::launch_rms_norm(x, H, T, H, L.post_norm, c.rms_eps, n, H, 1, 1, 0, stream);
-  }));
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
                             part, stream);
@@ -293,9 +295,16 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
     return dfl::launch_gemm(p_dn, p, F, L.down, true, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-    return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
-  }));
+  if (next_gamma) {
+    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
+      return dfl::launch_conv_residual_norm(u, d1, 2 * ng, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
+                                            c.rms_eps, n, stream);
+    }));
+  } else {
+    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
+      return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
+    }));
+  }
   return DFL_OK;
 }
 
@@ -556,7 +565,8 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   for (int li = 0; li < c.layers; ++li) {
     const uint16_t* Kl = Lmax > 0 ? K[li] : nullptr;
     const uint16_t* Vl = Lmax > 0 ? V[li] : nullptr;
-    DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, stream));
+    const uint16_t* next_gamma = li + 1 < c.layers ? d->layers[li + 1].in_norm : nullptr;
+    DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, li > 0, next_gamma, stream));
     xin = x;
   }
   // rows 1..G-1 of every block -> final norm -> head, selector
@@ -596,7 +606,7 @@ int dfl_block_layer(dfl_drafter* d, int layer, const dfl_bf16* x_in, dfl_bf16* x
   const DraftLayout lay = draft_layout(c, B, G, Lmax);
   DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
   return run_layer(d, layer, x_in, x_out, B, G, Lmax > 0 ? K : nullptr, Lmax > 0 ? V : nullptr, Lcap, Lmax, ctx_len,
-                   pos0, static_cast<char*>(ws), lay, stream);
+                   pos0, static_cast<char*>(ws), lay, false, nullptr, stream);
 }
 
 // ---------------------------------------------------------------- single steps
@@ -627,8 +637,9 @@ int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int 
   DFL_REQUIRE(ws_bytes >= pl.partial_bytes && (pl.partial_bytes == 0 || ws), DFL_E_WORKSPACE,
               "workspace %zu < %zu bytes", ws_bytes, pl.partial_bytes);
   DFL_REQUIRE(pl.partial_bytes == 0 || aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
-  hipError_t e = dfl::launch_gemm(pl, x, ldx, W, false, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy, nullptr,
-                                  0, 0, static_cast<float*>(ws), stream);
+  float* part = static_cast<float*>(ws);
+  hipError_t e = dfl::launch_gemm(pl, x, ldx, W, false, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy,
+                                  nullptr, 0, 0, part, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }
@@ -639,7 +650,8 @@ int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const d
   DFL_REQUIRE(rows >= 0 && heads > 0 && rows_per_req > 0 && ldx >= heads * D, DFL_E_INVALID, "bad sizes");
   DFL_REQUIRE(D == 64 || D == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128", D);
   DFL_REQUIRE(eps >= 0.f && theta > 0.f, DFL_E_INVALID, "eps < 0 or theta <= 0");
-  hipError_t e = dfl::launch_head_norm_rope(x, ldx, rows, heads, D, gamma, eps, theta, pos0, rows_per_req, 0, stream);
+  hipError_t e =
+      dfl::launch_head_norm_rope(x, ldx, rows, heads, heads, D, gamma, gamma, eps, theta, pos0, rows_per_req, 0, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }
@@ -731,10 +743,7 @@ int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* id
   return DFL_OK;
 }
 
-size_t dfl_selector_project_workspace_bytes(int N, int H, int R) {
-  if (N <= 0 || H <= 0 || R <= 0 || H % 64) return 0;
-  return dfl::plan_gemm(N, R, H).partial_bytes;
-}
+size_t dfl_selector_project_workspace_bytes(int N, int H, int R) { return dfl_linear_workspace_bytes(N, R, H); }
 
 int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z, void* ws,
                          size_t ws_bytes, hipStream_t stream) {

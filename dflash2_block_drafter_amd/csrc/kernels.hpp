@@ -35,11 +35,12 @@ hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const ui
                            float eps, uint16_t* y, int ldy, int out_per_grp, int in_per_grp,
                            int skip, hipStream_t stream);
 
-// Per-head RMSNorm + neox RoPE in place on `heads` heads of each row.
-hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int D,
-                                 const uint16_t* gamma, float eps, float theta,
-                                 const int32_t* pos0, int rows_per_req, int pos_offset,
-                                 hipStream_t stream);
+// Per-head RMSNorm + neox RoPE in place on `heads` heads of each row; heads below `split`
+// use gamma, the rest gamma2.
+hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int split, int D,
+                                 const uint16_t* gamma, const uint16_t* gamma2, float eps,
+                                 float theta, const int32_t* pos0, int rows_per_req,
+                                 int pos_offset, hipStream_t stream);
 
 // Context K/V store: kv [B*L, 2*NKV*D] (k then v) -> K/V caches [B, Lcap, NKV, D] at rows
 // row_offset + j with k_norm and RoPE at position row_offset + j.
@@ -47,6 +48,14 @@ hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, in
                                    const uint16_t* k_norm, float eps, float theta,
                                    int row_offset, int Lcap, uint16_t* K, uint16_t* V,
                                    hipStream_t stream);
+
+// Side-1 conv + residual, then RMSNorm of the new residual row: x_out = residual +
+// conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias residual.
+hipError_t launch_conv_residual_norm(const uint16_t* y, const float* coef, int ldc,
+                                     const uint16_t* base, int T, int H, int G, int grp,
+                                     const uint16_t* residual, uint16_t* x_out,
+                                     const uint16_t* gamma, float eps, uint16_t* n_out,
+                                     hipStream_t stream);
 
 // Grouped dynamic conv.  coef: fp32 deltas [T, 2 (tap), ng] at row stride ldc.
 // side selects base[side]; residual may be null.

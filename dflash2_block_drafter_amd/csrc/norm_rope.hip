@@ -87,9 +87,12 @@ __device__ __forceinline__ void norm_rope_head(const uint16_t* src, uint16_t* ds
   }
 }
 
+// Heads [0, split) use gamma, heads [split, heads) use gamma2 (q and k of one row in one
+// launch: q heads take q_norm, k heads k_norm).
 __global__ __launch_bounds__(256) void head_norm_rope_kernel(uint16_t* x, int ldx, int rows,
-                                                             int heads, int D,
+                                                             int heads, int split, int D,
                                                              const uint16_t* __restrict__ gamma,
+                                                             const uint16_t* __restrict__ gamma2,
                                                              float eps, double log_theta,
                                                              const int32_t* __restrict__ pos0,
                                                              int rows_per_req, int pos_offset) {
@@ -101,7 +104,8 @@ __global__ __launch_bounds__(256) void head_norm_rope_kernel(uint16_t* x, int ld
   float c = 1.f, s = 0.f;
   if (lane < (D >> 1)) rope_cs(pos, lane, D, log_theta, &c, &s);
   uint16_t* row = x + (size_t)r * ldx;
-  for (int h = wave; h < heads; h += 4) norm_rope_head(row + h * D, row + h * D, D, gamma, eps, c, s, lane);
+  for (int h = wave; h < heads; h += 4)
+    norm_rope_head(row + h * D, row + h * D, D, h < split ? gamma : gamma2, eps, c, s, lane);
 }
 
 // Context K/V (dflash2.ts diff, `#contextKV`): kv row (b, j) holds [k | v] for all KV heads;
@@ -138,13 +142,13 @@ hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const ui
   return hipGetLastError();
 }
 
-hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int D,
-                                 const uint16_t* gamma, float eps, float theta,
-                                 const int32_t* pos0, int rows_per_req, int pos_offset,
-                                 hipStream_t stream) {
+hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int split, int D,
+                                 const uint16_t* gamma, const uint16_t* gamma2, float eps,
+                                 float theta, const int32_t* pos0, int rows_per_req,
+                                 int pos_offset, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  head_norm_rope_kernel<<<rows, 256, 0, stream>>>(x, ldx, rows, heads, D, gamma, eps,
-                                                  log(static_cast<double>(theta)), pos0,
+  head_norm_rope_kernel<<<rows, 256, 0, stream>>>(x, ldx, rows, heads, split, D, gamma, gamma2,
+                                                  eps, log(static_cast<double>(theta)), pos0,
                                                   rows_per_req, pos_offset);
   return hipGetLastError();
 }
