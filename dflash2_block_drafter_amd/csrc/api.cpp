@@ -539,6 +539,9 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   DFL_REQUIRE(B > 0, DFL_E_INVALID, "B must be positive");
   DFL_REQUIRE(G >= 2 && G <= c.block_size, DFL_E_UNSUPPORTED, "G=%d outside [2, block_size=%d]", G, c.block_size);
   DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax %d must be in [0, Lcap=%d]", Lmax, Lcap);
+  DFL_REQUIRE((int64_t)Lcap * d->cfg.kv_heads * d->cfg.head_dim < (int64_t(1) << 31), DFL_E_SHAPE,
+              "one request's K/V (Lcap %d x %d x %d) must hold fewer than 2^31 elements", Lcap,
+              d->cfg.kv_heads, d->cfg.head_dim);
   DFL_REQUIRE((int64_t)B * G * std::max(c.vocab, c.intermediate * 2) < (1ll << 31), DFL_E_SHAPE, "B*G too large");
   if (Lmax > 0) {
     DFL_REQUIRE(K && V, DFL_E_INVALID, "K/V arrays are NULL");
@@ -600,6 +603,9 @@ int dfl_block_layer(dfl_drafter* d, int layer, const dfl_bf16* x_in, dfl_bf16* x
   DFL_REQUIRE(B > 0, DFL_E_INVALID, "B must be positive");
   DFL_REQUIRE(G >= 2 && G <= c.block_size, DFL_E_UNSUPPORTED, "G=%d outside [2, block_size=%d]", G, c.block_size);
   DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax %d must be in [0, Lcap=%d]", Lmax, Lcap);
+  DFL_REQUIRE((int64_t)Lcap * d->cfg.kv_heads * d->cfg.head_dim < (int64_t(1) << 31), DFL_E_SHAPE,
+              "one request's K/V (Lcap %d x %d x %d) must hold fewer than 2^31 elements", Lcap,
+              d->cfg.kv_heads, d->cfg.head_dim);
   DFL_REQUIRE(Lmax == 0 || (K && V), DFL_E_INVALID, "K/V NULL with Lmax > 0");
   DFL_REQUIRE((int64_t)B * G * std::max(c.vocab, c.intermediate * 2) < (1ll << 31), DFL_E_SHAPE, "B*G too large");
   DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
@@ -670,6 +676,8 @@ int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const df
   DFL_REQUIRE(D == 64 || D == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128", D);
   DFL_REQUIRE(G * (NH / NKV) <= 64, DFL_E_UNSUPPORTED, "more than 64 query rows per KV head");
   DFL_REQUIRE(Lmax >= 0 && Lmax <= Lcap, DFL_E_SHAPE, "Lmax outside [0, Lcap]");
+  DFL_REQUIRE((int64_t)Lcap * NKV * D < (int64_t(1) << 31), DFL_E_SHAPE,
+              "one request's K/V (Lcap %d x %d x %d) must hold fewer than 2^31 elements", Lcap, NKV, D);
   DFL_REQUIRE(Lmax == 0 || (K && V), DFL_E_INVALID, "K/V NULL with Lmax > 0");
   DFL_REQUIRE(ldq >= NH * D && ldkv >= NKV * D && ldo >= NH * D && ldq % 8 == 0 && ldkv % 8 == 0, DFL_E_SHAPE,
               "leading dimensions too small or not multiples of 8");

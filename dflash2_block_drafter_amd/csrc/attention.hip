@@ -38,9 +38,9 @@ struct AttnArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   constexpr int KS = D + 8;   // K tile row stride (bf16)
-  constexpr int VS = KT + 8;  // V^T tile row stride (bf16)
+  constexpr int VS = KT + 4;  // V^T tile row stride (bf16): 34 dwords, conflict-free reads
   constexpr int DT = D / 16;  // output d tiles
   constexpr int DK = D / 32;  // MFMA k steps over D
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KS];
@@ -96,30 +96,48 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int CPR = D / 8;             // 16-byte chunks per key row
-  constexpr int PER = KT * CPR / 256;    // chunks per thread per tile
-  for (int j0 = kbeg; j0 < kend; j0 += KT) {
-    const int nvalid = min(KT, kend - j0);
-    // stage K rows and V^T into LDS
+  // Staging map: thread t owns keys ROWS_PER*kg .. +ROWS_PER-1 of a tile at dims
+  // 8*dg .. +7, with kg running fastest, so a wavefront's V^T store covers whole LDS rows
+  // (one 8-byte pack of 4 keys per dim and lane, no bank conflicts).  The next tile is in
+  // flight in registers while this one is computed; rows past the chunk end are clamped
+  // to its last row so that every load is unconditional (a deeper register ring lost to
+  // the compiler's conservative load waits at the loop head).
+  constexpr int DG = D / 8;                  // 16-byte chunks per key row
+  static_assert(KT * DG % 256 == 0, "tile must split over 256 threads");
+  constexpr int ROWS_PER = (KT * DG) / 256;  // key rows per thread per tile (4 for D=128)
+  constexpr int NKG = KT / ROWS_PER;
+  const int kg = tid % NKG;
+  const int dg = tid / NKG;
+  u32x4_t kreg[1][ROWS_PER], vreg[1][ROWS_PER];  // the next tile, in flight during compute
+  const uint32_t kstride32 = static_cast<uint32_t>(kstride);  // host checks Lcap*NKV*D < 2^31
+  auto tile_load = [&](u32x4_t (&kr)[ROWS_PER], u32x4_t (&vr)[ROWS_PER], int j0) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / CPR;
-      const int dc = (c % CPR) * 8;
-      u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (r < nvalid) {
-        kv = *reinterpret_cast<const u32x4_t*>(ksrc + (size_t)(j0 + r) * kstride + dc);
-        vv = *reinterpret_cast<const u32x4_t*>(vsrc + (size_t)(j0 + r) * kstride + dc);
-      }
-      *reinterpret_cast<u32x4_t*>(&Ks[r * KS + dc]) = kv;
+    for (int i = 0; i < ROWS_PER; ++i) {
+      const uint32_t off =
+          static_cast<uint32_t>(min(j0 + kg * ROWS_PER + i, kend - 1)) * kstride32 + dg * 8;
+      kr[i] = *reinterpret_cast<const u32x4_t*>(ksrc + off);
+      vr[i] = *reinterpret_cast<const u32x4_t*>(vsrc + off);
+    }
+  };
+  auto tile_store = [&](const u32x4_t (&kr)[ROWS_PER], const u32x4_t (&vr)[ROWS_PER]) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(dc + 2 * e) * VS + r] = static_cast<uint16_t>(vv[e] & 0xFFFFu);
-        Vt[(dc + 2 * e + 1) * VS + r] = static_cast<uint16_t>(vv[e] >> 16);
+    for (int i = 0; i < ROWS_PER; ++i)
+      *reinterpret_cast<u32x4_t*>(&Ks[(kg * ROWS_PER + i) * KS + dg * 8]) = kr[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h[ROWS_PER];
+#pragma unroll
+      for (int i = 0; i < ROWS_PER; ++i) h[i] = (vr[i][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+      uint16_t* dst = &Vt[(dg * 8 + e) * VS + kg * ROWS_PER];
+      if constexpr (ROWS_PER == 4) {
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      } else {
+#pragma unroll
+        for (int i = 0; i < ROWS_PER; i += 2) *reinterpret_cast<uint32_t*>(dst + i) = h[i] | (h[i + 1] << 16);
       }
     }
-    __syncthreads();
-
+  };
+  auto tile_compute = [&](int nvalid) {
     // S^T tiles: s[kt] holds keys kt*16 + 4*lg + e for query (lane & 15)
     f32x4_t s[KT / 16];
 #pragma unroll
@@ -132,27 +150,31 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kt], 0, 0, 0);
       }
     }
-    // online softmax in the log2 domain
+    // online softmax in the log2 domain: p = 2^(s * scale_log2 - m); keys past a ragged
+    // tile's end get s = -inf (uniform branch, taken only on a chunk's last tile)
+    if (nvalid < KT) {
+#pragma unroll
+      for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kt * 16 + lg * 4 + e >= nvalid) s[kt][e] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kt * 16 + lg * 4 + e;
-        const float v = key < nvalid ? s[kt][e] * a.scale_log2 : -INFINITY;
-        s[kt][e] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      tmax = fmaxf(tmax, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = exp2f(m - mnew);  // m = -inf on the first tile: alpha = 0
+    const float mnew = fmaxf(m, tmax * a.scale_log2);
+    // v_exp_f32 directly: exponents here are <= 0, and results below fp32's normal range
+    // (weights under 2^-126) flush to zero
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf on the first tile: 0
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(s[kt][e] - mnew);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], a.scale_log2, -mnew));
         s[kt][e] = p;
         psum += p;
       }
@@ -183,7 +205,16 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
                                                         o[dt], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+  if (kbeg < kend) {
+    tile_load(kreg[0], vreg[0], kbeg);
+    for (int j0 = kbeg; j0 < kend; j0 += KT) {
+      tile_store(kreg[0], vreg[0]);
+      tile_load(kreg[0], vreg[0], j0 + KT);
+      __syncthreads();
+      tile_compute(min(KT, kend - j0));
+      __syncthreads();
+    }
   }
 
   if (!qvalid) return;
@@ -199,6 +230,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 }
 
 // Merge the chunks of one query row: weights 2^(m_c - max m) and the summed denominators.
+// The chunk statistics are read lane-parallel; an empty chunk has m = -inf, so its weight
+// is exactly 0 and its (zero) partial output adds nothing.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t* out, int ldo) {
   const int lane = threadIdx.x & 63;
@@ -209,18 +242,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t*
   const int g = row / a.qrows;
   const size_t base = ((size_t)b * a.NKV + g) * a.nchunks;
   float mx = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) mx = fmaxf(mx, a.part_ml[((base + c) * a.qrows + qi) * 2]);
+  for (int c = lane; c < a.nchunks; c += 64) mx = fmaxf(mx, a.part_ml[((base + c) * a.qrows + qi) * 2]);
+  mx = wave_max(mx);
+  float den = 0.f;
+  for (int c = lane; c < a.nchunks; c += 64) {
+    const size_t slot = (base + c) * a.qrows + qi;
+    den += exp2f(a.part_ml[slot * 2] - mx) * a.part_ml[slot * 2 + 1];
+  }
+  den = wave_sum(den);
   constexpr int PL = D / 64;  // values per lane
   float acc[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) acc[i] = 0.f;
-  float den = 0.f;
+#pragma unroll 4
   for (int c = 0; c < a.nchunks; ++c) {
     const size_t slot = (base + c) * a.qrows + qi;
-    const float mc = a.part_ml[slot * 2];
-    if (mc == -INFINITY) continue;
-    const float w = exp2f(mc - mx);
-    den += w * a.part_ml[slot * 2 + 1];
+    const float w = exp2f(a.part_ml[slot * 2] - mx);
 #pragma unroll
     for (int i = 0; i < PL; ++i) acc[i] += w * a.part_o[slot * D + lane + 64 * i];
   }
@@ -277,6 +314,7 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
   a.nchunks = pl.nchunks;
   a.qrows = pl.qrows;
   a.scale_log2 = kLog2e / sqrtf(static_cast<float>(D));
+  if (static_cast<size_t>(Lcap) * NKV * D >= (size_t(1) << 31)) return hipErrorInvalidValue;
   dim3 grid(pl.nchunks, NKV, B);
   const int rows = NKV * pl.qrows;  // per request
   dim3 cgrid((rows + 3) / 4, B);

@@ -133,7 +133,8 @@ size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
  *             ([P3] `mask_embeddings`: the drafter has no embedding of its own).
  *   anchors:  [B] int32 device, id of each request's last verified token.
  *   K, V:     host arrays of `layers` device pointers, [B, Lcap, NKV, D] bf16 each.
- *   ctx_len:  [B] int32 device, context rows attended per request (0..Lmax, Lmax <= Lcap).
+ *   ctx_len:  [B] int32 device, context rows attended per request (0..Lmax, Lmax <= Lcap);
+ *             values outside [0, Lmax] are clamped into it.  Lcap*NKV*D < 2^31 (DFL_E_SHAPE).
  *   pos0:     [B] int32 device, absolute position of block row 0 of each request.
  *   lm_head:  [V, H] bf16, the target's head, borrowed.
  *   tokens:   [B, G-1] int32 device output ([P2] returns the proposals on the device).
@@ -179,7 +180,8 @@ int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const d
 /* Bidirectional block attention over each request's context prefix plus the block's own
  * rows ([P2] header and `#block`: no mask, no window, scale 1/sqrt(D); GQA kv head =
  * h / (NH/NKV)).  q [B*G, NH*D] (ldq), kb/vb [B*G, NKV*D] (ldkv), K/V [B, Lcap, NKV, D],
- * ctx_len [B] device; out [B*G, NH*D] bf16 (ldo).  ws: dfl_attention_workspace_bytes. */
+ * ctx_len [B] device (clamped into [0, Lmax]); out [B*G, NH*D] bf16 (ldo); Lcap*NKV*D must be
+ * below 2^31 (DFL_E_SHAPE).  ws: dfl_attention_workspace_bytes. */
 size_t dfl_attention_workspace_bytes(int B, int G, int NH, int NKV, int D, int Lmax);
 int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const dfl_bf16* vb,
                         int ldkv, const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax,
