@@ -162,7 +162,7 @@ int check_config(const dfl_config* c) {
 }
 
 struct DraftLayout {
-  size_t x, n, a, d0, d1, qkv, ao, u, p, h, logits, z, cand, unary, scores, attn, topk, partial;
+  size_t x, n, a, qkv, ao, u, p, h, logits, z, cand, unary, scores, attn, topk, kpart, partial;
   size_t total;
 };
 
@@ -175,8 +175,6 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
   L.x = cv.off; cv.take<uint16_t>((size_t)T * H);
   L.n = cv.off; cv.take<uint16_t>((size_t)T * H);
   L.a = cv.off; cv.take<uint16_t>((size_t)T * H);
-  L.d0 = cv.off; cv.take<float>((size_t)T * 2 * ng);
-  L.d1 = cv.off; cv.take<float>((size_t)T * 2 * ng);
   L.qkv = cv.off; cv.take<uint16_t>((size_t)T * qkvw);
   L.ao = cv.off; cv.take<uint16_t>((size_t)T * c.heads * c.head_dim);
   L.u = cv.off; cv.take<uint16_t>((size_t)T * H);
@@ -189,10 +187,14 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
   L.scores = cv.off; cv.take<float>((size_t)N * c.top_k * c.top_k);
   L.attn = cv.off; cv.take<char>(dfl::plan_attention(B, G, c.heads, c.kv_heads, c.head_dim, Lmax).ws_bytes);
   L.topk = cv.off; cv.take<char>(dfl::plan_topk(N, c.vocab, c.top_k).ws_bytes);
-  size_t part = 0;
-  const int shapes[][3] = {{T, 4 * ng, H},    {T, qkvw, H},     {T, H, c.heads * c.head_dim},
-                           {T, 2 * F, H},     {T, H, F},        {N, c.vocab, H},
-                           {N, c.rank, H}};
+  // kernel-projection planes live from the projection to the half-layer's finish; the q|k|v
+  // planes and every other projection's split-K scratch share one region
+  auto planes_bytes = [](int M, int N, int K) {
+    return (size_t)dfl::plan_gemm(M, N, K).splits * M * N * sizeof(float);
+  };
+  L.kpart = cv.off; cv.take<char>(planes_bytes(T, 4 * ng, H));
+  size_t part = planes_bytes(T, qkvw, H);
+  const int shapes[][3] = {{T, H, c.heads * c.head_dim}, {T, 2 * F, H}, {T, H, F}, {N, c.vocab, H}, {N, c.rank, H}};
   for (auto& s : shapes) part = std::max(part, dfl::plan_gemm(s[0], s[1], s[2]).partial_bytes);
   L.partial = cv.off; cv.take<char>(part);
   L.total = cv.off;
@@ -239,11 +241,15 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
   uint16_t *n = u16(lay.n), *a = u16(lay.a), *qkv = u16(lay.qkv), *ao = u16(lay.ao);
   uint16_t *u = u16(lay.u), *p = u16(lay.p);
-  float *d0 = f32(lay.d0), *d1 = f32(lay.d1), *part = f32(lay.partial);
+  float *kpart = f32(lay.kpart), *part = f32(lay.partial);
   const dfl::AttnPlan apl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
   const dfl::GemmPlan p_kp = dfl::plan_gemm(T, 4 * ng, H), p_qkv = dfl::plan_gemm(T, qkvw, H),
                       p_o = dfl::plan_gemm(T, H, NH * D), p_gu = dfl::plan_gemm(T, 2 * F, H),
                       p_dn = dfl::plan_gemm(T, H, F);
+  // The kernel projection's columns are [side][tap][group]: side 0 feeds prepare, side 1 finish.
+  dfl::Planes coef0 = dfl::gemm_planes(p_kp, kpart, T, 4 * ng), coef1 = coef0;
+  coef1.p += 2 * ng;
+  const dfl::Planes none;
   const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
   const double norm_bytes = 4.0 * T * H;
   // attention half
@@ -253,40 +259,40 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     }));
   }
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng,
-                            2 * ng, part, stream);
+    return dfl::launch_gemm_partials(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, d0, 2 * ng, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, none, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_BF16), stream, [&] {
-    return dfl::launch_gemm(p_qkv, a, H, L.qkv, true, T, qkvw, H, dfl::EPI_BF16, qkv, qkvw, nullptr, 0, 0, part,
-                            stream);
+  DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm_partials(p_qkv, a, H, L.qkv, true, T, qkvw, H, part, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * (NH + NKV) * D, stream, [&] {
-    return dfl::launch_head_norm_rope(qkv, qkvw, T, NH + NKV, NH, D, L.q_norm, L.k_norm, c.rms_eps, c.rope_theta,
-                                      pos0, G, 0, stream);
+  DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * qkvw * p_qkv.splits + 2.0 * T * qkvw, stream, [&] {
+    return dfl::launch_head_norm_rope_planes(dfl::gemm_planes(p_qkv, part, T, qkvw), qkv, qkvw, T, NH + NKV, NH, D,
+                                             NKV * D, L.q_norm, L.k_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
+                                             stream);
   }));
   const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
   DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
     return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
                                  B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
   }));
+  // o and down keep a separate split-K reduce: their consumer, the residual conv + norm,
+  // runs one workgroup per row and reads bf16 rows far faster than it could sum planes
   DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
     return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
   }));
   // x = x_in + conv1(u), fused with the MLP half's input norm
   DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-    return dfl::launch_conv_residual_norm(u, d1, 2 * ng, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
+    return dfl::launch_conv_residual_norm(u, none, coef1, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
                                           c.rms_eps, n, stream);
   }));
   // MLP half
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, d1, 2 * ng, 2 * ng,
-                            part, stream);
+    return dfl::launch_gemm_partials(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, d0, 2 * ng, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, none, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
     return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
@@ -297,12 +303,12 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   }));
   if (next_gamma) {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-      return dfl::launch_conv_residual_norm(u, d1, 2 * ng, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
+      return dfl::launch_conv_residual_norm(u, none, coef1, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
                                             c.rms_eps, n, stream);
     }));
   } else {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-      return dfl::launch_conv(u, d1, 2 * ng, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
+      return dfl::launch_conv(u, none, coef1, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
     }));
   }
   return DFL_OK;
@@ -718,7 +724,11 @@ int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_
   hipError_t e = dfl::launch_gemm(pl, x, H, kproj, false, T, 4 * ng, H, dfl::EPI_F32, d0, 2 * ng, coef1, 2 * ng, 2 * ng,
                                   part, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
-  e = dfl::launch_conv(x, d0, 2 * ng, base, 0, T, H, G, grp, nullptr, out, stream);
+  dfl::Planes coef0;
+  coef0.p = d0;
+  coef0.S = 1;
+  coef0.ld = 2 * ng;
+  e = dfl::launch_conv(x, dfl::Planes(), coef0, base, 0, T, H, G, grp, nullptr, out, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }
@@ -728,7 +738,11 @@ int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base,
   DFL_REQUIRE(y && coef1 && base && out, DFL_E_INVALID, "NULL argument");
   DFL_TRY(check_conv(T, H, G, grp));
   DFL_REQUIRE(y != out, DFL_E_INVALID, "y must not alias out");
-  hipError_t e = dfl::launch_conv(y, coef1, 2 * (H / grp), base, 1, T, H, G, grp, residual, out, stream);
+  dfl::Planes coef;
+  coef.p = coef1;
+  coef.S = 1;
+  coef.ld = 2 * (H / grp);
+  hipError_t e = dfl::launch_conv(y, dfl::Planes(), coef, base, 1, T, H, G, grp, residual, out, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

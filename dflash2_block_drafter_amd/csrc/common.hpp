@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace dfl {
 
 constexpr int kWave = 64;
@@ -61,5 +63,48 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// Sum over the S planes of pl (fp32 split-K partials) of the VW values at element offset
+// `off` (VW = 1, 2, 4 or 8; off a multiple of min(VW, 4)), added in plane order 0, 1, 2, ...
+// as the split-K reduce adds them.  Planes are read eight at a time with the plane index
+// clamped to S-1, so each batch is one round of independent loads and the wait comes
+// once per batch; the clamped repeats are not added.
+template <int VW>
+__device__ __forceinline__ void planes_sum(const Planes& pl, size_t off, float* out) {
+  constexpr int NV = VW > 4 ? 2 : 1;   // loads per plane
+  constexpr int LW = VW > 4 ? 4 : VW;  // floats per load
+  typedef float lv_t __attribute__((ext_vector_type(LW)));
+  const float* q = pl.p + off;
+  lv_t acc[NV];
+  for (int s0 = 0; s0 < pl.S; s0 += 8) {
+    lv_t v[8][NV];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const size_t po = (size_t)min(s0 + i, pl.S - 1) * pl.plane;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) v[i][j] = *reinterpret_cast<const lv_t*>(q + po + j * LW);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i >= pl.S) break;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) acc[j] = (s0 + i == 0) ? v[i][j] : acc[j] + v[i][j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < LW; ++e) out[j * LW + e] = acc[j][e];
+}
+
+__device__ __forceinline__ void planes_sum8(const Planes& pl, size_t off, float* out) { planes_sum<8>(pl, off, out); }
+
+__device__ __forceinline__ float planes_sum1(const Planes& pl, size_t off) {
+  float v;
+  planes_sum<1>(pl, off, &v);
+  return v;
+}
 
 }  // namespace dfl

@@ -8,6 +8,9 @@
 // covers 2048 contiguous channels and every load is coalesced.  Both rows t and t-1 are
 // read by the thread; the t-1 read of a row hits in cache behind its own row's reader.
 // The block boundary is structural: the t-1 load is skipped at t % G == 0.
+// Inside the drafter the conv input (the o and down projections' output) and the
+// coefficients (the kernel projection's output) arrive as those projections' fp32
+// split-K planes, summed here in plane order instead of by a separate reduce launch.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,31 +18,64 @@ namespace dfl {
 
 namespace {
 
-__global__ __launch_bounds__(256) void conv_kernel(const uint16_t* __restrict__ y,
-                                                   const float* __restrict__ coef, int ldc,
-                                                   const uint16_t* __restrict__ base, int side,
-                                                   int H, int G, int grp,
-                                                   const uint16_t* residual, uint16_t* out) {
-  const int t = blockIdx.y;
-  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (c0 >= H) return;
-  const int ng = H / grp;
-  const int g = c0 / grp;
-  const float d0 = coef[(size_t)t * ldc + g];
-  const float d1 = coef[(size_t)t * ldc + ng + g];
+// 8 channels c0.. of conv input row t: bf16 rows, or bf16(sum) of fp32 planes (the
+// producing projection's split-K partials, rounded where that projection rounds).
+__device__ __forceinline__ void load_y8(const uint16_t* y, const Planes& yp, int t, int H, int c0, float* f) {
+  if (y) {
+    unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)t * H + c0), f);
+  } else {
+    planes_sum8(yp, (size_t)t * yp.ld + c0, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = round_bf16(f[e]);
+  }
+}
+
+// Coefficients of row t for groups [g0, g0 + n) into cs: cs[i] = tap 0 of group g0 + i,
+// cs[n + i] = tap 1, each summed over the planes; cooperative and coalesced, then a barrier.
+__device__ __forceinline__ void stage_coef(const Planes& coef, int t, int ng, int g0, int n, float* cs) {
+  const size_t crow = (size_t)t * coef.ld;
+  for (int i = threadIdx.x; i < 2 * n; i += blockDim.x) {
+    const int col = i < n ? g0 + i : ng + g0 + (i - n);
+    cs[i] = planes_sum1(coef, crow + col);
+  }
+  __syncthreads();
+}
+
+// Two-tap output for 8 channels of row t with deltas d0 (tap 0) and d1 (tap 1):
+// (b0 + d0) * y[t] + (b1 + d1) * y[t-1], y[t-1] = 0 at a block start.
+__device__ __forceinline__ void conv8(const uint16_t* y, const Planes& yp, float d0, float d1,
+                                      const uint16_t* b0p, const uint16_t* b1p, int t, int H, int G,
+                                      int c0, float* o) {
   float cur[8], prev[8], b0[8], b1[8];
-  unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)t * H + c0), cur);
+  load_y8(y, yp, t, H, c0, cur);
   if (t % G != 0) {
-    unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)(t - 1) * H + c0), prev);
+    load_y8(y, yp, t - 1, H, c0, prev);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) prev[e] = 0.f;
   }
-  unpack8(*reinterpret_cast<const u32x4_t*>(base + (size_t)(side * 2 + 0) * H + c0), b0);
-  unpack8(*reinterpret_cast<const u32x4_t*>(base + (size_t)(side * 2 + 1) * H + c0), b1);
-  float o[8];
+  unpack8(*reinterpret_cast<const u32x4_t*>(b0p + c0), b0);
+  unpack8(*reinterpret_cast<const u32x4_t*>(b1p + c0), b1);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (b0[e] + d0) * cur[e] + (b1[e] + d1) * prev[e];
+}
+
+__global__ __launch_bounds__(256) void conv_kernel(const uint16_t* y, Planes yp, Planes coef,
+                                                   const uint16_t* __restrict__ base, int side,
+                                                   int H, int G, int grp,
+                                                   const uint16_t* residual, uint16_t* out) {
+  __shared__ float cs[2 * 256];  // 2048 channels hold at most 256 groups (grp >= 8)
+  const int t = blockIdx.y;
+  const int cb = blockIdx.x * 2048;
+  const int g0 = cb / grp;
+  const int ngw = (min(H, cb + 2048) - 1) / grp - g0 + 1;  // groups touching [cb, cb + 2048)
+  stage_coef(coef, t, H / grp, g0, ngw, cs);
+  const int c0 = cb + threadIdx.x * 8;
+  if (c0 >= H) return;
+  const int gl = c0 / grp - g0;
+  float o[8];
+  conv8(y, yp, cs[gl], cs[ngw + gl], base + (size_t)(side * 2 + 0) * H, base + (size_t)(side * 2 + 1) * H, t, H,
+        G, c0, o);
   if (residual) {
     float r[8];
     unpack8(*reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c0), r);
@@ -55,15 +91,16 @@ __global__ __launch_bounds__(256) void conv_kernel(const uint16_t* __restrict__ 
 // m = rms(x) opens the next sublayer).
 template <int MAXC>
 __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
-    const uint16_t* __restrict__ y, const float* __restrict__ coef, int ldc,
-    const uint16_t* __restrict__ base, int H, int G, int grp, const uint16_t* residual,
-    uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps, uint16_t* __restrict__ n_out) {
+    const uint16_t* y, Planes yp, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
+    const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
+    uint16_t* __restrict__ n_out) {
   __shared__ float red[4];
+  __shared__ float cs[2 * MAXC * 256];  // the row's groups: H / grp <= H / 8 = MAXC * 256
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int ng = H / grp;
   const int chunks = H >> 3;
-  const bool has_prev = (t % G) != 0;
+  const int ng = H / grp;
+  stage_coef(coef, t, ng, 0, ng, cs);
   float xv[MAXC][8];
   float ss = 0.f;
 #pragma unroll
@@ -71,23 +108,12 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
     const int ch = tid + i * 256;
     if (ch < chunks) {
       const int c0 = ch * 8;
+      float o[8], r[8];
       const int g = c0 / grp;
-      const float d0 = coef[(size_t)t * ldc + g];
-      const float d1 = coef[(size_t)t * ldc + ng + g];
-      float cur[8], prev[8], b0[8], b1[8], r[8];
-      unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)t * H + c0), cur);
-      if (has_prev) {
-        unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)(t - 1) * H + c0), prev);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) prev[e] = 0.f;
-      }
-      unpack8(*reinterpret_cast<const u32x4_t*>(base + (size_t)2 * H + c0), b0);
-      unpack8(*reinterpret_cast<const u32x4_t*>(base + (size_t)3 * H + c0), b1);
+      conv8(y, yp, cs[g], cs[ng + g], base + (size_t)2 * H, base + (size_t)3 * H, t, H, G, c0, o);
       unpack8(*reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c0), r);
-      float o[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = r[e] + ((b0[e] + d0) * cur[e] + (b1[e] + d1) * prev[e]);
+      for (int e = 0; e < 8; ++e) o[e] = r[e] + o[e];
       const u32x4_t packed = pack8(o);
       *reinterpret_cast<u32x4_t*>(x_out + (size_t)t * H + c0) = packed;
       unpack8(packed, xv[i]);  // the norm reads the rounded residual, as a separate norm would
@@ -115,23 +141,24 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
 
 }  // namespace
 
-hipError_t launch_conv_residual_norm(const uint16_t* y, const float* coef, int ldc,
+hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& yp, const Planes& coef,
                                      const uint16_t* base, int T, int H, int G, int grp,
                                      const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out,
                                      hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, ldc, base, H, G, grp, residual, x_out,
+  if (H > 4 * 256 * 8) return hipErrorInvalidValue;  // MAXC = 4 chunks of 8 per thread
+  conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, yp, coef, base, H, G, grp, residual, x_out,
                                                       gamma, eps, n_out);
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const uint16_t* y, const float* coef, int ldc, const uint16_t* base,
+hipError_t launch_conv(const uint16_t* y, const Planes& yp, const Planes& coef, const uint16_t* base,
                        int side, int T, int H, int G, int grp, const uint16_t* residual,
                        uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   dim3 grid((H / 8 + 255) / 256, T);
-  conv_kernel<<<grid, 256, 0, stream>>>(y, coef, ldc, base, side, H, G, grp, residual, out);
+  conv_kernel<<<grid, 256, 0, stream>>>(y, yp, coef, base, side, H, G, grp, residual, out);
   return hipGetLastError();
 }
 

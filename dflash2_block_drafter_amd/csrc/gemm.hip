@@ -19,7 +19,8 @@
 //     step of a tile is one contiguous 32 KB block; the target's head stays row-major.
 //
 // Split-K: grid.z slices K; slices write fp32 partials and a separate kernel sums them
-// in slice order (deterministic, no float atomics) and applies the epilogue.
+// in slice order (deterministic, no float atomics) and applies the epilogue, or the
+// partials are left for the consuming kernel, which sums them in the same order.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -237,27 +238,36 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
       }
 }
 
-// Sum of split-K partials in slice order, then the epilogue.  One thread per output.
+// Sum of split-K partials in slice order, then the epilogue.  Each thread owns VW adjacent
+// outputs (VW = 4 when N and the column split are multiples of 4, else 1); planes_sum
+// issues the slices' loads in batches of eight and adds them in order 0, 1, 2, ...
+template <int VW>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int nout = p.epi == EPI_SILU_MUL ? p.N / 2 : p.N;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * VW;
   if (idx >= (size_t)p.M * nout) return;
   const int m = static_cast<int>(idx / nout);
   const int n = static_cast<int>(idx % nout);
-  const size_t plane = (size_t)p.M * p.N;
+  Planes pl;
+  pl.p = p.partial;
+  pl.S = p.splits;
+  pl.ld = p.N;
+  pl.plane = (size_t)p.M * p.N;
   if (p.epi == EPI_SILU_MUL) {
+    // gate columns of outputs n..n+VW-1 (within one group of 16); up columns at +16
     const int ng = (n >> 4) * 32 + (n & 15);
-    float g = 0.f, u = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      g += p.partial[s * plane + (size_t)m * p.N + ng];
-      u += p.partial[s * plane + (size_t)m * p.N + ng + 16];
-    }
-    static_cast<uint16_t*>(p.out0)[(size_t)m * p.ld0 + n] = f32_to_bf16(silu(g) * u);
+    float g[VW], u[VW];
+    planes_sum<VW>(pl, (size_t)m * p.N + ng, g);
+    planes_sum<VW>(pl, (size_t)m * p.N + ng + 16, u);
+    uint16_t* o = static_cast<uint16_t*>(p.out0) + (size_t)m * p.ld0 + n;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) o[e] = f32_to_bf16(silu(g[e]) * u[e]);
     return;
   }
-  float v = 0.f;
-  for (int s = 0; s < p.splits; ++s) v += p.partial[s * plane + (size_t)m * p.N + n];
-  store_out(p, m, n, v);
+  float v[VW];
+  planes_sum<VW>(pl, (size_t)m * p.N + n, v);
+#pragma unroll
+  for (int e = 0; e < VW; ++e) store_out(p, m, n + e, v[e]);
 }
 
 constexpr int kBM = 128, kBN = 256, kMaxSplits = 8;
@@ -333,8 +343,39 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uin
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int nout = epi == EPI_SILU_MUL ? N / 2 : N;
-  const size_t total = (size_t)M * nout;
-  splitk_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
+  if (nout % 4 == 0 && p.nsplit % 4 == 0) {
+    const size_t quads = (size_t)M * nout / 4;
+    splitk_reduce_kernel<4><<<(unsigned)((quads + 255) / 256), 256, 0, stream>>>(p);
+  } else {
+    const size_t total = (size_t)M * nout;
+    splitk_reduce_kernel<1><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
+                                bool w_tiled, int M, int N, int K, float* partial, hipStream_t stream) {
+  GemmArgs p;
+  p.A = A;
+  p.W = W;
+  p.lda = lda;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.k_per_split = pl.k_per_split;
+  p.epi = EPI_F32;
+  p.out0 = partial;  // one split: the plain fp32 result is plane 0
+  p.ld0 = N;
+  p.out1 = nullptr;
+  p.ld1 = 0;
+  p.nsplit = N;
+  p.partial = partial;
+  p.splits = pl.splits;
+  dim3 grid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM, pl.splits);
+  if (w_tiled)
+    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true><<<grid, 512, 0, stream>>>(p);
+  else
+    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false><<<grid, 512, 0, stream>>>(p);
   return hipGetLastError();
 }
 

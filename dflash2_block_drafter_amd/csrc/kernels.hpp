@@ -9,6 +9,16 @@ namespace dfl {
 
 enum Epilogue { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU_MUL = 2 };
 
+// S fp32 planes of rows at row stride ld, plane stride `plane` elements: the split-K
+// partials of a GEMM left for the consuming kernel to sum in plane order (the order of the
+// split-K reduce), or S = 1 plane of plain fp32 values.  S = 0 marks an absent source.
+struct Planes {
+  const float* p = nullptr;
+  int S = 0;
+  int ld = 0;
+  size_t plane = 0;
+};
+
 struct GemmPlan {
   int bm = 0, bn = 0;
   int splits = 1;
@@ -24,6 +34,18 @@ GemmPlan plan_gemm(int M, int N, int K);
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
                        int nsplit, float* partial, hipStream_t stream);
+// y = A . W^T left as fp32 planes for the consumer: pl.splits planes [M, N] at plane stride
+// M*N in `partial` (one plane, the plain result, when the plan does not split K).
+hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
+                                bool w_tiled, int M, int N, int K, float* partial, hipStream_t stream);
+inline Planes gemm_planes(const GemmPlan& pl, const float* partial, int M, int N) {
+  Planes p;
+  p.p = partial;
+  p.S = pl.splits;
+  p.ld = N;
+  p.plane = (size_t)M * N;
+  return p;
+}
 // Tile-contiguous copy of a row-major [N, K] weight: [ceil(N/256)][K/64][256][64], rows
 // past N zero.  tiled_weight_elems gives the destination size in bf16 elements.
 size_t tiled_weight_elems(int N, int K);
@@ -36,11 +58,20 @@ hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const ui
                            int skip, hipStream_t stream);
 
 // Per-head RMSNorm + neox RoPE in place on `heads` heads of each row; heads below `split`
-// use gamma, the rest gamma2.
+// use gamma, the rest gamma2.  Row r sits at position pos0[r / rows_per_req] +
+// r % rows_per_req + pos_offset.
 hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int split, int D,
                                  const uint16_t* gamma, const uint16_t* gamma2, float eps,
                                  float theta, const int32_t* pos0, int rows_per_req,
                                  int pos_offset, hipStream_t stream);
+
+// The same from fp32 planes (the q|k|v projection's split-K partials): row r of dst (ldd)
+// gets bf16(sum) of every column, then RMSNorm + RoPE on the first `rope_heads` heads;
+// the remaining `tail_cols` columns (the v heads) are only rounded.
+hipError_t launch_head_norm_rope_planes(const Planes& src, uint16_t* dst, int ldd, int rows, int rope_heads,
+                                        int split, int D, int tail_cols, const uint16_t* gamma,
+                                        const uint16_t* gamma2, float eps, float theta, const int32_t* pos0,
+                                        int rows_per_req, int pos_offset, hipStream_t stream);
 
 // Context K/V store: kv [B*L, 2*NKV*D] (k then v) -> K/V caches [B, Lcap, NKV, D] at rows
 // row_offset + j with k_norm and RoPE at position row_offset + j.
@@ -49,17 +80,20 @@ hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, in
                                    int row_offset, int Lcap, uint16_t* K, uint16_t* V,
                                    hipStream_t stream);
 
+// Grouped dynamic conv input y: bf16 rows [T, H] (y != nullptr), or bf16(sum) of fp32
+// planes (yp, when y is null).  coef: the side's fp32 deltas, tap 0 of group g at column g
+// and tap 1 at column ng + g of each row, summed over coef.S planes.
+//
 // Side-1 conv + residual, then RMSNorm of the new residual row: x_out = residual +
 // conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias residual.
-hipError_t launch_conv_residual_norm(const uint16_t* y, const float* coef, int ldc,
+hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& yp, const Planes& coef,
                                      const uint16_t* base, int T, int H, int G, int grp,
                                      const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out,
                                      hipStream_t stream);
 
-// Grouped dynamic conv.  coef: fp32 deltas [T, 2 (tap), ng] at row stride ldc.
-// side selects base[side]; residual may be null.
-hipError_t launch_conv(const uint16_t* y, const float* coef, int ldc, const uint16_t* base,
+// Grouped dynamic conv; side selects base[side]; residual may be null.
+hipError_t launch_conv(const uint16_t* y, const Planes& yp, const Planes& coef, const uint16_t* base,
                        int side, int T, int H, int G, int grp, const uint16_t* residual,
                        uint16_t* out, hipStream_t stream);
 

@@ -108,6 +108,52 @@ __global__ __launch_bounds__(256) void head_norm_rope_kernel(uint16_t* x, int ld
     norm_rope_head(row + h * D, row + h * D, D, h < split ? gamma : gamma2, eps, c, s, lane);
 }
 
+// q|k|v projection finish from its fp32 split-K planes, one wavefront per (row, head):
+// the head's columns become bf16(sum over planes); heads [0, rope_heads) then get RMSNorm
+// + RoPE (q_norm below `split`, k_norm above); later heads (v) are stored as rounded.
+// Lane l holds EPL = D/64 adjacent values; for l < 32 they are first-half elements, their
+// rotary partners sit in lane l ^ 32.
+template <int D>
+__global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
+    Planes src, uint16_t* __restrict__ dst, int ldd, int rows, int heads, int rope_heads, int split,
+    const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ gamma2, float eps, double log_theta,
+    const int32_t* __restrict__ pos0, int rows_per_req, int pos_offset) {
+  constexpr int EPL = D / 64;
+  const int r = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (r >= rows || h >= heads) return;
+  const int lane = threadIdx.x & 63;
+  const int half_lane = lane & 31;
+  const int e0 = (lane >> 5) * (D / 2) + half_lane * EPL;  // this lane's first element
+  float v[EPL];
+  planes_sum<EPL>(src, (size_t)r * src.ld + h * D + e0, v);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) v[e] = round_bf16(v[e]);
+  uint16_t* out = dst + (size_t)r * ldd + h * D + e0;
+  if (h >= rope_heads) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out[e] = f32_to_bf16(v[e]);
+    return;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ss += v[e] * v[e];
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
+  const uint16_t* g = h < split ? gamma : gamma2;
+  const int pos = pos0[r / rows_per_req] + r % rows_per_req + pos_offset;
+  const bool first = lane < 32;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float x = v[e] * inv * bf16_to_f32(g[e0 + e]);
+    const float partner = __shfl_xor(x, 32, 64);
+    float c, s;
+    rope_cs(pos, half_lane * EPL + e, D, log_theta, &c, &s);
+    // rotate_half: first half x1 c - x2 s, second half x2 c + x1 s
+    out[e] = f32_to_bf16(first ? x * c - partner * s : x * c + partner * s);
+  }
+}
+
 // Context K/V (dflash2.ts diff, `#contextKV`): kv row (b, j) holds [k | v] for all KV heads;
 // K[b, row_offset + j] = RoPE(k_norm(k)) at position row_offset + j, V = v.
 __global__ __launch_bounds__(256) void context_kv_store_kernel(
@@ -150,6 +196,24 @@ hipError_t launch_head_norm_rope(uint16_t* x, int ldx, int rows, int heads, int 
   head_norm_rope_kernel<<<rows, 256, 0, stream>>>(x, ldx, rows, heads, split, D, gamma, gamma2,
                                                   eps, log(static_cast<double>(theta)), pos0,
                                                   rows_per_req, pos_offset);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_norm_rope_planes(const Planes& src, uint16_t* dst, int ldd, int rows, int rope_heads,
+                                        int split, int D, int tail_cols, const uint16_t* gamma,
+                                        const uint16_t* gamma2, float eps, float theta, const int32_t* pos0,
+                                        int rows_per_req, int pos_offset, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (tail_cols % D != 0 || src.ld % 4 != 0 || (D != 64 && D != 128)) return hipErrorInvalidValue;
+  const int heads = rope_heads + tail_cols / D;
+  const dim3 grid(rows, (heads + 3) / 4);
+  const double lt = log(static_cast<double>(theta));
+  if (D == 128)
+    head_norm_rope_planes_kernel<128><<<grid, 256, 0, stream>>>(src, dst, ldd, rows, heads, rope_heads, split, gamma,
+                                                                gamma2, eps, lt, pos0, rows_per_req, pos_offset);
+  else
+    head_norm_rope_planes_kernel<64><<<grid, 256, 0, stream>>>(src, dst, ldd, rows, heads, rope_heads, split, gamma,
+                                                               gamma2, eps, lt, pos0, rows_per_req, pos_offset);
   return hipGetLastError();
 }
 
