@@ -249,7 +249,6 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   // The kernel projection's columns are [side][tap][group]: side 0 feeds prepare, side 1 finish.
   dfl::Planes coef0 = dfl::gemm_planes(p_kp, kpart, T, 4 * ng), coef1 = coef0;
   coef1.p += 2 * ng;
-  const dfl::Planes none;
   const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
   const double norm_bytes = 4.0 * T * H;
   // attention half
@@ -262,7 +261,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     return dfl::launch_gemm_partials(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, none, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm_partials(p_qkv, a, H, L.qkv, true, T, qkvw, H, part, stream);
@@ -284,7 +283,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   }));
   // x = x_in + conv1(u), fused with the MLP half's input norm
   DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-    return dfl::launch_conv_residual_norm(u, none, coef1, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
+    return dfl::launch_conv_residual_norm(u, coef1, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
                                           c.rms_eps, n, stream);
   }));
   // MLP half
@@ -292,7 +291,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     return dfl::launch_gemm_partials(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, none, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
     return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
@@ -303,12 +302,12 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   }));
   if (next_gamma) {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-      return dfl::launch_conv_residual_norm(u, none, coef1, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
+      return dfl::launch_conv_residual_norm(u, coef1, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
                                             c.rms_eps, n, stream);
     }));
   } else {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
-      return dfl::launch_conv(u, none, coef1, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
+      return dfl::launch_conv(u, coef1, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
     }));
   }
   return DFL_OK;
@@ -728,7 +727,7 @@ int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_
   coef0.p = d0;
   coef0.S = 1;
   coef0.ld = 2 * ng;
-  e = dfl::launch_conv(x, dfl::Planes(), coef0, base, 0, T, H, G, grp, nullptr, out, stream);
+  e = dfl::launch_conv(x, coef0, base, 0, T, H, G, grp, nullptr, out, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }
@@ -742,7 +741,7 @@ int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base,
   coef.p = coef1;
   coef.S = 1;
   coef.ld = 2 * (H / grp);
-  hipError_t e = dfl::launch_conv(y, dfl::Planes(), coef, base, 1, T, H, G, grp, residual, out, stream);
+  hipError_t e = dfl::launch_conv(y, coef, base, 1, T, H, G, grp, residual, out, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

@@ -8,27 +8,15 @@
 // covers 2048 contiguous channels and every load is coalesced.  Both rows t and t-1 are
 // read by the thread; the t-1 read of a row hits in cache behind its own row's reader.
 // The block boundary is structural: the t-1 load is skipped at t % G == 0.
-// Inside the drafter the conv input (the o and down projections' output) and the
-// coefficients (the kernel projection's output) arrive as those projections' fp32
-// split-K planes, summed here in plane order instead of by a separate reduce launch.
+// Inside the drafter the coefficients (the kernel projection's output) arrive as that
+// projection's fp32 split-K planes; each workgroup sums its row's slice once, in plane
+// order, into LDS instead of a separate reduce launch writing them out.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dfl {
 
 namespace {
-
-// 8 channels c0.. of conv input row t: bf16 rows, or bf16(sum) of fp32 planes (the
-// producing projection's split-K partials, rounded where that projection rounds).
-__device__ __forceinline__ void load_y8(const uint16_t* y, const Planes& yp, int t, int H, int c0, float* f) {
-  if (y) {
-    unpack8(*reinterpret_cast<const u32x4_t*>(y + (size_t)t * H + c0), f);
-  } else {
-    planes_sum8(yp, (size_t)t * yp.ld + c0, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = round_bf16(f[e]);
-  }
-}
 
 // Coefficients of row t for groups [g0, g0 + n) into cs: cs[i] = tap 0 of group g0 + i,
 // cs[n + i] = tap 1, each summed over the planes; cooperative and coalesced, then a barrier.
@@ -41,44 +29,56 @@ __device__ __forceinline__ void stage_coef(const Planes& coef, int t, int ng, in
   __syncthreads();
 }
 
-// Two-tap output for 8 channels of row t with deltas d0 (tap 0) and d1 (tap 1):
-// (b0 + d0) * y[t] + (b1 + d1) * y[t-1], y[t-1] = 0 at a block start.
-__device__ __forceinline__ void conv8(const uint16_t* y, const Planes& yp, float d0, float d1,
-                                      const uint16_t* b0p, const uint16_t* b1p, int t, int H, int G,
-                                      int c0, float* o) {
+// The raw inputs of 8 channels c0.. of row t, loaded before the coefficients are staged so
+// both sets of loads are in flight together.
+struct ConvIn {
+  u32x4_t cur, prev, b0, b1;
+};
+
+__device__ __forceinline__ ConvIn load_conv_in(const uint16_t* y, const uint16_t* b0p, const uint16_t* b1p,
+                                               int t, int H, bool has_prev, int c0) {
+  ConvIn in;
+  in.cur = *reinterpret_cast<const u32x4_t*>(y + (size_t)t * H + c0);
+  in.prev = has_prev ? *reinterpret_cast<const u32x4_t*>(y + (size_t)(t - 1) * H + c0) : u32x4_t{0u, 0u, 0u, 0u};
+  in.b0 = *reinterpret_cast<const u32x4_t*>(b0p + c0);
+  in.b1 = *reinterpret_cast<const u32x4_t*>(b1p + c0);
+  return in;
+}
+
+// (b0 + d0) * y[t] + (b1 + d1) * y[t-1]; y[t-1] is zero at a block start (prev = 0).
+__device__ __forceinline__ void conv8(const ConvIn& in, float d0, float d1, float* o) {
   float cur[8], prev[8], b0[8], b1[8];
-  load_y8(y, yp, t, H, c0, cur);
-  if (t % G != 0) {
-    load_y8(y, yp, t - 1, H, c0, prev);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) prev[e] = 0.f;
-  }
-  unpack8(*reinterpret_cast<const u32x4_t*>(b0p + c0), b0);
-  unpack8(*reinterpret_cast<const u32x4_t*>(b1p + c0), b1);
+  unpack8(in.cur, cur);
+  unpack8(in.prev, prev);
+  unpack8(in.b0, b0);
+  unpack8(in.b1, b1);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (b0[e] + d0) * cur[e] + (b1[e] + d1) * prev[e];
 }
 
-__global__ __launch_bounds__(256) void conv_kernel(const uint16_t* y, Planes yp, Planes coef,
+__global__ __launch_bounds__(256) void conv_kernel(const uint16_t* y, Planes coef,
                                                    const uint16_t* __restrict__ base, int side,
                                                    int H, int G, int grp,
                                                    const uint16_t* residual, uint16_t* out) {
-  __shared__ float cs[2 * 256];  // 2048 channels hold at most 256 groups (grp >= 8)
+  __shared__ float cs[2 * 256];  // 2048 channels touch at most 256 groups (grp >= 8)
   const int t = blockIdx.y;
   const int cb = blockIdx.x * 2048;
   const int g0 = cb / grp;
   const int ngw = (min(H, cb + 2048) - 1) / grp - g0 + 1;  // groups touching [cb, cb + 2048)
-  stage_coef(coef, t, H / grp, g0, ngw, cs);
   const int c0 = cb + threadIdx.x * 8;
+  const int cc = min(c0, H - 8);  // threads past H load the last chunk and store nothing
+  const ConvIn in = load_conv_in(y, base + (size_t)(side * 2 + 0) * H, base + (size_t)(side * 2 + 1) * H, t, H,
+                                 t % G != 0, cc);
+  u32x4_t rv = {0u, 0u, 0u, 0u};
+  if (residual) rv = *reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + cc);
+  stage_coef(coef, t, H / grp, g0, ngw, cs);
   if (c0 >= H) return;
   const int gl = c0 / grp - g0;
   float o[8];
-  conv8(y, yp, cs[gl], cs[ngw + gl], base + (size_t)(side * 2 + 0) * H, base + (size_t)(side * 2 + 1) * H, t, H,
-        G, c0, o);
+  conv8(in, cs[gl], cs[ngw + gl], o);
   if (residual) {
     float r[8];
-    unpack8(*reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c0), r);
+    unpack8(rv, r);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = r[e] + o[e];
   }
@@ -88,18 +88,27 @@ __global__ __launch_bounds__(256) void conv_kernel(const uint16_t* y, Planes yp,
 // conv finish + residual + the next sublayer's RMSNorm, one workgroup per row: the row's
 // new residual stays in registers between the conv and the norm, so x is written once and
 // the norm costs no extra read (dflash2.ts diff, `#block`: x = bf16(x + Conv1(..)), then
-// m = rms(x) opens the next sublayer).
+// m = rms(x) opens the next sublayer).  MAXC chunks of 8 channels per thread.
 template <int MAXC>
 __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
-    const uint16_t* y, Planes yp, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
+    const uint16_t* y, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
     const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
     uint16_t* __restrict__ n_out) {
   __shared__ float red[4];
-  __shared__ float cs[2 * MAXC * 256];  // the row's groups: H / grp <= H / 8 = MAXC * 256
+  __shared__ float cs[2 * MAXC * 256];  // the row's groups: H / grp <= H / 8 <= MAXC * 256
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int chunks = H >> 3;
   const int ng = H / grp;
+  ConvIn in[MAXC];
+  u32x4_t rv[MAXC], gv[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int cc = min(tid + i * 256, chunks - 1) * 8;  // clamped: every load unconditional
+    in[i] = load_conv_in(y, base + (size_t)2 * H, base + (size_t)3 * H, t, H, t % G != 0, cc);
+    rv[i] = *reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + cc);
+    gv[i] = *reinterpret_cast<const u32x4_t*>(gamma + cc);
+  }
   stage_coef(coef, t, ng, 0, ng, cs);
   float xv[MAXC][8];
   float ss = 0.f;
@@ -108,10 +117,10 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
     const int ch = tid + i * 256;
     if (ch < chunks) {
       const int c0 = ch * 8;
-      float o[8], r[8];
       const int g = c0 / grp;
-      conv8(y, yp, cs[g], cs[ng + g], base + (size_t)2 * H, base + (size_t)3 * H, t, H, G, c0, o);
-      unpack8(*reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c0), r);
+      float o[8], r[8];
+      conv8(in[i], cs[g], cs[ng + g], o);
+      unpack8(rv[i], r);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = r[e] + o[e];
       const u32x4_t packed = pack8(o);
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
     const int ch = tid + i * 256;
     if (ch < chunks) {
       float gm[8], o[8];
-      unpack8(*reinterpret_cast<const u32x4_t*>(gamma + ch * 8), gm);
+      unpack8(gv[i], gm);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = xv[i][e] * inv * gm[e];
       *reinterpret_cast<u32x4_t*>(n_out + (size_t)t * H + ch * 8) = pack8(o);
@@ -141,24 +150,35 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
 
 }  // namespace
 
-hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& yp, const Planes& coef,
-                                     const uint16_t* base, int T, int H, int G, int grp,
-                                     const uint16_t* residual, uint16_t* x_out,
-                                     const uint16_t* gamma, float eps, uint16_t* n_out,
-                                     hipStream_t stream) {
+hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
+                                     int G, int grp, const uint16_t* residual, uint16_t* x_out,
+                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  if (H > 4 * 256 * 8) return hipErrorInvalidValue;  // MAXC = 4 chunks of 8 per thread
-  conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, yp, coef, base, H, G, grp, residual, x_out,
-                                                      gamma, eps, n_out);
+  const int per = (H / 8 + 255) / 256;  // chunks of 8 channels per thread
+  switch (per) {
+    case 1:
+      conv_residual_norm_kernel<1><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      break;
+    case 2:
+      conv_residual_norm_kernel<2><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      break;
+    case 3:
+      conv_residual_norm_kernel<3><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      break;
+    case 4:
+      conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      break;
+    default:
+      return hipErrorInvalidValue;  // H > 8192
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const uint16_t* y, const Planes& yp, const Planes& coef, const uint16_t* base,
-                       int side, int T, int H, int G, int grp, const uint16_t* residual,
-                       uint16_t* out, hipStream_t stream) {
+hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* base, int side, int T, int H, int G,
+                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   dim3 grid((H / 8 + 255) / 256, T);
-  conv_kernel<<<grid, 256, 0, stream>>>(y, yp, coef, base, side, H, G, grp, residual, out);
+  conv_kernel<<<grid, 256, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
   return hipGetLastError();
 }
 

@@ -80,22 +80,19 @@ hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, in
                                    int row_offset, int Lcap, uint16_t* K, uint16_t* V,
                                    hipStream_t stream);
 
-// Grouped dynamic conv input y: bf16 rows [T, H] (y != nullptr), or bf16(sum) of fp32
-// planes (yp, when y is null).  coef: the side's fp32 deltas, tap 0 of group g at column g
-// and tap 1 at column ng + g of each row, summed over coef.S planes.
+// Grouped dynamic conv of bf16 rows y [T, H].  coef: the side's fp32 deltas, tap 0 of group
+// g at column g and tap 1 at column ng + g of each row, summed over coef.S planes.
 //
 // Side-1 conv + residual, then RMSNorm of the new residual row: x_out = residual +
-// conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias residual.
-hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& yp, const Planes& coef,
-                                     const uint16_t* base, int T, int H, int G, int grp,
-                                     const uint16_t* residual, uint16_t* x_out,
-                                     const uint16_t* gamma, float eps, uint16_t* n_out,
-                                     hipStream_t stream);
+// conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias
+// residual; H <= 8192.
+hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
+                                     int G, int grp, const uint16_t* residual, uint16_t* x_out,
+                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream);
 
 // Grouped dynamic conv; side selects base[side]; residual may be null.
-hipError_t launch_conv(const uint16_t* y, const Planes& yp, const Planes& coef, const uint16_t* base,
-                       int side, int T, int H, int G, int grp, const uint16_t* residual,
-                       uint16_t* out, hipStream_t stream);
+hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* base, int side, int T, int H, int G,
+                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
 struct AttnPlan {
   int chunk = 0;     // context rows per chunk (multiple of 64)
