@@ -162,7 +162,7 @@ int check_config(const dfl_config* c) {
 }
 
 struct DraftLayout {
-  size_t x, n, a, qkv, ao, u, p, h, logits, z, cand, unary, scores, attn, topk, kpart, partial;
+  size_t x, n, a, qkv, ao, u, p, h, logits, tmax, z, cand, unary, scores, attn, kpart, partial;
   size_t total;
 };
 
@@ -181,12 +181,12 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
   L.p = cv.off; cv.take<uint16_t>((size_t)T * F);
   L.h = cv.off; cv.take<uint16_t>((size_t)N * H);
   L.logits = cv.off; cv.take<float>((size_t)N * c.vocab);
+  L.tmax = cv.off; cv.take<float>((size_t)N * ((c.vocab + dfl::kGemmTileN - 1) / dfl::kGemmTileN));
   L.z = cv.off; cv.take<float>((size_t)N * c.rank);
   L.cand = cv.off; cv.take<int32_t>((size_t)N * c.top_k);
   L.unary = cv.off; cv.take<float>((size_t)N * c.top_k);
   L.scores = cv.off; cv.take<float>((size_t)N * c.top_k * c.top_k);
   L.attn = cv.off; cv.take<char>(dfl::plan_attention(B, G, c.heads, c.kv_heads, c.head_dim, Lmax).ws_bytes);
-  L.topk = cv.off; cv.take<char>(dfl::plan_topk(N, c.vocab, c.top_k).ws_bytes);
   // kernel-projection planes live from the projection to the half-layer's finish; the q|k|v
   // planes and every other projection's split-K scratch share one region
   auto planes_bytes = [](int M, int N, int K) {
@@ -566,7 +566,6 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   float* logits = logits_out ? logits_out : f32(lay.logits);
   int32_t* cand = reinterpret_cast<int32_t*>(W + lay.cand);
   float* part = f32(lay.partial);
-  const dfl::TopkPlan tpl = dfl::plan_topk(N, V_, Kc);
   const dfl::GemmPlan p_head = dfl::plan_gemm(N, V_, H), p_sel = dfl::plan_gemm(N, R, H);
 
   const uint16_t* xin = embeds;
@@ -581,14 +580,22 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * N * H, stream, [&] {
     return dfl::launch_rms_norm(xin, H, N, H, d->norm, c.rms_eps, h, H, S, G, 1, stream);
   }));
+  // An unsplit head also writes every 256-column tile's row maxima, which lets the top-K
+  // read only the few tiles that can hold a candidate; a split head leaves them to a pass
+  // over the logits.
+  const bool tiles_fused = p_head.splits == 1;
+  float* tmax = f32(lay.tmax);
   DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, V_, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_head, h, H, lm_head, false, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream);
+    return dfl::launch_gemm(p_head, h, H, lm_head, false, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream,
+                            tiles_fused ? tmax : nullptr);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_TOPK, 4.0 * N * V_, stream, [&] {
-    return dfl::launch_topk(tpl, logits, N, V_, Kc, cand, unary, W + lay.topk, stream);
+  DFL_TRY(timed(d, DFL_K_TOPK, tiles_fused ? 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) : 4.0 * N * V_,
+                stream, [&] {
+    return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream)
+                       : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream);
   }));
   DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (R + Kc + 2), stream, [&] {
     return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, V_, scores, stream);
@@ -748,7 +755,7 @@ int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base,
 
 size_t dfl_candidates_workspace_bytes(int N, int V, int K) {
   if (N <= 0 || V <= 0 || K <= 0) return 0;
-  return dfl::plan_topk(N, V, K).ws_bytes;
+  return dfl::topk_ws_bytes(N, V);
 }
 
 int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* ids, float* unary, void* ws,
@@ -756,10 +763,10 @@ int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* id
   DFL_REQUIRE(logits && ids && unary && ws, DFL_E_INVALID, "NULL argument");
   DFL_REQUIRE(N > 0 && V > 0 && K > 0, DFL_E_INVALID, "sizes must be positive");
   DFL_REQUIRE(K <= 32 && K <= V, DFL_E_UNSUPPORTED, "K=%d must be <= 32 and <= V", K);
-  const dfl::TopkPlan pl = dfl::plan_topk(N, V, K);
-  DFL_REQUIRE(ws_bytes >= pl.ws_bytes, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.ws_bytes);
+  const size_t need = dfl::topk_ws_bytes(N, V);
+  DFL_REQUIRE(ws_bytes >= need, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
-  hipError_t e = dfl::launch_topk(pl, logits, N, V, K, ids, unary, ws, stream);
+  hipError_t e = dfl::launch_topk(logits, N, V, K, ids, unary, ws, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

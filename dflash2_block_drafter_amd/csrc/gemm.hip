@@ -43,6 +43,7 @@ struct GemmArgs {
   int nsplit;
   float* partial;
   int splits;
+  float* tile_max;  // EPI_F32, one split: [M, gridDim.x] row maxima of each BN-column tile
 };
 
 __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, float v) {
@@ -236,6 +237,34 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
         const int n = ncol + j * 16;
         if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
       }
+  if (p.tile_max) {
+    // Row maxima of this tile over its columns < N: within a lane over its TN columns, then
+    // over the 16 lanes that share a row, then over the WN wavefronts through LDS.  fmaxf
+    // skips NaN, so a tile's maximum is NaN only when all of its values are.
+    __shared__ float rmax[WN][BM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          if (ncol + j * 16 < p.N) v = fmaxf(v, acc[i][j][e]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        if ((lane & 15) == 0) rmax[wn][wm * (TM * 16) + i * 16 + (lane >> 4) * 4 + e] = v;
+      }
+    __syncthreads();
+    for (int r = tid; r < BM; r += NT) {
+      const int m = m0 + r;
+      if (m < p.M) {
+        float v = rmax[0][r];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
+        p.tile_max[(size_t)m * gridDim.x + blockIdx.x] = v;
+      }
+    }
+  }
 }
 
 // Sum of split-K partials in slice order, then the epilogue.  Each thread owns VW adjacent
@@ -270,7 +299,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   for (int e = 0; e < VW; ++e) store_out(p, m, n + e, v[e]);
 }
 
-constexpr int kBM = 128, kBN = 256, kMaxSplits = 8;
+constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
 
 __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ src, int N, int K,
@@ -318,8 +347,10 @@ GemmPlan plan_gemm(int M, int N, int K) {
 
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
-                       float* partial, hipStream_t stream) {
+                       float* partial, hipStream_t stream, float* tile_max) {
+  if (tile_max && (epi != EPI_F32 || pl.splits != 1)) return hipErrorInvalidValue;
   GemmArgs p;
+  p.tile_max = tile_max;
   p.A = A;
   p.W = W;
   p.lda = lda;
@@ -356,6 +387,7 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uin
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
                                 bool w_tiled, int M, int N, int K, float* partial, hipStream_t stream) {
   GemmArgs p;
+  p.tile_max = nullptr;
   p.A = A;
   p.W = W;
   p.lda = lda;

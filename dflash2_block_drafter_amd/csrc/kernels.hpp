@@ -31,9 +31,12 @@ GemmPlan plan_gemm(int M, int N, int K);
 // written by launch_tile_weights.  EPI_BF16: out0 bf16 (ld0).  EPI_F32: columns < nsplit
 // to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL: W rows
 // interleaved per 16 as [gate|up]; out0 bf16 [M, N/2] = silu(gate) * up.
+// tile_max (EPI_F32 with an unsplit plan only): also write the row maxima of every
+// kGemmTileN-column tile, [M, ceil(N / kGemmTileN)].
+constexpr int kGemmTileN = 256;
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
-                       int nsplit, float* partial, hipStream_t stream);
+                       int nsplit, float* partial, hipStream_t stream, float* tile_max = nullptr);
 // y = A . W^T left as fp32 planes for the consumer: pl.splits planes [M, N] at plane stride
 // M*N in `partial` (one plane, the plain result, when the plan does not split K).
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
@@ -107,14 +110,16 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
                             int D, int Lmax, uint16_t* out, int ldo, void* ws,
                             hipStream_t stream);
 
-struct TopkPlan {
-  int chunk = 0;    // elements per stage-1 wave
-  int nchunks = 0;  // chunks per row
-  size_t ws_bytes = 0;
-};
-TopkPlan plan_topk(int N, int V, int K);
-hipError_t launch_topk(const TopkPlan& pl, const float* logits, int N, int V, int K,
-                       int32_t* ids, float* vals, void* ws, hipStream_t stream);
+// Top-K of each row guided by its tile maxima ([N, ceil(V / kGemmTileN)], as launch_gemm's
+// tile_max writes them): only tiles whose maximum reaches the K-th largest tile maximum
+// are read.
+hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
+                             int32_t* ids, float* vals, hipStream_t stream);
+// Exact top-K of each fp32 row (value descending, id ascending): tile maxima into ws
+// (topk_ws_bytes), then launch_topk_tiles.
+size_t topk_ws_bytes(int N, int V);
+hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, float* vals, void* ws,
+                       hipStream_t stream);
 
 hipError_t launch_score_edges(const int32_t* cand, const float* unary, const float* z,
                               const int32_t* anchors, int B, int S, int K, int R,

@@ -1,207 +1,184 @@
 // Candidate selector (MAX dflash2_qwen3_5: `compute_candidates`, `DFlash2CandidateSelector.
 // score_edges` and `select_path`; dflash2.ts diff: `#select`).
 //
-// Top-k (value descending, id ascending) runs in two stages.  Stage 1: one wavefront per
-// 4096-logit chunk of a row holds 64 values per lane; the K-th largest of the 64 lane
-// maxima is a value at least K chunk elements reach, so only elements >= it can be in the
-// chunk's top K.  Those few candidates are merged into a running top-K list with a
-// 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes K..63 take new candidates).
-// Stage 2 merges the per-chunk lists of a row the same way.  Ties on equal values are
-// ordered by id, so the result is exact and unique for any input, including constant rows.
+// Top-k (value descending, id ascending) is guided by the row maxima of 256-column tiles,
+// which the head projection writes with its logits (a separate pass computes them for
+// logits from elsewhere).  theta, the K-th largest tile maximum, is reached by K distinct
+// logits, so every top-K logit is >= theta and sits in a tile whose maximum is >= theta;
+// only those tiles are read (usually K of a row's V/256).  Their values are merged into a
+// running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes K..63
+// take new candidates).  Ties are ordered by id, so the result is exact and unique for any
+// input, including constant rows (where every tile qualifies).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace dfl {
 
 namespace {
 
-constexpr int kChunk = 4096;       // logits per stage-1 wavefront (64 lanes x 64 values)
-constexpr int kPerLane = kChunk / 64;
-constexpr int kNoId = 0x7FFFFFFF;
-
-// a precedes b in the candidate order
-__device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-// Sort (v, id) across the 64 lanes into the candidate order (lane 0 first).
-__device__ __forceinline__ void wave_bitonic_sort(float& v, int& id, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float ov = __shfl_xor(v, j, 64);
-      const int oi = __shfl_xor(id, j, 64);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0;  // this run ends in candidate order
-      // pair (lo, hi): in a candidate-order run lo must precede hi, otherwise hi precedes lo
-      const float lov = lower ? v : ov, hiv = lower ? ov : v;
-      const int loi = lower ? id : oi, hii = lower ? oi : id;
-      const bool swap = desc ? before(hiv, hii, lov, loi) : before(lov, loi, hiv, hii);
-      if (swap) {
-        v = ov;
-        id = oi;
-      }
-    }
-  }
-}
-
-// Running top-K list in lanes 0..K-1; candidates are staged in `stage` (64 - K slots) and
-// merged by one sort when the stage fills.
-struct TopkMerger {
-  float v;
-  int id;
-  int pending;
-  int K;
-  int lane;
-  float* sv;
-  int* si;
-
-  __device__ void init(int K_, int lane_, float* sv_, int* si_) {
-    K = K_;
-    lane = lane_;
-    sv = sv_;
-    si = si_;
-    v = -INFINITY;
-    id = kNoId;
-    pending = 0;
-  }
-  __device__ void flush() {
-    if (pending == 0) return;
-    __builtin_amdgcn_wave_barrier();
-    if (lane >= K) {
-      const int s = lane - K;
-      if (s < pending) {
-        v = sv[s];
-        id = si[s];
-      } else {
-        v = -INFINITY;
-        id = kNoId;
-      }
-    }
-    wave_bitonic_sort(v, id, lane);
-    pending = 0;
-    __builtin_amdgcn_wave_barrier();
-  }
-  // every lane offers (cv, cid) when take is true
-  __device__ void offer(bool take, float cv, int cid) {
-    uint64_t mask = __ballot(take);
-    const int cap = 64 - K;
-    while (mask) {
-      const int n = __popcll(mask);
-      const int room = cap - pending;
-      if (room == 0) {
-        flush();
-        continue;
-      }
-      // lanes whose rank among the remaining set bits is < room write this round
-      const uint64_t below = mask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane)));
-      const int rank = __popcll(below);
-      const bool mine = (mask >> lane) & 1ull;
-      if (mine && rank < room) {
-        sv[pending + rank] = cv;
-        si[pending + rank] = cid;
-      }
-      const int taken = n < room ? n : room;
-      pending += taken;
-      // clear the bits just written (the lowest `taken` set bits)
-      for (int i = 0; i < taken; ++i) mask &= mask - 1;
-      if (pending == cap) flush();
-    }
-  }
-};
-
-// Stage 1: each wavefront reduces one chunk of one row to its top K.
-__global__ __launch_bounds__(256) void topk_stage1_kernel(const float* __restrict__ logits, int V,
-                                                          int K, int nchunks,
-                                                          float* __restrict__ pv,
-                                                          int* __restrict__ pi) {
-  __shared__ float sv[4][64];
-  __shared__ int si[4][64];
+// Row maxima of every kGemmTileN-column tile of fp32 logits (the values the head projection
+// writes alongside its logits): one wavefront per (tile, row), kGemmTileN/64 values per lane.
+__global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restrict__ logits, int V, int ntiles,
+                                                          float* __restrict__ tile_max) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int row = blockIdx.y;
-  if (chunk >= nchunks) return;
+  if (t >= ntiles) return;
   const float* src = logits + (size_t)row * V;
-  const int base = chunk * kChunk;
-  float x[kPerLane];
-  const bool full = base + kChunk <= V && (V & 3) == 0;
-  if (full) {
+  float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kPerLane / 4; ++j) {
-      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(src + base + j * 256 + lane * 4);
-      x[4 * j] = q[0];
-      x[4 * j + 1] = q[1];
-      x[4 * j + 2] = q[2];
-      x[4 * j + 3] = q[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerLane / 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = base + j * 256 + lane * 4 + e;
-        x[4 * j + e] = idx < V ? src[idx] : -INFINITY;
-      }
+  for (int q = 0; q < kGemmTileN / 64; ++q) {
+    const int col = t * kGemmTileN + q * 64 + lane;
+    if (col < V) m = fmaxf(m, src[col]);
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) mx = fmaxf(mx, x[i]);
-  // K-th largest lane maximum
-  float sm = mx;
-  int sid = lane;
-  wave_bitonic_sort(sm, sid, lane);
-  const float theta = __shfl(sm, K - 1, 64);
-
-  TopkMerger mg;
-  mg.init(K, lane, sv[wave], si[wave]);
-#pragma unroll
-  for (int j = 0; j < kPerLane / 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float val = x[4 * j + e];
-      const int idx = base + j * 256 + lane * 4 + e;
-      const bool take = val >= theta && idx < V;
-      if (__ballot(take)) mg.offer(take, val, idx);
-    }
-  mg.flush();
-  if (lane < K) {
-    const size_t o = ((size_t)row * nchunks + chunk) * K + lane;
-    pv[o] = mg.v;
-    pi[o] = mg.id;
-  }
+  m = wave_max(m);
+  if (lane == 0) tile_max[(size_t)row * ntiles + t] = m;
 }
 
-// Stage 2: one wavefront merges a row's nchunks lists.
-__global__ __launch_bounds__(64) void topk_stage2_kernel(const float* __restrict__ pv,
-                                                         const int* __restrict__ pi, int K,
-                                                         int nchunks, int32_t* __restrict__ ids,
-                                                         float* __restrict__ vals) {
-  __shared__ float sv[64];
-  __shared__ int si[64];
-  const int lane = threadIdx.x;
-  const int row = blockIdx.x;
-  const int n = nchunks * K;
-  const float* rv = pv + (size_t)row * n;
-  const int* ri = pi + (size_t)row * n;
-  TopkMerger mg;
-  mg.init(K, lane, sv, si);
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    float cv = -INFINITY;
-    int ci = kNoId;
-    if (i < n) {
-      cv = rv[i];
-      ci = ri[i];
-    }
-    // the running list is sorted: its K-th entry bounds what can still enter
+// Top-K of a row from its tile maxima (tiles of kGemmTileN columns).  theta, the K-th
+// largest tile maximum in candidate order, is a value that K distinct logits reach, so
+// every top-K logit is >= theta and lies in a tile whose maximum is >= theta: only those
+// tiles (ties included) are scanned.  One workgroup of four wavefronts per row.  Tile
+// maxima are read 64 * kTmPerLane at a time into registers (one round of loads); the four
+// wavefronts each merge a quarter of them and wavefront 0 merges the four lists into theta;
+// then the qualifying tiles are listed in LDS, each wavefront loads kTilesInFlight of them
+// at once into its own list, and wavefront 0 merges the four candidate lists.
+constexpr int kTmPerLane = 16;
+constexpr int kTilesInFlight = 4;
+
+// Merge lanes 0..K-1 of the other three wavefronts' lists (lv/li) into wavefront 0's list.
+__device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*lv)[64], const int (*li)[64],
+                                                 int K, int lane) {
+  for (int w = 1; w < 4; ++w) {
+    const float cv = lv[w][lane];
+    const int ci = li[w][lane];
     const float kth = __shfl(mg.v, K - 1, 64);
     const int kthi = __shfl(mg.id, K - 1, 64);
-    const bool take = i < n && ci != kNoId && before(cv, ci, kth, kthi);
+    const bool take = lane < K && ci != kNoId && before(cv, ci, kth, kthi);
     if (__ballot(take)) mg.offer(take, cv, ci);
   }
   mg.flush();
+}
+
+__global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict__ logits, int V,
+                                                         const float* __restrict__ tile_max, int ntiles,
+                                                         int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ vals) {
+  constexpr int TW = kGemmTileN;
+  constexpr int TPL = TW / 64;                 // values of a tile per lane
+  constexpr int CH = 64 * kTmPerLane;          // tile maxima per round
+  __shared__ float sv[4][64];
+  __shared__ int si[4][64];
+  __shared__ float lv[4][64];
+  __shared__ int li[4][64];
+  __shared__ int tl[CH];                       // qualifying tiles of the current round
+  __shared__ float theta_s;
+  __shared__ int tcount;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;
+  const float* tm = tile_max + (size_t)row * ntiles;
+  const float* src = logits + (size_t)row * V;
+  TopkMerger mg;
+
+  // theta: the K-th largest tile maximum; wavefront w merges slots w, w+4, w+8, ... of a round
+  mg.init(K, lane, sv[wave], si[wave]);
+  for (int c0 = 0; c0 < ntiles; c0 += CH) {
+    float t[kTmPerLane / 4];
+#pragma unroll
+    for (int j = 0; j < kTmPerLane / 4; ++j) {
+      const int i = c0 + (j * 4 + wave) * 64 + lane;
+      t[j] = i < ntiles ? tm[i] : -INFINITY;
+    }
+    // floor: the K-th largest lane maximum, reached by K of this round's values, so only
+    // values >= it are offered (a handful, instead of a whole first batch)
+    float lm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kTmPerLane / 4; ++j) lm = fmaxf(lm, t[j]);
+    int lid = lane;
+    wave_bitonic_sort(lm, lid, lane);
+    const float floor_v = __shfl(lm, K - 1, 64);
+#pragma unroll
+    for (int j = 0; j < kTmPerLane / 4; ++j) {
+      const int i = c0 + (j * 4 + wave) * 64 + lane;
+      const float kth = __shfl(mg.v, K - 1, 64);
+      const int kthi = __shfl(mg.id, K - 1, 64);
+      const bool take = i < ntiles && t[j] >= floor_v && before(t[j], i, kth, kthi);
+      if (__ballot(take)) mg.offer(take, t[j], i);
+    }
+  }
+  mg.flush();
+  lv[wave][lane] = mg.v;
+  li[wave][lane] = mg.id;
+  __syncthreads();
+  if (wave == 0) {
+    merge_wave_lists(mg, lv, li, K, lane);
+    const float th = __shfl(mg.v, K - 1, 64);  // -inf when fewer than K tiles
+    if (lane == 0) theta_s = th;              // (the shuffle itself runs on every lane)
+  }
+  __syncthreads();
+  const float theta = theta_s;
+
+  // scan the qualifying tiles: per round wavefront 0 lists them in LDS, then wavefront w
+  // takes list entries [w*F, w*F + F), [w*F + 4F, ...), F = kTilesInFlight at a time
+  mg.init(K, lane, sv[wave], si[wave]);
+  for (int c0 = 0; c0 < ntiles; c0 += CH) {
+    if (wave == 0) {
+      float t[kTmPerLane];
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) {
+        const int i = c0 + j * 64 + lane;
+        t[j] = i < ntiles ? tm[i] : -INFINITY;
+      }
+      int cnt = 0;
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) {
+        const int i = c0 + j * 64 + lane;
+        const bool q = i < ntiles && t[j] >= theta;
+        const uint64_t mask = __ballot(q);
+        if (q) tl[cnt + __popcll(mask & below)] = i;
+        cnt += __popcll(mask);
+      }
+      if (lane == 0) tcount = cnt;
+    }
+    __syncthreads();
+    const int cnt = tcount;
+    for (int b0 = wave * kTilesInFlight; b0 < cnt; b0 += 4 * kTilesInFlight) {
+      const int n = min(kTilesInFlight, cnt - b0);
+      int tile[kTilesInFlight];
+      float x[kTilesInFlight][TPL];
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q) tile[q] = tl[b0 + min(q, n - 1)];
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q)
+#pragma unroll
+        for (int e = 0; e < TPL; ++e) {
+          const int col = tile[q] * TW + e * 64 + lane;
+          x[q][e] = col < V ? src[col] : -INFINITY;
+        }
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q)
+#pragma unroll
+        for (int e = 0; e < TPL; ++e) {
+          const int col = tile[q] * TW + e * 64 + lane;
+          const float kth = __shfl(mg.v, K - 1, 64);
+          const int kthi = __shfl(mg.id, K - 1, 64);
+          // q >= n: a repeat of the last tile (n < F), not offered twice; below theta a
+          // value cannot be in the top K
+          const bool take = q < n && col < V && x[q][e] >= theta && before(x[q][e], col, kth, kthi);
+          if (__ballot(take)) mg.offer(take, x[q][e], col);
+        }
+    }
+    __syncthreads();  // tl is rewritten next round
+  }
+  mg.flush();
+  lv[wave][lane] = mg.v;
+  li[wave][lane] = mg.id;
+  __syncthreads();
+  if (wave != 0) return;
+  merge_wave_lists(mg, lv, li, K, lane);
   if (lane < K) {
     ids[(size_t)row * K + lane] = mg.id;
     vals[(size_t)row * K + lane] = mg.v;
@@ -272,23 +249,26 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
 
 }  // namespace
 
-TopkPlan plan_topk(int N, int V, int K) {
-  TopkPlan pl;
-  pl.chunk = kChunk;
-  pl.nchunks = (V + kChunk - 1) / kChunk;
-  const size_t entries = (size_t)N * pl.nchunks * K;
-  pl.ws_bytes = entries * (sizeof(float) + sizeof(int));
-  return pl;
+size_t topk_ws_bytes(int N, int V) {
+  return (size_t)N * ((V + kGemmTileN - 1) / kGemmTileN) * sizeof(float);
 }
 
-hipError_t launch_topk(const TopkPlan& pl, const float* logits, int N, int V, int K,
-                       int32_t* ids, float* vals, void* ws, hipStream_t stream) {
+hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, float* vals, void* ws,
+                       hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  float* pv = static_cast<float*>(ws);
-  int* pi = reinterpret_cast<int*>(pv + (size_t)N * pl.nchunks * K);
-  dim3 g1((pl.nchunks + 3) / 4, N);
-  topk_stage1_kernel<<<g1, 256, 0, stream>>>(logits, V, K, pl.nchunks, pv, pi);
-  topk_stage2_kernel<<<N, 64, 0, stream>>>(pv, pi, K, pl.nchunks, ids, vals);
+  const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
+  float* tmax = static_cast<float*>(ws);
+  tile_rowmax_kernel<<<dim3((ntiles + 3) / 4, N), 256, 0, stream>>>(logits, V, ntiles, tmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_tiles(logits, N, V, K, tmax, ids, vals, stream);
+}
+
+hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
+                             int32_t* ids, float* vals, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
+  topk_tiles_kernel<<<N, 256, 0, stream>>>(logits, V, tile_max, ntiles, K, ids, vals);
   return hipGetLastError();
 }
 

@@ -206,7 +206,9 @@ int dfl_conv_finish(const dfl_bf16* y, const float* coef1, const dfl_bf16* base,
                     int G, int grp, const dfl_bf16* residual, dfl_bf16* out, hipStream_t stream);
 
 /* Top-k of each row of fp32 logits ([P3] `compute_candidates`; [P2] `#select`), listed by
- * value descending then id ascending.  logits [N, V]; ids int32 [N, K]; unary fp32 [N, K]. */
+ * value descending then id ascending.  logits [N, V]; ids int32 [N, K]; unary fp32 [N, K];
+ * 1 <= K <= min(32, V).  ws: dfl_candidates_workspace_bytes, one fp32 row maximum per
+ * 256-column tile (the top-k reads only the tiles whose maximum can hold a candidate). */
 size_t dfl_candidates_workspace_bytes(int N, int V, int K);
 int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* ids, float* unary,
                            void* ws, size_t ws_bytes, hipStream_t stream);

@@ -156,6 +156,9 @@ def test_conv_block_boundary_on_gpu():
     (4, 9001, 16, "ties"),         # V not a multiple of 4, many equal values
     (2, 5000, 16, "constant"),     # every value equal: ids 0..K-1
     (3, 70, 32, "normal"),         # fewer elements than a chunk, K = 32
+    (4, 248320, 16, "hot_tile"),   # every candidate inside one 256-column tile
+    (3, 10000, 16, "hot_last"),    # maxima in the ragged last tile
+    (3, 5000, 16, "neg_inf"),      # most of each row -inf: fewer finite tiles than K
 ])
 def test_compute_candidates_bitexact(N, V, K, kind):
     g = torch.Generator(device=DEV).manual_seed(71)
@@ -163,6 +166,18 @@ def test_compute_candidates_bitexact(N, V, K, kind):
         logits = torch.randn((N, V), generator=g, device=DEV) * 3
     elif kind == "ties":
         logits = torch.randint(-4, 5, (N, V), generator=g, device=DEV).float()
+    elif kind == "hot_tile":
+        logits = torch.randn((N, V), generator=g, device=DEV)
+        for r in range(N):
+            t = 37 * (r + 1) % (V // 256)
+            logits[r, t * 256:(t + 1) * 256] += 20.0
+    elif kind == "hot_last":
+        logits = torch.randn((N, V), generator=g, device=DEV)
+        logits[:, (V // 256) * 256:] += 20.0
+    elif kind == "neg_inf":
+        logits = torch.full((N, V), float("-inf"), device=DEV)
+        logits[:, 300:310] = torch.randn((N, 10), generator=g, device=DEV)
+        logits[:, 4000:4003] = 1.5
     else:
         logits = torch.full((N, V), 0.25, device=DEV)
     ids = torch.empty((N, K), dtype=torch.int32, device=DEV)
