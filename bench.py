@@ -31,7 +31,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="full", choices=["full", "long", "tiny"])
+    p.add_argument("--workload", default="full", choices=["full", "long", "tiny", "conv", "selector"],
+                   help="full/long/tiny: draft_block; conv, selector: the grouped-conv and "
+                        "candidate-selector microbenchmarks")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB copy (counter calibration) and exit")
@@ -64,6 +66,10 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in ("conv", "selector"):
+        (bench_conv if args.workload == "conv" else bench_selector)(args)
+        return
 
     import numpy as np
     import torch
@@ -140,11 +146,21 @@ def main():
 
     launch_ms = ms_dom / n_dom
     bytes_per_launch = by_dom / n_dom
-    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
-    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
-                "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    flops = gemm_flops(dominant, d, Bq, G)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+    if flops is not None and flops / bytes_per_launch > ridge:
+        # a projection with more flops per byte than the ridge is bounded by the matrix cores
+        achieved = flops / (launch_ms * 1e-3) / 1e12
+        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
+                    "algorithmic_flops_per_launch": int(flops), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    else:
+        achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
+                    "algorithmic_bytes_per_launch": int(bytes_per_launch)}
 
     def frac(cls):
         b = breakdown.get(cls)
@@ -186,6 +202,121 @@ def main():
     }
     print(json.dumps(out), flush=True)
     dr.close()
+
+
+def gemm_flops(cls: str, d, Bq: int, G: int):
+    """Dense flops of one launch of a projection class (None for other classes)."""
+    T, N = Bq * G, Bq * (G - 1)
+    H, F, D = d.hidden, d.intermediate, d.head_dim
+    ng = H // d.conv_group
+    shapes = {"gemm_head": (N, d.vocab, H), "gemm_gateup": (T, 2 * F, H), "gemm_down": (T, H, F),
+              "gemm_qkv": (T, (d.heads + 2 * d.kv_heads) * D, H), "gemm_o": (T, H, d.heads * D),
+              "gemm_kproj": (T, 4 * ng, H), "gemm_selproj": (N, d.rank, H)}
+    if cls not in shapes:
+        return None
+    m, n, k = shapes[cls]
+    return 2.0 * m * n * k
+
+
+def _time_calls(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per call of fn (which enqueues on torch's current stream),
+    bracketed by HIP events on that stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_conv(args):
+    """Grouped conv microbenchmark: T = 64 blocks of 16 rows, H = 5120, groups of 16.
+    Timed: one conv application (dfl_conv_finish: the conv kernel alone, side-1 deltas
+    given) and the kernel projection GEMM (dfl_linear, fp32 out)."""
+    import torch
+    from dflash2_block_drafter_amd import binding as B_
+    from dflash2_block_drafter_amd import configs, synth
+    c = configs.CONV_BENCH
+    T, H, G, grp = c["T"], c["hidden"], c["block"], c["group"]
+    ng = H // grp
+    inp = synth.conv_inputs(T, H, grp, c["seed"], device="cuda")
+    a = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(a)
+    coef1 = torch.empty((T, 2 * ng), dtype=torch.float32, device="cuda")
+    d = torch.empty((T, 4 * ng), dtype=torch.float32, device="cuda")
+    ws = B_.workspace(max(B_.dfl_conv_prepare_workspace_bytes(T, H, grp), B_.dfl_linear_workspace_bytes(T, 4 * ng, H)))
+    B_.dfl_conv_prepare(inp["x"], T, H, G, grp, inp["kproj"], inp["base"], a, coef1, ws)
+    conv_ms = _time_calls(lambda: B_.dfl_conv_finish(a, coef1, inp["base"], T, H, G, grp, None, y),
+                          args.steps, args.warmup)
+    gemm_ms = _time_calls(lambda: B_.dfl_linear(inp["x"], T, H, H, inp["kproj"], 4 * ng, d, 4 * ng, True, ws),
+                          args.steps, args.warmup)
+    prep_ms = _time_calls(lambda: B_.dfl_conv_prepare(inp["x"], T, H, G, grp, inp["kproj"], inp["base"], a, coef1,
+                                                      ws), args.steps, args.warmup)
+    conv_bytes = 2.0 * T * H + 4.0 * T * 2 * ng + 2.0 * 2 * H + 2.0 * T * H  # y, deltas, base side, out
+    gemm_flop = 2.0 * T * 4 * ng * H
+    achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "grouped conv application time (T=1024 rows in 16-row blocks, H=5120, groups of 16)",
+        "value": round(conv_ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "conv: T=1024 H=5120 G=16 grp=16, kernel projection 5120 -> 1280"},
+        "roofline": {"kernel": "conv_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(conv_bytes)},
+        "kernel_projection_gemm": {"us": round(gemm_ms * 1e3, 2),
+                                   "tflops": round(gemm_flop / (gemm_ms * 1e-3) / 1e12, 1),
+                                   "weight_GBps": round(2.0 * 4 * ng * H / (gemm_ms * 1e-3) / 1e9, 1)},
+        "conv_prepare_us": round(prep_ms * 1e3, 2),
+        "cpu_baseline": None,
+    }), flush=True)
+
+
+def bench_selector(args):
+    """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
+    Timed: compute_candidates + selector_project + score_edges + select_path."""
+    import torch
+    from dflash2_block_drafter_amd import binding as B_
+    from dflash2_block_drafter_amd import configs, synth
+    c = configs.SELECTOR_BENCH
+    Bq, S, H, K, V, R = c["B"], c["S"], c["hidden"], c["top_k"], c["vocab"], c["rank"]
+    N = Bq * S
+    inp = synth.selector_inputs(Bq, S, H, K, V, R, c["seed"], device="cuda")
+    ids = torch.empty((N, K), dtype=torch.int32, device="cuda")
+    unary = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    z = torch.empty((N, R), dtype=torch.float32, device="cuda")
+    scores = torch.empty((Bq, S, K, K), dtype=torch.float32, device="cuda")
+    tokens = torch.empty((Bq, S), dtype=torch.int32, device="cuda")
+    ws_c = B_.workspace(B_.dfl_candidates_workspace_bytes(N, V, K))
+    ws_p = B_.workspace(B_.dfl_selector_project_workspace_bytes(N, H, R))
+    logits = inp["logits"].reshape(N, V)
+    hidden = inp["hidden"].reshape(N, H)
+
+    def chain():
+        B_.dfl_compute_candidates(logits, N, V, K, ids, unary, ws_c)
+        B_.dfl_selector_project(hidden, N, H, inp["proj"], R, z, ws_p)
+        B_.dfl_score_edges(ids, unary, z, inp["anchors"], Bq, S, K, R, inp["pred"], inp["succ"], V, scores)
+        B_.dfl_select_path(scores, ids, Bq, S, K, tokens)
+
+    ms = _time_calls(chain, args.steps, args.warmup)
+    topk_ms = _time_calls(lambda: B_.dfl_compute_candidates(logits, N, V, K, ids, unary, ws_c), args.steps, args.warmup)
+    total_bytes = 4.0 * N * V + 2.0 * N * H + 2.0 * R * H + 4.0 * N * R + 2.0 * 2 * N * K * R + 4.0 * N * K * K
+    achieved = total_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "candidate selector time (B=32, S=15, V=248320, K=16, R=64): top-k + projection + edges + walk",
+        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16"},
+        "roofline": {"kernel": "selector chain", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},
+        "compute_candidates_us": round(topk_ms * 1e3, 2),
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def cpu_baseline(w, weights, tgt, budget_s: float = 10.0):

@@ -719,6 +719,7 @@ int dfl_conv_prepare(const dfl_bf16* x, int T, int H, int G, int grp, const dfl_
                      dfl_bf16* out, float* coef1, void* ws, size_t ws_bytes, hipStream_t stream) {
   DFL_REQUIRE(x && kproj && base && out && coef1 && ws, DFL_E_INVALID, "NULL argument");
   DFL_TRY(check_conv(T, H, G, grp));
+  DFL_REQUIRE(x != out, DFL_E_INVALID, "x must not alias out");
   DFL_REQUIRE(H % 64 == 0, DFL_E_UNSUPPORTED, "H must be a multiple of 64");
   DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
   const size_t need = dfl_conv_prepare_workspace_bytes(T, H, grp);

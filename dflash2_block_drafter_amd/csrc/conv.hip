@@ -56,33 +56,63 @@ __device__ __forceinline__ void conv8(const ConvIn& in, float d0, float d1, floa
   for (int e = 0; e < 8; ++e) o[e] = (b0[e] + d0) * cur[e] + (b1[e] + d1) * prev[e];
 }
 
-__global__ __launch_bounds__(256) void conv_kernel(const uint16_t* y, Planes coef,
-                                                   const uint16_t* __restrict__ base, int side,
-                                                   int H, int G, int grp,
-                                                   const uint16_t* residual, uint16_t* out) {
-  __shared__ float cs[2 * 256];  // 2048 channels touch at most 256 groups (grp >= 8)
-  const int t = blockIdx.y;
-  const int cb = blockIdx.x * 2048;
+// R consecutive rows of one block (R divides G) for kConvCh channels per workgroup of
+// kConvCh/8 threads: the R + 1 input rows are loaded once (row t-1 of the first row only
+// when it is in the block) and each later row reuses its predecessor from registers.
+constexpr int kConvCh = 1024;
+
+template <int R>
+__global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Planes coef,
+                                                           const uint16_t* __restrict__ base, int side,
+                                                           int H, int G, int grp,
+                                                           const uint16_t* residual, uint16_t* out) {
+  __shared__ float cs[R][2 * (kConvCh / 8)];  // kConvCh channels touch at most kConvCh/8 groups
+  const int t0 = blockIdx.y * R;
+  const int cb = blockIdx.x * kConvCh;
   const int g0 = cb / grp;
-  const int ngw = (min(H, cb + 2048) - 1) / grp - g0 + 1;  // groups touching [cb, cb + 2048)
+  const int ngw = (min(H, cb + kConvCh) - 1) / grp - g0 + 1;  // groups touching [cb, cb + kConvCh)
   const int c0 = cb + threadIdx.x * 8;
   const int cc = min(c0, H - 8);  // threads past H load the last chunk and store nothing
-  const ConvIn in = load_conv_in(y, base + (size_t)(side * 2 + 0) * H, base + (size_t)(side * 2 + 1) * H, t, H,
-                                 t % G != 0, cc);
-  u32x4_t rv = {0u, 0u, 0u, 0u};
-  if (residual) rv = *reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + cc);
-  stage_coef(coef, t, H / grp, g0, ngw, cs);
+  const uint16_t* b0p = base + (size_t)(side * 2 + 0) * H;
+  const uint16_t* b1p = base + (size_t)(side * 2 + 1) * H;
+  u32x4_t cur[R + 1], rv[R];
+  cur[0] = t0 % G != 0 ? *reinterpret_cast<const u32x4_t*>(y + (size_t)(t0 - 1) * H + cc) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    cur[r + 1] = *reinterpret_cast<const u32x4_t*>(y + (size_t)(t0 + r) * H + cc);
+    rv[r] = residual ? *reinterpret_cast<const u32x4_t*>(residual + (size_t)(t0 + r) * H + cc) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  const u32x4_t b0v = *reinterpret_cast<const u32x4_t*>(b0p + cc);
+  const u32x4_t b1v = *reinterpret_cast<const u32x4_t*>(b1p + cc);
+  const int ng = H / grp;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t crow = (size_t)(t0 + r) * coef.ld;
+    for (int i = threadIdx.x; i < 2 * ngw; i += blockDim.x) {
+      const int col = i < ngw ? g0 + i : ng + g0 + (i - ngw);
+      cs[r][i] = planes_sum1(coef, crow + col);
+    }
+  }
+  __syncthreads();
   if (c0 >= H) return;
   const int gl = c0 / grp - g0;
-  float o[8];
-  conv8(in, cs[gl], cs[ngw + gl], o);
-  if (residual) {
-    float r[8];
-    unpack8(rv, r);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = r[e] + o[e];
+  for (int r = 0; r < R; ++r) {
+    ConvIn in;
+    in.cur = cur[r + 1];
+    in.prev = cur[r];  // row t0 + r - 1: zero at a block start (R divides G, so only r = 0 can be one)
+    in.b0 = b0v;
+    in.b1 = b1v;
+    float o[8];
+    conv8(in, cs[r][gl], cs[r][ngw + gl], o);
+    if (residual) {
+      float rr[8];
+      unpack8(rv[r], rr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rr[e] + o[e];
+    }
+    *reinterpret_cast<u32x4_t*>(out + (size_t)(t0 + r) * H + c0) = pack8(o);
   }
-  *reinterpret_cast<u32x4_t*>(out + (size_t)t * H + c0) = pack8(o);
 }
 
 // conv finish + residual + the next sublayer's RMSNorm, one workgroup per row: the row's
@@ -177,8 +207,26 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
 hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* base, int side, int T, int H, int G,
                        int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((H / 8 + 255) / 256, T);
-  conv_kernel<<<grid, 256, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+  // rows per workgroup: the largest of 4, 2, 1 dividing G that still leaves >= 512 workgroups
+  const int chunks = (H + kConvCh - 1) / kConvCh;
+  int R = 1;
+  for (int r : {4, 2}) {
+    if (G % r == 0 && T % r == 0 && (long)chunks * (T / r) >= 512) {
+      R = r;
+      break;
+    }
+  }
+  const dim3 grid(chunks, T / R);
+  switch (R) {
+    case 4:
+      conv_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+      break;
+    case 2:
+      conv_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+      break;
+    default:
+      conv_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+  }
   return hipGetLastError();
 }
 

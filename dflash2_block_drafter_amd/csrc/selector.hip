@@ -18,22 +18,49 @@ namespace dfl {
 namespace {
 
 // Row maxima of every kGemmTileN-column tile of fp32 logits (the values the head projection
-// writes alongside its logits): one wavefront per (tile, row), kGemmTileN/64 values per lane.
+// writes alongside its logits).  A quarter-wavefront (16 lanes, 4 x float4 each) covers one
+// tile; a wavefront takes kRowmaxTiles consecutive tiles of a row, so each lane has
+// kRowmaxTiles/4 x 4 float4 loads in flight before any reduction.
+constexpr int kRowmaxTiles = 16;
+
 __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restrict__ logits, int V, int ntiles,
                                                           float* __restrict__ tile_max) {
+  constexpr int TQ = kGemmTileN / 64;  // float4 per lane per tile (16 lanes per tile)
+  constexpr int PASS = kRowmaxTiles / 4;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int q = lane >> 4;     // which of the wavefront's 4 tiles in a pass
+  const int l16 = lane & 15;
+  const int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowmaxTiles;
   const int row = blockIdx.y;
-  if (t >= ntiles) return;
+  if (t0 >= ntiles) return;
   const float* src = logits + (size_t)row * V;
-  float m = -INFINITY;
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  float m[PASS];
 #pragma unroll
-  for (int q = 0; q < kGemmTileN / 64; ++q) {
-    const int col = t * kGemmTileN + q * 64 + lane;
-    if (col < V) m = fmaxf(m, src[col]);
+  for (int p = 0; p < PASS; ++p) {
+    const int t = t0 + p * 4 + q;
+    float acc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      const int col = t * kGemmTileN + j * 64 + l16 * 4;
+      if (vec && col + 4 <= V) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + col);
+        acc = fmaxf(acc, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < V) acc = fmaxf(acc, src[col + e]);
+      }
+    }
+    m[p] = acc;
   }
-  m = wave_max(m);
-  if (lane == 0) tile_max[(size_t)row * ntiles + t] = m;
+#pragma unroll
+  for (int p = 0; p < PASS; ++p) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m[p] = fmaxf(m[p], __shfl_xor(m[p], o, 64));
+    const int t = t0 + p * 4 + q;
+    if (l16 == 0 && t < ntiles) tile_max[(size_t)row * ntiles + t] = m[p];
+  }
 }
 
 // Top-K of a row from its tile maxima (tiles of kGemmTileN columns).  theta, the K-th
@@ -258,7 +285,8 @@ hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, f
   if (N <= 0) return hipSuccess;
   const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
   float* tmax = static_cast<float*>(ws);
-  tile_rowmax_kernel<<<dim3((ntiles + 3) / 4, N), 256, 0, stream>>>(logits, V, ntiles, tmax);
+  const int waves = (ntiles + kRowmaxTiles - 1) / kRowmaxTiles;
+  tile_rowmax_kernel<<<dim3((waves + 3) / 4, N), 256, 0, stream>>>(logits, V, ntiles, tmax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_tiles(logits, N, V, K, tmax, ids, vals, stream);
