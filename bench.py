@@ -109,6 +109,9 @@ def main():
 
     ws = dr.workspace(Bq, G, L)
     tokens = torch.empty((Bq, G - 1), dtype=torch.int32, device=dev)
+    # the target's head is bound once (copied to the tile-contiguous layout), as a serving
+    # loop binds its target before drafting; every step still streams all of it
+    dr.bind_target(tgt["lm_head"])
 
     def step():
         dr.draft(tgt["embeds"], tgt["anchors"], K, V, L, tgt["ctx_len"], tgt["pos0"], tgt["lm_head"],

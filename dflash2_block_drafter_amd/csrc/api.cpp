@@ -76,6 +76,8 @@ struct dfl_drafter {
   void* arena = nullptr;
   uint16_t *fc, *hidden_norm, *norm, *sel_proj, *pred, *succ;
   std::vector<LayerBuf> layers;
+  uint16_t* head = nullptr;          // the bound target head, tile-contiguous (dfl_bind_target)
+  const void* head_src = nullptr;    // the caller pointer it was copied from
   int timed_class = DFL_K_NONE;
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> pool;
@@ -478,7 +480,32 @@ void dfl_drafter_free(dfl_drafter* d) {
   }
   for (auto e : d->pool) (void)hipEventDestroy(e);
   if (d->arena) (void)hipFree(d->arena);
+  if (d->head) (void)hipFree(d->head);
   delete d;
+}
+
+int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, hipStream_t stream) {
+  DFL_REQUIRE(d && lm_head, DFL_E_INVALID, "NULL argument");
+  if (d->head_src) {
+    DFL_REQUIRE(d->head_src == lm_head, DFL_E_INVALID, "a different target head is already bound");
+    return DFL_OK;
+  }
+  const int V = d->cfg.vocab, H = d->cfg.hidden;
+  void* buf = nullptr;
+  if (hipMalloc(&buf, dfl::tiled_weight_elems(V, H) * sizeof(uint16_t)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DFL_E_NOMEM, "could not allocate the bound head (%zu bytes)",
+                dfl::tiled_weight_elems(V, H) * sizeof(uint16_t));
+  }
+  hipError_t e = dfl::launch_tile_weights(lm_head, V, H, static_cast<uint16_t*>(buf), stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(buf);
+    return fail(DFL_E_DEVICE, "binding the head: %s", hipGetErrorString(e));
+  }
+  d->head = static_cast<uint16_t*>(buf);
+  d->head_src = lm_head;
+  return DFL_OK;
 }
 
 size_t dfl_context_workspace_bytes(const dfl_drafter* d, int B, int L) {
@@ -538,8 +565,10 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
                     const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
                     int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
-  DFL_REQUIRE(d && embeds && anchors && ctx_len && pos0 && lm_head && tokens && ws, DFL_E_INVALID,
-              "NULL argument");
+  DFL_REQUIRE(d && embeds && anchors && ctx_len && pos0 && tokens && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(lm_head || d->head, DFL_E_INVALID, "lm_head is NULL and no target head is bound");
+  // the bound (tile-contiguous) copy serves a NULL head or the pointer it was bound from
+  const bool bound_head = d->head && (!lm_head || lm_head == d->head_src);
   const dfl_config& c = d->cfg;
   DFL_REQUIRE(B > 0, DFL_E_INVALID, "B must be positive");
   DFL_REQUIRE(G >= 2 && G <= c.block_size, DFL_E_UNSUPPORTED, "G=%d outside [2, block_size=%d]", G, c.block_size);
@@ -586,7 +615,8 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   const bool tiles_fused = p_head.splits == 1;
   float* tmax = f32(lay.tmax);
   DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, V_, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_head, h, H, lm_head, false, N, V_, H, dfl::EPI_F32, logits, V_, nullptr, 0, 0, part, stream,
+    return dfl::launch_gemm(p_head, h, H, bound_head ? d->head : lm_head, bound_head, N, V_, H, dfl::EPI_F32, logits,
+                            V_, nullptr, 0, 0, part, stream,
                             tiles_fused ? tmax : nullptr);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {

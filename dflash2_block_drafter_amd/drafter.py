@@ -24,6 +24,11 @@ class Drafter:
         except Exception:
             pass
 
+    def bind_target(self, lm_head: torch.Tensor):
+        """Copy the target's head once into the drafter's tile-contiguous layout; draft()
+        then accepts lm_head=None (or the same tensor) and streams the copy."""
+        B_.dfl_bind_target(self.handle, lm_head)
+
     def alloc_kv(self, B: int, Lcap: int, device="cuda"):
         d = self.dims
         shape = (B, Lcap, d.kv_heads, d.head_dim)

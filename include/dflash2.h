@@ -127,6 +127,15 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
  * Lmax rows. */
 size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
 
+/* Bind the target's head once ([P2] `bindTarget`: the drafter binds to one target; binding
+ * a different one afterwards is an error).  lm_head [V, H] bf16 row-major is copied, once,
+ * into an owned tile-contiguous buffer (tiled_weight layout, about V*H*2 bytes) that the
+ * head projection streams faster than the row-major original; the values are snapshotted,
+ * so later changes to lm_head are not seen.  Synchronises `stream`.  Errors: a second call
+ * with another pointer -> DFL_E_INVALID (the same pointer is a no-op); allocation ->
+ * DFL_E_NOMEM; HIP failure -> DFL_E_DEVICE. */
+int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, hipStream_t stream);
+
 /* One draft block per request ([P2] `#block` then `#select`; [P3] `forward_block`,
  * `compute_candidates`, `score_edges`, `select_path`):
  *   embeds:   [B, G, H] bf16, the target's embedding of [anchor, MASK x (G-1)]
@@ -136,7 +145,8 @@ size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
  *   ctx_len:  [B] int32 device, context rows attended per request (0..Lmax, Lmax <= Lcap);
  *             values outside [0, Lmax] are clamped into it.  Lcap*NKV*D < 2^31 (DFL_E_SHAPE).
  *   pos0:     [B] int32 device, absolute position of block row 0 of each request.
- *   lm_head:  [V, H] bf16, the target's head, borrowed.
+ *   lm_head:  [V, H] bf16, the target's head, borrowed; NULL, or the pointer given to
+ *             dfl_bind_target, selects the bound copy.
  *   tokens:   [B, G-1] int32 device output ([P2] returns the proposals on the device).
  *   logits_out: NULL or [B, G-1, V] float32 device output of the head.
  *   G must satisfy 2 <= G <= block_size ([P3] `supports_zero_draft_rows` is false). */

@@ -76,3 +76,23 @@ def test_tiny_draft_is_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(tokens, t2) and torch.equal(logits, l2)
     dr.close()
+
+
+def test_bound_head_matches_borrowed_head():
+    # binding the target's head (a tile-contiguous copy) changes how the head projection
+    # reads it, not what it computes: tokens and logits are identical bit for bit
+    from dflash2_block_drafter_amd import binding as B_
+    w = configs.with_batch(configs.TINY, 3)
+    dr, _, _, K, V, tokens, logits = _run_tiny(w)
+    tgt = {k: v.to(DEV) for k, v in synth.target_inputs(w).items()}
+    dr.bind_target(tgt["lm_head"])
+    dr.bind_target(tgt["lm_head"])                     # the same head again: a no-op
+    with pytest.raises(B_.DflError) as err:
+        dr.bind_target(tgt["lm_head"].clone())          # a different target: refused
+    assert err.value.code == B_.DFL_E_INVALID
+    for head in (None, tgt["lm_head"]):
+        t2, l2 = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], head,
+                          want_logits=True)
+        torch.cuda.synchronize()
+        assert torch.equal(tokens, t2) and torch.equal(logits, l2)
+    dr.close()

@@ -86,7 +86,8 @@ def test_long_context_layer_matches_oracle():
 
 def test_full_drafter_end_to_end_properties():
     """The full draft block in the bench's launch configuration: every drafted token is a
-    valid id among its slot's top-K head logits, and two runs agree bit for bit."""
+    valid id among its slot's top-K head logits, two runs agree bit for bit, and a run with
+    the target head bound (tile-contiguous copy) agrees with them bit for bit."""
     w = configs.FULL
     d = w.dims
     say("full drafter end to end (B=8, L=2048)")
@@ -100,8 +101,13 @@ def test_full_drafter_end_to_end_properties():
         outs.append(dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
                              tgt["lm_head"], want_logits=True))
     torch.cuda.synchronize()
-    (t1, l1), (t2, l2) = outs
+    dr.bind_target(tgt["lm_head"])   # the bench's setup: the head streamed from the bound copy
+    outs.append(dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
+                         None, want_logits=True))
+    torch.cuda.synchronize()
+    (t1, l1), (t2, l2), (t3, l3) = outs
     assert torch.equal(t1, t2) and torch.equal(l1, l2)
+    assert torch.equal(t1, t3) and torch.equal(l1, l3), "bound head must match the borrowed one bit for bit"
     tok, lg = t1.cpu().numpy(), l1.cpu().numpy()
     assert tok.min() >= 0 and tok.max() < d.vocab
     _drafted_tokens_are_topk(tok, lg, d.top_k)
