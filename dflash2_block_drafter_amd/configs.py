@@ -29,6 +29,8 @@ class DrafterDims:
     rms_eps: float = 1e-6
     rope_theta: float = 1e7
     conv_taps: int = 2
+    sliding_window: int = 0             # 0: every layer attends to all of its context
+    sliding_layers: tuple | None = None # per-layer sliding flags; None: all layers slide
 
     @property
     def groups(self) -> int:
@@ -59,6 +61,10 @@ FULL_DIMS = DrafterDims(hidden=5120, layers=5, heads=32, kv_heads=8, head_dim=12
 
 # Tiny drafter: 1 layer, B=1, G=8, 32 context rows from 2 taps.
 TINY = Workload("tiny", TINY_DIMS, batch=1, ctx_len=32, seed=1)
+# Tiny drafter with a sliding layer followed by a full-attention layer: window of 20
+# positions over 32 context rows, so block row t sees context rows 13 + t .. 31.
+TINY_SW = Workload("tiny_sw", replace(TINY_DIMS, layers=2, sliding_window=20, sliding_layers=(True, False)),
+                   batch=2, ctx_len=32, seed=6)
 # Full 5-layer drafter shaped like the 27B-target drafter: B=8, G=16, L=2048.
 FULL = Workload("full", FULL_DIMS, batch=8, ctx_len=2048, seed=4)
 # Long context, large batch: B=64, L=8192, context K/V given as N(0,1).

@@ -169,10 +169,16 @@ def conv_finish(y: np.ndarray, deltas1: np.ndarray, base: np.ndarray, block: int
 
 
 def attention(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, k_blk: np.ndarray,
-              v_blk: np.ndarray, ctx_len: np.ndarray) -> np.ndarray:
+              v_blk: np.ndarray, ctx_len: np.ndarray, pos0=None, window: int = 0) -> np.ndarray:
     """Bidirectional block attention over the request's context prefix plus the
-    block's own rows ([P2] header: "bidirectional within the block", no window;
-    `#block` passes the block's k/v to `context.attend` with scale 1/sqrt(D)).
+    block's own rows ([P2] header: "bidirectional within the block"; `#block` passes
+    the block's k/v to `context.attend` with scale 1/sqrt(D)).
+
+    window > 0 is a sliding-attention layer ([P3] `DFlash2Qwen3_5` `layer_types`;
+    [P3] `construct_kv_params`: the drafter's mask reaches back at most the window):
+    block row t of request b sits at position pos0[b] + t and sees context row j
+    (position j) only when j >= pos0[b] + t - window + 1.  The block's own rows are
+    always seen.
 
     q: [B, G, NH, D]; k_ctx, v_ctx: [B, Lcap, NKV, D]; k_blk, v_blk: [B, G, NKV, D];
     ctx_len: [B] context rows used per request.  Returns [B, G, NH, D].
@@ -187,14 +193,29 @@ def attention(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, k_blk: np.nda
         L = int(ctx_len[b])
         keys = np.concatenate([kc[b, :L], kb[b]], axis=0)      # [L+G, NKV, D]
         vals = np.concatenate([vc[b, :L], vb[b]], axis=0)
+        seen = np.ones((G, L + G), dtype=bool)
+        if window > 0:
+            first = int(pos0[b]) + np.arange(G) - window + 1    # first visible context row per block row
+            seen[:, :L] = np.arange(L)[None, :] >= first[:, None]
         for h in range(NH):
             g = h // rep
             s = q[b, :, h, :] @ keys[:, g, :].T / np.sqrt(D)   # [G, L+G]
+            s = np.where(seen, s, -np.inf)
             s = s - s.max(axis=-1, keepdims=True)
             p = np.exp(s)
             p = p / p.sum(axis=-1, keepdims=True)
             out[b, :, h, :] = p @ vals[:, g, :]
     return out
+
+
+def layer_window(dims, i: int) -> int:
+    """Window of layer i: dims.sliding_window for a sliding layer, 0 for full attention
+    ([P3] `layer_types`: None applies the window to every layer)."""
+    w = getattr(dims, "sliding_window", 0) or 0
+    kinds = getattr(dims, "sliding_layers", None)
+    if w <= 0 or (kinds is not None and not kinds[i]):
+        return 0
+    return int(w)
 
 
 def mlp(i: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, bf16_points=False):
@@ -240,7 +261,8 @@ def context_kv(c: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, k_norm: np.ndarr
     return kr, v
 
 
-def block_layer(x: np.ndarray, lw: dict, k_ctx, v_ctx, ctx_len, pos0, dims, bf16_points=False):
+def block_layer(x: np.ndarray, lw: dict, k_ctx, v_ctx, ctx_len, pos0, dims, bf16_points=False,
+                window: int = 0):
     """One drafter layer on the block ([P3] `DFlash2TransformerBlock`: r = x;
     h = norm(r); h = conv.prepare(h); h = attn(h); h = conv.finish(h); r += h;
     the same for the MLP; [P2] `#block`, whose q/k norm precedes RoPE).
@@ -266,7 +288,7 @@ def block_layer(x: np.ndarray, lw: dict, k_ctx, v_ctx, ctx_len, pos0, dims, bf16
     q = rnd(rope_neox(rnd(rms_norm(q, lw["self_attn.q_norm.weight"], eps)), positions, theta))
     k = rnd(rope_neox(rnd(rms_norm(k, lw["self_attn.k_norm.weight"], eps)), positions, theta))
     o = attention(q.reshape(B, G, NH, D), k_ctx, v_ctx, k.reshape(B, G, NKV, D),
-                  v.reshape(B, G, NKV, D), ctx_len)
+                  v.reshape(B, G, NKV, D), ctx_len, pos0, window)
     o = rnd(o.reshape(T, NH * D))
     u = rnd(linear(o, lw["self_attn.o_proj.weight"]))
     xf = x.reshape(T, H) + conv_finish(u, d1, lw["attention_conv.base_kernel"], G, grp)
@@ -310,7 +332,7 @@ def draft_hidden(embeds, weights: dict, k_ctx: list, v_ctx: list, ctx_len, pos0,
     x = as_f64(embeds)
     for i in range(dims.layers):
         x = block_layer(x, layer_weights(weights, i), k_ctx[i], v_ctx[i], ctx_len, pos0, dims,
-                        bf16_points)
+                        bf16_points, layer_window(dims, i))
     return _maybe_round(rms_norm(x[:, 1:, :], weights["norm.weight"], dims.rms_eps), bf16_points)
 
 

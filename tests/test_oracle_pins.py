@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from dflash2_block_drafter_amd import configs
 from oracle import dflash2 as O
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -262,6 +263,50 @@ def test_attention_brute_force_loops(rng):
             z = sum(w)
             want = [sum(w[j] * vals[j][d] for j in range(len(keys))) / z for d in range(D)]
             assert np.allclose(got[0, t, h], want, rtol=1e-12)
+
+
+def test_sliding_window_is_attention_over_the_window(rng):
+    """A sliding layer equals, row by row, plain attention over the context rows its window
+    keeps (the unwindowed oracle above, pinned to the library SDPA, on a sliced context);
+    a window covering every position changes nothing; the library's boolean-mask SDPA
+    gives the same numbers."""
+    B, G, NH, NKV, D, Lcap = 2, 4, 4, 2, 16, 12
+    q = rng.standard_normal((B, G, NH, D))
+    kc, vc = rng.standard_normal((B, Lcap, NKV, D)), rng.standard_normal((B, Lcap, NKV, D))
+    kb, vb = rng.standard_normal((B, G, NKV, D)), rng.standard_normal((B, G, NKV, D))
+    ctx_len = np.array([12, 7])
+    pos0 = np.array([12, 9])                     # block row 0 sits at position pos0 (>= context)
+    window = 6
+    got = O.attention(q, kc, vc, kb, vb, ctx_len, pos0, window)
+    for b in range(B):
+        for t in range(G):
+            first = max(0, int(pos0[b]) + t - window + 1)
+            L = int(ctx_len[b])
+            sl = O.attention(q[b:b + 1], kc[b:b + 1, first:L], vc[b:b + 1, first:L], kb[b:b + 1], vb[b:b + 1],
+                             np.array([max(0, L - first)]))
+            assert np.allclose(got[b, t], sl[0, t], rtol=1e-12, atol=1e-13), (b, t)
+    wide = O.attention(q, kc, vc, kb, vb, ctx_len, pos0, window=int(pos0.max()) + G)
+    assert np.array_equal(wide, O.attention(q, kc, vc, kb, vb, ctx_len))
+    # boolean-mask form through the library
+    rep = NH // NKV
+    for b in range(B):
+        L = int(ctx_len[b])
+        keys = torch.as_tensor(np.concatenate([kc[b, :L], kb[b]], 0)).permute(1, 0, 2).repeat_interleave(rep, 0)
+        vals = torch.as_tensor(np.concatenate([vc[b, :L], vb[b]], 0)).permute(1, 0, 2).repeat_interleave(rep, 0)
+        mask = np.ones((G, L + G), dtype=bool)
+        for t in range(G):
+            mask[t, :L] = np.arange(L) >= int(pos0[b]) + t - window + 1
+        o = torch.nn.functional.scaled_dot_product_attention(torch.as_tensor(q[b]).permute(1, 0, 2), keys, vals,
+                                                             attn_mask=torch.as_tensor(mask))
+        assert np.allclose(got[b], o.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_layer_window_selection():
+    d = configs.TINY_SW.dims
+    assert [O.layer_window(d, i) for i in range(d.layers)] == [20, 0]
+    from dataclasses import replace
+    assert [O.layer_window(replace(d, sliding_layers=None), i) for i in range(d.layers)] == [20, 20]
+    assert [O.layer_window(replace(d, sliding_window=0), i) for i in range(d.layers)] == [0, 0]
 
 
 # ---------------------------------------------------------------- MLP
