@@ -33,7 +33,8 @@ class dfl_config(C.Structure):
                 ("hidden", "layers", "heads", "kv_heads", "head_dim", "intermediate", "n_taps",
                  "block_size", "conv_taps", "conv_group", "top_k", "rank", "vocab")] + \
                [("rms_eps", C.c_float), ("rope_theta", C.c_float),
-                ("tap_layer_ids", C.POINTER(C.c_int32))]
+                ("tap_layer_ids", C.POINTER(C.c_int32)), ("sliding_window", C.c_int32),
+                ("sliding_layers", C.POINTER(C.c_int32))]
 
 
 LAYER_FIELDS = ("input_norm", "post_norm", "q_proj", "k_proj", "v_proj", "o_proj", "q_norm",
@@ -66,8 +67,8 @@ _SIGS = {
     "dfl_linear": (_I, [_P, _I, _I, _I, _P, _I, _P, _I, _I, _P, _Z, _P]),
     "dfl_head_norm_rope": (_I, [_P, _I, _I, _I, _I, _P, _F, _F, _P, _I, _P]),
     "dfl_attention_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
-    "dfl_block_attention": (_I, [_P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _I,
-                                 _P, _Z, _P]),
+    "dfl_block_attention": (_I, [_P, _I, _P, _P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P,
+                                 _I, _P, _Z, _P]),
     "dfl_conv_prepare_workspace_bytes": (_Z, [_I, _I, _I]),
     "dfl_conv_prepare": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "dfl_conv_finish": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
@@ -157,11 +158,16 @@ def make_config(dims, tap_layer_ids=None) -> tuple[dfl_config, object]:
     ids = None
     if tap_layer_ids is not None:
         ids = (C.c_int32 * len(tap_layer_ids))(*tap_layer_ids)
+    kinds = None
+    if getattr(dims, "sliding_layers", None) is not None:
+        kinds = (C.c_int32 * dims.layers)(*[1 if f else 0 for f in dims.sliding_layers])
     cfg = dfl_config(dims.hidden, dims.layers, dims.heads, dims.kv_heads, dims.head_dim,
                      dims.intermediate, dims.n_taps, dims.block_size, dims.conv_taps,
                      dims.conv_group, dims.top_k, dims.rank, dims.vocab, dims.rms_eps,
-                     dims.rope_theta, C.cast(ids, C.POINTER(C.c_int32)) if ids is not None else None)
-    return cfg, ids
+                     dims.rope_theta, C.cast(ids, C.POINTER(C.c_int32)) if ids is not None else None,
+                     int(getattr(dims, "sliding_window", 0) or 0),
+                     C.cast(kinds, C.POINTER(C.c_int32)) if kinds is not None else None)
+    return cfg, (ids, kinds)
 
 
 def dfl_drafter_load(dims, weights: dict, tap_layer_ids=None, stream=None) -> int:
@@ -247,10 +253,10 @@ def dfl_attention_workspace_bytes(B, G, NH, NKV, D, Lmax) -> int:
 
 
 def dfl_block_attention(q, ldq, kb, vb, ldkv, K, V, Lcap, Lmax, ctx_len, B, G, NH, NKV, D, out, ldo, ws,
-                        stream=None):
+                        stream=None, pos0=None, window=0):
     _check(lib().dfl_block_attention(_bf(q), ldq, _bf(kb), _bf(vb), ldkv, _bf(K), _bf(V), Lcap, Lmax,
-                                     _i32(ctx_len), B, G, NH, NKV, D, _bf(out), ldo, _ptr(ws), ws.numel(),
-                                     _stream(stream)))
+                                     _i32(ctx_len), _i32(pos0), int(window), B, G, NH, NKV, D, _bf(out), ldo,
+                                     _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def dfl_conv_prepare_workspace_bytes(T, H, grp) -> int:

@@ -76,6 +76,7 @@ struct dfl_drafter {
   void* arena = nullptr;
   uint16_t *fc, *hidden_norm, *norm, *sel_proj, *pred, *succ;
   std::vector<LayerBuf> layers;
+  std::vector<int> window;           // per layer: 0 = full attention, W = sliding window
   uint16_t* head = nullptr;          // the bound target head, tile-contiguous (dfl_bind_target)
   const void* head_src = nullptr;    // the caller pointer it was copied from
   int timed_class = DFL_K_NONE;
@@ -154,6 +155,7 @@ int check_config(const dfl_config* c) {
               "block_size x heads/kv_heads = %d query rows per KV head exceeds 64",
               c->block_size * (c->heads / c->kv_heads));
   DFL_REQUIRE(c->rms_eps >= 0.f && c->rope_theta > 0.f, DFL_E_INVALID, "rms_eps must be >= 0, rope_theta > 0");
+  DFL_REQUIRE(c->sliding_window >= 0, DFL_E_INVALID, "sliding_window %d must be >= 0", c->sliding_window);
   if (c->tap_layer_ids) {
     std::set<int> seen;
     for (int i = 0; i < c->n_taps; ++i)
@@ -276,7 +278,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
   DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
     return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
-                                 B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
+                                 pos0, d->window[li], B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
   }));
   // o and down keep a separate split-K reduce: their consumer, the residual conv + norm,
   // runs one workgroup per row and reads bf16 rows far faster than it could sum planes
@@ -373,6 +375,10 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
   DFL_REQUIRE(d, DFL_E_NOMEM, "host allocation failed");
   d->cfg = c;
   d->cfg.tap_layer_ids = nullptr;
+  d->cfg.sliding_layers = nullptr;
+  d->window.assign(c.layers, 0);
+  for (int i = 0; i < c.layers; ++i)
+    if (c.sliding_window > 0 && (!c.sliding_layers || c.sliding_layers[i])) d->window[i] = c.sliding_window;
   if (hipMalloc(&d->arena, cv.off) != hipSuccess) {
     delete d;
     return fail(DFL_E_NOMEM, "hipMalloc of %zu bytes for the drafter weights failed", cv.off);
@@ -710,10 +716,12 @@ size_t dfl_attention_workspace_bytes(int B, int G, int NH, int NKV, int D, int L
 }
 
 int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const dfl_bf16* vb, int ldkv,
-                        const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax, const int32_t* ctx_len, int B,
-                        int G, int NH, int NKV, int D, dfl_bf16* out, int ldo, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
+                        const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax, const int32_t* ctx_len,
+                        const int32_t* pos0, int window, int B, int G, int NH, int NKV, int D, dfl_bf16* out, int ldo,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
   DFL_REQUIRE(q && kb && vb && ctx_len && out && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(window >= 0, DFL_E_INVALID, "window %d must be >= 0", window);
+  DFL_REQUIRE(window == 0 || pos0, DFL_E_INVALID, "a sliding window needs pos0");
   DFL_REQUIRE(B > 0 && G > 0 && NH > 0 && NKV > 0 && NH % NKV == 0, DFL_E_INVALID, "bad head counts");
   DFL_REQUIRE(D == 64 || D == 128, DFL_E_UNSUPPORTED, "head_dim %d must be 64 or 128", D);
   DFL_REQUIRE(G * (NH / NKV) <= 64, DFL_E_UNSUPPORTED, "more than 64 query rows per KV head");
@@ -726,8 +734,8 @@ int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const df
   DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
   const dfl::AttnPlan pl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
   DFL_REQUIRE(ws_bytes >= pl.ws_bytes, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, pl.ws_bytes);
-  hipError_t e = dfl::launch_attention(pl, q, ldq, kb, vb, ldkv, K, V, Lcap, ctx_len, B, G, NH, NKV, D, Lmax, out,
-                                       ldo, ws, stream);
+  hipError_t e = dfl::launch_attention(pl, q, ldq, kb, vb, ldkv, K, V, Lcap, ctx_len, pos0, window, B, G, NH, NKV,
+                                       D, Lmax, out, ldo, ws, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

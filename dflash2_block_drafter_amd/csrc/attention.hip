@@ -14,6 +14,13 @@
 // softmax row statistics need only two cross-lane steps; then O^T += V^T . P^T, where
 // P^T comes straight from the S^T accumulators and V is staged transposed in LDS with
 // the same key order per lane.
+//
+// A sliding-window layer (MAX DFlash2Qwen3_5 `layer_types`) starts each context chunk at
+// block row 0's first visible row and masks, per query lane, the keys before that
+// query's own window start; a query with every key of a tile masked keeps its running
+// (max, sum, output) unchanged.
+#include <climits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,9 +38,11 @@ struct AttnArgs {
   const uint16_t* K;
   const uint16_t* V;
   const int32_t* ctx_len;
+  const int32_t* pos0;  // [B] position of block row 0 (sliding window only)
   float* part_o;   // [B, NKV, nchunks, QR, D]
   float* part_ml;  // [B, NKV, nchunks, QR, 2]
   int ldq, ldkv, Lcap, Lmax, G, NH, NKV, chunk, nchunks, qrows;
+  int window;  // 0: every context row; W: row t sees context rows >= pos0 + t - W + 1
   float scale_log2;
 };
 
@@ -70,6 +79,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   } else {
     kbeg = chunk * a.chunk;
     kend = min(ctx, kbeg + a.chunk);
+    if (a.window > 0) kbeg = max(kbeg, a.pos0[b] - a.window + 1);  // block row 0's first visible row
     ksrc = a.K + ((size_t)b * a.Lcap * a.NKV + g) * D;
     vsrc = a.V + ((size_t)b * a.Lcap * a.NKV + g) * D;
     kstride = (size_t)a.NKV * D;
@@ -78,6 +88,11 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   // this wavefront's 16 queries as MFMA B operands (column = query, k = d)
   const int qi = wave * 16 + (lane & 15);
   const bool qvalid = qi < a.qrows;
+  // sliding window: this lane's query (block row qi / hpg) sees context keys >= kmin; tiles
+  // starting at or past kmin_hi (the largest kmin of the workgroup) need no mask
+  const bool windowed = a.window > 0 && !block_chunk;
+  const int kmin = windowed ? a.pos0[b] + qi / hpg - a.window + 1 : INT_MIN;
+  const int kmin_hi = windowed ? a.pos0[b] + (a.G - 1) - a.window + 1 : INT_MIN;
   bf16x8_t qf[DK];
   {
     const int t = qi / hpg;
@@ -137,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   };
-  auto tile_compute = [&](int nvalid) {
+  auto tile_compute = [&](int j0, int nvalid) {
     // S^T tiles: s[kt] holds keys kt*16 + 4*lg + e for query (lane & 15)
     f32x4_t s[KT / 16];
 #pragma unroll
@@ -159,6 +174,13 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e)
           if (kt * 16 + lg * 4 + e >= nvalid) s[kt][e] = -INFINITY;
     }
+    if (j0 < kmin_hi) {  // uniform: only tiles that reach below some query's window start
+#pragma unroll
+      for (int kt = 0; kt < KT / 16; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j0 + kt * 16 + lg * 4 + e < kmin) s[kt][e] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
@@ -166,15 +188,18 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(m, tmax * a.scale_log2);
+    // a query whose keys so far are all masked (sliding window) keeps m = -inf, l = 0, o = 0:
+    // msafe keeps the exponents finite so that every weight below is exactly 0
+    const float msafe = mnew == -INFINITY ? 0.f : mnew;
     // v_exp_f32 directly: exponents here are <= 0, and results below fp32's normal range
     // (weights under 2^-126) flush to zero
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // m = -inf on the first tile: 0
+    const float alpha = __builtin_amdgcn_exp2f(m - msafe);  // m = -inf on the first tile: 0
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], a.scale_log2, -mnew));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][e], a.scale_log2, -msafe));
         s[kt][e] = p;
         psum += p;
       }
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       tile_store(kreg[0], vreg[0]);
       tile_load(kreg[0], vreg[0], j0 + KT);
       __syncthreads();
-      tile_compute(min(KT, kend - j0));
+      tile_compute(j0, min(KT, kend - j0));
       __syncthreads();
     }
   }
@@ -290,8 +315,8 @@ AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax) {
 
 hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, const uint16_t* kb,
                             const uint16_t* vb, int ldkv, const uint16_t* K, const uint16_t* V,
-                            int Lcap, const int32_t* ctx_len, int B, int G, int NH, int NKV,
-                            int D, int Lmax, uint16_t* out, int ldo, void* ws,
+                            int Lcap, const int32_t* ctx_len, const int32_t* pos0, int window, int B,
+                            int G, int NH, int NKV, int D, int Lmax, uint16_t* out, int ldo, void* ws,
                             hipStream_t stream) {
   AttnArgs a;
   a.q = q;
@@ -300,6 +325,8 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
   a.K = K;
   a.V = V;
   a.ctx_len = ctx_len;
+  a.pos0 = pos0;
+  a.window = window > 0 && pos0 ? window : 0;
   const size_t slots = (size_t)B * NKV * pl.nchunks * pl.qrows;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = a.part_o + slots * D;

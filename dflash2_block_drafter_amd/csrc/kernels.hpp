@@ -104,10 +104,12 @@ struct AttnPlan {
   size_t ws_bytes = 0;
 };
 AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax);
+// window > 0: block row t of request b (position pos0[b] + t) sees context rows
+// j >= pos0[b] + t - window + 1 only; the block's own rows are always seen.
 hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, const uint16_t* kb,
                             const uint16_t* vb, int ldkv, const uint16_t* K, const uint16_t* V,
-                            int Lcap, const int32_t* ctx_len, int B, int G, int NH, int NKV,
-                            int D, int Lmax, uint16_t* out, int ldo, void* ws,
+                            int Lcap, const int32_t* ctx_len, const int32_t* pos0, int window, int B,
+                            int G, int NH, int NKV, int D, int Lmax, uint16_t* out, int ldo, void* ws,
                             hipStream_t stream);
 
 // Top-K of each row guided by its tile maxima ([N, ceil(V / kGemmTileN)], as launch_gemm's

@@ -68,6 +68,11 @@ typedef struct {
   float rope_theta;
   const int32_t* tap_layer_ids; /* host array of n_taps target layer ids; must be distinct
                                    ([P3] `build_module` rejects repeated tap ids); may be NULL */
+  int32_t sliding_window;       /* 0: every layer attends to all of its context; W > 0: a sliding
+                                   layer's block row at position p sees context rows >= p - W + 1
+                                   ([P3] `DFlash2Qwen3_5` `layer_types`, `construct_kv_params`) */
+  const int32_t* sliding_layers; /* host array of `layers` flags (nonzero: sliding), read at load;
+                                   NULL: every layer slides when sliding_window > 0 */
 } dfl_config;
 
 /* One layer's tensors under the checkpoint layout ([P2] `Layer`: weights are [out, in]). */
@@ -191,12 +196,16 @@ int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const d
  * rows ([P2] header and `#block`: no mask, no window, scale 1/sqrt(D); GQA kv head =
  * h / (NH/NKV)).  q [B*G, NH*D] (ldq), kb/vb [B*G, NKV*D] (ldkv), K/V [B, Lcap, NKV, D],
  * ctx_len [B] device (clamped into [0, Lmax]); out [B*G, NH*D] bf16 (ldo); Lcap*NKV*D must be
- * below 2^31 (DFL_E_SHAPE).  ws: dfl_attention_workspace_bytes. */
+ * below 2^31 (DFL_E_SHAPE).  window > 0: sliding attention ([P3] `layer_types`): block row t
+ * of request b (position pos0[b] + t, pos0 [B] device) sees context rows j >= pos0[b] + t -
+ * window + 1 only; window = 0: all context rows (pos0 may then be NULL).
+ * ws: dfl_attention_workspace_bytes. */
 size_t dfl_attention_workspace_bytes(int B, int G, int NH, int NKV, int D, int Lmax);
 int dfl_block_attention(const dfl_bf16* q, int ldq, const dfl_bf16* kb, const dfl_bf16* vb,
                         int ldkv, const dfl_bf16* K, const dfl_bf16* V, int Lcap, int Lmax,
-                        const int32_t* ctx_len, int B, int G, int NH, int NKV, int D,
-                        dfl_bf16* out, int ldo, void* ws, size_t ws_bytes, hipStream_t stream);
+                        const int32_t* ctx_len, const int32_t* pos0, int window, int B, int G, int NH,
+                        int NKV, int D, dfl_bf16* out, int ldo, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Grouped dynamic conv, side 0 ([P3] `DFlash2GroupedConv.prepare`; [P2] `#coefficients`
  * and `#conv`): D = x . kproj^T read as [side][tap][group]; out[t,c] = sum_tap

@@ -75,8 +75,13 @@ def test_validation_errors_before_any_launch():
     # head_dim not 64/128
     assert L.dfl_head_norm_rope(P, 4, 2, 96, 192, P, 1e-6, 1e4, P, 4, None) == B.DFL_E_UNSUPPORTED
     # more than 64 query rows per KV head
-    assert L.dfl_block_attention(P, 8192, P, P, 8192, P, P, 10, 10, P, 1, 32, 32, 8, 128, P, 4096, P,
+    assert L.dfl_block_attention(P, 8192, P, P, 8192, P, P, 10, 10, P, None, 0, 1, 32, 32, 8, 128, P, 4096, P,
                                  1 << 30, None) == B.DFL_E_UNSUPPORTED
+    # a sliding window needs the block positions, and a window is never negative
+    assert L.dfl_block_attention(P, 8192, P, P, 8192, P, P, 10, 10, P, None, 64, 1, 16, 32, 8, 128, P, 4096, P,
+                                 1 << 30, None) == B.DFL_E_INVALID
+    assert L.dfl_block_attention(P, 8192, P, P, 8192, P, P, 10, 10, P, P, -1, 1, 16, 32, 8, 128, P, 4096, P,
+                                 1 << 30, None) == B.DFL_E_INVALID
     # misaligned workspace
     assert L.dfl_compute_candidates(P, 4, 100, 4, P, P, P + 8, 1 << 20, None) == B.DFL_E_INVALID
 
@@ -98,6 +103,7 @@ def _config(**kw):
     ("top_k", 33, B.DFL_E_UNSUPPORTED),
     ("conv_group", 12, B.DFL_E_UNSUPPORTED),
     ("hidden", 0, B.DFL_E_INVALID),
+    ("sliding_window", -1, B.DFL_E_INVALID),
 ])
 def test_load_rejects_bad_config(field, value, code):
     cfg, keep = _config(**{field: value})

@@ -96,3 +96,41 @@ def test_bound_head_matches_borrowed_head():
         torch.cuda.synchronize()
         assert torch.equal(tokens, t2) and torch.equal(logits, l2)
     dr.close()
+
+
+def _tiny_parity(w, G=None):
+    """Draft a tiny workload (optionally with a block narrower than block_size) on the GPU
+    and compare it with the oracle at the bf16 rounding points."""
+    d = w.dims
+    weights_cpu = synth.drafter_weights(w)
+    tgt_cpu = synth.target_inputs(w)
+    if G is not None:
+        tgt_cpu["embeds"] = tgt_cpu["embeds"][:, :G].contiguous()
+    weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
+    tgt = {k: v.to(DEV) for k, v in tgt_cpu.items()}
+    dr = Drafter(d, weights)
+    K, V = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(tgt["taps"], K, V)
+    tokens, logits = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
+                              tgt["lm_head"], want_logits=True)
+    torch.cuda.synchronize()
+    wh, th = _host(weights_cpu), _host(tgt_cpu)
+    ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
+    ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
+                        bf16_points=True, return_all=True)
+    assert_composed_close(logits, ref["logits"], "head logits")
+    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    dr.close()
+    return ref
+
+
+def test_tiny_sliding_window_end_to_end():
+    # layer 0 slides (window 20 over 32 context rows), layer 1 attends to everything
+    ref = _tiny_parity(configs.TINY_SW)
+    assert ref["tokens"].shape == (configs.TINY_SW.batch, configs.TINY_SW.dims.block_size - 1)
+
+
+def test_tiny_variable_block_width():
+    # a block drafting 4 tokens (G = 5) on a drafter whose block_size is 8
+    ref = _tiny_parity(configs.with_batch(configs.TINY, 2), G=5)
+    assert ref["tokens"].shape == (2, 4)

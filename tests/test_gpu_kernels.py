@@ -101,6 +101,37 @@ def test_block_attention(D, NH, NKV, G, ctx):
     assert_bf16_close(out.reshape(Bq, G, NH, D), want, "attention")
 
 
+@pytest.mark.parametrize("D,NH,NKV,G,ctx,pos,window", [
+    (128, 32, 8, 16, [700, 2048], [700, 2048], 300),    # window inside one chunk, several tiles masked
+    (128, 32, 8, 16, [5000, 129], [5000, 140], 2048),   # long context: earlier chunks skipped
+    (64, 4, 2, 8, [40, 3], [45, 3], 5),                 # window < block: early rows see no context
+    (64, 4, 2, 8, [33, 20], [33, 20], 100),             # a window wider than every context
+])
+def test_block_attention_sliding_window(D, NH, NKV, G, ctx, pos, window):
+    Bq = len(ctx)
+    Lmax = max(ctx)
+    Lcap = Lmax + 3
+    T = Bq * G
+    qkvw = (NH + 2 * NKV) * D
+    qkv = bf((T, qkvw), 44)
+    K = bf((Bq, Lcap, NKV, D), 45)
+    V = bf((Bq, Lcap, NKV, D), 46)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    pos0 = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    out = torch.empty((T, NH * D), dtype=torch.bfloat16, device=DEV)
+    ws = B.workspace(B.dfl_attention_workspace_bytes(Bq, G, NH, NKV, D, Lmax))
+    flat = qkv.view(-1)
+    B.dfl_block_attention(qkv, qkvw, flat[NH * D:], flat[(NH + NKV) * D:], qkvw, K, V, Lcap, Lmax,
+                          ctx_len, Bq, G, NH, NKV, D, out, NH * D, ws, pos0=pos0, window=window)
+    torch.cuda.synchronize()
+    q_h = O.as_f64(h(qkv))
+    q = q_h[:, :NH * D].reshape(Bq, G, NH, D)
+    kb = q_h[:, NH * D:(NH + NKV) * D].reshape(Bq, G, NKV, D)
+    vb = q_h[:, (NH + NKV) * D:].reshape(Bq, G, NKV, D)
+    want = O.attention(q, h(K), h(V), kb, vb, np.array(ctx), np.array(pos), window)
+    assert_bf16_close(out.reshape(Bq, G, NH, D), want, "sliding-window attention")
+
+
 @pytest.mark.parametrize("T,H,G,grp", [(64, 512, 16, 16), (1024, 5120, 16, 16), (24, 256, 8, 16)])
 def test_conv_prepare_finish(T, H, G, grp):
     x = bf((T, H), 51)
