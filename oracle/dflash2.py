@@ -403,13 +403,22 @@ def select_path(scores: np.ndarray, cand: np.ndarray, seed_index: int = 0) -> np
 
 
 def draft_block(embeds, weights: dict, lm_head, anchors, k_ctx: list, v_ctx: list, ctx_len,
-                pos0, dims, bf16_points=False, return_all=False):
+                pos0, dims, bf16_points=False, return_all=False, vocab_ids=None):
     """The whole block: layers, head, candidates, score_edges and the walk
     ([P2] `#block` and `#select`; [P3] `forward_block`, `compute_candidates`,
-    `score_edges`, `select_path`).  Returns tokens [B, G-1] int32."""
+    `score_edges`, `select_path`).  Returns tokens [B, G-1] int32.
+
+    vocab_ids: a draft vocabulary ([P2] `#block` and `#select`: a target that lists one is
+    projected onto those rows of its head only, and the chosen columns map to the listed
+    token ids before the path walk); None: the columns are the token ids."""
     h = draft_hidden(embeds, weights, k_ctx, v_ctx, ctx_len, pos0, dims, bf16_points)
+    if vocab_ids is not None:
+        vocab_ids = np.asarray(vocab_ids, dtype=np.int64)
+        lm_head = np.asarray(lm_head)[vocab_ids]
     logits = head_logits(h, lm_head).astype(np.float32)
     cand, unary = compute_candidates(logits, dims.top_k)
+    if vocab_ids is not None:
+        cand = vocab_ids[cand].astype(np.int32)
     z = selector_project(h, weights["candidate_selector.hidden_projection.weight"])
     scores = score_edges(cand, unary, z, anchors, weights["candidate_selector.predecessor_codebook"],
                          weights["candidate_selector.successor_codebook"]).astype(np.float32)

@@ -90,3 +90,25 @@ def test_bf16_points_stay_close(tiny):
     hr = O.draft_hidden(tgt["embeds"], weights, ks, vs, tgt["ctx_len"], tgt["pos0"], d, bf16_points=True)
     assert np.all(np.abs(hr - h) <= 2e-3 + 2e-2 * np.abs(h))
     assert not np.array_equal(hr, h)
+
+
+def test_draft_vocabulary_reduces_to_masked_full_head(tiny):
+    """A draft vocabulary listing every id in order is the plain path; an ascending subset
+    gives exactly the top-K of the full head's logits with the unlisted columns at -inf
+    (the plain top-k routine, pinned by brute force), mapped to token ids."""
+    w, weights, tgt = tiny
+    d = w.dims
+    ks, vs = O.materialize_context(tgt["taps"], weights, d)
+    args = (tgt["embeds"], weights, tgt["lm_head"], tgt["anchors"], ks, vs, tgt["ctx_len"], tgt["pos0"], d)
+    full = O.draft_block(*args, return_all=True)
+    same = O.draft_block(*args, return_all=True, vocab_ids=np.arange(d.vocab))
+    assert np.array_equal(full["tokens"], same["tokens"]) and np.array_equal(full["logits"], same["logits"])
+    rng = np.random.default_rng(12)
+    ids = np.sort(rng.choice(d.vocab, size=300, replace=False))
+    sub = O.draft_block(*args, return_all=True, vocab_ids=ids)
+    masked = np.full_like(full["logits"], -np.inf)
+    masked[..., ids] = full["logits"][..., ids]
+    cand, unary = O.compute_candidates(masked, d.top_k)
+    assert np.array_equal(sub["cand"], cand) and np.array_equal(sub["unary"], unary)
+    assert np.array_equal(sub["logits"], full["logits"][..., ids])
+    assert np.isin(sub["tokens"], ids).all()
