@@ -78,7 +78,7 @@ _SIGS = {
     "dfl_selector_project": (_I, [_P, _I, _I, _P, _I, _P, _P, _Z, _P]),
     "dfl_score_edges": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
-    "dfl_bind_target": (_I, [_P, _P, _P]),
+    "dfl_bind_target": (_I, [_P, _P, _P, _I, _P]),
     "dfl_set_timed_kernel": (_I, [_P, _I]),
     "dfl_read_kernel_time": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64),
                                   C.POINTER(C.c_double)]),
@@ -300,8 +300,13 @@ def dfl_select_path(scores, cand, B, S, K, tokens, stream=None):
     _check(lib().dfl_select_path(_f32(scores), _i32(cand), B, S, K, _i32(tokens), _stream(stream)))
 
 
-def dfl_bind_target(handle, lm_head, stream=None):
-    _check(lib().dfl_bind_target(handle, _bf(lm_head), _stream(stream)))
+def dfl_bind_target(handle, lm_head, vocab_ids=None, stream=None):
+    """vocab_ids: optional host sequence of token ids (a draft vocabulary)."""
+    ids = None
+    if vocab_ids is not None:
+        ids = (C.c_int32 * len(vocab_ids))(*[int(i) for i in vocab_ids])
+    _check(lib().dfl_bind_target(handle, _bf(lm_head), C.cast(ids, C.c_void_p) if ids is not None else None,
+                                 len(vocab_ids) if vocab_ids is not None else 0, _stream(stream)))
 
 
 def dfl_set_timed_kernel(handle, kclass: int | str):

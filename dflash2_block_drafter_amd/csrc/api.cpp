@@ -79,6 +79,8 @@ struct dfl_drafter {
   std::vector<int> window;           // per layer: 0 = full attention, W = sliding window
   uint16_t* head = nullptr;          // the bound target head, tile-contiguous (dfl_bind_target)
   const void* head_src = nullptr;    // the caller pointer it was copied from
+  int head_cols = 0;                 // its rows: the vocabulary, or the listed draft vocabulary
+  int32_t* head_ids = nullptr;       // device [head_cols] token ids of a draft vocabulary, else NULL
   int timed_class = DFL_K_NONE;
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> pool;
@@ -487,30 +489,55 @@ void dfl_drafter_free(dfl_drafter* d) {
   for (auto e : d->pool) (void)hipEventDestroy(e);
   if (d->arena) (void)hipFree(d->arena);
   if (d->head) (void)hipFree(d->head);
+  if (d->head_ids) (void)hipFree(d->head_ids);
   delete d;
 }
 
-int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, hipStream_t stream) {
+int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* vocab_ids, int n_vocab,
+                    hipStream_t stream) {
   DFL_REQUIRE(d && lm_head, DFL_E_INVALID, "NULL argument");
+  const int V = d->cfg.vocab, H = d->cfg.hidden;
   if (d->head_src) {
     DFL_REQUIRE(d->head_src == lm_head, DFL_E_INVALID, "a different target head is already bound");
+    DFL_REQUIRE(vocab_ids ? n_vocab == d->head_cols && d->head_ids : d->head_ids == nullptr, DFL_E_INVALID,
+                "the target is already bound with a different vocabulary");
     return DFL_OK;
   }
-  const int V = d->cfg.vocab, H = d->cfg.hidden;
-  void* buf = nullptr;
-  if (hipMalloc(&buf, dfl::tiled_weight_elems(V, H) * sizeof(uint16_t)) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(DFL_E_NOMEM, "could not allocate the bound head (%zu bytes)",
-                dfl::tiled_weight_elems(V, H) * sizeof(uint16_t));
+  int cols = V;
+  if (vocab_ids) {
+    DFL_REQUIRE(n_vocab >= d->cfg.top_k && n_vocab <= V, DFL_E_SHAPE, "draft vocabulary of %d ids outside [top_k=%d, V=%d]",
+                n_vocab, d->cfg.top_k, V);
+    std::set<int> seen;
+    for (int i = 0; i < n_vocab; ++i) {
+      DFL_REQUIRE(vocab_ids[i] >= 0 && vocab_ids[i] < V, DFL_E_INVALID, "draft vocabulary id %d outside [0, %d)",
+                  vocab_ids[i], V);
+      DFL_REQUIRE(seen.insert(vocab_ids[i]).second, DFL_E_INVALID, "draft vocabulary id %d repeats", vocab_ids[i]);
+    }
+    cols = n_vocab;
   }
-  hipError_t e = dfl::launch_tile_weights(lm_head, V, H, static_cast<uint16_t*>(buf), stream);
+  void* buf = nullptr;
+  void* ids = nullptr;
+  const size_t bytes = dfl::tiled_weight_elems(cols, H) * sizeof(uint16_t);
+  if (hipMalloc(&buf, bytes) != hipSuccess ||
+      (vocab_ids && hipMalloc(&ids, (size_t)cols * sizeof(int32_t)) != hipSuccess)) {
+    (void)hipGetLastError();
+    if (buf) (void)hipFree(buf);
+    return fail(DFL_E_NOMEM, "could not allocate the bound head (%zu bytes)", bytes);
+  }
+  hipError_t e = hipSuccess;
+  if (ids) e = hipMemcpyAsync(ids, vocab_ids, (size_t)cols * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = dfl::launch_tile_weights(lm_head, cols, H, static_cast<uint16_t*>(buf), stream, static_cast<int32_t*>(ids));
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     (void)hipFree(buf);
+    if (ids) (void)hipFree(ids);
     return fail(DFL_E_DEVICE, "binding the head: %s", hipGetErrorString(e));
   }
   d->head = static_cast<uint16_t*>(buf);
   d->head_src = lm_head;
+  d->head_cols = cols;
+  d->head_ids = static_cast<int32_t*>(ids);
   return DFL_OK;
 }
 
@@ -592,7 +619,9 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   DFL_REQUIRE(ws_bytes >= lay.total, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, lay.total);
 
   const int H = c.hidden, S = G - 1, N = B * S;
-  const int V_ = c.vocab, R = c.rank, Kc = c.top_k;
+  // the head's columns: the bound draft vocabulary's rows when it is used, else the vocabulary
+  const int V_ = bound_head ? d->head_cols : c.vocab, R = c.rank, Kc = c.top_k;
+  const int32_t* id_map = bound_head ? d->head_ids : nullptr;
   char* W = static_cast<char*>(ws);
   auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
@@ -630,11 +659,12 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   }));
   DFL_TRY(timed(d, DFL_K_TOPK, tiles_fused ? 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) : 4.0 * N * V_,
                 stream, [&] {
-    return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream)
-                       : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream);
+    return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map)
+                       : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream, id_map);
   }));
   DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (R + Kc + 2), stream, [&] {
-    return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, V_, scores, stream);
+    return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, c.vocab, scores,
+                                   stream);
   }));
   DFL_TRY(timed(d, DFL_K_SELECT_PATH, 4.0 * N * Kc, stream, [&] {
     return dfl::launch_select_path(scores, cand, B, S, Kc, tokens, stream);

@@ -303,6 +303,7 @@ constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
 
 __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ src, int N, int K,
+                                                           const int32_t* __restrict__ rows,
                                                            uint16_t* __restrict__ dst, size_t chunks) {
   const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= chunks) return;
@@ -316,7 +317,10 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __res
   const int t = static_cast<int>(ts / steps);
   const int n = t * kBN + r;
   u32x4_t v = {0u, 0u, 0u, 0u};
-  if (n < N) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)n * K + sstep * BK + q * 8);
+  if (n < N) {
+    const size_t row = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
+    v = *reinterpret_cast<const u32x4_t*>(src + row * K + sstep * BK + q * 8);
+  }
   *reinterpret_cast<u32x4_t*>(dst + c * 8) = v;
 }
 
@@ -324,9 +328,10 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __res
 
 size_t tiled_weight_elems(int N, int K) { return (size_t)((N + kBN - 1) / kBN) * kBN * K; }
 
-hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream) {
+hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream,
+                               const int32_t* rows) {
   const size_t chunks = tiled_weight_elems(N, K) / 8;
-  tile_weights_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(src, N, K, dst, chunks);
+  tile_weights_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(src, N, K, rows, dst, chunks);
   return hipGetLastError();
 }
 

@@ -50,9 +50,11 @@ inline Planes gemm_planes(const GemmPlan& pl, const float* partial, int M, int N
   return p;
 }
 // Tile-contiguous copy of a row-major [N, K] weight: [ceil(N/256)][K/64][256][64], rows
-// past N zero.  tiled_weight_elems gives the destination size in bf16 elements.
+// past N zero.  tiled_weight_elems gives the destination size in bf16 elements.  rows
+// (device, optional): destination row n copies source row rows[n] (a gathered subset).
 size_t tiled_weight_elems(int N, int K);
-hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream);
+hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream,
+                               const int32_t* rows = nullptr);
 
 // RMSNorm of `rows` rows.  Input row r is row in_row(r) = (r / out_per_grp) * in_per_grp +
 // skip + r % out_per_grp, so the final norm can drop the anchor row of every block.
@@ -115,13 +117,14 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
 // Top-K of each row guided by its tile maxima ([N, ceil(V / kGemmTileN)], as launch_gemm's
 // tile_max writes them): only tiles whose maximum reaches the K-th largest tile maximum
 // are read.
+// id_map (device, optional): the reported id of column c is id_map[c] (a draft vocabulary).
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
-                             int32_t* ids, float* vals, hipStream_t stream);
+                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map = nullptr);
 // Exact top-K of each fp32 row (value descending, id ascending): tile maxima into ws
 // (topk_ws_bytes), then launch_topk_tiles.
 size_t topk_ws_bytes(int N, int V);
 hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, float* vals, void* ws,
-                       hipStream_t stream);
+                       hipStream_t stream, const int32_t* id_map = nullptr);
 
 hipError_t launch_score_edges(const int32_t* cand, const float* unary, const float* z,
                               const int32_t* anchors, int B, int S, int K, int R,

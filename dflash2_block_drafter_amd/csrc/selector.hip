@@ -91,7 +91,8 @@ __device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*l
 __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict__ logits, int V,
                                                          const float* __restrict__ tile_max, int ntiles,
                                                          int K, int32_t* __restrict__ ids,
-                                                         float* __restrict__ vals) {
+                                                         float* __restrict__ vals,
+                                                         const int32_t* __restrict__ id_map) {
   constexpr int TW = kGemmTileN;
   constexpr int TPL = TW / 64;                 // values of a tile per lane
   constexpr int CH = 64 * kTmPerLane;          // tile maxima per round
@@ -207,7 +208,9 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
   if (wave != 0) return;
   merge_wave_lists(mg, lv, li, K, lane);
   if (lane < K) {
-    ids[(size_t)row * K + lane] = mg.id;
+    // the list is ordered by (value, column); a draft vocabulary reports its listed ids
+    const int col = mg.id;
+    ids[(size_t)row * K + lane] = id_map && col >= 0 && col < V ? id_map[col] : col;
     vals[(size_t)row * K + lane] = mg.v;
   }
 }
@@ -281,7 +284,7 @@ size_t topk_ws_bytes(int N, int V) {
 }
 
 hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, float* vals, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const int32_t* id_map) {
   if (N <= 0) return hipSuccess;
   const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
   float* tmax = static_cast<float*>(ws);
@@ -289,14 +292,14 @@ hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, f
   tile_rowmax_kernel<<<dim3((waves + 3) / 4, N), 256, 0, stream>>>(logits, V, ntiles, tmax);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_topk_tiles(logits, N, V, K, tmax, ids, vals, stream);
+  return launch_topk_tiles(logits, N, V, K, tmax, ids, vals, stream, id_map);
 }
 
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
-                             int32_t* ids, float* vals, hipStream_t stream) {
+                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map) {
   if (N <= 0) return hipSuccess;
   const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
-  topk_tiles_kernel<<<N, 256, 0, stream>>>(logits, V, tile_max, ntiles, K, ids, vals);
+  topk_tiles_kernel<<<N, 256, 0, stream>>>(logits, V, tile_max, ntiles, K, ids, vals, id_map);
   return hipGetLastError();
 }
 

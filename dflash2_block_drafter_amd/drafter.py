@@ -24,10 +24,13 @@ class Drafter:
         except Exception:
             pass
 
-    def bind_target(self, lm_head: torch.Tensor):
-        """Copy the target's head once into the drafter's tile-contiguous layout; draft()
-        then accepts lm_head=None (or the same tensor) and streams the copy."""
-        B_.dfl_bind_target(self.handle, lm_head)
+    def bind_target(self, lm_head: torch.Tensor, vocab_ids=None):
+        """Copy the target's head once into the drafter's tile-contiguous layout (only the
+        rows of a draft vocabulary, when vocab_ids lists one); draft() then accepts
+        lm_head=None (or the same tensor) and streams the copy."""
+        B_.dfl_bind_target(self.handle, lm_head, vocab_ids)
+        self.head_cols = len(vocab_ids) if vocab_ids is not None else self.dims.vocab
+        self._bound_ptr = lm_head.data_ptr()
 
     def alloc_kv(self, B: int, Lcap: int, device="cuda"):
         d = self.dims
@@ -55,7 +58,9 @@ class Drafter:
         if tokens is None:
             tokens = torch.empty((Bq, G - 1), dtype=torch.int32, device=embeds.device)
         if want_logits and logits is None:
-            logits = torch.empty((Bq, G - 1, self.dims.vocab), dtype=torch.float32, device=embeds.device)
+            bound = lm_head is None or lm_head.data_ptr() == getattr(self, "_bound_ptr", None)
+            cols = getattr(self, "head_cols", self.dims.vocab) if bound else self.dims.vocab
+            logits = torch.empty((Bq, G - 1, cols), dtype=torch.float32, device=embeds.device)
         ws = ws if ws is not None else self.workspace(Bq, G, Lmax)
         B_.dfl_draft_block(self.handle, embeds, anchors, Bq, G, K, V, Lcap, Lmax, ctx_len, pos0, lm_head,
                            tokens, logits, ws)

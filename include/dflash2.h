@@ -134,12 +134,18 @@ size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
 
 /* Bind the target's head once ([P2] `bindTarget`: the drafter binds to one target; binding
  * a different one afterwards is an error).  lm_head [V, H] bf16 row-major is copied, once,
- * into an owned tile-contiguous buffer (tiled_weight layout, about V*H*2 bytes) that the
- * head projection streams faster than the row-major original; the values are snapshotted,
- * so later changes to lm_head are not seen.  Synchronises `stream`.  Errors: a second call
- * with another pointer -> DFL_E_INVALID (the same pointer is a no-op); allocation ->
- * DFL_E_NOMEM; HIP failure -> DFL_E_DEVICE. */
-int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, hipStream_t stream);
+ * into an owned tile-contiguous buffer that the head projection streams faster than the
+ * row-major original; the values are snapshotted, so later changes to lm_head are not seen.
+ * vocab_ids (host, optional): a draft vocabulary ([P2] `#block`, `#select`:
+ * `DraftProjection.vocabulary`), n_vocab distinct token ids in [0, V), top_k <= n_vocab: only
+ * those rows are copied, drafts that use the bound head project onto them (logits_out then
+ * has n_vocab columns, in list order) and their candidates are the listed ids.  NULL: the
+ * whole vocabulary.  Synchronises `stream`.  Errors: a second call with another pointer or
+ * vocabulary -> DFL_E_INVALID (the same binding again is a no-op); bad ids -> DFL_E_INVALID;
+ * n_vocab out of range -> DFL_E_SHAPE; allocation -> DFL_E_NOMEM; HIP failure ->
+ * DFL_E_DEVICE. */
+int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* vocab_ids, int n_vocab,
+                    hipStream_t stream);
 
 /* One draft block per request ([P2] `#block` then `#select`; [P3] `forward_block`,
  * `compute_candidates`, `score_edges`, `select_path`):
@@ -153,7 +159,8 @@ int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, hipStream_t stream)
  *   lm_head:  [V, H] bf16, the target's head, borrowed; NULL, or the pointer given to
  *             dfl_bind_target, selects the bound copy.
  *   tokens:   [B, G-1] int32 device output ([P2] returns the proposals on the device).
- *   logits_out: NULL or [B, G-1, V] float32 device output of the head.
+ *   logits_out: NULL or [B, G-1, V] float32 device output of the head ([B, G-1, n_vocab]
+ *             when a bound draft vocabulary is used).
  *   G must satisfy 2 <= G <= block_size ([P3] `supports_zero_draft_rows` is false). */
 int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
                     const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,

@@ -134,3 +134,35 @@ def test_tiny_variable_block_width():
     # a block drafting 4 tokens (G = 5) on a drafter whose block_size is 8
     ref = _tiny_parity(configs.with_batch(configs.TINY, 2), G=5)
     assert ref["tokens"].shape == (2, 4)
+
+
+@pytest.mark.parametrize("order", ["ascending", "permuted"])
+def test_tiny_draft_vocabulary(order):
+    # a bound draft vocabulary: the head projects onto the listed rows, the candidates are
+    # the listed token ids (oracle: the same composition with vocab_ids)
+    w = configs.with_batch(configs.TINY, 2)
+    d = w.dims
+    rng = np.random.default_rng(21)
+    ids = np.sort(rng.choice(d.vocab, size=300, replace=False))
+    if order == "permuted":
+        ids = rng.permutation(ids)
+    weights_cpu = synth.drafter_weights(w)
+    tgt_cpu = synth.target_inputs(w)
+    weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
+    tgt = {k: v.to(DEV) for k, v in tgt_cpu.items()}
+    dr = Drafter(d, weights)
+    K, V = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(tgt["taps"], K, V)
+    dr.bind_target(tgt["lm_head"], vocab_ids=ids.tolist())
+    tokens, logits = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], None,
+                              want_logits=True)
+    torch.cuda.synchronize()
+    assert logits.shape == (w.batch, d.block_size - 1, len(ids))
+    wh, th = _host(weights_cpu), _host(tgt_cpu)
+    ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
+    ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
+                        bf16_points=True, return_all=True, vocab_ids=ids)
+    assert_composed_close(logits, ref["logits"], "draft-vocabulary logits")
+    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    assert np.isin(tokens.cpu().numpy(), ids).all()
+    dr.close()
