@@ -79,6 +79,8 @@ _SIGS = {
     "dfl_score_edges": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dfl_bind_target": (_I, [_P, _P, _P, _I, _P]),
+    "dfl_context_append_workspace_bytes": (_Z, [_P, _I, _I]),
+    "dfl_context_append": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "dfl_set_timed_kernel": (_I, [_P, _I]),
     "dfl_read_kernel_time": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64),
                                   C.POINTER(C.c_double)]),
@@ -209,6 +211,18 @@ def dfl_context_workspace_bytes(handle, B, L) -> int:
 def dfl_context_materialize(handle, taps, B, L, row_offset, Lcap, K: list, V: list, ws, stream=None):
     _check(lib().dfl_context_materialize(handle, _bf(taps), B, L, row_offset, Lcap, _ptr_array(K),
                                          _ptr_array(V), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_context_append_workspace_bytes(handle, B, rows) -> int:
+    return lib().dfl_context_append_workspace_bytes(handle, B, rows)
+
+
+def dfl_context_append(handle, taps, row_offsets, starts, B, Lcap, K: list, V: list, ws, stream=None):
+    """row_offsets, starts: host integer sequences (B+1 and B entries)."""
+    offs = (C.c_int32 * (B + 1))(*[int(x) for x in row_offsets])
+    st = (C.c_int32 * B)(*[int(x) for x in starts])
+    _check(lib().dfl_context_append(handle, _bf(taps), C.cast(offs, C.c_void_p), C.cast(st, C.c_void_p), B, Lcap,
+                                    _ptr_array(K), _ptr_array(V), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def dfl_draft_workspace_bytes(handle, B, G, Lmax) -> int:

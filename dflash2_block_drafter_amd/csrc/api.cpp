@@ -588,6 +588,66 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
   return DFL_OK;
 }
 
+size_t dfl_context_append_workspace_bytes(const dfl_drafter* d, int B, int rows) {
+  if (!d || B <= 0 || rows <= 0) return 0;
+  return ctx_layout(d->cfg, 1, rows).total + align_up((size_t)(2 * B + 1) * sizeof(int32_t));
+}
+
+int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_offsets, const int32_t* starts,
+                       int B, int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  DFL_REQUIRE(d && taps && row_offsets && starts && K && V && ws, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(B > 0 && Lcap > 0, DFL_E_INVALID, "B and Lcap must be positive");
+  DFL_REQUIRE(row_offsets[0] == 0, DFL_E_SHAPE, "row_offsets[0] must be 0");
+  for (int b = 0; b < B; ++b) {
+    const int n = row_offsets[b + 1] - row_offsets[b];
+    DFL_REQUIRE(n >= 0, DFL_E_SHAPE, "row_offsets decrease at request %d", b);
+    DFL_REQUIRE(starts[b] >= 0 && (int64_t)starts[b] + n <= Lcap, DFL_E_SHAPE,
+                "request %d: rows [%d, %d) outside the cache of %d rows", b, starts[b], starts[b] + n, Lcap);
+  }
+  const int rows = row_offsets[B];
+  if (rows == 0) return DFL_OK;
+  DFL_REQUIRE(rows <= (1 << 30), DFL_E_SHAPE, "too many rows");
+  const dfl_config& c = d->cfg;
+  for (int i = 0; i < c.layers; ++i) DFL_REQUIRE(K[i] && V[i], DFL_E_INVALID, "K/V pointer of layer %d is NULL", i);
+  DFL_REQUIRE((int64_t)Lcap * c.kv_heads * c.head_dim < (int64_t(1) << 31), DFL_E_SHAPE, "Lcap too large");
+  DFL_REQUIRE(aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  const size_t need = dfl_context_append_workspace_bytes(d, B, rows);
+  DFL_REQUIRE(ws_bytes >= need, DFL_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const CtxLayout lay = ctx_layout(c, 1, rows);
+  char* W = static_cast<char*>(ws);
+  uint16_t* craw = reinterpret_cast<uint16_t*>(W + lay.craw);
+  uint16_t* cc = reinterpret_cast<uint16_t*>(W + lay.c);
+  uint16_t* kv = reinterpret_cast<uint16_t*>(W + lay.kv);
+  float* part = reinterpret_cast<float*>(W + lay.partial);
+  int32_t* offs_d = reinterpret_cast<int32_t*>(W + lay.total);
+  int32_t* starts_d = offs_d + (B + 1);
+  DFL_HIP(hipMemcpyAsync(offs_d, row_offsets, (size_t)(B + 1) * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+  DFL_HIP(hipMemcpyAsync(starts_d, starts, (size_t)B * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+  const int M = rows, H = c.hidden, kvw = 2 * c.kv_heads * c.head_dim;
+  const dfl::GemmPlan pfc = dfl::plan_gemm(M, H, c.n_taps * H);
+  DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, H, c.n_taps * H, dfl::EPI_BF16), stream, [&] {
+    return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, true, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
+                            0, 0, part, stream);
+  }));
+  DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * M * H, stream, [&] {
+    return dfl::launch_rms_norm(craw, H, M, H, d->hidden_norm, c.rms_eps, cc, H, 1, 1, 0, stream);
+  }));
+  const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
+  for (int i = 0; i < c.layers; ++i) {
+    const LayerBuf& Lb = d->layers[i];
+    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16), stream, [&] {
+      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, true, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
+                              stream);
+    }));
+    DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
+      return dfl::launch_context_kv_store_ragged(kv, M, B, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,
+                                                 offs_d, starts_d, Lcap, K[i], V[i], stream);
+    }));
+  }
+  return DFL_OK;
+}
+
 size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax) {
   if (!d || B <= 0 || G < 2 || Lmax < 0) return 0;
   return draft_layout(d->cfg, B, G, Lmax).total;

@@ -85,6 +85,13 @@ hipError_t launch_context_kv_store(const uint16_t* kv, int B, int L, int NKV, in
                                    int row_offset, int Lcap, uint16_t* K, uint16_t* V,
                                    hipStream_t stream);
 
+// Ragged store: kv [rows, 2*NKV*D] packs the new rows of B requests back to back; device
+// offsets [B+1] (offsets[0] = 0, nondecreasing, offsets[B] = rows) and starts [B]: packed row
+// r of request b goes to cache row starts[b] + r - offsets[b] at that position.
+hipError_t launch_context_kv_store_ragged(const uint16_t* kv, int rows, int B, int NKV, int D, const uint16_t* k_norm,
+                                          float eps, float theta, const int32_t* offsets, const int32_t* starts,
+                                          int Lcap, uint16_t* K, uint16_t* V, hipStream_t stream);
+
 // Grouped dynamic conv of bf16 rows y [T, H].  coef: the side's fp32 deltas, tap 0 of group
 // g at column g and tap 1 at column ng + g of each row, summed over coef.S planes.
 //

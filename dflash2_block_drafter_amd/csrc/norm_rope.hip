@@ -177,7 +177,46 @@ __global__ __launch_bounds__(256) void context_kv_store_kernel(
         *reinterpret_cast<const u32x4_t*>(src + NKV * D + i * 8);
 }
 
+// Ragged context K/V store ([P3] `materialize` with `input_row_offsets`; [P2] committed rows
+// projected at their absolute positions): packed kv row r belongs to request b with
+// offsets[b] <= r < offsets[b+1] and goes to K/V row starts[b] + r - offsets[b] of b.
+__global__ __launch_bounds__(256) void context_kv_store_ragged_kernel(
+    const uint16_t* __restrict__ kv, int NKV, int D, const uint16_t* __restrict__ k_norm, float eps,
+    double log_theta, const int32_t* __restrict__ offsets, const int32_t* __restrict__ starts, int B, int Lcap,
+    uint16_t* __restrict__ K, uint16_t* __restrict__ V) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int lo = 0, hi = B - 1;  // the last b with offsets[b] <= r (offsets nondecreasing, checked on the host)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int pos = starts[b] + (r - offsets[b]);
+  if (pos < 0 || pos >= Lcap) return;  // the host validates; never write past the cache
+  const uint16_t* src = kv + (size_t)r * (2 * NKV * D);
+  const size_t dst_row = ((size_t)b * Lcap + pos) * NKV * D;
+  float c = 1.f, s = 0.f;
+  if (lane < (D >> 1)) rope_cs(pos, lane, D, log_theta, &c, &s);
+  for (int h = wave; h < NKV; h += 4)
+    norm_rope_head(src + h * D, K + dst_row + h * D, D, k_norm, eps, c, s, lane);
+  const int vchunks = NKV * D / 8;
+  for (int i = threadIdx.x; i < vchunks; i += 256)
+    *reinterpret_cast<u32x4_t*>(V + dst_row + i * 8) = *reinterpret_cast<const u32x4_t*>(src + NKV * D + i * 8);
+}
+
 }  // namespace
+
+hipError_t launch_context_kv_store_ragged(const uint16_t* kv, int rows, int B, int NKV, int D, const uint16_t* k_norm,
+                                          float eps, float theta, const int32_t* offsets, const int32_t* starts,
+                                          int Lcap, uint16_t* K, uint16_t* V, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  context_kv_store_ragged_kernel<<<rows, 256, 0, stream>>>(kv, NKV, D, k_norm, eps, log(static_cast<double>(theta)),
+                                                           offsets, starts, B, Lcap, K, V);
+  return hipGetLastError();
+}
 
 hipError_t launch_rms_norm(const uint16_t* x, int ldx, int rows, int H, const uint16_t* gamma,
                            float eps, uint16_t* y, int ldy, int out_per_grp, int in_per_grp,

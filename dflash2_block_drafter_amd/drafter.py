@@ -45,6 +45,14 @@ class Drafter:
         B_.dfl_context_materialize(self.handle, taps, Bq, L, row_offset, K[0].shape[1], K, V, ws)
         return ws
 
+    def append(self, taps: torch.Tensor, row_offsets, starts, K: list, V: list):
+        """Ragged append: taps [rows, n_taps*H] packs each request's new rows; request b's
+        rows are taps[row_offsets[b]:row_offsets[b+1]], written from cache row starts[b]."""
+        Bq = len(starts)
+        ws = B_.workspace(B_.dfl_context_append_workspace_bytes(self.handle, Bq, int(row_offsets[-1])))
+        B_.dfl_context_append(self.handle, taps, row_offsets, starts, Bq, K[0].shape[1], K, V, ws)
+        return ws
+
     def workspace(self, B: int, G: int, Lmax: int) -> torch.Tensor:
         need = B_.dfl_draft_workspace_bytes(self.handle, B, G, Lmax)
         if self._ws is None or self._ws.numel() < need:

@@ -128,6 +128,20 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
                             int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* Ragged context append ([P3] `materialize` with `input_row_offsets`; [P2] committed rows
+ * projected at their absolute positions): each request appends its own number of new rows.
+ *   taps:        [rows, n_taps*H] bf16, the new rows of all requests packed back to back.
+ *   row_offsets: host [B+1], row_offsets[0] = 0, nondecreasing, row_offsets[B] = rows:
+ *                request b's rows are taps rows [row_offsets[b], row_offsets[b+1]).
+ *   starts:      host [B], the absolute position (and cache row) of each request's first new
+ *                row; starts[b] + its row count <= Lcap (DFL_E_SHAPE otherwise).
+ *   K, V:        as for dfl_context_materialize.  Rows outside the appended ranges are not
+ *                touched.  ws: dfl_context_append_workspace_bytes(d, B, rows). */
+size_t dfl_context_append_workspace_bytes(const dfl_drafter* d, int B, int rows);
+int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_offsets,
+                       const int32_t* starts, int B, int Lcap, dfl_bf16* const* K,
+                       dfl_bf16* const* V, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace of dfl_draft_block for B requests of G rows whose context holds at most
  * Lmax rows. */
 size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);

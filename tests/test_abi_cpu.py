@@ -84,6 +84,14 @@ def test_validation_errors_before_any_launch():
                                  1 << 30, None) == B.DFL_E_INVALID
     # misaligned workspace
     assert L.dfl_compute_candidates(P, 4, 100, 4, P, P, P + 8, 1 << 20, None) == B.DFL_E_INVALID
+    # ragged append: offsets that decrease, and rows past the cache
+    offs = (C.c_int32 * 3)(0, 4, 2)
+    st = (C.c_int32 * 2)(0, 0)
+    ptrs = (C.c_void_p * 1)(P)
+    assert L.dfl_context_append(P, P, offs, st, 2, 64, ptrs, ptrs, P, 1 << 20, None) == B.DFL_E_SHAPE
+    offs = (C.c_int32 * 3)(0, 4, 8)
+    st = (C.c_int32 * 2)(0, 61)
+    assert L.dfl_context_append(P, P, offs, st, 2, 64, ptrs, ptrs, P, 1 << 20, None) == B.DFL_E_SHAPE
 
 
 def _config(**kw):

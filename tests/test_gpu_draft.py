@@ -166,3 +166,39 @@ def test_tiny_draft_vocabulary(order):
     assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
     assert np.isin(tokens.cpu().numpy(), ids).all()
     dr.close()
+
+
+def test_ragged_context_append():
+    # each request appends its own rows at its own positions; the packed rows are projected
+    # as the oracle projects each request's rows at those positions, other rows untouched
+    w = configs.with_batch(configs.TINY, 3)
+    d = w.dims
+    counts, starts = [5, 0, 9], [10, 0, 2]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).tolist()
+    rows = offsets[-1]
+    weights_cpu = synth.drafter_weights(w)
+    taps_cpu = synth.normal((rows, 1, d.n_taps * d.hidden), 0.0, 1.0, seed=77)
+    weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
+    taps = taps_cpu.reshape(rows, d.n_taps * d.hidden).to(DEV)
+    dr = Drafter(d, weights)
+    K, V = dr.alloc_kv(w.batch, 40)
+    dr.append(taps, offsets, starts, K, V)
+    torch.cuda.synchronize()
+    wh = _host(weights_cpu)
+    th = synth.host(taps_cpu)
+    for b in range(w.batch):
+        n, s = counts[b], starts[b]
+        kk = [k[b].float().cpu() for k in K]
+        vv = [v[b].float().cpu() for v in V]
+        outside = np.ones(40, dtype=bool)
+        outside[s:s + n] = False
+        for i in range(d.layers):
+            assert not kk[i][outside].any() and not vv[i][outside].any(), f"request {b}: rows outside were written"
+        if n == 0:
+            continue
+        ks, vs = O.materialize_context(th[offsets[b]:offsets[b + 1]].reshape(1, n, -1), wh, d,
+                                       positions=s + np.arange(n), bf16_points=True)
+        for i in range(d.layers):
+            assert_composed_close(K[i][b:b + 1, s:s + n], ks[i], f"request {b} K layer {i}")
+            assert_composed_close(V[i][b:b + 1, s:s + n], vs[i], f"request {b} V layer {i}")
+    dr.close()
