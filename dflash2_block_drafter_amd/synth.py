@@ -165,6 +165,19 @@ def conv_inputs(T: int, H: int, grp: int, seed: int, device="cpu"):
     }
 
 
+def affine4_weight(N: int, K: int, *, seed: int, device="cpu"):
+    """A 4-bit affine projection of N rows over K inputs (groups of 64): packed int32 words
+    [N, K/8] of uniform 4-bit fields, scales [N, K/64] ~ |N(0.003, 0.001)| and biases
+    = -7.5 * scale + N(0, 0.002), both bf16, so the weights span about +-0.02 around 0."""
+    g = _gen("cpu", seed)
+    q = torch.randint(0, 16, (N, K // 8, 8), generator=g, dtype=torch.int64)
+    words = (q << (4 * torch.arange(8, dtype=torch.int64))).sum(-1)
+    words = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
+    scales = (torch.randn((N, K // 64), generator=g) * 0.001 + 0.003).abs().to(torch.bfloat16)
+    biases = (-7.5 * scales.float() + torch.randn((N, K // 64), generator=g) * 0.002).to(torch.bfloat16)
+    return words.to(device), scales.to(device), biases.to(device)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Host copy of a bf16 tensor as its raw uint16 bit patterns."""
     assert t.dtype == torch.bfloat16

@@ -110,6 +110,26 @@ def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     return as_f64(x) @ as_f64(w).T
 
 
+def dequant_affine4(packed, scales, biases, group: int = 64, bf16_weights=False) -> np.ndarray:
+    """Weights of a 4-bit affine projection ([P2] `quantizedWeight`: groups of 64 along the
+    input dimension, affine mode, a scale and a bias per group):
+    w[n, k] = scale[n, k // 64] * q[n, k] + bias[n, k // 64], q[n, k] in 0..15.
+
+    packed: [N, K/8] uint32 (or int32 bit patterns); field k of row n sits at bits
+    4 * (k % 8) of word k // 8, lowest bits first.  scales, biases: [N, K/64] bf16.
+    `bf16_weights` rounds w to bf16, where a kernel feeding bf16 matrix units holds it.
+    Returns float64 [N, K]."""
+    p = np.asarray(packed).astype(np.int64) & 0xFFFFFFFF
+    N, words = p.shape
+    K = words * 8
+    shifts = 4 * np.arange(8)
+    q = ((p[:, :, None] >> shifts[None, None, :]) & 0xF).reshape(N, K).astype(F64)
+    s = np.repeat(as_f64(scales), group, axis=1)
+    b = np.repeat(as_f64(biases), group, axis=1)
+    w = s * q + b
+    return round_to_bf16(w) if bf16_weights else w
+
+
 def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 

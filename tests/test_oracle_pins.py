@@ -309,6 +309,30 @@ def test_layer_window_selection():
     assert [O.layer_window(replace(d, sliding_window=0), i) for i in range(d.layers)] == [0, 0]
 
 
+def test_affine4_dequant_brute_force(rng):
+    """4-bit fields are read lowest bits first, eight per word; each group of 64 inputs has
+    its own scale and bias (explicit loops over fields and groups)."""
+    N, K = 3, 128
+    q = rng.integers(0, 16, size=(N, K))
+    words = np.zeros((N, K // 8), dtype=np.uint64)
+    for n in range(N):
+        for k in range(K):
+            words[n, k // 8] |= np.uint64(q[n, k]) << np.uint64(4 * (k % 8))
+    ones = np.full((N, K // 64), 0x3F80, dtype=np.uint16)       # bf16 1.0
+    zeros = np.zeros((N, K // 64), dtype=np.uint16)
+    assert np.array_equal(O.dequant_affine4(words.astype(np.uint32), ones, zeros), q)
+    sc = rng.integers(0x3A00, 0x3C00, size=(N, K // 64)).astype(np.uint16)   # small positive bf16
+    bi = rng.integers(0xBC00, 0xBD00, size=(N, K // 64)).astype(np.uint16)   # small negative bf16
+    got = O.dequant_affine4(words.astype(np.uint32).view(np.int32), sc, bi)
+    for n in range(N):
+        for k in range(K):
+            want = O.widen_bf16(sc[n, k // 64]) * q[n, k] + O.widen_bf16(bi[n, k // 64])
+            assert got[n, k] == want
+    # bf16_weights rounds each weight once, to nearest even
+    r = O.dequant_affine4(words.astype(np.uint32), sc, bi, bf16_weights=True)
+    assert np.array_equal(r, O.round_to_bf16(got))
+
+
 # ---------------------------------------------------------------- MLP
 
 def test_swiglu_matches_torch(rng):
