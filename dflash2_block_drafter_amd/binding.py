@@ -80,6 +80,7 @@ _SIGS = {
     "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dfl_bind_target": (_I, [_P, _P, _P, _I, _P]),
     "dfl_context_append_workspace_bytes": (_Z, [_P, _I, _I]),
+    "dfl_linear_q4": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _I, _P, _Z, _P]),
     "dfl_context_append": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "dfl_set_timed_kernel": (_I, [_P, _I]),
     "dfl_read_kernel_time": (_I, [_P, C.POINTER(C.c_double), C.POINTER(C.c_int64),
@@ -255,6 +256,14 @@ def dfl_linear(x, M, K, ldx, W, N, y, ldy, out_f32, ws, stream=None):
     _check(lib().dfl_linear(_bf(x), M, K, ldx, _bf(W), N, _ptr(y, torch.float32 if out_f32 else torch.bfloat16),
                             ldy, int(out_f32), _ptr(ws) if ws is not None else None,
                             ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def dfl_linear_q4(x, M, K, ldx, packed, scales, biases, N, y, ldy, out_f32, ws, stream=None):
+    """packed: int32 tensor [N, K/8] of 4-bit fields (bit patterns of the uint32 words)."""
+    _check(lib().dfl_linear_q4(_bf(x), M, K, ldx, _i32(packed), _bf(scales), _bf(biases), N,
+                               _ptr(y, torch.float32 if out_f32 else torch.bfloat16), ldy, int(out_f32),
+                               _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
+                               _stream(stream)))
 
 
 def dfl_head_norm_rope(x, rows, heads, D, ldx, gamma, eps, theta, pos0, rows_per_req, stream=None):

@@ -788,6 +788,27 @@ int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int 
   return DFL_OK;
 }
 
+int dfl_linear_q4(const dfl_bf16* x, int M, int K, int ldx, const uint32_t* packed, const dfl_bf16* scales,
+                  const dfl_bf16* biases, int N, void* y, int ldy, int out_f32, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  DFL_REQUIRE(x && packed && scales && biases && y, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(M > 0 && N > 0 && K > 0 && ldx >= K && ldy >= N, DFL_E_INVALID, "bad sizes");
+  DFL_REQUIRE(K % 64 == 0 && ldx % 8 == 0, DFL_E_UNSUPPORTED, "K must be a multiple of 64 and ldx of 8");
+  DFL_REQUIRE(reinterpret_cast<uintptr_t>(packed) % 16 == 0, DFL_E_INVALID, "packed weights must be 16-byte aligned");
+  const dfl::GemmPlan pl = dfl::plan_gemm(M, N, K);
+  DFL_REQUIRE(ws_bytes >= pl.partial_bytes && (pl.partial_bytes == 0 || ws), DFL_E_WORKSPACE,
+              "workspace %zu < %zu bytes", ws_bytes, pl.partial_bytes);
+  DFL_REQUIRE(pl.partial_bytes == 0 || aligned(ws), DFL_E_INVALID, "workspace must be %zu-byte aligned", kAlign);
+  dfl::WeightRef w;
+  w.q = packed;
+  w.scales = scales;
+  w.biases = biases;
+  hipError_t e = dfl::launch_gemm(pl, x, ldx, w, M, N, K, out_f32 ? dfl::EPI_F32 : dfl::EPI_BF16, y, ldy, nullptr, 0,
+                                  0, static_cast<float*>(ws), stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
 int dfl_head_norm_rope(dfl_bf16* x, int rows, int heads, int D, int ldx, const dfl_bf16* gamma, float eps,
                        float theta, const int32_t* pos0, int rows_per_req, hipStream_t stream) {
   DFL_REQUIRE(x && gamma && pos0, DFL_E_INVALID, "NULL argument");

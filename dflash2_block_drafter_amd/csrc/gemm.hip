@@ -21,6 +21,8 @@
 // Split-K: grid.z slices K; slices write fp32 partials and a separate kernel sums them
 // in slice order (deterministic, no float atomics) and applies the epilogue, or the
 // partials are left for the consuming kernel, which sums them in the same order.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,6 +46,11 @@ struct GemmArgs {
   float* partial;
   int splits;
   float* tile_max;  // EPI_F32, one split: [M, gridDim.x] row maxima of each BN-column tile
+  // 4-bit affine weights (used instead of W): row-major packed [N, K/8] words with scales and
+  // biases [N, K/64] bf16, or tile-contiguous blocks (q4_tiled_words)
+  const uint32_t* Wq;
+  const uint16_t* Ws;
+  const uint16_t* Wb;
 };
 
 __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, float v) {
@@ -109,15 +116,70 @@ struct TileLoader {
   }
 };
 
+// 4-bit affine weights ([P2] `quantizedWeight`: groups of 64 inputs, w = scale * q + bias).
+// A K step is one group per row: each thread loads one 16-byte chunk of packed fields (32
+// weights of one row) and that row's (scale, bias), and dequantizes in fp32 (one fma per
+// weight, rounded once to bf16) while parking the step in LDS, so the tile compute is the
+// bf16 one.  TILED: per (N tile, K step) a block of BN rows x 8 words followed by BN words
+// of scale | bias << 16, written once by tile_q4_kernel.
+template <int BM, int BN, int BKS, int NT, bool TILED>
+struct TileLoaderQ4 {
+  static constexpr int CPR = BKS / 8;
+  static constexpr int A_PER = BM * CPR / NT;
+  static_assert(A_PER * NT == BM * CPR, "A tile must split evenly over threads");
+  static_assert(BKS == 64 && BN * 2 == NT, "one 16-byte chunk of packed fields per thread");
+  u32x4_t a[A_PER];
+  u32x4_t w;
+  uint32_t sb;
+
+  __device__ __forceinline__ void load(const GemmArgs& p, int m0, int n0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + i * NT;
+      const int gm = min(m0 + c / CPR, p.M - 1);
+      a[i] = *reinterpret_cast<const u32x4_t*>(p.A + (size_t)gm * p.lda + k0 + (c % CPR) * 8);
+    }
+    const int row = tid >> 1, half = tid & 1;
+    if (TILED) {
+      const uint32_t* blk = p.Wq + ((size_t)(n0 / BN) * (p.K / BKS) + k0 / BKS) * (BN * 9);
+      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + row * 8 + half * 4));
+      sb = blk[BN * 8 + row];
+    } else {
+      const int gn = min(n0 + row, p.N - 1);
+      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.Wq + (size_t)gn * (p.K / 8) + k0 / 8 + half * 4));
+      const size_t g = (size_t)gn * (p.K / BKS) + k0 / BKS;
+      sb = static_cast<uint32_t>(p.Ws[g]) | (static_cast<uint32_t>(p.Wb[g]) << 16);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* sA, uint16_t* sB, int tid) const {
+    constexpr int LS = BKS + 8;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const int c = tid + i * NT;
+      *reinterpret_cast<u32x4_t*>(&sA[(c / CPR) * LS + (c % CPR) * 8]) = a[i];
+    }
+    const float sc = bf16_to_f32(static_cast<uint16_t>(sb & 0xFFFFu));
+    const float bi = bf16_to_f32(static_cast<uint16_t>(sb >> 16));
+    const int row = tid >> 1, half = tid & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = fmaf(sc, static_cast<float>((w[j] >> (4 * e)) & 0xFu), bi);
+      *reinterpret_cast<u32x4_t*>(&sB[row * LS + half * 32 + j * 8]) = pack8(f);
+    }
+  }
+};
+
 // W rows for EPI_SILU_MUL are interleaved per 16: [gate 16 | up 16] ... so output
 // column j pairs accumulator columns (j/16)*32 + j%16 (gate) and +16 (up).
-template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED>
+template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED, bool Q4 = false>
 __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM / 16;
   constexpr int TN = BN / WN / 16;
   constexpr int LDS_STRIDE = BKS + 8;  // +16 bytes: 16-byte reads of 16 rows hit distinct banks
-  using Loader = TileLoader<BM, BN, BKS, NT, TILED>;
+  using Loader = std::conditional_t<Q4, TileLoaderQ4<BM, BN, BKS, NT, TILED>, TileLoader<BM, BN, BKS, NT, TILED>>;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
 
@@ -324,7 +386,49 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __res
   *reinterpret_cast<u32x4_t*>(dst + c * 8) = v;
 }
 
+// Tile-contiguous 4-bit weights: per (N tile t, K step s) a block of kBN rows x 8 packed words
+// followed by kBN words of scale | bias << 16; rows past N are zero (weights 0).  rows
+// (optional): destination row n takes source row rows[n].
+__global__ __launch_bounds__(256) void tile_q4_kernel(const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
+                                                      const uint16_t* __restrict__ bi, int N, int K,
+                                                      const int32_t* __restrict__ rows, uint32_t* __restrict__ dst,
+                                                      size_t words) {
+  const size_t w = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= words) return;
+  constexpr int BLK = kBN * 9;
+  const size_t block = w / BLK;
+  const int within = static_cast<int>(w % BLK);
+  const int steps = K / BK;
+  const int sstep = static_cast<int>(block % steps);
+  const int t = static_cast<int>(block / steps);
+  uint32_t v = 0;
+  if (within < kBN * 8) {
+    const int n = t * kBN + within / 8;
+    if (n < N) {
+      const size_t src = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
+      v = q[src * (K / 8) + sstep * 8 + within % 8];
+    }
+  } else {
+    const int n = t * kBN + (within - kBN * 8);
+    if (n < N) {
+      const size_t src = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
+      const size_t g = src * (K / BK) + sstep;
+      v = static_cast<uint32_t>(sc[g]) | (static_cast<uint32_t>(bi[g]) << 16);
+    }
+  }
+  dst[w] = v;
+}
+
 }  // namespace
+
+size_t q4_tiled_words(int N, int K) { return (size_t)((N + kBN - 1) / kBN) * (K / BK) * kBN * 9; }
+
+hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint16_t* biases, int N, int K,
+                          uint32_t* dst, hipStream_t stream, const int32_t* rows) {
+  const size_t words = q4_tiled_words(N, K);
+  tile_q4_kernel<<<(unsigned)((words + 255) / 256), 256, 0, stream>>>(q, scales, biases, N, K, rows, dst, words);
+  return hipGetLastError();
+}
 
 size_t tiled_weight_elems(int N, int K) { return (size_t)((N + kBN - 1) / kBN) * kBN * K; }
 
@@ -350,14 +454,16 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return pl;
 }
 
-hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
-                       int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
-                       float* partial, hipStream_t stream, float* tile_max) {
-  if (tile_max && (epi != EPI_F32 || pl.splits != 1)) return hipErrorInvalidValue;
+namespace {
+
+GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K, int epi,
+                   void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial, float* tile_max) {
   GemmArgs p;
-  p.tile_max = tile_max;
   p.A = A;
-  p.W = W;
+  p.W = W.w;
+  p.Wq = W.q;
+  p.Ws = W.scales;
+  p.Wb = W.biases;
   p.lda = lda;
   p.M = M;
   p.N = N;
@@ -371,49 +477,73 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uin
   p.nsplit = epi == EPI_F32 ? (out1 ? nsplit : N) : N;
   p.partial = partial;
   p.splits = pl.splits;
-  dim3 grid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM, pl.splits);
-  if (w_tiled)
-    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true><<<grid, 512, 0, stream>>>(p);
-  else
-    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false><<<grid, 512, 0, stream>>>(p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.splits == 1) return e;
-  const int nout = epi == EPI_SILU_MUL ? N / 2 : N;
+  p.tile_max = tile_max;
+  return p;
+}
+
+hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {
+  const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM, pl.splits);
+  if (W.q) {
+    if (W.tiled)
+      gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true, true><<<grid, 512, 0, stream>>>(p);
+    else
+      gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false, true><<<grid, 512, 0, stream>>>(p);
+  } else {
+    if (W.tiled)
+      gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true><<<grid, 512, 0, stream>>>(p);
+    else
+      gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false><<<grid, 512, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const GemmArgs& p, hipStream_t stream) {
+  const int nout = p.epi == EPI_SILU_MUL ? p.N / 2 : p.N;
   if (nout % 4 == 0 && p.nsplit % 4 == 0) {
-    const size_t quads = (size_t)M * nout / 4;
+    const size_t quads = (size_t)p.M * nout / 4;
     splitk_reduce_kernel<4><<<(unsigned)((quads + 255) / 256), 256, 0, stream>>>(p);
   } else {
-    const size_t total = (size_t)M * nout;
+    const size_t total = (size_t)p.M * nout;
     splitk_reduce_kernel<1><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
+                       int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
+                       hipStream_t stream, float* tile_max) {
+  if (tile_max && (epi != EPI_F32 || pl.splits != 1)) return hipErrorInvalidValue;
+  if (W.q && K % BK != 0) return hipErrorInvalidValue;
+  const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max);
+  hipError_t e = launch_main(p, pl, W, stream);
+  if (e != hipSuccess || pl.splits == 1) return e;
+  return launch_reduce(p, stream);
+}
+
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
+                       int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
+                       float* partial, hipStream_t stream, float* tile_max) {
+  WeightRef w;
+  w.w = W;
+  w.tiled = w_tiled;
+  return launch_gemm(pl, A, lda, w, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, stream, tile_max);
+}
+
+hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,
+                                int K, float* partial, hipStream_t stream) {
+  // one split: the plain fp32 result is plane 0
+  const GemmArgs p = make_args(pl, A, lda, W, M, N, K, EPI_F32, partial, N, nullptr, 0, N, partial, nullptr);
+  return launch_main(p, pl, W, stream);
+}
+
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
                                 bool w_tiled, int M, int N, int K, float* partial, hipStream_t stream) {
-  GemmArgs p;
-  p.tile_max = nullptr;
-  p.A = A;
-  p.W = W;
-  p.lda = lda;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.k_per_split = pl.k_per_split;
-  p.epi = EPI_F32;
-  p.out0 = partial;  // one split: the plain fp32 result is plane 0
-  p.ld0 = N;
-  p.out1 = nullptr;
-  p.ld1 = 0;
-  p.nsplit = N;
-  p.partial = partial;
-  p.splits = pl.splits;
-  dim3 grid((N + kBN - 1) / kBN, (M + kBM - 1) / kBM, pl.splits);
-  if (w_tiled)
-    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, true><<<grid, 512, 0, stream>>>(p);
-  else
-    gemm_bf16_kernel<kBM, kBN, BK, 2, 4, 2, 1, false><<<grid, 512, 0, stream>>>(p);
-  return hipGetLastError();
+  WeightRef w;
+  w.w = W;
+  w.tiled = w_tiled;
+  return launch_gemm_partials(pl, A, lda, w, M, N, K, partial, stream);
 }
 
 }  // namespace dfl

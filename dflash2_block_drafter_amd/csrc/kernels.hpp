@@ -27,6 +27,26 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int M, int N, int K);
+
+// A projection weight [N, K]: bf16 w (row-major, or tile-contiguous when tiled), or 4-bit
+// affine q (row-major packed words [N, K/8] with scales and biases [N, K/64] bf16, or the
+// tile-contiguous blocks of launch_tile_q4 when tiled).
+struct WeightRef {
+  const uint16_t* w = nullptr;
+  const uint32_t* q = nullptr;
+  const uint16_t* scales = nullptr;
+  const uint16_t* biases = nullptr;
+  bool tiled = false;
+};
+hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
+                       int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
+                       hipStream_t stream, float* tile_max = nullptr);
+hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,
+                                int K, float* partial, hipStream_t stream);
+// Tile-contiguous 4-bit weights: q4_tiled_words 32-bit words; rows as for launch_tile_weights.
+size_t q4_tiled_words(int N, int K);
+hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint16_t* biases, int N, int K,
+                          uint32_t* dst, hipStream_t stream, const int32_t* rows = nullptr);
 // y = A . W^T.  A [M, K] (lda).  W: row-major [N, K], or tile-contiguous (w_tiled) as
 // written by launch_tile_weights.  EPI_BF16: out0 bf16 (ld0).  EPI_F32: columns < nsplit
 // to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL: W rows

@@ -205,6 +205,16 @@ size_t dfl_linear_workspace_bytes(int M, int N, int K);
 int dfl_linear(const dfl_bf16* x, int M, int K, int ldx, const dfl_bf16* W, int N, void* y,
                int ldy, int out_f32, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Dense projection with 4-bit affine weights ([P2] `quantizedWeight`: groups of 64 inputs
+ * along K, a scale and a bias per group, w = scale * q + bias with q in 0..15).
+ * packed [N, K/8] uint32, 16-byte aligned: field k of row n at bits 4*(k % 8) of word
+ * k / 8; scales, biases [N, K/64] bf16.  The weights are dequantized in fp32 and rounded to
+ * bf16 on the way into the bf16 matrix units; accumulation is fp32.  Other arguments,
+ * outputs and errors as dfl_linear (same workspace size). */
+int dfl_linear_q4(const dfl_bf16* x, int M, int K, int ldx, const uint32_t* packed,
+                  const dfl_bf16* scales, const dfl_bf16* biases, int N, void* y, int ldy,
+                  int out_f32, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Per-head RMSNorm then neox RoPE, in place ([P2] `#block`: q/k norm before RoPE;
  * [P1] per-head RMSNorm and split-half RoPE docstrings).  x holds rows of `heads`
  * heads of D values at leading dimension ldx; row r sits at position

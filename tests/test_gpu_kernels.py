@@ -101,6 +101,23 @@ def test_block_attention(D, NH, NKV, G, ctx):
     assert_bf16_close(out.reshape(Bq, G, NH, D), want, "attention")
 
 
+@pytest.mark.parametrize("M,N,K,out_f32", [
+    (128, 6144, 5120, False),   # the fused q|k|v shape, split K
+    (120, 1000, 1024, True),    # ragged N tile, fp32 out
+    (7, 300, 128, False),       # ragged M and N, two groups
+])
+def test_linear_q4(M, N, K, out_f32):
+    x = bf((M, K), 61)
+    packed, sc, bi = synth.affine4_weight(N, K, seed=62, device=DEV)
+    y = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.bfloat16, device=DEV)
+    ws = B.workspace(B.dfl_linear_workspace_bytes(M, N, K))
+    B.dfl_linear_q4(x, M, K, K, packed, sc, bi, N, y, N, out_f32, ws)
+    torch.cuda.synchronize()
+    w = O.dequant_affine4(packed.cpu().numpy(), h(sc), h(bi), bf16_weights=True)
+    want = O.linear(h(x), w)
+    (assert_f32_close if out_f32 else assert_bf16_close)(y, want, "4-bit affine projection")
+
+
 @pytest.mark.parametrize("D,NH,NKV,G,ctx,pos,window", [
     (128, 32, 8, 16, [700, 2048], [700, 2048], 300),    # window inside one chunk, several tiles masked
     (128, 32, 8, 16, [5000, 129], [5000, 140], 2048),   # long context: earlier chunks skipped
