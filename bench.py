@@ -34,6 +34,9 @@ def parse():
     p.add_argument("--workload", default="full", choices=["full", "long", "tiny", "conv", "selector"],
                    help="full/long/tiny: draft_block; conv, selector: the grouped-conv and "
                         "candidate-selector microbenchmarks")
+    p.add_argument("--weights", default="bf16", choices=["bf16", "q4"],
+                   help="layer projection weights: bf16, or 4-bit affine (groups of 64); the q4 line "
+                        "reports no cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB copy (counter calibration) and exit")
@@ -84,8 +87,13 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.time()
     weights = synth.drafter_weights(w, device=dev)
+    q4 = synth.drafter_q4_weights(w, device=dev) if args.weights == "q4" else None
+    if q4 is not None:
+        for name in q4:
+            del weights[name + ".weight"]
     tgt = synth.target_inputs(w, device=dev, with_taps=not w.kv_given)
-    dr = Drafter(d, weights)
+    dr = Drafter(d, weights, q4_weights=q4)
+    del q4
     Bq, G, L = w.batch, d.block_size, w.ctx_len
     if w.kv_given:
         K, V = [], []
@@ -177,7 +185,7 @@ def main():
            "walk": round(walk_bytes / (walk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if walk_ms else None}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.weights == "bf16":
         print("# cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, weights, tgt)
 
@@ -196,7 +204,9 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/embeddings)",
         "config": {"workload": f"{w.name}: {d.layers}-layer drafter H={d.hidden} NH/NKV/D="
                                f"{d.heads}/{d.kv_heads}/{d.head_dim} F={d.intermediate} V={d.vocab}, "
-                               f"B={Bq} G={G} L={L}", "B": Bq, "G": G, "L": L},
+                               f"B={Bq} G={G} L={L}" + (", 4-bit affine layer projections" if args.weights == "q4"
+                                                        else ""),
+                   "B": Bq, "G": G, "L": L, "weights": args.weights},
         "roofline": roofline,
         "hbm_frac": hbm,
         "breakdown_ms": {k: v["ms"] for k, v in breakdown.items()},

@@ -46,9 +46,20 @@ class dfl_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in LAYER_FIELDS]
 
 
+class dfl_q4_weight(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("packed", "scales", "biases")]
+
+
+Q4_FIELDS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+
+class dfl_q4_layer(C.Structure):
+    _fields_ = [(n, dfl_q4_weight) for n in Q4_FIELDS]
+
+
 class dfl_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("fc", "hidden_norm", "norm", "sel_proj", "pred", "succ")] + \
-               [("layers", C.POINTER(dfl_layer_weights))]
+               [("layers", C.POINTER(dfl_layer_weights)), ("q4_layers", C.POINTER(dfl_q4_layer))]
 
 
 _P, _I, _F, _Z = C.c_void_p, C.c_int, C.c_float, C.c_size_t
@@ -173,10 +184,14 @@ def make_config(dims, tap_layer_ids=None) -> tuple[dfl_config, object]:
     return cfg, (ids, kinds)
 
 
-def dfl_drafter_load(dims, weights: dict, tap_layer_ids=None, stream=None) -> int:
-    """weights: checkpoint name -> bf16 device tensor (the drafter's checkpoint names)."""
+def dfl_drafter_load(dims, weights: dict, tap_layer_ids=None, stream=None, q4_weights=None) -> int:
+    """weights: checkpoint name -> bf16 device tensor (the drafter's checkpoint names).
+    q4_weights: None, or checkpoint name of a layer projection without ".weight" ->
+    (packed int32 [N, K/8], scales bf16 [N, K/64], biases bf16 [N, K/64]); the projections
+    then load from these and their bf16 entries in `weights` are not read."""
     cfg, keep = make_config(dims, tap_layer_ids)
     layers = (dfl_layer_weights * dims.layers)()
+    q4_layers = None
     names = {"input_norm": "input_layernorm.weight", "post_norm": "post_attention_layernorm.weight",
              "q_proj": "self_attn.q_proj.weight", "k_proj": "self_attn.k_proj.weight",
              "v_proj": "self_attn.v_proj.weight", "o_proj": "self_attn.o_proj.weight",
@@ -187,13 +202,22 @@ def dfl_drafter_load(dims, weights: dict, tap_layer_ids=None, stream=None) -> in
              "mlp_base": "mlp_conv.base_kernel", "mlp_kproj": "mlp_conv.kernel_projection.weight"}
     for i in range(dims.layers):
         for f, n in names.items():
+            if q4_weights is not None and f in Q4_FIELDS:
+                continue
             setattr(layers[i], f, _bf(weights[f"layers.{i}.{n}"]))
+    if q4_weights is not None:
+        q4_layers = (dfl_q4_layer * dims.layers)()
+        for i in range(dims.layers):
+            for f in Q4_FIELDS:
+                packed, sc, bi = q4_weights[f"layers.{i}.{names[f][:-len('.weight')]}"]
+                setattr(q4_layers[i], f, dfl_q4_weight(_i32(packed), _bf(sc), _bf(bi)))
     w = dfl_weights(_bf(weights["fc.weight"]), _bf(weights["hidden_norm.weight"]),
                     _bf(weights["norm.weight"]),
                     _bf(weights["candidate_selector.hidden_projection.weight"]),
                     _bf(weights["candidate_selector.predecessor_codebook"]),
                     _bf(weights["candidate_selector.successor_codebook"]),
-                    C.cast(layers, C.POINTER(dfl_layer_weights)))
+                    C.cast(layers, C.POINTER(dfl_layer_weights)),
+                    C.cast(q4_layers, C.POINTER(dfl_q4_layer)) if q4_layers is not None else None)
     h = C.c_void_p()
     _check(lib().dfl_drafter_load(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
     del keep

@@ -62,7 +62,19 @@ struct LayerBuf {
   uint16_t *qkv, *o, *gateup, *down;
   uint16_t *attn_base, *attn_kproj, *mlp_base, *mlp_kproj;
   uint16_t* kv_ctx;  // [k | v] rows for the context path
+  // 4-bit drafters: the same five projections as tile-contiguous 4-bit blocks (the bf16
+  // pointers above are then NULL)
+  uint32_t *qkv_q4 = nullptr, *o_q4 = nullptr, *gateup_q4 = nullptr, *down_q4 = nullptr, *kv_ctx_q4 = nullptr;
 };
+
+// the weight of one of a layer's projections, bf16 or 4-bit, both tile-contiguous
+dfl::WeightRef wref(const uint16_t* bf, const uint32_t* q4) {
+  dfl::WeightRef w;
+  w.w = bf;
+  w.q = q4;
+  w.tiled = true;
+  return w;
+}
 
 struct TimedLaunch {
   hipEvent_t start, stop;
@@ -76,6 +88,7 @@ struct dfl_drafter {
   void* arena = nullptr;
   uint16_t *fc, *hidden_norm, *norm, *sel_proj, *pred, *succ;
   std::vector<LayerBuf> layers;
+  bool q4 = false;                   // the layer projections hold 4-bit weights
   std::vector<int> window;           // per layer: 0 = full attention, W = sliding window
   uint16_t* head = nullptr;          // the bound target head, tile-contiguous (dfl_bind_target)
   const void* head_src = nullptr;    // the caller pointer it was copied from
@@ -126,9 +139,11 @@ int timed(dfl_drafter* d, int k, double bytes, hipStream_t s, F&& f) {
     if (rc_ != DFL_OK) return rc_; \
   } while (0)
 
-double gemm_bytes(int M, int N, int K, int epi) {
+// Algorithmic bytes of y = A . W^T: A and the output once, the weight at 2 bytes per
+// element, or (q4) at half a byte plus a bf16 scale and bias per 64.
+double gemm_bytes(int M, int N, int K, int epi, bool q4 = false) {
   const double out = epi == dfl::EPI_F32 ? 4.0 * M * N : (epi == dfl::EPI_SILU_MUL ? 1.0 * M * N : 2.0 * M * N);
-  return 2.0 * M * K + 2.0 * N * K + out;
+  return 2.0 * M * K + (q4 ? 0.5625 : 2.0) * N * K + out;
 }
 
 int check_config(const dfl_config* c) {
@@ -269,8 +284,8 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
     return dfl::launch_conv(n, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm_partials(p_qkv, a, H, L.qkv, true, T, qkvw, H, part, stream);
+  DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32, d->q4), stream, [&] {
+    return dfl::launch_gemm_partials(p_qkv, a, H, wref(L.qkv, L.qkv_q4), T, qkvw, H, part, stream);
   }));
   DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * T * qkvw * p_qkv.splits + 2.0 * T * qkvw, stream, [&] {
     return dfl::launch_head_norm_rope_planes(dfl::gemm_planes(p_qkv, part, T, qkvw), qkv, qkvw, T, NH + NKV, NH, D,
@@ -284,8 +299,9 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   }));
   // o and down keep a separate split-K reduce: their consumer, the residual conv + norm,
   // runs one workgroup per row and reads bf16 rows far faster than it could sum planes
-  DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16), stream, [&] {
-    return dfl::launch_gemm(p_o, ao, NH * D, L.o, true, T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+  DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16, d->q4), stream, [&] {
+    return dfl::launch_gemm(p_o, ao, NH * D, wref(L.o, L.o_q4), T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0,
+                            part, stream);
   }));
   // x = x_in + conv1(u), fused with the MLP half's input norm
   DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
@@ -299,12 +315,13 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
     return dfl::launch_conv(n, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL), stream, [&] {
-    return dfl::launch_gemm(p_gu, a, H, L.gateup, true, T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part,
-                            stream);
+  DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL, d->q4), stream, [&] {
+    return dfl::launch_gemm(p_gu, a, H, wref(L.gateup, L.gateup_q4), T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr,
+                            0, 0, part, stream);
   }));
-  DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16), stream, [&] {
-    return dfl::launch_gemm(p_dn, p, F, L.down, true, T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part, stream);
+  DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16, d->q4), stream, [&] {
+    return dfl::launch_gemm(p_dn, p, F, wref(L.down, L.down_q4), T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part,
+                            stream);
   }));
   if (next_gamma) {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
@@ -334,12 +351,19 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
   DFL_REQUIRE(w && w->fc && w->hidden_norm && w->norm && w->sel_proj && w->pred && w->succ && w->layers,
               DFL_E_INVALID, "a drafter weight pointer is NULL");
   const dfl_config& c = *cfg;
+  const bool q4 = w->q4_layers != nullptr;
   for (int i = 0; i < c.layers; ++i) {
     const dfl_layer_weights& L = w->layers[i];
-    DFL_REQUIRE(L.input_norm && L.post_norm && L.q_proj && L.k_proj && L.v_proj && L.o_proj && L.q_norm &&
-                    L.k_norm && L.gate_proj && L.up_proj && L.down_proj && L.attn_base && L.attn_kproj &&
-                    L.mlp_base && L.mlp_kproj,
+    DFL_REQUIRE(L.input_norm && L.post_norm && L.q_norm && L.k_norm && L.attn_base && L.attn_kproj && L.mlp_base &&
+                    L.mlp_kproj && (q4 || (L.q_proj && L.k_proj && L.v_proj && L.o_proj && L.gate_proj &&
+                                           L.up_proj && L.down_proj)),
                 DFL_E_INVALID, "layer %d has a NULL weight pointer", i);
+    if (q4) {
+      const dfl_q4_layer& Q = w->q4_layers[i];
+      for (const dfl_q4_weight* qw : {&Q.q_proj, &Q.k_proj, &Q.v_proj, &Q.o_proj, &Q.gate_proj, &Q.up_proj,
+                                      &Q.down_proj})
+        DFL_REQUIRE(qw->packed && qw->scales && qw->biases, DFL_E_INVALID, "layer %d has a NULL 4-bit weight", i);
+    }
   }
   const size_t H = c.hidden, D = c.head_dim, NH = c.heads, NKV = c.kv_heads, F = c.intermediate;
   const size_t ng = H / c.conv_group, V = c.vocab, R = c.rank;
@@ -361,15 +385,26 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
     off_post = lc.off; lc.take<uint16_t>(H);
     off_qn = lc.off; lc.take<uint16_t>(D);
     off_kn = lc.off; lc.take<uint16_t>(D);
-    off_qkv = lc.off; lc.take<uint16_t>(tiled(qkvw, H));
-    off_o = lc.off; lc.take<uint16_t>(tiled(H, NH * D));
-    off_gu = lc.off; lc.take<uint16_t>(tiled(2 * F, H));
-    off_dn = lc.off; lc.take<uint16_t>(tiled(H, F));
+    if (q4) {  // 32-bit words of 4-bit blocks
+      off_qkv = lc.off; lc.take<uint32_t>(dfl::q4_tiled_words((int)qkvw, (int)H));
+      off_o = lc.off; lc.take<uint32_t>(dfl::q4_tiled_words((int)H, (int)(NH * D)));
+      off_gu = lc.off; lc.take<uint32_t>(dfl::q4_tiled_words((int)(2 * F), (int)H));
+      off_dn = lc.off; lc.take<uint32_t>(dfl::q4_tiled_words((int)H, (int)F));
+    } else {
+      off_qkv = lc.off; lc.take<uint16_t>(tiled(qkvw, H));
+      off_o = lc.off; lc.take<uint16_t>(tiled(H, NH * D));
+      off_gu = lc.off; lc.take<uint16_t>(tiled(2 * F, H));
+      off_dn = lc.off; lc.take<uint16_t>(tiled(H, F));
+    }
     off_ab = lc.off; lc.take<uint16_t>(4 * H);
     off_ak = lc.off; lc.take<uint16_t>(tiled(4 * ng, H));
     off_mb = lc.off; lc.take<uint16_t>(4 * H);
     off_mk = lc.off; lc.take<uint16_t>(tiled(4 * ng, H));
-    off_kv = lc.off; lc.take<uint16_t>(tiled(2 * NKV * D, H));
+    if (q4) {
+      off_kv = lc.off; lc.take<uint32_t>(dfl::q4_tiled_words((int)(2 * NKV * D), (int)H));
+    } else {
+      off_kv = lc.off; lc.take<uint16_t>(tiled(2 * NKV * D, H));
+    }
     cv.off += lc.off * c.layers;
   }
   const size_t per_layer = (cv.off - layer0) / c.layers;
@@ -378,6 +413,7 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
   d->cfg = c;
   d->cfg.tap_layer_ids = nullptr;
   d->cfg.sliding_layers = nullptr;
+  d->q4 = q4;
   d->window.assign(c.layers, 0);
   for (int i = 0; i < c.layers; ++i)
     if (c.sliding_window > 0 && (!c.sliding_layers || c.sliding_layers[i])) d->window[i] = c.sliding_window;
@@ -420,6 +456,31 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
       if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "weight tiling: %s", hipGetErrorString(e));
     }
   };
+  auto tile4 = [&](const uint32_t* q, const void* sc, const void* bi, size_t n, size_t k, uint32_t* dst) {
+    if (rc == DFL_OK) {
+      hipError_t e = dfl::launch_tile_q4(q, static_cast<const uint16_t*>(sc), static_cast<const uint16_t*>(bi),
+                                         (int)n, (int)k, dst, stream);
+      if (e != hipSuccess) rc = fail(DFL_E_DEVICE, "4-bit weight tiling: %s", hipGetErrorString(e));
+    }
+  };
+  // 4-bit staging of the fused K = H projections: packed words, then scales, then biases,
+  // each row-major over the fused rows (fits the bf16 staging: 9/16 of its bytes)
+  const size_t nmax = std::max({qkvw, 2 * F, 2 * NKV * D});
+  uint32_t* sq = reinterpret_cast<uint32_t*>(stage);
+  uint16_t* ss = reinterpret_cast<uint16_t*>(sq + nmax * H / 8);
+  uint16_t* sb = ss + nmax * H / 64;
+  // rows [row0, row0 + n) of the staging from one K = H weight
+  auto q4_rows = [&](const dfl_q4_weight& qw, size_t row0, size_t n) {
+    cp(sq + row0 * H / 8, qw.packed, n * H / 2);
+    cp(ss + row0 * H / 64, qw.scales, n * H / 32);
+    cp(sb + row0 * H / 64, qw.biases, n * H / 32);
+  };
+  // gate (row0 = 0) or up (row0 = 16) into the staging interleaved per 16 rows
+  auto q4_interleave = [&](const dfl_q4_weight& qw, size_t row0) {
+    cp2d(sq + row0 * H / 8, 32 * H / 2, qw.packed, 16 * H / 2, 16 * H / 2, F / 16);
+    cp2d(ss + row0 * H / 64, 32 * H / 32, qw.scales, 16 * H / 32, 16 * H / 32, F / 16);
+    cp2d(sb + row0 * H / 64, 32 * H / 32, qw.biases, 16 * H / 32, 16 * H / 32, F / 16);
+  };
   tile(w->fc, H, c.n_taps * H, d->fc);
   cp(d->hidden_norm, w->hidden_norm, H * 2);
   cp(d->norm, w->norm, H * 2);
@@ -435,19 +496,46 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
     L.post_norm = at(lb + off_post);
     L.q_norm = at(lb + off_qn);
     L.k_norm = at(lb + off_kn);
-    L.qkv = at(lb + off_qkv);
-    L.o = at(lb + off_o);
-    L.gateup = at(lb + off_gu);
-    L.down = at(lb + off_dn);
     L.attn_base = at(lb + off_ab);
     L.attn_kproj = at(lb + off_ak);
     L.mlp_base = at(lb + off_mb);
     L.mlp_kproj = at(lb + off_mk);
-    L.kv_ctx = at(lb + off_kv);
     cp(L.in_norm, s.input_norm, H * 2);
     cp(L.post_norm, s.post_norm, H * 2);
     cp(L.q_norm, s.q_norm, D * 2);
     cp(L.k_norm, s.k_norm, D * 2);
+    cp(L.attn_base, s.attn_base, 4 * H * 2);
+    tile(s.attn_kproj, 4 * ng, H, L.attn_kproj);
+    cp(L.mlp_base, s.mlp_base, 4 * H * 2);
+    tile(s.mlp_kproj, 4 * ng, H, L.mlp_kproj);
+    if (q4) {
+      const dfl_q4_layer& Q = w->q4_layers[i];
+      auto at4 = [&](size_t off) { return reinterpret_cast<uint32_t*>(A + off); };
+      L.qkv = L.o = L.gateup = L.down = L.kv_ctx = nullptr;
+      L.qkv_q4 = at4(lb + off_qkv);
+      L.o_q4 = at4(lb + off_o);
+      L.gateup_q4 = at4(lb + off_gu);
+      L.down_q4 = at4(lb + off_dn);
+      L.kv_ctx_q4 = at4(lb + off_kv);
+      q4_rows(Q.q_proj, 0, NH * D);
+      q4_rows(Q.k_proj, NH * D, NKV * D);
+      q4_rows(Q.v_proj, (NH + NKV) * D, NKV * D);
+      tile4(sq, ss, sb, qkvw, H, L.qkv_q4);
+      tile4(Q.o_proj.packed, Q.o_proj.scales, Q.o_proj.biases, H, NH * D, L.o_q4);
+      q4_interleave(Q.gate_proj, 0);
+      q4_interleave(Q.up_proj, 16);
+      tile4(sq, ss, sb, 2 * F, H, L.gateup_q4);
+      tile4(Q.down_proj.packed, Q.down_proj.scales, Q.down_proj.biases, H, F, L.down_q4);
+      q4_rows(Q.k_proj, 0, NKV * D);
+      q4_rows(Q.v_proj, NKV * D, NKV * D);
+      tile4(sq, ss, sb, 2 * NKV * D, H, L.kv_ctx_q4);
+      continue;
+    }
+    L.qkv = at(lb + off_qkv);
+    L.o = at(lb + off_o);
+    L.gateup = at(lb + off_gu);
+    L.down = at(lb + off_dn);
+    L.kv_ctx = at(lb + off_kv);
     cp(stage, s.q_proj, NH * D * H * 2);
     cp(stage + NH * D * H, s.k_proj, NKV * D * H * 2);
     cp(stage + (NH + NKV) * D * H, s.v_proj, NKV * D * H * 2);
@@ -458,10 +546,6 @@ int dfl_drafter_load(const dfl_config* cfg, const dfl_weights* w, hipStream_t st
     cp2d(stage + 16 * H, 32 * H * 2, s.up_proj, 16 * H * 2, 16 * H * 2, F / 16);
     tile(stage, 2 * F, H, L.gateup);
     tile(s.down_proj, H, F, L.down);
-    cp(L.attn_base, s.attn_base, 4 * H * 2);
-    tile(s.attn_kproj, 4 * ng, H, L.attn_kproj);
-    cp(L.mlp_base, s.mlp_base, 4 * H * 2);
-    tile(s.mlp_kproj, 4 * ng, H, L.mlp_kproj);
     cp(stage, s.k_proj, NKV * D * H * 2);
     cp(stage + NKV * D * H, s.v_proj, NKV * D * H * 2);
     tile(stage, 2 * NKV * D, H, L.kv_ctx);
@@ -576,9 +660,9 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
   const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
   for (int i = 0; i < c.layers; ++i) {
     const LayerBuf& Lb = d->layers[i];
-    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, true, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
-                              stream);
+    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16, d->q4), stream, [&] {
+      return dfl::launch_gemm(pkv, cc, H, wref(Lb.kv_ctx, Lb.kv_ctx_q4), M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr,
+                              0, 0, part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
       return dfl::launch_context_kv_store(kv, B, L, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,
@@ -636,9 +720,9 @@ int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_
   const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
   for (int i = 0; i < c.layers; ++i) {
     const LayerBuf& Lb = d->layers[i];
-    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16), stream, [&] {
-      return dfl::launch_gemm(pkv, cc, H, Lb.kv_ctx, true, M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr, 0, 0, part,
-                              stream);
+    DFL_TRY(timed(d, DFL_K_GEMM_CONTEXT, gemm_bytes(M, kvw, H, dfl::EPI_BF16, d->q4), stream, [&] {
+      return dfl::launch_gemm(pkv, cc, H, wref(Lb.kv_ctx, Lb.kv_ctx_q4), M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr,
+                              0, 0, part, stream);
     }));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
       return dfl::launch_context_kv_store_ragged(kv, M, B, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,

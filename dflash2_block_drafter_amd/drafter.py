@@ -8,9 +8,9 @@ from . import binding as B_
 
 
 class Drafter:
-    def __init__(self, dims, weights: dict, tap_layer_ids=None):
+    def __init__(self, dims, weights: dict, tap_layer_ids=None, q4_weights=None):
         self.dims = dims
-        self.handle = B_.dfl_drafter_load(dims, weights, tap_layer_ids)
+        self.handle = B_.dfl_drafter_load(dims, weights, tap_layer_ids, q4_weights=q4_weights)
         self._ws = None
 
     def close(self):

@@ -169,13 +169,33 @@ def affine4_weight(N: int, K: int, *, seed: int, device="cpu"):
     """A 4-bit affine projection of N rows over K inputs (groups of 64): packed int32 words
     [N, K/8] of uniform 4-bit fields, scales [N, K/64] ~ |N(0.003, 0.001)| and biases
     = -7.5 * scale + N(0, 0.002), both bf16, so the weights span about +-0.02 around 0."""
-    g = _gen("cpu", seed)
-    q = torch.randint(0, 16, (N, K // 8, 8), generator=g, dtype=torch.int64)
-    words = (q << (4 * torch.arange(8, dtype=torch.int64))).sum(-1)
+    g = _gen(device, seed)
+    q = torch.randint(0, 16, (N, K // 8, 8), generator=g, dtype=torch.int64, device=device)
+    words = (q << (4 * torch.arange(8, dtype=torch.int64, device=device))).sum(-1)
+    del q
     words = torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
-    scales = (torch.randn((N, K // 64), generator=g) * 0.001 + 0.003).abs().to(torch.bfloat16)
-    biases = (-7.5 * scales.float() + torch.randn((N, K // 64), generator=g) * 0.002).to(torch.bfloat16)
-    return words.to(device), scales.to(device), biases.to(device)
+    scales = (torch.randn((N, K // 64), generator=g, device=device) * 0.001 + 0.003).abs().to(torch.bfloat16)
+    biases = (-7.5 * scales.float() + torch.randn((N, K // 64), generator=g, device=device) * 0.002).to(torch.bfloat16)
+    return words, scales, biases
+
+
+def q4_projection_shapes(d: DrafterDims, i: int) -> dict[str, tuple[int, int]]:
+    """The seven projections of layer i that a 4-bit drafter quantizes: checkpoint name
+    without ".weight" -> (N, K)."""
+    H, NH, NKV, D, F = d.hidden, d.heads, d.kv_heads, d.head_dim, d.intermediate
+    p = f"layers.{i}"
+    return {f"{p}.self_attn.q_proj": (NH * D, H), f"{p}.self_attn.k_proj": (NKV * D, H),
+            f"{p}.self_attn.v_proj": (NKV * D, H), f"{p}.self_attn.o_proj": (H, NH * D),
+            f"{p}.mlp.gate_proj": (F, H), f"{p}.mlp.up_proj": (F, H), f"{p}.mlp.down_proj": (H, F)}
+
+
+def drafter_q4_weights(w: Workload, device="cpu") -> dict[str, tuple[torch.Tensor, torch.Tensor, torch.Tensor]]:
+    """4-bit affine layer projections (affine4_weight each, seeded by name)."""
+    out = {}
+    for i in range(w.dims.layers):
+        for name, (N, K) in q4_projection_shapes(w.dims, i).items():
+            out[name] = affine4_weight(N, K, seed=seed_for(w.seed, name + ".q4"), device=device)
+    return out
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

@@ -94,6 +94,21 @@ typedef struct {
   const dfl_bf16* mlp_kproj;   /* [2*2*H/grp, H] */
 } dfl_layer_weights;
 
+/* A 4-bit affine projection [N, K] ([P2] `quantizedWeight`: affine mode, groups of 64 along
+ * K): packed [N, K/8] uint32 (field k at bits 4*(k % 8) of word k / 8), scales and biases
+ * [N, K/64] bf16, w = scale * q + bias. */
+typedef struct {
+  const uint32_t* packed;
+  const dfl_bf16* scales;
+  const dfl_bf16* biases;
+} dfl_q4_weight;
+
+/* The projections [P2] quantizes (the drafter's load: "projections only"; convs, norms and
+ * codebooks stay bf16). */
+typedef struct {
+  dfl_q4_weight q_proj, k_proj, v_proj, o_proj, gate_proj, up_proj, down_proj;
+} dfl_q4_layer;
+
 typedef struct {
   const dfl_bf16* fc;          /* [H, n_taps*H] */
   const dfl_bf16* hidden_norm; /* [H] */
@@ -102,6 +117,10 @@ typedef struct {
   const dfl_bf16* pred;        /* predecessor codebook [V, R] */
   const dfl_bf16* succ;        /* successor codebook [V, R] */
   const dfl_layer_weights* layers; /* host array of `layers` entries */
+  const dfl_q4_layer* q4_layers;   /* NULL, or a host array of `layers` entries: the seven layer
+                                      projections (and the context k|v) then run on these 4-bit
+                                      weights, and the layer entries' q/k/v/o/gate/up/down
+                                      pointers are not read */
 } dfl_weights;
 
 /* Copy and repack every drafter weight into buffers the handle owns ([P2] constructor

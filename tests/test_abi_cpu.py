@@ -136,3 +136,25 @@ def test_load_rejects_null_weights():
     out = C.c_void_p()
     w = B.dfl_weights()
     assert B.lib().dfl_drafter_load(C.byref(cfg), C.byref(w), None, C.byref(out)) == B.DFL_E_INVALID
+
+
+@needs_no_gpu
+def test_load_rejects_null_q4_weight():
+    # a 4-bit drafter: the bf16 projection pointers are not needed, every 4-bit field is
+    cfg, keep = _config()
+    d = configs.TINY_DIMS
+    layers = (B.dfl_layer_weights * d.layers)()
+    q4 = (B.dfl_q4_layer * d.layers)()
+    for i in range(d.layers):
+        for f in B.LAYER_FIELDS:
+            if f not in B.Q4_FIELDS:
+                setattr(layers[i], f, FAKE)
+        for f in B.Q4_FIELDS:
+            setattr(q4[i], f, B.dfl_q4_weight(FAKE, FAKE, FAKE))
+    q4[d.layers - 1].down_proj.biases = None
+    w = B.dfl_weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.cast(layers, C.POINTER(B.dfl_layer_weights)),
+                      C.cast(q4, C.POINTER(B.dfl_q4_layer)))
+    out = C.c_void_p()
+    code, msg = _err(B.lib().dfl_drafter_load(C.byref(cfg), C.byref(w), None, C.byref(out)))
+    assert code == B.DFL_E_INVALID and "4-bit" in msg
+    assert out.value is None

@@ -98,23 +98,31 @@ def test_bound_head_matches_borrowed_head():
     dr.close()
 
 
-def _tiny_parity(w, G=None):
-    """Draft a tiny workload (optionally with a block narrower than block_size) on the GPU
-    and compare it with the oracle at the bf16 rounding points."""
+def _tiny_parity(w, G=None, q4=False):
+    """Draft a tiny workload (optionally with a block narrower than block_size, or with 4-bit
+    layer projections) on the GPU and compare it with the oracle at the bf16 rounding points."""
     d = w.dims
     weights_cpu = synth.drafter_weights(w)
     tgt_cpu = synth.target_inputs(w)
     if G is not None:
         tgt_cpu["embeds"] = tgt_cpu["embeds"][:, :G].contiguous()
+    q4_cpu = synth.drafter_q4_weights(w) if q4 else None
     weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
     tgt = {k: v.to(DEV) for k, v in tgt_cpu.items()}
-    dr = Drafter(d, weights)
+    q4_dev = {k: tuple(t.to(DEV) for t in v) for k, v in q4_cpu.items()} if q4 else None
+    dr = Drafter(d, weights, q4_weights=q4_dev)
     K, V = dr.alloc_kv(w.batch, w.ctx_len)
     dr.materialize(tgt["taps"], K, V)
     tokens, logits = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
                               tgt["lm_head"], want_logits=True)
     torch.cuda.synchronize()
     wh, th = _host(weights_cpu), _host(tgt_cpu)
+    if q4:
+        # the oracle takes the dequantized weights, rounded to bf16 where the kernel feeds
+        # them to the matrix units
+        for name, (packed, sc, bi) in q4_cpu.items():
+            wh[name + ".weight"] = O.dequant_affine4(packed.numpy(), synth.bits(sc), synth.bits(bi),
+                                                     bf16_weights=True)
     ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
@@ -127,6 +135,12 @@ def _tiny_parity(w, G=None):
 def test_tiny_sliding_window_end_to_end():
     # layer 0 slides (window 20 over 32 context rows), layer 1 attends to everything
     ref = _tiny_parity(configs.TINY_SW)
+    assert ref["tokens"].shape == (configs.TINY_SW.batch, configs.TINY_SW.dims.block_size - 1)
+
+
+def test_tiny_q4_projections_end_to_end():
+    # the seven layer projections (and the context k|v) on 4-bit affine weights
+    ref = _tiny_parity(configs.TINY_SW, q4=True)
     assert ref["tokens"].shape == (configs.TINY_SW.batch, configs.TINY_SW.dims.block_size - 1)
 
 
