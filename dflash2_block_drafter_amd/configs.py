@@ -65,6 +65,11 @@ TINY = Workload("tiny", TINY_DIMS, batch=1, ctx_len=32, seed=1)
 # positions over 32 context rows, so block row t sees context rows 13 + t .. 31.
 TINY_SW = Workload("tiny_sw", replace(TINY_DIMS, layers=2, sliding_window=20, sliding_layers=(True, False)),
                    batch=2, ctx_len=32, seed=6)
+# Medium drafter: one layer whose gate/up projection (65536 x 1024 weights) is large enough
+# for the weight-streaming GEMM; B=1, G=8, 32 context rows.
+MEDIUM = Workload("medium", replace(TINY_DIMS, hidden=1024, heads=8, kv_heads=2, head_dim=128,
+                                    intermediate=32768, vocab=2048, rank=32),
+                  batch=1, ctx_len=32, seed=7)
 # Full 5-layer drafter shaped like the 27B-target drafter: B=8, G=16, L=2048.
 FULL = Workload("full", FULL_DIMS, batch=8, ctx_len=2048, seed=4)
 # Long context, large batch: B=64, L=8192, context K/V given as N(0,1).

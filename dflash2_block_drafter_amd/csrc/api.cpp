@@ -215,8 +215,9 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
   };
   L.kpart = cv.off; cv.take<char>(planes_bytes(T, 4 * ng, H));
   size_t part = planes_bytes(T, qkvw, H);
-  const int shapes[][3] = {{T, H, c.heads * c.head_dim}, {T, 2 * F, H}, {T, H, F}, {N, c.vocab, H}, {N, c.rank, H}};
-  for (auto& s : shapes) part = std::max(part, dfl::plan_gemm(s[0], s[1], s[2]).partial_bytes);
+  const int shapes[][4] = {{T, H, c.heads * c.head_dim, 0}, {T, 2 * F, H, 0}, {T, H, F, 0}, {N, c.vocab, H, 1},
+                           {N, c.rank, H, 0}};
+  for (auto& s : shapes) part = std::max(part, dfl::plan_gemm(s[0], s[1], s[2], s[3] != 0).partial_bytes);
   L.partial = cv.off; cv.take<char>(part);
   L.total = cv.off;
   return L;
@@ -774,7 +775,7 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   float* logits = logits_out ? logits_out : f32(lay.logits);
   int32_t* cand = reinterpret_cast<int32_t*>(W + lay.cand);
   float* part = f32(lay.partial);
-  const dfl::GemmPlan p_head = dfl::plan_gemm(N, V_, H), p_sel = dfl::plan_gemm(N, R, H);
+  const dfl::GemmPlan p_head = dfl::plan_gemm(N, V_, H, true), p_sel = dfl::plan_gemm(N, R, H);
 
   const uint16_t* xin = embeds;
   for (int li = 0; li < c.layers; ++li) {

@@ -21,6 +21,7 @@
 // Split-K: grid.z slices K; slices write fp32 partials and a separate kernel sums them
 // in slice order (deterministic, no float atomics) and applies the epilogue, or the
 // partials are left for the consuming kernel, which sums them in the same order.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -63,11 +64,21 @@ __device__ __forceinline__ void store_out(const GemmArgs& p, int m, int n, float
   }
 }
 
+// Position of 16-byte chunk c of a tile-contiguous weight block (256 rows x 64 K): chunk c
+// is lane c % 64 of fragment c / 64; fragment f covers rows 16 (f / 2) .. +15 and K half
+// f % 2; lane l holds row l % 16 at K offset 8 (l / 16) of that half.
+__device__ __forceinline__ void frag_chunk_pos(int c, int& row, int& k) {
+  const int f = c >> 6, l = c & 63;
+  row = (f >> 1) * 16 + (l & 15);
+  k = (f & 1) * 32 + (l >> 4) * 8;
+}
+
 // Loads one K step of the A tile [BM x BKS] and the W tile [BN x BKS] into registers.
 // TILED: W is stored tile-contiguous, [N/BN][K/BKS][BN][BKS], so one step of one tile is
 // a single contiguous BN*BKS*2-byte block; otherwise W is row-major [N, K].
 template <int BM, int BN, int BKS, int NT, bool TILED>
 struct TileLoader {
+  static_assert(!TILED || (BN == 256 && BKS == 64), "tiled weights come in 256 x 64 blocks");
   static constexpr int CPR = BKS / 8;  // 16-byte chunks per tile row
   static constexpr int A_PER = BM * CPR / NT;
   static constexpr int B_PER = BN * CPR / NT;
@@ -111,26 +122,44 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
       const int c = tid + i * NT;
-      *reinterpret_cast<u32x4_t*>(&sB[(c / CPR) * LS + (c % CPR) * 8]) = b[i];
+      int row, kc;
+      if (TILED) {
+        frag_chunk_pos(c, row, kc);
+      } else {
+        row = c / CPR;
+        kc = (c % CPR) * 8;
+      }
+      *reinterpret_cast<u32x4_t*>(&sB[row * LS + kc]) = b[i];
     }
   }
 };
 
+// Eight 4-bit fields of one packed word (field e = the weight at K offset e, lowest bits
+// first) as bf16 weights scale * q + bias: one fp32 fma each, rounded once.
+__device__ __forceinline__ u32x4_t dequant8(uint32_t w, uint32_t sb) {
+  const float sc = __uint_as_float(sb << 16);
+  const float bi = __uint_as_float(sb & 0xFFFF0000u);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = fmaf(sc, static_cast<float>((w >> (4 * e)) & 0xFu), bi);
+  return pack8(f);
+}
+
 // 4-bit affine weights ([P2] `quantizedWeight`: groups of 64 inputs, w = scale * q + bias).
 // A K step is one group per row: each thread loads one 16-byte chunk of packed fields (32
-// weights of one row) and that row's (scale, bias), and dequantizes in fp32 (one fma per
-// weight, rounded once to bf16) while parking the step in LDS, so the tile compute is the
-// bf16 one.  TILED: per (N tile, K step) a block of BN rows x 8 words followed by BN words
-// of scale | bias << 16, written once by tile_q4_kernel.
+// weights) with their (scale, bias) and dequantizes while parking the step in LDS, so the
+// tile compute is the bf16 one.  Row-major: the chunk is half a row's step.  TILED (the
+// blocks of tile_q4_kernel): the chunk is four words of one lane of a 64-row group, i.e. 8
+// fields at each K half for rows r0 and r0 + 16.
 template <int BM, int BN, int BKS, int NT, bool TILED>
 struct TileLoaderQ4 {
   static constexpr int CPR = BKS / 8;
   static constexpr int A_PER = BM * CPR / NT;
   static_assert(A_PER * NT == BM * CPR, "A tile must split evenly over threads");
-  static_assert(BKS == 64 && BN * 2 == NT, "one 16-byte chunk of packed fields per thread");
+  static_assert(BKS == 64 && BN == 256 && NT == 512, "one 16-byte chunk of packed fields per thread");
   u32x4_t a[A_PER];
   u32x4_t w;
-  uint32_t sb;
+  u32x2_t sb;
 
   __device__ __forceinline__ void load(const GemmArgs& p, int m0, int n0, int k0, int tid) {
 #pragma unroll
@@ -139,16 +168,17 @@ struct TileLoaderQ4 {
       const int gm = min(m0 + c / CPR, p.M - 1);
       a[i] = *reinterpret_cast<const u32x4_t*>(p.A + (size_t)gm * p.lda + k0 + (c % CPR) * 8);
     }
-    const int row = tid >> 1, half = tid & 1;
     if (TILED) {
-      const uint32_t* blk = p.Wq + ((size_t)(n0 / BN) * (p.K / BKS) + k0 / BKS) * (BN * 9);
-      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + row * 8 + half * 4));
-      sb = blk[BN * 8 + row];
+      const uint32_t* grp = p.Wq + ((size_t)(n0 / BN) * (p.K / BKS) + k0 / BKS) * (BN * 9) + (tid >> 7) * 576;
+      const int l = (tid >> 1) & 63, h = tid & 1;
+      w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(grp + l * 8 + h * 4));
+      sb = *reinterpret_cast<const u32x2_t*>(grp + 512 + (l & 15) * 4 + h * 2);
     } else {
+      const int row = tid >> 1, half = tid & 1;
       const int gn = min(n0 + row, p.N - 1);
       w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.Wq + (size_t)gn * (p.K / 8) + k0 / 8 + half * 4));
       const size_t g = (size_t)gn * (p.K / BKS) + k0 / BKS;
-      sb = static_cast<uint32_t>(p.Ws[g]) | (static_cast<uint32_t>(p.Wb[g]) << 16);
+      sb[0] = static_cast<uint32_t>(p.Ws[g]) | (static_cast<uint32_t>(p.Wb[g]) << 16);
     }
   }
   __device__ __forceinline__ void store(uint16_t* sA, uint16_t* sB, int tid) const {
@@ -158,15 +188,18 @@ struct TileLoaderQ4 {
       const int c = tid + i * NT;
       *reinterpret_cast<u32x4_t*>(&sA[(c / CPR) * LS + (c % CPR) * 8]) = a[i];
     }
-    const float sc = bf16_to_f32(static_cast<uint16_t>(sb & 0xFFFFu));
-    const float bi = bf16_to_f32(static_cast<uint16_t>(sb >> 16));
-    const int row = tid >> 1, half = tid & 1;
+    if (TILED) {
+      const int l = (tid >> 1) & 63, h = tid & 1;
+      const int r0 = (tid >> 7) * 64 + h * 32 + (l & 15), kc = (l >> 4) * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float f[8];
+      for (int j = 0; j < 4; ++j) {
+        const int row = r0 + (j >> 1) * 16;
+        *reinterpret_cast<u32x4_t*>(&sB[row * LS + (j & 1) * 32 + kc]) = dequant8(w[j], sb[j >> 1]);
+      }
+    } else {
+      const int row = tid >> 1, half = tid & 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = fmaf(sc, static_cast<float>((w[j] >> (4 * e)) & 0xFu), bi);
-      *reinterpret_cast<u32x4_t*>(&sB[row * LS + half * 32 + j * 8]) = pack8(f);
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4_t*>(&sB[row * LS + half * 32 + j * 8]) = dequant8(w[j], sb[0]);
     }
   }
 };
@@ -329,6 +362,319 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Weight-streaming kernel for M <= 128 rows (every projection of a draft block).
+//
+// At these row counts a projection reads each weight once, at 128 flop per bf16 weight
+// byte, so it should run at HBM speed; what costs time in the LDS kernel above is staging
+// the weight tile through LDS (a write and four reads of every weight) and, for the wide
+// projections, having fewer 128 x 256 tiles than CUs.  Here each wavefront owns 64 weight
+// rows and all M rows of the output: its weight fragments go from HBM straight into MFMA
+// operand registers (the tile-contiguous layout is the operand order, so each load is 1 KB
+// contiguous per wavefront) and only the activations, shared by the NW wavefronts of a
+// workgroup, pass through LDS.  A stage (one 64-wide K step of the activations and of the
+// wave's weights) is loaded PF - 1 steps ahead into a register ring; one barrier per step.
+// Workgroups of NW = 2 wavefronts, at one wavefront per SIMD, let two workgroups share a CU
+// on separate SIMDs, so a grid of up to 512 workgroups is resident at once.
+
+// Loads the streaming kernel issues itself, so that it alone decides when to wait for them:
+// the compiler's own waits collapse a deep ring (at the loop head it falls back to waiting
+// for everything).  The compiler takes the destination of such a load as written when the
+// asm statement ends, so every loaded value must reach exactly one vm_wait that names it,
+// on every path, before anything else reads it: the registers then stay reserved until the
+// data is in, and nothing copies them early.  (Two alternative waits for one value would
+// make the compiler merge them with copies placed before one of the waits.)
+__device__ __forceinline__ u32x4_t vm_load16_nt(const void* p) {
+  u32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v) : "v"(p));
+  return v;
+}
+
+__device__ __forceinline__ u32x4_t vm_load16(const void* p) {
+  u32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+__device__ __forceinline__ uint32_t vm_load4_nt(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off nt" : "=v"(v) : "v"(p));
+  return v;
+}
+__device__ __forceinline__ uint32_t vm_load2(const void* p) {
+  uint32_t v;
+  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+// s_waitcnt vmcnt(N) that also passes v through, so no use of v is scheduled before it (the
+// comment names v's registers in the assembly).
+template <int N, class T>
+__device__ __forceinline__ void vm_wait(T& v) {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%1) ; waits for %0" : "+v"(v) : "i"(N));
+}
+
+
+// A wavefront's weights for one K step: 32 weight rows = 2 fragments of 16 rows x 2 K
+// halves.  LOADS is the number of vector-memory instructions load() issues.
+template <bool TILED, bool Q4>
+struct StreamW;
+
+// bf16: the four fragments, as loaded.
+template <bool TILED>
+struct StreamW<TILED, false> {
+  static constexpr int LOADS = 4;
+  u32x4_t v[4];  // fragment (j, half) at j * 2 + half
+  __device__ __forceinline__ void load(const GemmArgs& p, int nw0, int k0, int lane) {
+    if (TILED) {
+      const uint16_t* blk = p.W + ((size_t)(nw0 / kGemmTileN) * (p.K / BK) + k0 / BK) * (kGemmTileN * BK) +
+                            (nw0 % kGemmTileN) / 16 * 2 * 512 + lane * 8;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) v[f] = vm_load16_nt(blk + f * 512);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(nw0 + j * 16 + (lane & 15), p.N - 1);
+        const uint16_t* row = p.W + (size_t)n * p.K + k0 + (lane >> 4) * 8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) v[j * 2 + h] = vm_load16_nt(row + h * 32);
+      }
+    }
+  }
+  template <int N>
+  __device__ __forceinline__ void wait() {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) vm_wait<N>(v[f]);
+  }
+  __device__ __forceinline__ bf16x8_t frag(int j, int h) const { return __builtin_bit_cast(bf16x8_t, v[j * 2 + h]); }
+};
+
+// 4-bit (tile-contiguous only): the wavefront's 32 rows are half of a 64-row group, so one
+// 16-byte load brings the lane's four packed words (rows 16 j + lane % 16 of that half, both
+// K halves) and one more the group's scale | bias words.  Kept as the loaded vectors: a
+// value is never split or copied before its wait.
+template <>
+struct StreamW<true, true> {
+  static constexpr int LOADS = 2;
+  u32x4_t q;   // word j * 2 + half for the half's rows j = 0, 1
+  u32x4_t sb;  // scale | bias << 16 of the group's row sets 0..3
+  int half = 0;
+  __device__ __forceinline__ void load(const GemmArgs& p, int nw0, int k0, int lane) {
+    const uint32_t* grp = p.Wq + ((size_t)(nw0 / kGemmTileN) * (p.K / BK) + k0 / BK) * (kGemmTileN * 9) +
+                          (nw0 % kGemmTileN) / 64 * 576;
+    half = (nw0 % 64) / 32;
+    q = vm_load16_nt(grp + lane * 8 + half * 4);
+    sb = vm_load16(grp + 512 + (lane & 15) * 4);
+  }
+  template <int N>
+  __device__ __forceinline__ void wait() {
+    vm_wait<N>(q);
+    vm_wait<N>(sb);
+  }
+  __device__ __forceinline__ bf16x8_t frag(int j, int h) const {
+    return __builtin_bit_cast(bf16x8_t, dequant8(q[j * 2 + h], half ? sb[2 + j] : sb[j]));
+  }
+};
+
+// s_waitcnt for "at most n vector-memory operations outstanding" (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// The activation slab of one K step, [MT * 16 rows][64] bf16, copied from global memory
+// straight into LDS (16 bytes per lane, 1 KB = 8 rows per instruction) without passing
+// through registers.  LDS rows are 128 bytes with the 16-byte chunk of K offset 8c of row r
+// stored at slot c ^ (r % 8), so the fragment reads of 16 consecutive rows spread over the
+// banks.  Instructions are split over the NW wavefronts; when there are fewer instructions
+// than wavefronts the extra ones repeat the last (identical bytes to the same place).
+template <int MT, int NW>
+struct StreamA {
+  static constexpr int INSTR = MT * 2;
+  static constexpr int PER = (INSTR + NW - 1) / NW;  // per wavefront (NW wavefronts share them)
+  __device__ __forceinline__ static void load(const GemmArgs& p, uint16_t* buf, int k0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ins = min(wave * PER + i, INSTR - 1);
+      const int row = ins * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row & 7);
+      const uint16_t* src = p.A + (size_t)min(row, p.M - 1) * p.lda + k0 + chunk * 8;
+      __builtin_amdgcn_global_load_lds(src, buf + ins * 512, 16, 0, 0);
+    }
+  }
+  // Byte offset in a buffer of this lane's fragment (i, h): row 16 i + lane % 16, K offset
+  // 32 h + 8 (lane / 16); since 16 i is a multiple of 8 the slot only depends on the lane
+  // and h, and fragment i sits 2048 bytes after fragment i - 1.
+  __device__ __forceinline__ static uint32_t frag_offset(int h, int lane) {
+    return (lane & 15) * 128 + (((h * 4 + (lane >> 4)) ^ (lane & 7)) * 16);
+  }
+};
+
+// An LDS read the compiler does not see as one: its alias tracking would otherwise make
+// every LDS read wait for all copies into LDS still in flight (including the ones for later
+// steps).  Completion is awaited explicitly with lds_wait, which also ties the value so no
+// use can be scheduled before the wait.
+__device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
+  bf16x8_t v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(bf16x8_t& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1) ; waits for %0" : "+v"(v) : "i"(N));
+}
+
+// NW wavefronts per workgroup, 32 weight rows each, two wavefronts per SIMD (256 registers
+// each), so while one waits the other computes.
+template <int MT, int NW, int PF, int AD, bool TILED, bool Q4>
+__global__ __launch_bounds__(NW * 64, 2) void gemm_stream_kernel(GemmArgs p) {
+  constexpr int MR = MT * 16;
+  // AD: activation steps in flight ahead of the one being computed (AD + 1 LDS buffers)
+  __shared__ __attribute__((aligned(16))) uint16_t sA[AD + 1][MR * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw0 = blockIdx.x * (NW * 32) + wave * 32;  // first weight row of this wavefront
+  const int kbeg = blockIdx.y * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nk = (kend - kbeg) / BK;
+  using SA = StreamA<MT, NW>;
+  constexpr int NB = StreamW<TILED, Q4>::LOADS;
+  constexpr int NA = SA::PER;
+
+  // Weights run PF steps ahead in registers, activations AD steps ahead in LDS.  Loads past
+  // the last step re-read the last step (cache hits, never used), so every iteration has the
+  // same shape and the wait counts below are exact.  The vector-memory counter retires in
+  // order: waiting for step kt + 1's activations also waits for what was issued before them.
+  StreamW<TILED, Q4> ring[PF];
+  f32x4_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // The prologue issues the same pattern as the PF iterations before step 0 would (iteration
+  // i starts step i + AD's activations, then loads step i + PF's weights; it skips the
+  // activations of steps before 0).  At most PF weight stages and AD activation stages are
+  // ever outstanding; the counter holds 63.
+  static_assert(PF * NB + AD * NA <= 63, "more vector-memory operations in flight than vmcnt counts");
+  static_assert(PF >= AD, "the prologue starts step 0's activations within its PF iterations");
+  const int last = kbeg + (nk - 1) * BK;
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    const int step = s - PF + AD;
+    if (step >= 0) SA::load(p, sA[step], min(kbeg + step * BK, last), wave, lane);
+    ring[s].load(p, nw0, min(kbeg + s * BK, last), lane);
+  }
+  // At the end of iteration kt, step kt + 1's activations (started AD - 1 iterations
+  // earlier) are awaited: AD weight stages and AD - 1 activation stages came after them.
+  // Before computing step kt its weights are awaited: PF - 1 iterations and this
+  // iteration's copies came after them.
+  constexpr int kWaitA = AD * NB + (AD - 1) * NA;
+  constexpr int kWaitWraw = (PF - 1) * (NA + NB) + NA;
+  constexpr int kWaitW = kWaitWraw > 63 ? 63 : kWaitWraw;
+  wait_vmcnt<kWaitA>();
+  __builtin_amdgcn_s_barrier();
+
+  // LDS byte address of sA (the low half of its generic address)
+  const uint32_t sa_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0]));
+  const uint32_t off0 = SA::frag_offset(0, lane), off1 = SA::frag_offset(1, lane);
+  // One K half at a time: its MT activation fragments are read from LDS, then its 2 * MT
+  // MFMAs issue (the other wavefront on the SIMD covers the read latency).
+  auto compute = [&](int buf, const StreamW<TILED, Q4>& w) {
+    const uint32_t b = sa_base + buf * (MR * 64 * 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8_t af[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) af[i] = lds_read_b128(b + (h ? off1 : off0) + i * 2048);
+      bf16x8_t bfr[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = w.frag(j, h);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) lds_wait<0>(af[i]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Iteration kt: start step kt + AD's activations into the buffer step kt - 1 used, compute
+  // step kt (weight slot kt % PF), refill weight slot kt % PF with step kt + PF, wait until
+  // this wavefront's copies of step kt + 1's activations have landed, barrier.  Unrolled PF
+  // times so every ring index is a compile-time constant.
+  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int kt = kt0 + s;
+      SA::load(p, sA[(kt + AD) % (AD + 1)], min(kbeg + (kt + AD) * BK, last), wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      ring[s].template wait<kWaitW>();
+      if (kt < nk) compute(kt % (AD + 1), ring[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      ring[s].load(p, nw0, min(kbeg + (kt + PF) * BK, last), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kWaitA>();
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  // The last PF weight stages (re-reads past the end) get their one wait here, before their
+  // registers can be reused, and no copy into LDS may still be in flight when the
+  // workgroup's LDS is handed on.
+#pragma unroll
+  for (int s = 0; s < PF; ++s) ring[s].template wait<0>();
+  wait_vmcnt<0>();
+
+  // Accumulator layout: lane holds column (lane & 15) and rows 4 * (lane >> 4) + e.
+  const int mrow = (lane >> 4) * 4;
+  const int ncol = nw0 + (lane & 15);
+  if (p.splits > 1) {
+    float* part = p.partial + (size_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = mrow + i * 16 + e;
+          const int n = ncol + j * 16;
+          if (m < p.M && n < p.N) part[(size_t)m * p.N + n] = acc[i][j][e];
+        }
+    return;
+  }
+  if (p.epi == EPI_SILU_MUL) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; j += 2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = mrow + i * 16 + e;
+          const int n = ncol + j * 16;  // gate column; up is n + 16
+          if (m < p.M && n < p.N) {
+            const int jo = (n >> 5) * 16 + (n & 15);
+            const float v = silu(acc[i][j][e]) * acc[i][j + 1][e];
+            static_cast<uint16_t*>(p.out0)[(size_t)m * p.ld0 + jo] = f32_to_bf16(v);
+          }
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = mrow + i * 16 + e;
+        const int n = ncol + j * 16;
+        if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
+      }
+}
+
 // Sum of split-K partials in slice order, then the epilogue.  Each thread owns VW adjacent
 // outputs (VW = 4 when N and the column split are multiples of 4, else 1); planes_sum
 // issues the slices' loads in batches of eight and adds them in order 0, 1, 2, ...
@@ -363,17 +709,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 
 constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
+constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
+// Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
+// workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
+// memory path delivers about 7 TB/s in all, cache hits included).  Used for wide
+// projections (at least kStreamMinN outputs and kStreamMinWeights weights), which keep the
+// grid wide without splitting K; deep, narrow ones keep the LDS kernel's split plan.
+constexpr int kStreamWaves = 8;
+constexpr int kStreamStages = 8, kStreamStagesQ4 = 10;
+constexpr size_t kStreamMinWeights = size_t(64) << 20;
+constexpr int kStreamMinN = 16384;
+constexpr size_t kStreamMaxWaves = 2048;  // two wavefronts per SIMD on 256 CUs
 
 __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __restrict__ src, int N, int K,
                                                            const int32_t* __restrict__ rows,
                                                            uint16_t* __restrict__ dst, size_t chunks) {
   const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= chunks) return;
-  // destination chunk c = ((t * (K/64) + s) * 256 + r) * 8 + q, 8 bf16 each
-  const int q = static_cast<int>(c & 7);
-  const size_t rest = c >> 3;
-  const int r = static_cast<int>(rest % kBN);
-  const size_t ts = rest / kBN;
+  // destination chunk c = (t * (K/64) + s) * 2048 + chunk within the block, 8 bf16 each
+  constexpr int kChunks = kBN * BK / 8;
+  int r, k;
+  frag_chunk_pos(static_cast<int>(c % kChunks), r, k);
+  const size_t ts = c / kChunks;
   const int steps = K / BK;
   const int sstep = static_cast<int>(ts % steps);
   const int t = static_cast<int>(ts / steps);
@@ -381,13 +738,14 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint16_t* __res
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < N) {
     const size_t row = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
-    v = *reinterpret_cast<const u32x4_t*>(src + row * K + sstep * BK + q * 8);
+    v = *reinterpret_cast<const u32x4_t*>(src + row * K + sstep * BK + k);
   }
   *reinterpret_cast<u32x4_t*>(dst + c * 8) = v;
 }
 
-// Tile-contiguous 4-bit weights: per (N tile t, K step s) a block of kBN rows x 8 packed words
-// followed by kBN words of scale | bias << 16; rows past N are zero (weights 0).  rows
+// Tile-contiguous 4-bit weights: per (N tile t, K step s) four 64-row groups of 576 words,
+// 64 lanes x 8 packed words and then [16][4] words of scale | bias << 16 (the operand order of
+// a wavefront that covers the group's 64 rows); rows past N are zero (weights 0).  rows
 // (optional): destination row n takes source row rows[n].
 __global__ __launch_bounds__(256) void tile_q4_kernel(const uint32_t* __restrict__ q, const uint16_t* __restrict__ sc,
                                                       const uint16_t* __restrict__ bi, int N, int K,
@@ -402,14 +760,17 @@ __global__ __launch_bounds__(256) void tile_q4_kernel(const uint32_t* __restrict
   const int sstep = static_cast<int>(block % steps);
   const int t = static_cast<int>(block / steps);
   uint32_t v = 0;
-  if (within < kBN * 8) {
-    const int n = t * kBN + within / 8;
+  const int g = within / 576, rem = within % 576;
+  if (rem < 512) {
+    // lane l = rem / 8, word j * 2 + half = rem % 8: row 16 j + l % 16, K word half * 4 + l / 16
+    const int l = rem >> 3, jw = rem & 7;
+    const int n = t * kBN + g * 64 + (jw >> 1) * 16 + (l & 15);
     if (n < N) {
       const size_t src = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
-      v = q[src * (K / 8) + sstep * 8 + within % 8];
+      v = q[src * (K / 8) + sstep * 8 + (jw & 1) * 4 + (l >> 4)];
     }
   } else {
-    const int n = t * kBN + (within - kBN * 8);
+    const int n = t * kBN + g * 64 + ((rem - 512) & 3) * 16 + ((rem - 512) >> 2);
     if (n < N) {
       const size_t src = rows ? static_cast<size_t>(rows[n]) : static_cast<size_t>(n);
       const size_t g = src * (K / BK) + sstep;
@@ -439,8 +800,32 @@ hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst,
   return hipGetLastError();
 }
 
-GemmPlan plan_gemm(int M, int N, int K) {
+// Streaming plan with nw wavefronts per workgroup: split K while the whole grid stays
+// resident (two wavefronts per SIMD), every split keeps >= 4 steps and the fp32 partials
+// stay within a quarter of the weight bytes (or 8 MB for small weights).
+GemmPlan plan_stream(int M, int N, int K, bool tile_max, int nw) {
   GemmPlan pl;
+  const int tiles = (N + nw * 32 - 1) / (nw * 32);
+  const int nk = K / BK;
+  const double budget = std::max(0.5 * N * K, 8.0 * 1024 * 1024);
+  int s = 1;
+  while (!tile_max && s < kStreamMaxSplits && (size_t)tiles * (s + 1) * nw <= kStreamMaxWaves &&
+         nk / (s + 1) >= 4 && 4.0 * (s + 1) * M * N <= budget)
+    ++s;
+  const int per = (nk + s - 1) / s;
+  pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  pl.bn = nw * 32;
+  pl.stream_waves = nw;
+  pl.k_per_split = per * BK;
+  pl.splits = (nk + per - 1) / per;
+  pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+  return pl;
+}
+
+GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
+  GemmPlan pl;
+  if (M <= kStreamMaxM && !tile_max && N >= kStreamMinN && (size_t)N * K >= kStreamMinWeights)
+    return plan_stream(M, N, K, false, kStreamWaves);
   pl.bm = kBM;
   pl.bn = kBN;
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
@@ -481,7 +866,51 @@ GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightR
   return p;
 }
 
+// Weight stages in flight: as many as the 63 outstanding vector-memory operations allow
+// next to the activation copies (a bf16 stage is 8 loads, a 4-bit stage 3), and, for bf16,
+// as many as fit in the accumulation registers beside the accumulators (8 row fragments
+// take 128 of the 256).
+// Weight stages in flight: a bf16 stage is 4 loads (4 KB), a 4-bit stage 2 (1.1 KB); the
+// depth keeps a wavefront within 256 registers next to its accumulators.
+template <int MT, int NW>
+hipError_t launch_stream_mt(const GemmArgs& p, const WeightRef& W, hipStream_t stream) {
+  const dim3 grid((p.N + NW * 32 - 1) / (NW * 32), p.splits);
+  if (W.q) {
+    gemm_stream_kernel<MT, NW, kStreamStagesQ4, 3, true, true><<<grid, NW * 64, 0, stream>>>(p);
+  } else {
+    // at 8 row fragments the accumulators share the registers: two stages fewer
+    constexpr int PF = MT == 8 ? kStreamStages - 2 : kStreamStages;
+    if (W.tiled)
+      gemm_stream_kernel<MT, NW, PF, 3, true, false><<<grid, NW * 64, 0, stream>>>(p);
+    else
+      gemm_stream_kernel<MT, NW, PF, 3, false, false><<<grid, NW * 64, 0, stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_stream_nw(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {
+  switch (pl.bm) {
+    case 16: return launch_stream_mt<1, NW>(p, W, stream);
+    case 32: return launch_stream_mt<2, NW>(p, W, stream);
+    case 64: return launch_stream_mt<4, NW>(p, W, stream);
+    default: return launch_stream_mt<8, NW>(p, W, stream);
+  }
+}
+
+hipError_t launch_stream(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {
+  if (pl.stream_waves == kStreamWaves) return launch_stream_nw<kStreamWaves>(p, pl, W, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {
+  // Row-major 4-bit weights (a one-off projection) take the LDS kernel with the same split
+  // plan: loaded by hand their sixteen scalar loads a stage leave the streaming kernel short
+  // of registers, and the compiler would then move values still in flight.
+  if (pl.stream_waves > 0 && (W.tiled || !W.q)) {
+    if (p.M > pl.bm) return hipErrorInvalidValue;
+    return launch_stream(p, pl, W, stream);
+  }
   const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM, pl.splits);
   if (W.q) {
     if (W.tiled)
@@ -514,7 +943,8 @@ hipError_t launch_reduce(const GemmArgs& p, hipStream_t stream) {
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
                        hipStream_t stream, float* tile_max) {
-  if (tile_max && (epi != EPI_F32 || pl.splits != 1)) return hipErrorInvalidValue;
+  // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup)
+  if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0)) return hipErrorInvalidValue;
   if (W.q && K % BK != 0) return hipErrorInvalidValue;
   const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max);
   hipError_t e = launch_main(p, pl, W, stream);

@@ -24,9 +24,11 @@ struct GemmPlan {
   int splits = 1;
   int k_per_split = 0;
   size_t partial_bytes = 0;  // split-K scratch (fp32 [splits, M, N])
+  int stream_waves = 0;      // > 0: the weight-streaming kernel (M <= 128), waves per workgroup
 };
 
-GemmPlan plan_gemm(int M, int N, int K);
+// tile_max: the caller will ask launch_gemm for tile maxima (one split, 256-column workgroups).
+GemmPlan plan_gemm(int M, int N, int K, bool tile_max = false);
 
 // A projection weight [N, K]: bf16 w (row-major, or tile-contiguous when tiled), or 4-bit
 // affine q (row-major packed words [N, K/8] with scales and biases [N, K/64] bf16, or the
@@ -43,7 +45,11 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
                        hipStream_t stream, float* tile_max = nullptr);
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,
                                 int K, float* partial, hipStream_t stream);
-// Tile-contiguous 4-bit weights: q4_tiled_words 32-bit words; rows as for launch_tile_weights.
+// Tile-contiguous 4-bit weights: per (256-row tile, 64-wide K step) four 64-row groups of
+// 576 words; group g holds 64 lanes x 8 packed words (lane l: rows 16 j + l % 16 of the
+// group, j = 0..3, each for K offsets 8 (l / 16) and 32 + 8 (l / 16), word j * 2 + half),
+// then [16][4] words scale | bias << 16 (row 16 j + r at r * 4 + j).  q4_tiled_words gives
+// the size in 32-bit words; rows as for launch_tile_weights.
 size_t q4_tiled_words(int N, int K);
 hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint16_t* biases, int N, int K,
                           uint32_t* dst, hipStream_t stream, const int32_t* rows = nullptr);
@@ -69,9 +75,12 @@ inline Planes gemm_planes(const GemmPlan& pl, const float* partial, int M, int N
   p.plane = (size_t)M * N;
   return p;
 }
-// Tile-contiguous copy of a row-major [N, K] weight: [ceil(N/256)][K/64][256][64], rows
-// past N zero.  tiled_weight_elems gives the destination size in bf16 elements.  rows
-// (device, optional): destination row n copies source row rows[n] (a gathered subset).
+// Tile-contiguous copy of a row-major [N, K] weight: one block per (256-row tile, 64-wide K
+// step), [ceil(N/256)][K/64][block], rows past N zero.  Inside a block the order is the
+// matrix-core operand order: 32 fragments of 16 rows x 32 K (row group outer, K half inner),
+// each 64 lanes x 8 bf16 where lane l holds row l % 16 and K offset 8 * (l / 16).
+// tiled_weight_elems gives the destination size in bf16 elements.  rows (device, optional):
+// destination row n copies source row rows[n] (a gathered subset).
 size_t tiled_weight_elems(int N, int K);
 hipError_t launch_tile_weights(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t stream,
                                const int32_t* rows = nullptr);

@@ -7,7 +7,7 @@ import torch
 from dflash2_block_drafter_amd import configs, synth
 from dflash2_block_drafter_amd.drafter import Drafter
 from oracle import dflash2 as O
-from tests.helpers import assert_composed_close, compare_tokens
+from tests.helpers import COMPOSED_REL, assert_composed_close, compare_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -32,7 +32,7 @@ def _run_tiny(w):
     return dr, _host(weights_cpu), _host(tgt_cpu), K, V, tokens, logits
 
 
-@pytest.mark.parametrize("batch", [1, 3])
+@pytest.mark.parametrize("batch", [1, 3, 6])   # 8, 24 and 48 block rows: 1, 2 and 4 row fragments
 def test_tiny_drafter_end_to_end(batch):
     w = configs.with_batch(configs.TINY, batch)
     d = w.dims
@@ -98,7 +98,7 @@ def test_bound_head_matches_borrowed_head():
     dr.close()
 
 
-def _tiny_parity(w, G=None, q4=False):
+def _tiny_parity(w, G=None, q4=False, rel=COMPOSED_REL):
     """Draft a tiny workload (optionally with a block narrower than block_size, or with 4-bit
     layer projections) on the GPU and compare it with the oracle at the bf16 rounding points."""
     d = w.dims
@@ -126,7 +126,7 @@ def _tiny_parity(w, G=None, q4=False):
     ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
-    assert_composed_close(logits, ref["logits"], "head logits")
+    assert_composed_close(logits, ref["logits"], "head logits", rel=rel)
     assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
     dr.close()
     return ref
@@ -138,10 +138,26 @@ def test_tiny_sliding_window_end_to_end():
     assert ref["tokens"].shape == (configs.TINY_SW.batch, configs.TINY_SW.dims.block_size - 1)
 
 
-def test_tiny_q4_projections_end_to_end():
+@pytest.mark.parametrize("batch", [None, 5])
+def test_tiny_q4_projections_end_to_end(batch):
     # the seven layer projections (and the context k|v) on 4-bit affine weights
-    ref = _tiny_parity(configs.TINY_SW, q4=True)
-    assert ref["tokens"].shape == (configs.TINY_SW.batch, configs.TINY_SW.dims.block_size - 1)
+    w = configs.TINY_SW if batch is None else configs.with_batch(configs.TINY, batch)
+    ref = _tiny_parity(w, q4=True)
+    assert ref["tokens"].shape == (w.batch, w.dims.block_size - 1)
+
+
+@pytest.mark.parametrize("batch,q4", [(1, False), (6, False), (3, True)])
+def test_medium_streamed_projection_end_to_end(batch, q4):
+    # gate/up (65536 x 1024) runs on the weight-streaming GEMM, tile-contiguous bf16 or 4-bit
+    # weights, at 8, 48 and 24 block rows (1, 4 and 2 row fragments)
+    # The medium drafter's logits (one layer with a 32768-wide MLP and a 2048-row head) reach
+    # 2.4% of the row-scaled bound in their tail against the oracle at the bf16 rounding
+    # points (p50 0.2%, p99 1.0%), identically whether its projections run on the streaming
+    # or the LDS kernel: the rounding points, not a kernel, set that tail, so the bound here
+    # is 3e-2.
+    w = configs.with_batch(configs.MEDIUM, batch)
+    ref = _tiny_parity(w, q4=q4, rel=3e-2)
+    assert ref["tokens"].shape == (batch, w.dims.block_size - 1)
 
 
 def test_tiny_variable_block_width():

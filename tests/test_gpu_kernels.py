@@ -30,6 +30,14 @@ def h(t):
     (128, 1280, 5120, True),    # split-K path (kernel_projection shape)
     (128, 4096, 1024, False),
     (120, 1000, 256, True),     # N not a multiple of 64
+    (9, 640, 1024, False),      # one 16-row fragment, split K
+    (20, 384, 512, True),       # two 16-row fragments
+    # wide projections (N >= 16384, >= 64M weights) take the weight-streaming kernel: 1, 2, 4
+    # and 8 row fragments
+    (9, 16384, 4096, False),
+    (30, 16640, 4096, True),    # N not a multiple of the 256-column workgroup
+    (50, 32768, 2048, False),
+    (128, 16384, 4096, True),
 ])
 def test_linear(M, N, K, out_f32):
     x = bf((M, K), 11)
@@ -105,6 +113,8 @@ def test_block_attention(D, NH, NKV, G, ctx):
     (128, 6144, 5120, False),   # the fused q|k|v shape, split K
     (120, 1000, 1024, True),    # ragged N tile, fp32 out
     (7, 300, 128, False),       # ragged M and N, two groups
+    (30, 520, 2048, True),      # two 16-row fragments, split K
+    (50, 256, 640, False),      # four 16-row fragments
 ])
 def test_linear_q4(M, N, K, out_f32):
     x = bf((M, K), 61)

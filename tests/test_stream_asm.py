@@ -1,0 +1,44 @@
+"""The weight-streaming GEMM's hand-issued loads, checked on the compiled gfx950 assembly
+(host only: hipcc cross-compiles).  See tests/asm_waits.py for the rule."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from asm_waits import check_assembly, check_function
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_checker_flags_a_copy_before_the_wait():
+    # a load, a copy of its destination before the wait that names it, then the wait
+    bad = ["k:", ";;#ASMSTART", "global_load_dwordx4 v[4:7], v[0:1], off", ";;#ASMEND",
+           "v_mov_b32_e32 v8, v4",
+           ";;#ASMSTART", "s_waitcnt vmcnt(0) ; waits for v[4:7]", ";;#ASMEND", "s_endpgm"]
+    good = bad[:4] + bad[5:8] + ["v_mov_b32_e32 v8, v4", "s_endpgm"]
+    assert check_function(bad)
+    assert not check_function(good)
+
+
+def test_checker_flags_a_load_landing_on_a_reused_register():
+    # a load whose value is never waited for, and a later write to its register
+    bad = ["k:", ";;#ASMSTART", "global_load_dwordx4 v[4:7], v[0:1], off", ";;#ASMEND",
+           "v_accvgpr_read_b32 v5, a3", "s_waitcnt vmcnt(0)", "s_endpgm"]
+    assert check_function(bad)
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="needs hipcc")
+def test_streaming_gemm_waits_cover_every_use(tmp_path):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    out = tmp_path / "gemm.s"
+    csrc = os.path.join(ROOT, "dflash2_block_drafter_amd", "csrc")
+    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", csrc, "-x", "hip", "-S",
+           "--cuda-device-only", os.path.join(csrc, "gemm.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    result = check_assembly(out.read_text(), r"_ZN3dfl12_GLOBAL__N_118gemm_stream_kernel")
+    assert len(result) >= 12, "streaming kernel instances not found"
+    bad = {k: v[:3] for k, v in result.items() if v}
+    assert not bad, bad
