@@ -5,9 +5,12 @@
 //
 // Work split: one workgroup per (request b, KV head g, key chunk).  The Q tile is the
 // G x NH/NKV query rows that share KV head g (<= 64 rows, 16 per wavefront), so every
-// K/V row read from HBM serves all of them.  Chunks 0..nchunks-2 cover context rows,
-// the last chunk the block's own G keys; each writes (max, sum, unnormalised O) in fp32
-// and a combine kernel merges the chunks with their log-sum-exp weights.
+// K/V row read from HBM serves all of them.  The chunks split the context rows, and the
+// last one also takes the block's own G keys as one more tile (its first); each writes
+// (max, sum, unnormalised O) in fp32 and a combine kernel merges the chunks with their
+// log-sum-exp weights.  A workgroup keeps R tiles of K/V in flight: R = 4 for long chunks,
+// sized so that the whole grid is resident at once (two workgroups per CU); R = 1 for short
+// ones, where three workgroups per CU and more chunks hide more latency than a deep ring.
 //
 // Per 64-key tile a wavefront computes S^T = K . Q^T (keys on rows, its 16 queries on
 // columns) with v_mfma_f32_16x16x32_bf16, so each lane holds one query's scores and the
@@ -19,10 +22,12 @@
 // block row 0's first visible row and masks, per query lane, the keys before that
 // query's own window start; a query with every key of a tile masked keeps its running
 // (max, sum, output) unchanged.
+#include <algorithm>
 #include <climits>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "vmem.hpp"
 
 namespace dfl {
 
@@ -30,6 +35,7 @@ namespace {
 
 constexpr int KT = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kDeepMinTiles = 8;  // tiles per chunk below which the shallow ring is used
 
 struct AttnArgs {
   const uint16_t* q;
@@ -46,7 +52,7 @@ struct AttnArgs {
   float scale_log2;
 };
 
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   constexpr int KS = D + 8;   // K tile row stride (bf16)
   constexpr int VS = KT + 4;  // V^T tile row stride (bf16): 34 dwords, conflict-free reads
@@ -64,33 +70,27 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   const int hpg = a.NH / a.NKV;
   const int lg = lane >> 4;  // lane group
 
-  // key range of this chunk
-  const bool block_chunk = chunk == a.nchunks - 1;
+  // context key range of this chunk; the last chunk also takes the block's own G keys as
+  // one more tile, its first
+  const bool has_block = chunk == a.nchunks - 1;
   const int ctx = min(max(a.ctx_len[b], 0), a.Lmax);  // never past the rows the plan covers
-  int kbeg, kend;
-  const uint16_t *ksrc, *vsrc;
-  size_t kstride;
-  if (block_chunk) {
-    kbeg = 0;
-    kend = a.G;
-    ksrc = a.kb + (size_t)b * a.G * a.ldkv + g * D;
-    vsrc = a.vb + (size_t)b * a.G * a.ldkv + g * D;
-    kstride = a.ldkv;
-  } else {
-    kbeg = chunk * a.chunk;
-    kend = min(ctx, kbeg + a.chunk);
-    if (a.window > 0) kbeg = max(kbeg, a.pos0[b] - a.window + 1);  // block row 0's first visible row
-    ksrc = a.K + ((size_t)b * a.Lcap * a.NKV + g) * D;
-    vsrc = a.V + ((size_t)b * a.Lcap * a.NKV + g) * D;
-    kstride = (size_t)a.NKV * D;
-  }
+  int kbeg = chunk * a.chunk;
+  const int kend = min(ctx, kbeg + a.chunk);
+  if (a.window > 0) kbeg = max(kbeg, a.pos0[b] - a.window + 1);  // block row 0's first visible row
+  const int ctx_tiles = kbeg < kend ? (kend - kbeg + KT - 1) / KT : 0;
+  const int ntiles = ctx_tiles + (has_block ? 1 : 0);
+  const uint16_t* kctx = a.K + ((size_t)b * a.Lcap * a.NKV + g) * D;
+  const uint16_t* vctx = a.V + ((size_t)b * a.Lcap * a.NKV + g) * D;
+  const uint16_t* kblk = a.kb + (size_t)b * a.G * a.ldkv + g * D;
+  const uint16_t* vblk = a.vb + (size_t)b * a.G * a.ldkv + g * D;
+  const uint32_t ctx_stride = static_cast<uint32_t>(a.NKV * D);  // host checks Lcap*NKV*D < 2^31, so byte offsets fit 32 bits
 
   // this wavefront's 16 queries as MFMA B operands (column = query, k = d)
   const int qi = wave * 16 + (lane & 15);
   const bool qvalid = qi < a.qrows;
   // sliding window: this lane's query (block row qi / hpg) sees context keys >= kmin; tiles
   // starting at or past kmin_hi (the largest kmin of the workgroup) need no mask
-  const bool windowed = a.window > 0 && !block_chunk;
+  const bool windowed = a.window > 0;
   const int kmin = windowed ? a.pos0[b] + qi / hpg - a.window + 1 : INT_MIN;
   const int kmin_hi = windowed ? a.pos0[b] + (a.G - 1) - a.window + 1 : INT_MIN;
   bf16x8_t qf[DK];
@@ -112,26 +112,42 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   for (int i = 0; i < DT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Staging map: thread t owns keys ROWS_PER*kg .. +ROWS_PER-1 of a tile at dims
-  // 8*dg .. +7, with kg running fastest, so a wavefront's V^T store covers whole LDS rows
-  // (one 8-byte pack of 4 keys per dim and lane, no bank conflicts).  The next tile is in
-  // flight in registers while this one is computed; rows past the chunk end are clamped
-  // to its last row so that every load is unconditional (a deeper register ring lost to
-  // the compiler's conservative load waits at the loop head).
+  // 8*dg .. +7, with dg running fastest, so each load instruction of a wavefront reads
+  // whole key rows (DG lanes per row) and each V^T store is one 8-byte pack of ROWS_PER
+  // keys per dim and lane.  The next R tiles are in flight in a register ring while
+  // one is computed (hand-issued loads, each awaited once by name); loads past the last
+  // tile or row repeat it, so that every load is unconditional.
   constexpr int DG = D / 8;                  // 16-byte chunks per key row
   static_assert(KT * DG % 256 == 0, "tile must split over 256 threads");
   constexpr int ROWS_PER = (KT * DG) / 256;  // key rows per thread per tile (4 for D=128)
-  constexpr int NKG = KT / ROWS_PER;
-  const int kg = tid % NKG;
-  const int dg = tid / NKG;
-  u32x4_t kreg[1][ROWS_PER], vreg[1][ROWS_PER];  // the next tile, in flight during compute
-  const uint32_t kstride32 = static_cast<uint32_t>(kstride);  // host checks Lcap*NKV*D < 2^31
-  auto tile_load = [&](u32x4_t (&kr)[ROWS_PER], u32x4_t (&vr)[ROWS_PER], int j0) {
+  constexpr int LOADS = 2 * ROWS_PER;        // vector loads per thread per tile
+  static_assert(R * LOADS <= 63, "ring deeper than vmcnt can count");
+  const int dg = tid % DG;
+  const int kg = tid / DG;
+  u32x4_t kreg[R][ROWS_PER], vreg[R][ROWS_PER];
+  // tile t of this workgroup (uniform); tiles past the last repeat it, rows past a tile's
+  // end repeat its last row
+  auto tile_load = [&](u32x4_t (&kr)[ROWS_PER], u32x4_t (&vr)[ROWS_PER], int t) {
+    t = min(t, ntiles - 1);
+    const bool blk = has_block && t == 0;
+    const uint16_t* kp = blk ? kblk : kctx;
+    const uint16_t* vp = blk ? vblk : vctx;
+    const uint32_t stride = blk ? static_cast<uint32_t>(a.ldkv) * 2u : ctx_stride * 2u;  // bytes
+    const int r0 = blk ? 0 : kbeg + (t - (has_block ? 1 : 0)) * KT;
+    const int rlast = blk ? a.G - 1 : kend - 1;
 #pragma unroll
     for (int i = 0; i < ROWS_PER; ++i) {
-      const uint32_t off =
-          static_cast<uint32_t>(min(j0 + kg * ROWS_PER + i, kend - 1)) * kstride32 + dg * 8;
-      kr[i] = *reinterpret_cast<const u32x4_t*>(ksrc + off);
-      vr[i] = *reinterpret_cast<const u32x4_t*>(vsrc + off);
+      const uint32_t off = static_cast<uint32_t>(min(r0 + kg * ROWS_PER + i, rlast)) * stride + dg * 16;
+      kr[i] = vm_load16(kp, off);
+      vr[i] = vm_load16(vp, off);
+    }
+  };
+  // every load but the newest n tiles' is in
+  auto tile_wait = [&](u32x4_t (&kr)[ROWS_PER], u32x4_t (&vr)[ROWS_PER]) {
+#pragma unroll
+    for (int i = 0; i < ROWS_PER; ++i) {
+      vm_wait<(R - 1) * LOADS>(kr[i]);
+      vm_wait<(R - 1) * LOADS>(vr[i]);
     }
   };
   auto tile_store = [&](const u32x4_t (&kr)[ROWS_PER], const u32x4_t (&vr)[ROWS_PER]) {
@@ -152,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   };
-  auto tile_compute = [&](int j0, int nvalid) {
+  auto tile_compute = [&](int j0, int nvalid, bool window_tile) {
     // S^T tiles: s[kt] holds keys kt*16 + 4*lg + e for query (lane & 15)
     f32x4_t s[KT / 16];
 #pragma unroll
@@ -174,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e)
           if (kt * 16 + lg * 4 + e >= nvalid) s[kt][e] = -INFINITY;
     }
-    if (j0 < kmin_hi) {  // uniform: only tiles that reach below some query's window start
+    if (window_tile && j0 < kmin_hi) {  // uniform: only tiles that reach below some query's window start
 #pragma unroll
       for (int kt = 0; kt < KT / 16; ++kt)
 #pragma unroll
@@ -231,15 +247,33 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   };
-  if (kbeg < kend) {
-    tile_load(kreg[0], vreg[0], kbeg);
-    for (int j0 = kbeg; j0 < kend; j0 += KT) {
-      tile_store(kreg[0], vreg[0]);
-      tile_load(kreg[0], vreg[0], j0 + KT);
-      __syncthreads();
-      tile_compute(j0, min(KT, kend - j0));
-      __syncthreads();
+  if (ntiles > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile_load(kreg[r], vreg[r], r);
+    for (int t0 = 0; t0 < ntiles; t0 += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int t = t0 + r;  // uniform over the workgroup
+        tile_wait(kreg[r], vreg[r]);
+        if (t < ntiles) tile_store(kreg[r], vreg[r]);
+        tile_load(kreg[r], vreg[r], t + R);
+        __syncthreads();
+        if (t < ntiles) {
+          const bool ctx_tile = !(has_block && t == 0);  // else the block's own keys, all visible
+          const int j0 = kbeg + (t - (has_block ? 1 : 0)) * KT;
+          tile_compute(j0, ctx_tile ? min(KT, kend - j0) : a.G, ctx_tile);
+        }
+        __syncthreads();
+      }
     }
+    // the ring's last loads (clamped re-reads) are awaited before their registers go
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < ROWS_PER; ++i) {
+        vm_wait<0>(kreg[r][i]);
+        vm_wait<0>(vreg[r][i]);
+      }
   }
 
   if (!qvalid) return;
@@ -255,8 +289,12 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
 }
 
 // Merge the chunks of one query row: weights 2^(m_c - max m) and the summed denominators.
-// The chunk statistics are read lane-parallel; an empty chunk has m = -inf, so its weight
-// is exactly 0 and its (zero) partial output adds nothing.
+// Lane c holds chunk c's statistics (the plan keeps nchunks <= 64); the partial outputs of
+// up to kCombineBatch chunks are loaded before the statistics are reduced, so one round trip
+// to memory covers a typical row.  An empty chunk has m = -inf, so its weight is exactly 0
+// and its (zero) partial output adds nothing.  Chunks are summed in order.
+constexpr int kCombineBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t* out, int ldo) {
   const int lane = threadIdx.x & 63;
@@ -266,25 +304,38 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t*
   const int qi = row % a.qrows;
   const int g = row / a.qrows;
   const size_t base = ((size_t)b * a.NKV + g) * a.nchunks;
-  float mx = -INFINITY;
-  for (int c = lane; c < a.nchunks; c += 64) mx = fmaxf(mx, a.part_ml[((base + c) * a.qrows + qi) * 2]);
-  mx = wave_max(mx);
-  float den = 0.f;
-  for (int c = lane; c < a.nchunks; c += 64) {
-    const size_t slot = (base + c) * a.qrows + qi;
-    den += exp2f(a.part_ml[slot * 2] - mx) * a.part_ml[slot * 2 + 1];
-  }
-  den = wave_sum(den);
   constexpr int PL = D / 64;  // values per lane
+  const float* po = a.part_o + (base * a.qrows + qi) * D + lane;
+  const size_t cstride = (size_t)a.qrows * D;  // floats from one chunk's row to the next
+  const int n0 = min(a.nchunks, kCombineBatch);
+  float v[kCombineBatch][PL];
+#pragma unroll
+  for (int c = 0; c < kCombineBatch; ++c)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) v[c][i] = c < n0 ? po[c * cstride + 64 * i] : 0.f;
+  float mc = -INFINITY, lc = 0.f;
+  if (lane < a.nchunks) {
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.part_ml + ((base + lane) * a.qrows + qi) * 2);
+    mc = ml[0];
+    lc = ml[1];
+  }
+  const float mx = wave_max(mc);
+  const float wl = mc == -INFINITY ? 0.f : exp2f(mc - mx);
+  const float den = wave_sum(wl * lc);
   float acc[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < a.nchunks; ++c) {
-    const size_t slot = (base + c) * a.qrows + qi;
-    const float w = exp2f(a.part_ml[slot * 2] - mx);
 #pragma unroll
-    for (int i = 0; i < PL; ++i) acc[i] += w * a.part_o[slot * D + lane + 64 * i];
+  for (int c = 0; c < kCombineBatch; ++c) {
+    if (c >= n0) break;
+    const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c));
+#pragma unroll
+    for (int i = 0; i < PL; ++i) acc[i] += w * v[c][i];
+  }
+  for (int c = n0; c < a.nchunks; ++c) {
+    const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c));
+#pragma unroll
+    for (int i = 0; i < PL; ++i) acc[i] += w * po[c * cstride + 64 * i];
   }
   const float inv = 1.f / den;
   const int hpg = a.NH / a.NKV;
@@ -300,14 +351,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, uint16_t*
 AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax) {
   AttnPlan pl;
   pl.qrows = G * (NH / NKV);
+  // Deep ring: one resident round of 256 CUs x 2 workgroups split over the (b, g) pairs.
+  // When that leaves fewer than kDeepMinTiles tiles per chunk, the ring would be mostly
+  // fill, so the shallow ring takes chunks of 256 keys (or what fills 2048 workgroups).
+  // Either way nchunks <= 64, one chunk per lane in the combine.
   const int pairs = B * NKV;
-  const int want = (2048 + pairs - 1) / pairs;  // chunks per (b, g) to fill the chip
-  int chunk = (Lmax + want - 1) / want;
-  chunk = ((chunk + KT - 1) / KT) * KT;
-  if (chunk < 256) chunk = 256;
-  pl.chunk = chunk;
-  const int ctx_chunks = Lmax > 0 ? (Lmax + chunk - 1) / chunk : 0;
-  pl.nchunks = ctx_chunks + 1;
+  auto chunk_for = [&](int want) {
+    int c = (Lmax + want - 1) / want;
+    c = std::max(c, (Lmax + 63) / 64);
+    c = ((c + KT - 1) / KT) * KT;
+    return std::max(c, 256);
+  };
+  pl.chunk = chunk_for(std::max(1, 512 / pairs));
+  pl.stages = 4;
+  if (pl.chunk / KT < kDeepMinTiles) {
+    pl.chunk = chunk_for(std::max(1, 2048 / pairs));
+    pl.stages = 1;
+  }
+  const int ctx_chunks = Lmax > 0 ? (Lmax + pl.chunk - 1) / pl.chunk : 0;
+  pl.nchunks = std::max(ctx_chunks, 1);
   const size_t slots = (size_t)B * NKV * pl.nchunks * pl.qrows;
   pl.ws_bytes = slots * D * sizeof(float) + slots * 2 * sizeof(float);
   return pl;
@@ -346,10 +408,16 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
   const int rows = NKV * pl.qrows;  // per request
   dim3 cgrid((rows + 3) / 4, B);
   if (D == 128) {
-    attn_chunk_kernel<128><<<grid, 256, 0, stream>>>(a);
+    if (pl.stages == 4)
+      attn_chunk_kernel<128, 4><<<grid, 256, 0, stream>>>(a);
+    else
+      attn_chunk_kernel<128, 1><<<grid, 256, 0, stream>>>(a);
     attn_combine_kernel<128><<<cgrid, 256, 0, stream>>>(a, out, ldo);
   } else {
-    attn_chunk_kernel<64><<<grid, 256, 0, stream>>>(a);
+    if (pl.stages == 4)
+      attn_chunk_kernel<64, 4><<<grid, 256, 0, stream>>>(a);
+    else
+      attn_chunk_kernel<64, 1><<<grid, 256, 0, stream>>>(a);
     attn_combine_kernel<64><<<cgrid, 256, 0, stream>>>(a, out, ldo);
   }
   return hipGetLastError();

@@ -26,6 +26,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "vmem.hpp"
 
 namespace dfl {
 
@@ -377,43 +378,6 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
 // Workgroups of NW = 2 wavefronts, at one wavefront per SIMD, let two workgroups share a CU
 // on separate SIMDs, so a grid of up to 512 workgroups is resident at once.
 
-// Loads the streaming kernel issues itself, so that it alone decides when to wait for them:
-// the compiler's own waits collapse a deep ring (at the loop head it falls back to waiting
-// for everything).  The compiler takes the destination of such a load as written when the
-// asm statement ends, so every loaded value must reach exactly one vm_wait that names it,
-// on every path, before anything else reads it: the registers then stay reserved until the
-// data is in, and nothing copies them early.  (Two alternative waits for one value would
-// make the compiler merge them with copies placed before one of the waits.)
-__device__ __forceinline__ u32x4_t vm_load16_nt(const void* p) {
-  u32x4_t v;
-  asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(v) : "v"(p));
-  return v;
-}
-
-__device__ __forceinline__ u32x4_t vm_load16(const void* p) {
-  u32x4_t v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
-  return v;
-}
-__device__ __forceinline__ uint32_t vm_load4_nt(const void* p) {
-  uint32_t v;
-  asm volatile("global_load_dword %0, %1, off nt" : "=v"(v) : "v"(p));
-  return v;
-}
-__device__ __forceinline__ uint32_t vm_load2(const void* p) {
-  uint32_t v;
-  asm volatile("global_load_ushort %0, %1, off" : "=v"(v) : "v"(p));
-  return v;
-}
-// s_waitcnt vmcnt(N) that also passes v through, so no use of v is scheduled before it (the
-// comment names v's registers in the assembly).
-template <int N, class T>
-__device__ __forceinline__ void vm_wait(T& v) {
-  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%1) ; waits for %0" : "+v"(v) : "i"(N));
-}
-
-
 // A wavefront's weights for one K step: 32 weight rows = 2 fragments of 16 rows x 2 K
 // halves.  LOADS is the number of vector-memory instructions load() issues.
 template <bool TILED, bool Q4>
@@ -474,14 +438,6 @@ struct StreamW<true, true> {
     return __builtin_bit_cast(bf16x8_t, dequant8(q[j * 2 + h], half ? sb[2 + j] : sb[j]));
   }
 };
-
-// s_waitcnt for "at most n vector-memory operations outstanding" (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int n = N > 63 ? 63 : N;
-  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // The activation slab of one K step, [MT * 16 rows][64] bf16, copied from global memory
 // straight into LDS (16 bytes per lane, 1 KB = 8 rows per instruction) without passing

@@ -137,7 +137,8 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
 
 struct AttnPlan {
   int chunk = 0;     // context rows per chunk (multiple of 64)
-  int nchunks = 0;   // context chunks + 1 block chunk
+  int nchunks = 0;   // chunks (<= 64); the last one also takes the block's own keys
+  int stages = 4;    // K/V tiles in flight per workgroup (4 or 1)
   int qrows = 0;     // G * NH / NKV
   size_t ws_bytes = 0;
 };

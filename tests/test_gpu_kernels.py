@@ -84,6 +84,11 @@ def test_head_norm_rope(D, heads, G):
     (128, 8, 2, 16, [600, 0, 257]),   # several 64-key tiles and chunks, empty and ragged contexts
     (64, 4, 2, 8, [32]),              # tiny drafter shape
     (128, 32, 8, 16, [2048, 2048]),   # full drafter head layout
+    (128, 32, 8, 16, [2048, 100]),    # a short request: its last chunk holds only the block's keys
+    (64, 4, 2, 8, [0, 0]),            # no context at all: one chunk of block keys
+    # 32 requests x 8 KV heads: chunks of 9 tiles, taken by the 4-deep K/V ring; ragged
+    # lengths, one empty context and one whole number of tiles
+    (128, 32, 8, 16, [0, 1088] + [int(x) for x in np.random.default_rng(9).integers(500, 1100, 30)]),
 ])
 def test_block_attention(D, NH, NKV, G, ctx):
     Bq = len(ctx)
@@ -133,6 +138,9 @@ def test_linear_q4(M, N, K, out_f32):
     (128, 32, 8, 16, [5000, 129], [5000, 140], 2048),   # long context: earlier chunks skipped
     (64, 4, 2, 8, [40, 3], [45, 3], 5),                 # window < block: early rows see no context
     (64, 4, 2, 8, [33, 20], [33, 20], 100),             # a window wider than every context
+    # the 4-deep K/V ring (32 requests x 8 KV heads, chunks of 9 tiles) under a window
+    (128, 32, 8, 16, [int(x) for x in np.random.default_rng(10).integers(600, 1100, 32)],
+     [int(x) for x in np.random.default_rng(10).integers(600, 1100, 32)], 700),
 ])
 def test_block_attention_sliding_window(D, NH, NKV, G, ctx, pos, window):
     Bq = len(ctx)

@@ -1,5 +1,6 @@
-"""The weight-streaming GEMM's hand-issued loads, checked on the compiled gfx950 assembly
-(host only: hipcc cross-compiles).  See tests/asm_waits.py for the rule."""
+"""The hand-issued loads of the weight-streaming GEMM and of the attention chunks' K/V ring,
+checked on the compiled gfx950 assembly (host only: hipcc cross-compiles).  See
+tests/asm_waits.py for the rule."""
 import os
 import shutil
 import subprocess
@@ -28,17 +29,33 @@ def test_checker_flags_a_load_landing_on_a_reused_register():
     assert check_function(bad)
 
 
-@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
-                    reason="needs hipcc")
-def test_streaming_gemm_waits_cover_every_use(tmp_path):
+def _device_assembly(tmp_path, source):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    out = tmp_path / "gemm.s"
+    out = tmp_path / (source + ".s")
     csrc = os.path.join(ROOT, "dflash2_block_drafter_amd", "csrc")
     cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", csrc, "-x", "hip", "-S",
-           "--cuda-device-only", os.path.join(csrc, "gemm.hip"), "-o", str(out)]
+           "--cuda-device-only", os.path.join(csrc, source), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
-    result = check_assembly(out.read_text(), r"_ZN3dfl12_GLOBAL__N_118gemm_stream_kernel")
+    return out.read_text()
+
+
+needs_hipcc = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                                 reason="needs hipcc")
+
+
+@needs_hipcc
+def test_streaming_gemm_waits_cover_every_use(tmp_path):
+    result = check_assembly(_device_assembly(tmp_path, "gemm.hip"), r"_ZN3dfl12_GLOBAL__N_118gemm_stream_kernel")
     assert len(result) >= 12, "streaming kernel instances not found"
+    bad = {k: v[:3] for k, v in result.items() if v}
+    assert not bad, bad
+
+
+@needs_hipcc
+def test_attention_ring_waits_cover_every_use(tmp_path):
+    asm = _device_assembly(tmp_path, "attention.hip")
+    result = check_assembly(asm, r"_ZN3dfl12_GLOBAL__N_117attn_chunk_kernel")
+    assert len(result) == 4, "attention chunk kernel instances (D = 64, 128; rings of 1 and 4) not found"
     bad = {k: v[:3] for k, v in result.items() if v}
     assert not bad, bad
