@@ -665,6 +665,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 
 constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
+// Wide-M projections with at least a round of 256 x 256 tiles take those (one workgroup per
+// CU, 148 KB of LDS): each wavefront then computes a 128 x 64 block, so a K step reads 43
+// flop per LDS byte instead of 32 and LDS bandwidth stops bounding the matrix units as early.
+// One weight stage in flight keeps the 128 accumulators within 256 registers.
+constexpr int kBigBM = 256;
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
 // Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
 // workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
@@ -784,6 +789,11 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
     return plan_stream(M, N, K, false, kStreamWaves);
   pl.bm = kBM;
   pl.bn = kBN;
+  if (M > kBM && (size_t)((M + kBigBM - 1) / kBigBM) * ((N + kBN - 1) / kBN) >= (size_t)kTargetWorkgroups) {
+    pl.bm = kBigBM;
+    pl.k_per_split = K;
+    return pl;
+  }
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int nk = K / BK;
   int s = 1;
@@ -822,10 +832,6 @@ GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightR
   return p;
 }
 
-// Weight stages in flight: as many as the 63 outstanding vector-memory operations allow
-// next to the activation copies (a bf16 stage is 8 loads, a 4-bit stage 3), and, for bf16,
-// as many as fit in the accumulation registers beside the accumulators (8 row fragments
-// take 128 of the 256).
 // Weight stages in flight: a bf16 stage is 4 loads (4 KB), a 4-bit stage 2 (1.1 KB); the
 // depth keeps a wavefront within 256 registers next to its accumulators.
 template <int MT, int NW>
@@ -866,6 +872,22 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
   if (pl.stream_waves > 0 && (W.tiled || !W.q)) {
     if (p.M > pl.bm) return hipErrorInvalidValue;
     return launch_stream(p, pl, W, stream);
+  }
+  if (pl.bm == kBigBM) {
+    if (pl.splits != 1) return hipErrorInvalidValue;
+    const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBigBM - 1) / kBigBM, 1);
+    if (W.q) {
+      if (W.tiled)
+        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, true, true><<<grid, 512, 0, stream>>>(p);
+      else
+        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, false, true><<<grid, 512, 0, stream>>>(p);
+    } else {
+      if (W.tiled)
+        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, true><<<grid, 512, 0, stream>>>(p);
+      else
+        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, false><<<grid, 512, 0, stream>>>(p);
+    }
+    return hipGetLastError();
   }
   const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM, pl.splits);
   if (W.q) {

@@ -78,6 +78,29 @@ def test_tiny_draft_is_deterministic():
     dr.close()
 
 
+def test_wide_head_on_big_tiles():
+    # 37 blocks of 8 rows and a 32768-word vocabulary: the head (259 rows) fills a round of
+    # 256 x 256 workgroup tiles, with the tile-maxima epilogue; borrowed (row-major) and bound
+    # (tile-contiguous) heads
+    import dataclasses
+    w = configs.with_batch(configs.TINY, 37)
+    w = dataclasses.replace(w, name="tiny_wide_head", dims=dataclasses.replace(w.dims, vocab=32768))
+    d = w.dims
+    dr, wh, th, K, V, tokens, logits = _run_tiny(w)
+    ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
+    ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
+                        bf16_points=True, return_all=True)
+    assert_composed_close(logits, ref["logits"], "head logits")
+    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    tgt = {k: v.to(DEV) for k, v in synth.target_inputs(w).items()}
+    dr.bind_target(tgt["lm_head"])
+    t2, l2 = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], None,
+                      want_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(tokens, t2) and torch.equal(logits, l2)
+    dr.close()
+
+
 def test_bound_head_matches_borrowed_head():
     # binding the target's head (a tile-contiguous copy) changes how the head projection
     # reads it, not what it computes: tokens and logits are identical bit for bit

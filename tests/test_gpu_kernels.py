@@ -38,6 +38,9 @@ def h(t):
     (30, 16640, 4096, True),    # N not a multiple of the 256-column workgroup
     (50, 32768, 2048, False),
     (128, 16384, 4096, True),
+    # 256 x 256 workgroup tiles once they fill a round of 256 workgroups
+    (512, 32768, 256, False),
+    (300, 32868, 320, True),    # ragged M and N
 ])
 def test_linear(M, N, K, out_f32):
     x = bf((M, K), 11)
@@ -120,6 +123,7 @@ def test_block_attention(D, NH, NKV, G, ctx):
     (7, 300, 128, False),       # ragged M and N, two groups
     (30, 520, 2048, True),      # two 16-row fragments, split K
     (50, 256, 640, False),      # four 16-row fragments
+    (300, 32768, 256, True),    # 256 x 256 workgroup tiles, ragged M
 ])
 def test_linear_q4(M, N, K, out_f32):
     x = bf((M, K), 61)
