@@ -177,12 +177,20 @@ def main():
         b = breakdown.get(cls)
         return None if b is None else round(b["GBps"] / HBM_PEAK_GBS, 4)
 
+    # The candidate walk (top-k, score_edges, select_path) against the bytes it cannot avoid:
+    # the head's tile maxima, K logit tiles of 256 per row (at least one per candidate when the
+    # tile maxima guide the top-k), the candidates' predecessor and successor codebook rows
+    # (bf16), and the edge scores written and read back.  A lower bound on what it moves, so
+    # the fraction is too; at these sizes the walk is a latency chain (15 dependent slots).
     walk_cls = ["topk", "score_edges", "select_path"]
     walk_ms = sum(breakdown[c]["ms"] for c in walk_cls if c in breakdown)
     N = Bq * (G - 1)
-    walk_bytes = 4.0 * N * d.vocab + 4.0 * N * d.top_k * (d.rank + d.top_k + 2)
+    K_, R_ = d.top_k, d.rank
+    walk_bytes = (4.0 * N * ((d.vocab + 255) // 256) + 4.0 * N * K_ * 256 + 2.0 * 2 * N * K_ * R_
+                  + 2 * 4.0 * N * K_ * K_)
     hbm = {"conv_prepare": frac("conv_prepare"), "conv_finish": frac("conv_finish"),
-           "walk": round(walk_bytes / (walk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if walk_ms else None}
+           "walk": round(walk_bytes / (walk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if walk_ms else None,
+           "walk_us": round(walk_ms * 1e3, 1) if walk_ms else None}
 
     cpu = None
     if not args.no_cpu_baseline and args.weights == "bf16":

@@ -665,6 +665,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 
 constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
+constexpr int kMaxSplitsSmall = 16;     // K splits when all partial planes fit kSmallPartialBytes
+constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // Wide-M projections with at least a round of 256 x 256 tiles take those (one workgroup per
 // CU, 148 KB of LDS): each wavefront then computes a 128 x 64 block, so a K step reads 43
 // flop per LDS byte instead of 32 and LDS bandwidth stops bounding the matrix units as early.
@@ -796,8 +798,15 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
   }
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int nk = K / BK;
+  // Narrow projections whose partial planes stay small (the kernel projection: 0.66 MB a
+  // plane) split deeper: with few tiles each workgroup's serial K loop is the time, and the
+  // consumers read the extra planes in batches.
+  const size_t plane = (size_t)M * N * sizeof(float);
+  const bool small = plane * kMaxSplitsSmall <= kSmallPartialBytes;
+  const int max_splits = small ? kMaxSplitsSmall : kMaxSplits;
+  const int min_steps = small ? 4 : 6;
   int s = 1;
-  while (s < kMaxSplits && tiles * (s + 1) <= kTargetWorkgroups && nk / (s + 1) >= 6) ++s;
+  while (s < max_splits && tiles * (s + 1) <= kTargetWorkgroups && nk / (s + 1) >= min_steps) ++s;
   int per = (nk + s - 1) / s;
   pl.k_per_split = per * BK;
   pl.splits = (nk + per - 1) / per;
