@@ -183,7 +183,7 @@ int check_config(const dfl_config* c) {
 }
 
 struct DraftLayout {
-  size_t x, n, a, qkv, ao, u, p, h, logits, tmax, z, cand, unary, scores, attn, kpart, partial;
+  size_t x, n, a, qkv, ao, u, p, h, logits, tmax, z, cand, unary, scores, attn, kpart, coef1, partial;
   size_t total;
 };
 
@@ -214,6 +214,7 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
     return (size_t)dfl::plan_gemm(M, N, K).splits * M * N * sizeof(float);
   };
   L.kpart = cv.off; cv.take<char>(planes_bytes(T, 4 * ng, H));
+  L.coef1 = cv.off; cv.take<float>((size_t)T * 2 * ng);  // side-1 coefficients, summed by prepare
   size_t part = planes_bytes(T, qkvw, H);
   const int shapes[][4] = {{T, H, c.heads * c.head_dim, 0}, {T, 2 * F, H, 0}, {T, H, F, 0}, {N, c.vocab, H, 1},
                            {N, c.rank, H, 0}};
@@ -263,14 +264,19 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(W + off); };
   uint16_t *n = u16(lay.n), *a = u16(lay.a), *qkv = u16(lay.qkv), *ao = u16(lay.ao);
   uint16_t *u = u16(lay.u), *p = u16(lay.p);
-  float *kpart = f32(lay.kpart), *part = f32(lay.partial);
+  float *kpart = f32(lay.kpart), *part = f32(lay.partial), *c1 = f32(lay.coef1);
   const dfl::AttnPlan apl = dfl::plan_attention(B, G, NH, NKV, D, Lmax);
   const dfl::GemmPlan p_kp = dfl::plan_gemm(T, 4 * ng, H), p_qkv = dfl::plan_gemm(T, qkvw, H),
                       p_o = dfl::plan_gemm(T, H, NH * D), p_gu = dfl::plan_gemm(T, 2 * F, H),
                       p_dn = dfl::plan_gemm(T, H, F);
   // The kernel projection's columns are [side][tap][group]: side 0 feeds prepare, side 1 finish.
-  dfl::Planes coef0 = dfl::gemm_planes(p_kp, kpart, T, 4 * ng), coef1 = coef0;
-  coef1.p += 2 * ng;
+  // prepare sums side 1's coefficients into one plane as it sums its own
+  const dfl::Planes coef0 = dfl::gemm_planes(p_kp, kpart, T, 4 * ng);
+  dfl::Planes coef1;
+  coef1.p = c1;
+  coef1.S = 1;
+  coef1.ld = 2 * ng;
+  coef1.plane = (size_t)T * 2 * ng;
   const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
   const double norm_bytes = 4.0 * T * H;
   // attention half
@@ -283,7 +289,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     return dfl::launch_gemm_partials(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream, c1);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32, d->q4), stream, [&] {
     return dfl::launch_gemm_partials(p_qkv, a, H, wref(L.qkv, L.qkv_q4), T, qkvw, H, part, stream);
@@ -314,7 +320,7 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     return dfl::launch_gemm_partials(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
-    return dfl::launch_conv(n, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream);
+    return dfl::launch_conv(n, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream, c1);
   }));
   DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL, d->q4), stream, [&] {
     return dfl::launch_gemm(p_gu, a, H, wref(L.gateup, L.gateup_q4), T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr,

@@ -56,16 +56,42 @@ __device__ __forceinline__ void conv8(const ConvIn& in, float d0, float d1, floa
   for (int e = 0; e < 8; ++e) o[e] = (b0[e] + d0) * cur[e] + (b1[e] + d1) * prev[e];
 }
 
+// Sums of two entries of the planes, in plane order, with the loads of both issued together
+// (one round trip per batch of eight planes).
+__device__ __forceinline__ void planes_sum_pair(const Planes& pl, size_t off0, size_t off1, float& s0, float& s1) {
+  const float* q = pl.p;
+  for (int b = 0; b < pl.S; b += 8) {
+    float v0[8], v1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const size_t po = (size_t)min(b + i, pl.S - 1) * pl.plane;
+      v0[i] = q[po + off0];
+      v1[i] = q[po + off1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (b + i >= pl.S) break;
+      s0 = b + i == 0 ? v0[i] : s0 + v0[i];
+      s1 = b + i == 0 ? v1[i] : s1 + v1[i];
+    }
+  }
+}
+
 // R consecutive rows of one block (R divides G) for kConvCh channels per workgroup of
 // kConvCh/8 threads: the R + 1 input rows are loaded once (row t-1 of the first row only
 // when it is in the block) and each later row reuses its predecessor from registers.
+// With coef_next set (side 0 only), the workgroup also sums the other side's coefficients
+// of its rows and groups, which lie 2 * ng columns further in the same planes, and writes
+// them as one fp32 plane [T, 2 * ng] (tap 0 groups, then tap 1): the finish then reads one
+// plane instead of every split of the kernel projection.
 constexpr int kConvCh = 1024;
 
 template <int R>
 __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Planes coef,
                                                            const uint16_t* __restrict__ base, int side,
                                                            int H, int G, int grp,
-                                                           const uint16_t* residual, uint16_t* out) {
+                                                           const uint16_t* residual, uint16_t* out,
+                                                           float* __restrict__ coef_next) {
   __shared__ float cs[R][2 * (kConvCh / 8)];  // kConvCh channels touch at most kConvCh/8 groups
   const int t0 = blockIdx.y * R;
   const int cb = blockIdx.x * kConvCh;
@@ -90,7 +116,14 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Pl
     const size_t crow = (size_t)(t0 + r) * coef.ld;
     for (int i = threadIdx.x; i < 2 * ngw; i += blockDim.x) {
       const int col = i < ngw ? g0 + i : ng + g0 + (i - ngw);
-      cs[r][i] = planes_sum1(coef, crow + col);
+      if (coef_next) {
+        float here, next;
+        planes_sum_pair(coef, crow + col, crow + 2 * ng + col, here, next);
+        cs[r][i] = here;
+        coef_next[(size_t)(t0 + r) * 2 * ng + col] = next;
+      } else {
+        cs[r][i] = planes_sum1(coef, crow + col);
+      }
     }
   }
   __syncthreads();
@@ -205,8 +238,9 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
 }
 
 hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* base, int side, int T, int H, int G,
-                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream, float* coef_next) {
   if (T <= 0) return hipSuccess;
+  if (coef_next && side != 0) return hipErrorInvalidValue;
   // rows per workgroup: the largest of 4, 2, 1 dividing G that still leaves >= 512 workgroups
   const int chunks = (H + kConvCh - 1) / kConvCh;
   int R = 1;
@@ -219,13 +253,13 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
   const dim3 grid(chunks, T / R);
   switch (R) {
     case 4:
-      conv_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+      conv_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
       break;
     case 2:
-      conv_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+      conv_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
       break;
     default:
-      conv_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out);
+      conv_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
   }
   return hipGetLastError();
 }

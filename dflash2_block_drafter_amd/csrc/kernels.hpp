@@ -131,9 +131,12 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream);
 
-// Grouped dynamic conv; side selects base[side]; residual may be null.
+// Grouped dynamic conv; side selects base[side]; residual may be null.  coef_next (side 0
+// only; coef then holds both sides, side 1 at column 2 * ng): also write side 1's summed
+// coefficients as one fp32 plane [T, 2 * ng] for the finish.
 hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* base, int side, int T, int H, int G,
-                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream);
+                       int grp, const uint16_t* residual, uint16_t* out, hipStream_t stream,
+                       float* coef_next = nullptr);
 
 struct AttnPlan {
   int chunk = 0;     // context rows per chunk (multiple of 64)
