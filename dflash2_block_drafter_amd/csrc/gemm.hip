@@ -207,6 +207,10 @@ struct TileLoaderQ4 {
 
 // W rows for EPI_SILU_MUL are interleaved per 16: [gate 16 | up 16] ... so output
 // column j pairs accumulator columns (j/16)*32 + j%16 (gate) and +16 (up).
+// Multiplier of the workgroup index that staggers where each workgroup starts its K loop
+// (coprime with the usual step counts: 80 for K = 5120, 64, 272, 400).
+constexpr unsigned kKRotate = 13;
+
 template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED, bool Q4 = false>
 __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
@@ -227,6 +231,14 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
   const int kbeg = blockIdx.z * p.k_per_split;
   const int kend = min(p.K, kbeg + p.k_per_split);
   const int nk = (kend - kbeg) / BKS;
+  // Step kt reads K block (kt + rot) mod nk: workgroups start their K loops at different
+  // blocks, so at any moment they read weights spread over the HBM channels instead of all
+  // at the same offset of their (equally sized, aligned) weight slabs.
+  const int rot = nk > 0 ? static_cast<int>((blockIdx.x * kKRotate) % static_cast<unsigned>(nk)) : 0;
+  auto kof = [&](int kt) {
+    const int q = kt + rot;
+    return kbeg + (q >= nk ? q - nk : q) * BKS;
+  };
 
   Loader ring[PF];
   f32x4_t acc[TM][TN];
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
 
 #pragma unroll
   for (int s = 0; s < PF; ++s)
-    if (s < nk) ring[s].load(p, m0, n0, kbeg + s * BKS, tid);
+    if (s < nk) ring[s].load(p, m0, n0, kof(s), tid);
   if (nk > 0) ring[0].store(sA[0], sB[0], tid);
 
   auto compute = [&](int buf) {
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int kt = kt0 + s;
-      ring[s].load(p, m0, n0, kbeg + (kt + PF) * BKS, tid);
+      ring[s].load(p, m0, n0, kof(kt + PF), tid);
       __syncthreads();
       compute(kt & 1);
       ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
@@ -282,7 +294,7 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
   for (int s = 0; s < 2 * PF; ++s) {
     const int kt = kt0 + s;
     if (kt < nk) {
-      if (kt + PF < nk) ring[s % PF].load(p, m0, n0, kbeg + (kt + PF) * BKS, tid);
+      if (kt + PF < nk) ring[s % PF].load(p, m0, n0, kof(kt + PF), tid);
       __syncthreads();
       compute(kt & 1);
       if (kt + 1 < nk) ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
@@ -517,12 +529,18 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_stream_kernel(GemmArgs p) {
   // ever outstanding; the counter holds 63.
   static_assert(PF * NB + AD * NA <= 63, "more vector-memory operations in flight than vmcnt counts");
   static_assert(PF >= AD, "the prologue starts step 0's activations within its PF iterations");
-  const int last = kbeg + (nk - 1) * BK;
+  // Step kt's K block is (kt + rot) mod nk, staggered across workgroups as in the LDS kernel;
+  // steps past the last clamp to it.
+  const int rot = nk > 0 ? static_cast<int>((blockIdx.x * kKRotate) % static_cast<unsigned>(nk)) : 0;
+  auto kof = [&](int step) {
+    const int q = min(step, nk - 1) + rot;
+    return kbeg + (q >= nk ? q - nk : q) * BK;
+  };
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     const int step = s - PF + AD;
-    if (step >= 0) SA::load(p, sA[step], min(kbeg + step * BK, last), wave, lane);
-    ring[s].load(p, nw0, min(kbeg + s * BK, last), lane);
+    if (step >= 0) SA::load(p, sA[step], kof(step), wave, lane);
+    ring[s].load(p, nw0, kof(s), lane);
   }
   // At the end of iteration kt, step kt + 1's activations (started AD - 1 iterations
   // earlier) are awaited: AD weight stages and AD - 1 activation stages came after them.
@@ -567,12 +585,12 @@ __global__ __launch_bounds__(NW * 64, 2) void gemm_stream_kernel(GemmArgs p) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int kt = kt0 + s;
-      SA::load(p, sA[(kt + AD) % (AD + 1)], min(kbeg + (kt + AD) * BK, last), wave, lane);
+      SA::load(p, sA[(kt + AD) % (AD + 1)], kof(kt + AD), wave, lane);
       __builtin_amdgcn_sched_barrier(0);
       ring[s].template wait<kWaitW>();
       if (kt < nk) compute(kt % (AD + 1), ring[s]);
       __builtin_amdgcn_sched_barrier(0);
-      ring[s].load(p, nw0, min(kbeg + (kt + PF) * BK, last), lane);
+      ring[s].load(p, nw0, kof(kt + PF), lane);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<kWaitA>();
       __builtin_amdgcn_s_barrier();
