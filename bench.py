@@ -255,38 +255,82 @@ def _time_calls(fn, steps: int, warmup: int) -> float:
     return a.elapsed_time(b) / steps
 
 
+def _time_graph(calls, replays: int, warmup: int) -> float:
+    """Average milliseconds per call of a list of enqueueing closures, captured once into a
+    HIP graph and replayed: events on the replay stream bracket `replays` replays, so the
+    figure is GPU time per call without the host's per-call launch cost."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for fn in calls:  # eager pass before capture
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in calls:
+            fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * len(calls))
+
+
 def bench_conv(args):
     """Grouped conv microbenchmark: T = 64 blocks of 16 rows, H = 5120, groups of 16.
     Timed: one conv application (dfl_conv_finish: the conv kernel alone, side-1 deltas
-    given) and the kernel projection GEMM (dfl_linear, fp32 out)."""
+    given), the kernel projection GEMM (dfl_linear, fp32 out) and a whole dfl_conv_prepare.
+    Each is captured over NSETS distinct input/output sets (more than twice the 256 MB
+    Infinity Cache in total) and the graph is replayed, so every launch reads cold HBM."""
     import torch
     from dflash2_block_drafter_amd import binding as B_
     from dflash2_block_drafter_amd import configs, synth
     c = configs.CONV_BENCH
     T, H, G, grp = c["T"], c["hidden"], c["block"], c["group"]
     ng = H // grp
-    inp = synth.conv_inputs(T, H, grp, c["seed"], device="cuda")
-    a = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    y = torch.empty_like(a)
-    coef1 = torch.empty((T, 2 * ng), dtype=torch.float32, device="cuda")
-    d = torch.empty((T, 4 * ng), dtype=torch.float32, device="cuda")
+    nsets = 24
+    sets = []
+    for i in range(nsets):
+        inp = synth.conv_inputs(T, H, grp, c["seed"] + i, device="cuda")
+        sets.append({"x": inp["x"], "kproj": inp["kproj"], "base": inp["base"],
+                     "a": torch.empty((T, H), dtype=torch.bfloat16, device="cuda"),
+                     "y": torch.empty((T, H), dtype=torch.bfloat16, device="cuda"),
+                     "coef1": torch.empty((T, 2 * ng), dtype=torch.float32, device="cuda"),
+                     "d": torch.empty((T, 4 * ng), dtype=torch.float32, device="cuda")})
     ws = B_.workspace(max(B_.dfl_conv_prepare_workspace_bytes(T, H, grp), B_.dfl_linear_workspace_bytes(T, 4 * ng, H)))
-    B_.dfl_conv_prepare(inp["x"], T, H, G, grp, inp["kproj"], inp["base"], a, coef1, ws)
-    conv_ms = _time_calls(lambda: B_.dfl_conv_finish(a, coef1, inp["base"], T, H, G, grp, None, y),
-                          args.steps, args.warmup)
-    gemm_ms = _time_calls(lambda: B_.dfl_linear(inp["x"], T, H, H, inp["kproj"], 4 * ng, d, 4 * ng, True, ws),
-                          args.steps, args.warmup)
-    prep_ms = _time_calls(lambda: B_.dfl_conv_prepare(inp["x"], T, H, G, grp, inp["kproj"], inp["base"], a, coef1,
-                                                      ws), args.steps, args.warmup)
+    for st in sets:
+        B_.dfl_conv_prepare(st["x"], T, H, G, grp, st["kproj"], st["base"], st["a"], st["coef1"], ws)
+    torch.cuda.synchronize()
+    finish = [lambda st=st: B_.dfl_conv_finish(st["a"], st["coef1"], st["base"], T, H, G, grp, None, st["y"])
+              for st in sets]
+    reps = max(1, args.steps // nsets)
+    conv_ms = _time_graph(finish, reps, 2)
+    # the replayed graph computes what an eager call computes
+    last = sets[-1]
+    eager = torch.empty_like(last["y"])
+    B_.dfl_conv_finish(last["a"], last["coef1"], last["base"], T, H, G, grp, None, eager)
+    torch.cuda.synchronize()
+    assert torch.equal(eager, last["y"]), "graph-replayed conv differs from an eager call"
+    gemm_ms = _time_graph([lambda st=st: B_.dfl_linear(st["x"], T, H, H, st["kproj"], 4 * ng, st["d"], 4 * ng, True, ws)
+                           for st in sets[:8]], reps * 3, 2)
+    prep_ms = _time_graph([lambda st=st: B_.dfl_conv_prepare(st["x"], T, H, G, grp, st["kproj"], st["base"], st["a"],
+                                                            st["coef1"], ws) for st in sets[:8]], reps * 3, 2)
     conv_bytes = 2.0 * T * H + 4.0 * T * 2 * ng + 2.0 * 2 * H + 2.0 * T * H  # y, deltas, base side, out
     gemm_flop = 2.0 * T * 4 * ng * H
     achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "grouped conv application time (T=1024 rows in 16-row blocks, H=5120, groups of 16)",
-        "value": round(conv_ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "value": round(conv_ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * nsets,
         "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "conv: T=1024 H=5120 G=16 grp=16, kernel projection 5120 -> 1280"},
-        "roofline": {"kernel": "conv_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        "config": {"workload": "conv: T=1024 H=5120 G=16 grp=16, kernel projection 5120 -> 1280; "
+                               f"{nsets} input sets rotated (cold HBM), graph-replayed launches"},
+        "roofline": {"kernel": "conv_plane_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(conv_bytes)},
         "kernel_projection_gemm": {"us": round(gemm_ms * 1e3, 2),
@@ -299,39 +343,51 @@ def bench_conv(args):
 
 def bench_selector(args):
     """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
-    Timed: compute_candidates + selector_project + score_edges + select_path."""
+    Timed: compute_candidates + selector_project + score_edges + select_path, the four C-ABI
+    calls in order, over two input sets (0.95 GB of logits, more than the 256 MB Infinity
+    Cache), captured into a HIP graph and replayed."""
     import torch
     from dflash2_block_drafter_amd import binding as B_
     from dflash2_block_drafter_amd import configs, synth
     c = configs.SELECTOR_BENCH
     Bq, S, H, K, V, R = c["B"], c["S"], c["hidden"], c["top_k"], c["vocab"], c["rank"]
     N = Bq * S
-    inp = synth.selector_inputs(Bq, S, H, K, V, R, c["seed"], device="cuda")
-    ids = torch.empty((N, K), dtype=torch.int32, device="cuda")
-    unary = torch.empty((N, K), dtype=torch.float32, device="cuda")
-    z = torch.empty((N, R), dtype=torch.float32, device="cuda")
-    scores = torch.empty((Bq, S, K, K), dtype=torch.float32, device="cuda")
-    tokens = torch.empty((Bq, S), dtype=torch.int32, device="cuda")
+    sets = []
+    for i in range(2):
+        inp = synth.selector_inputs(Bq, S, H, K, V, R, c["seed"] + i, device="cuda")
+        sets.append({"inp": inp, "logits": inp["logits"].reshape(N, V), "hidden": inp["hidden"].reshape(N, H),
+                     "ids": torch.empty((N, K), dtype=torch.int32, device="cuda"),
+                     "unary": torch.empty((N, K), dtype=torch.float32, device="cuda"),
+                     "z": torch.empty((N, R), dtype=torch.float32, device="cuda"),
+                     "scores": torch.empty((Bq, S, K, K), dtype=torch.float32, device="cuda"),
+                     "tokens": torch.empty((Bq, S), dtype=torch.int32, device="cuda")})
     ws_c = B_.workspace(B_.dfl_candidates_workspace_bytes(N, V, K))
     ws_p = B_.workspace(B_.dfl_selector_project_workspace_bytes(N, H, R))
-    logits = inp["logits"].reshape(N, V)
-    hidden = inp["hidden"].reshape(N, H)
 
-    def chain():
-        B_.dfl_compute_candidates(logits, N, V, K, ids, unary, ws_c)
-        B_.dfl_selector_project(hidden, N, H, inp["proj"], R, z, ws_p)
-        B_.dfl_score_edges(ids, unary, z, inp["anchors"], Bq, S, K, R, inp["pred"], inp["succ"], V, scores)
-        B_.dfl_select_path(scores, ids, Bq, S, K, tokens)
+    def chain(st):
+        inp = st["inp"]
+        B_.dfl_compute_candidates(st["logits"], N, V, K, st["ids"], st["unary"], ws_c)
+        B_.dfl_selector_project(st["hidden"], N, H, inp["proj"], R, st["z"], ws_p)
+        B_.dfl_score_edges(st["ids"], st["unary"], st["z"], inp["anchors"], Bq, S, K, R, inp["pred"], inp["succ"], V,
+                           st["scores"])
+        B_.dfl_select_path(st["scores"], st["ids"], Bq, S, K, st["tokens"])
 
-    ms = _time_calls(chain, args.steps, args.warmup)
-    topk_ms = _time_calls(lambda: B_.dfl_compute_candidates(logits, N, V, K, ids, unary, ws_c), args.steps, args.warmup)
+    reps = max(1, args.steps // 2)
+    ms = _time_graph([lambda st=st: chain(st) for st in sets], reps, 2)
+    got = sets[-1]["tokens"].clone()
+    chain(sets[-1])
+    torch.cuda.synchronize()
+    assert torch.equal(got, sets[-1]["tokens"]), "graph-replayed selector differs from an eager call"
+    topk_ms = _time_graph([lambda st=st: B_.dfl_compute_candidates(st["logits"], N, V, K, st["ids"], st["unary"], ws_c)
+                           for st in sets], reps, 2)
     total_bytes = 4.0 * N * V + 2.0 * N * H + 2.0 * R * H + 4.0 * N * R + 2.0 * 2 * N * K * R + 4.0 * N * K * K
     achieved = total_bytes / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "candidate selector time (B=32, S=15, V=248320, K=16, R=64): top-k + projection + edges + walk",
-        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": args.warmup,
         "higher_is_better": False, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16"},
+        "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16; "
+                               "2 input sets rotated, graph-replayed chain"},
         "roofline": {"kernel": "selector chain", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},

@@ -813,11 +813,11 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
     return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map)
                        : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream, id_map);
   }));
-  DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (R + Kc + 2), stream, [&] {
+  DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (2 * R + Kc + 2) + 4.0 * N * R, stream, [&] {
     return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, c.vocab, scores,
                                    stream);
   }));
-  DFL_TRY(timed(d, DFL_K_SELECT_PATH, 4.0 * N * Kc, stream, [&] {
+  DFL_TRY(timed(d, DFL_K_SELECT_PATH, 4.0 * N * Kc * (Kc + 1), stream, [&] {
     return dfl::launch_select_path(scores, cand, B, S, Kc, tokens, stream);
   }));
   return DFL_OK;

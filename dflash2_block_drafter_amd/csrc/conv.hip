@@ -148,6 +148,52 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Pl
   }
 }
 
+// The same conv when the coefficients are one fp32 plane [T, 2 * ng] (the finish's side-1
+// deltas, or a standalone prepare's): each thread loads its own group's two coefficients
+// per row next to its inputs, so there is no LDS staging and no barrier, and the only wait
+// is the one round trip for all of a thread's loads.  R rows of a block per thread, as in
+// conv_kernel; kConvCh / 8 threads cover kConvCh channels.
+template <int R>
+__global__ __launch_bounds__(kConvCh / 8) void conv_plane_kernel(const uint16_t* __restrict__ y,
+                                                                 const float* __restrict__ coef, int ld,
+                                                                 const uint16_t* __restrict__ base, int side,
+                                                                 int H, int G, int grp,
+                                                                 const uint16_t* residual,
+                                                                 uint16_t* out) {  // may be residual
+  const int t0 = blockIdx.y * R;
+  const int c0 = blockIdx.x * kConvCh + threadIdx.x * 8;
+  if (c0 >= H) return;
+  const int g = c0 / grp;
+  const int ng = H / grp;
+  u32x4_t cur[R + 1], rv[R];
+  float d0[R], d1[R];
+  cur[0] = t0 % G != 0 ? *reinterpret_cast<const u32x4_t*>(y + (size_t)(t0 - 1) * H + c0) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    cur[r + 1] = *reinterpret_cast<const u32x4_t*>(y + (size_t)(t0 + r) * H + c0);
+    rv[r] = residual ? *reinterpret_cast<const u32x4_t*>(residual + (size_t)(t0 + r) * H + c0) : u32x4_t{0u, 0u, 0u, 0u};
+    d0[r] = coef[(size_t)(t0 + r) * ld + g];
+    d1[r] = coef[(size_t)(t0 + r) * ld + ng + g];
+  }
+  ConvIn in;
+  in.b0 = *reinterpret_cast<const u32x4_t*>(base + (size_t)(side * 2) * H + c0);
+  in.b1 = *reinterpret_cast<const u32x4_t*>(base + (size_t)(side * 2 + 1) * H + c0);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    in.cur = cur[r + 1];
+    in.prev = cur[r];  // zero at a block start (R divides G, so only r = 0 can be one)
+    float o[8];
+    conv8(in, d0[r], d1[r], o);
+    if (residual) {
+      float rr[8];
+      unpack8(rv[r], rr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rr[e] + o[e];
+    }
+    *reinterpret_cast<u32x4_t*>(out + (size_t)(t0 + r) * H + c0) = pack8(o);
+  }
+}
+
 // conv finish + residual + the next sublayer's RMSNorm, one workgroup per row: the row's
 // new residual stays in registers between the conv and the norm, so x is written once and
 // the norm costs no extra read (dflash2.ts diff, `#block`: x = bf16(x + Conv1(..)), then
@@ -251,6 +297,19 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
     }
   }
   const dim3 grid(chunks, T / R);
+  if (coef.S == 1 && !coef_next) {
+    switch (R) {
+      case 4:
+        conv_plane_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        break;
+      case 2:
+        conv_plane_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        break;
+      default:
+        conv_plane_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+    }
+    return hipGetLastError();
+  }
   switch (R) {
     case 4:
       conv_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);

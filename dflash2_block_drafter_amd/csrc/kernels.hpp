@@ -173,4 +173,5 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
                               int32_t* tokens, hipStream_t stream);
 
+
 }  // namespace dfl

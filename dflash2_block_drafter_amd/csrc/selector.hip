@@ -9,6 +9,8 @@
 // running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes K..63
 // take new candidates).  Ties are ordered by id, so the result is exact and unique for any
 // input, including constant rows (where every tile qualifies).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -215,65 +217,212 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
   }
 }
 
-// score_edges: one wavefront per (b, l).  pred[pid] * z and succ[cand] are gathered into
-// LDS in fp32, then every lane computes K*K/64 dot products of length R in order.
-__global__ __launch_bounds__(64) void score_edges_kernel(
-    const int32_t* __restrict__ cand, const float* __restrict__ unary, const float* __restrict__ z,
-    const int32_t* __restrict__ anchors, int S, int K, int R, const uint16_t* __restrict__ pred,
-    const uint16_t* __restrict__ succ, int V, float* __restrict__ scores) {
-  __shared__ float pz[32 * 128];
-  __shared__ float sc[32 * 128];
-  __shared__ int cid[32], pid[32];
-  const int lane = threadIdx.x;
-  const int l = blockIdx.x;
+// score_edges, one wavefront per (b, l) slot, NW wavefronts per workgroup.  Three memory
+// round trips per slot, every load of a round issued before its first use: (1) the slot's
+// candidate ids, predecessor ids (the anchor at l = 0, else the previous slot's
+// candidates), unary scores and z; (2) the K predecessor and K successor codebook rows,
+// 16 bytes a load when R is a multiple of 8 (VEC), else one element; (3) the scores out.
+// The rows go to the wavefront's LDS as fp32 rows padded to R + 1 floats (pred * z, and
+// succ), so the K * K dot products read distinct banks; lane outputs o = lane, lane + 64,
+// ... (predecessor o / K, candidate o % K), each summing r = 0..R-1 in order.
+constexpr int kMaxRowChunks = 8;  // 16-byte chunks per lane: K * R / 8 <= 32 * 128 / 8 = 512
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void score_edges_kernel(const int32_t* __restrict__ cand,
+                                                          const float* __restrict__ unary,
+                                                          const float* __restrict__ z,
+                                                          const int32_t* __restrict__ anchors, int S, int K, int R,
+                                                          const uint16_t* __restrict__ pred,
+                                                          const uint16_t* __restrict__ succ, int V,
+                                                          float* __restrict__ scores) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
+  const int l = blockIdx.x * (blockDim.x >> 6) + wave;
+  if (l >= S) return;
+  const int RP = R + 1;
+  float* pz = smem + (size_t)wave * (2 * K * RP + R);
+  float* sc = pz + K * RP;
+  float* zs = sc + K * RP;
   const size_t bl = (size_t)b * S + l;
   auto clampv = [V](int t) { return t < 0 ? 0 : (t >= V ? V - 1 : t); };
+  // (1) ids, unary, z
+  int cid = 0, pid = 0;
+  float u = 0.f;
   if (lane < K) {
-    cid[lane] = clampv(cand[bl * K + lane]);
-    pid[lane] = clampv(l == 0 ? anchors[b] : cand[(bl - 1) * K + lane]);
+    cid = clampv(cand[bl * K + lane]);
+    pid = clampv(l == 0 ? anchors[b] : cand[(bl - 1) * K + lane]);
+    u = unary[bl * K + lane];
   }
-  __syncthreads();
-  for (int i = lane; i < K * R; i += 64) {
-    const int p = i / R, r = i % R;
-    pz[i] = bf16_to_f32(pred[(size_t)pid[p] * R + r]) * z[bl * R + r];
-    sc[i] = bf16_to_f32(succ[(size_t)cid[p] * R + r]);
+  const float z0 = lane < R ? z[bl * R + lane] : 0.f;
+  const float z1 = lane + 64 < R ? z[bl * R + lane + 64] : 0.f;
+  if (lane < R) zs[lane] = z0;
+  if (lane + 64 < R) zs[lane + 64] = z1;
+  wave_lds_sync();
+  // (2) codebook rows
+  if (VEC) {
+    const int per_row = R / 8;
+    u32x4_t pv[kMaxRowChunks], sv[kMaxRowChunks];
+#pragma unroll
+    for (int i = 0; i < kMaxRowChunks; ++i) {
+      const int idx = lane + 64 * i;
+      const int p = min(idx / per_row, K - 1);
+      const int pi = __shfl(pid, p, 64);
+      const int ci = __shfl(cid, p, 64);
+      if (idx < K * per_row) {
+        const int r0 = (idx % per_row) * 8;
+        pv[i] = *reinterpret_cast<const u32x4_t*>(pred + (size_t)pi * R + r0);
+        sv[i] = *reinterpret_cast<const u32x4_t*>(succ + (size_t)ci * R + r0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxRowChunks; ++i) {
+      const int idx = lane + 64 * i;
+      if (idx < K * per_row) {
+        const int p = idx / per_row, r0 = (idx % per_row) * 8;
+        float pf[8], sf[8];
+        unpack8(pv[i], pf);
+        unpack8(sv[i], sf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pz[p * RP + r0 + e] = pf[e] * zs[r0 + e];
+          sc[p * RP + r0 + e] = sf[e];
+        }
+      }
+    }
+  } else {
+    for (int i0 = 0; i0 < K * R; i0 += 64 * kMaxRowChunks) {
+      float pf[kMaxRowChunks], sf[kMaxRowChunks];
+#pragma unroll
+      for (int i = 0; i < kMaxRowChunks; ++i) {
+        const int idx = i0 + lane + 64 * i;
+        const int p = min(idx / R, K - 1);
+        const int pi = __shfl(pid, p, 64);
+        const int ci = __shfl(cid, p, 64);
+        if (idx < K * R) {
+          pf[i] = bf16_to_f32(pred[(size_t)pi * R + idx % R]);
+          sf[i] = bf16_to_f32(succ[(size_t)ci * R + idx % R]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMaxRowChunks; ++i) {
+        const int idx = i0 + lane + 64 * i;
+        if (idx < K * R) {
+          const int p = idx / R, r = idx % R;
+          pz[p * RP + r] = pf[i] * zs[r];
+          sc[p * RP + r] = sf[i];
+        }
+      }
+    }
   }
-  __syncthreads();
-  for (int o = lane; o < K * K; o += 64) {
-    const int p = o / K, c = o % K;
+  wave_lds_sync();
+  // (3) the K * K scores
+  for (int o0 = 0; o0 < K * K; o0 += 64) {
+    const int o = o0 + lane;
+    const int p = min(o / K, K - 1), c = o % K;
+    const float uc = __shfl(u, c, 64);
+    const float* a = pz + p * RP;
+    const float* w = sc + c * RP;
     float acc = 0.f;
-    for (int r = 0; r < R; ++r) acc += pz[p * R + r] * sc[c * R + r];
-    scores[bl * K * K + o] = unary[bl * K + c] + acc;
+    for (int r = 0; r < R; ++r) acc += a[r] * w[r];
+    if (o < K * K) scores[bl * K * K + o] = uc + acc;
   }
 }
 
-// Greedy walk: one wavefront per request, lane c holds candidate c's score on the current
-// predecessor row; argmax with the lowest c on ties.
+// One greedy step on the current predecessor row (K scores in LDS): the argmax with the
+// lowest candidate on ties.  Every lane agrees for finite scores; lane 0's winner is taken
+// so that a NaN can never send a lane past the K candidates.
+__device__ __forceinline__ int walk_step(const float* row, int K, int lane) {
+  float v = lane < K ? row[lane] : -INFINITY;
+  int c = lane < K ? lane : kNoId;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oc = __shfl_xor(c, o, 64);
+    if (before(ov, oc, v, c)) {
+      v = ov;
+      c = oc;
+    }
+  }
+  const int j = __shfl(c, 0, 64);
+  return (j >= 0 && j < K) ? j : 0;
+}
+
+// Greedy walk over given scores: one wavefront per request.  Chunks of slots are copied into
+// LDS with coalesced loads (every load of a chunk in flight at once), then walked there.
+constexpr int kWalkLdsFloats = 4096;
+
 __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict__ scores,
-                                                         const int32_t* __restrict__ cand, int S,
-                                                         int K, int32_t* __restrict__ tokens) {
+                                                         const int32_t* __restrict__ cand, int S, int K,
+                                                         int32_t* __restrict__ tokens) {
+  __shared__ __attribute__((aligned(16))) float sc[kWalkLdsFloats];
+  __shared__ int ids[kWalkLdsFloats];  // the chunk's candidate ids (n * K <= kWalkLdsFloats / K)
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
+  const int KK = K * K;
+  const int chunk = max(1, min(S, kWalkLdsFloats / KK));
   int j = 0;
-  for (int l = 0; l < S; ++l) {
-    const size_t bl = (size_t)b * S + l;
-    float v = lane < K ? scores[(bl * K + j) * K + lane] : -INFINITY;
-    int c = lane < K ? lane : kNoId;
+  for (int l0 = 0; l0 < S; l0 += chunk) {
+    const int n = min(chunk, S - l0);
+    const float* src = scores + ((size_t)b * S + l0) * KK;
+    const int m = n * KK;
+    if (((reinterpret_cast<uintptr_t>(src) & 15) | (m & 3)) == 0) {
+      // the chunk as float4: at most kWalkLdsFloats / 4 / 64 = 16 loads a lane, all in flight
+      f32x4_t v[kWalkLdsFloats / 256];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(v, o, 64);
-      const int oc = __shfl_xor(c, o, 64);
-      if (before(ov, oc, v, c)) {
-        v = ov;
-        c = oc;
+      for (int i = 0; i < kWalkLdsFloats / 256; ++i) {
+        const int q = lane + 64 * i;
+        if (q < m / 4) v[i] = reinterpret_cast<const f32x4_t*>(src)[q];
+      }
+#pragma unroll
+      for (int i = 0; i < kWalkLdsFloats / 256; ++i) {
+        const int q = lane + 64 * i;
+        if (q < m / 4) reinterpret_cast<f32x4_t*>(sc)[q] = v[i];
+      }
+    } else {
+      for (int i0 = 0; i0 < m; i0 += 64 * 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = i0 + lane + 64 * i;
+          if (q < m) v[i] = src[q];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = i0 + lane + 64 * i;
+          if (q < m) sc[q] = v[i];
+        }
       }
     }
-    // every lane agrees for finite scores; take lane 0's winner so a NaN can never send a
-    // lane past the K candidates
-    j = __shfl(c, 0, 64);
-    j = (j >= 0 && j < K) ? j : 0;
-    if (lane == 0) tokens[bl] = cand[bl * K + j];
+    // the chunk's candidate ids, so that no step of the walk waits on a global load
+    const int32_t* csrc = cand + ((size_t)b * S + l0) * K;
+    for (int i0 = 0; i0 < n * K; i0 += 64 * 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = i0 + lane + 64 * i;
+        if (q < n * K) v[i] = csrc[q];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int q = i0 + lane + 64 * i;
+        if (q < n * K) ids[q] = v[i];
+      }
+    }
+    __syncthreads();
+    for (int w = 0; w < n; ++w) {
+      const size_t bl = (size_t)b * S + l0 + w;
+      j = walk_step(sc + (size_t)w * KK + (size_t)j * K, K, lane);
+      if (lane == 0) tokens[bl] = ids[w * K + j];
+    }
+    __syncthreads();
   }
 }
 
@@ -308,8 +457,18 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
                               const uint16_t* pred, const uint16_t* succ, int V, float* scores,
                               hipStream_t stream) {
   if (B <= 0 || S <= 0) return hipSuccess;
-  score_edges_kernel<<<dim3(S, B), 64, 0, stream>>>(cand, unary, z, anchors, S, K, R, pred, succ,
-                                                     V, scores);
+  if (K > 32 || R > 128) return hipErrorInvalidValue;
+  // wavefronts per workgroup: up to 4 slots, within 64 KB of LDS
+  const size_t per_wave = (2 * (size_t)K * (R + 1) + R) * sizeof(float);
+  const int nw = (int)std::max<size_t>(1, std::min<size_t>(4, (64 << 10) / per_wave));
+  const dim3 grid((S + nw - 1) / nw, B);
+  const bool vec = R % 8 == 0 && ((reinterpret_cast<uintptr_t>(pred) | reinterpret_cast<uintptr_t>(succ)) & 15) == 0;
+  if (vec)
+    score_edges_kernel<true><<<grid, 64 * nw, per_wave * nw, stream>>>(cand, unary, z, anchors, S, K, R, pred, succ, V,
+                                                                       scores);
+  else
+    score_edges_kernel<false><<<grid, 64 * nw, per_wave * nw, stream>>>(cand, unary, z, anchors, S, K, R, pred, succ,
+                                                                        V, scores);
   return hipGetLastError();
 }
 

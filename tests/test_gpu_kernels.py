@@ -273,7 +273,8 @@ def _selector_inputs(Bq, S, K, R, V, seed, book_std=0.5):
     return logits, pred, succ, z, anchors, cand, unary
 
 
-@pytest.mark.parametrize("Bq,S,K,R,V", [(3, 5, 16, 64, 5000), (1, 7, 4, 16, 1024), (2, 15, 32, 128, 300)])
+@pytest.mark.parametrize("Bq,S,K,R,V", [(3, 5, 16, 64, 5000), (1, 7, 4, 16, 1024), (2, 15, 32, 128, 300),
+                                         (2, 6, 8, 12, 700)])   # R % 8 != 0: element gathers
 def test_score_edges(Bq, S, K, R, V):
     _, pred, succ, z, anchors, cand, unary = _selector_inputs(Bq, S, K, R, V, 81)
     scores = torch.empty((Bq, S, K, K), dtype=torch.float32, device=DEV)
@@ -286,7 +287,8 @@ def test_score_edges(Bq, S, K, R, V):
     assert np.all(s[:, 0] == s[:, 0, :1]), "slot-0 rows must be identical across predecessors"
 
 
-@pytest.mark.parametrize("Bq,S,K", [(32, 15, 16), (1, 7, 4), (3, 4, 32)])
+@pytest.mark.parametrize("Bq,S,K", [(32, 15, 16), (1, 7, 4), (3, 4, 32),
+                                    (2, 20, 16), (2, 3, 64)])   # several LDS chunks of slots
 def test_select_path_bitexact(Bq, S, K):
     g = torch.Generator().manual_seed(91)
     scores = (torch.randn((Bq, S, K, K), generator=g) * 2).float()
