@@ -47,7 +47,7 @@ struct GemmArgs {
   int nsplit;
   float* partial;
   int splits;
-  float* tile_max;  // EPI_F32, one split: [M, gridDim.x] row maxima of each BN-column tile
+  float* tile_max;  // EPI_F32, one split: [M, ceil(N / 256)] row maxima of each 256-column tile
   // 4-bit affine weights (used instead of W): row-major packed [N, K/8] words with scales and
   // biases [N, K/64] bf16, or tile-contiguous blocks (q4_tiled_words)
   const uint32_t* Wq;
@@ -211,97 +211,35 @@ struct TileLoaderQ4 {
 // (coprime with the usual step counts: 80 for K = 5120, 64, 272, 400).
 constexpr unsigned kKRotate = 13;
 
-template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED, bool Q4 = false>
-__global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM / 16;
-  constexpr int TN = BN / WN / 16;
-  constexpr int LDS_STRIDE = BKS + 8;  // +16 bytes: 16-byte reads of 16 rows hit distinct banks
-  using Loader = std::conditional_t<Q4, TileLoaderQ4<BM, BN, BKS, NT, TILED>, TileLoader<BM, BN, BKS, NT, TILED>>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int kbeg = blockIdx.z * p.k_per_split;
-  const int kend = min(p.K, kbeg + p.k_per_split);
-  const int nk = (kend - kbeg) / BKS;
-  // Step kt reads K block (kt + rot) mod nk: workgroups start their K loops at different
-  // blocks, so at any moment they read weights spread over the HBM channels instead of all
-  // at the same offset of their (equally sized, aligned) weight slabs.
-  const int rot = nk > 0 ? static_cast<int>((blockIdx.x * kKRotate) % static_cast<unsigned>(nk)) : 0;
-  auto kof = [&](int kt) {
-    const int q = kt + rot;
-    return kbeg + (q >= nk ? q - nk : q) * BKS;
-  };
-
-  Loader ring[PF];
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (s < nk) ring[s].load(p, m0, n0, kof(s), tid);
-  if (nk > 0) ring[0].store(sA[0], sB[0], tid);
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < BKS / 32; ++ks) {
-      const int kk = ks * 32 + (lane >> 4) * 8;
-      bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * (TM * 16) + i * 16 + (lane & 15);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][row * LDS_STRIDE + kk]);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = wn * (TN * 16) + j * 16 + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][col * LDS_STRIDE + kk]);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Iteration kt: refill ring slot kt%PF with step kt+PF, compute step kt from LDS buffer
-  // kt%2, then move step kt+1 (ring slot (kt+1)%PF) into LDS buffer (kt+1)%2.  The main
-  // loop runs while every refill is in range and is unrolled PF times so every ring index
-  // is a compile-time constant; the last steps run in a guarded tail without refills.
-  int kt0 = 0;
-  for (; kt0 + 2 * PF <= nk; kt0 += PF) {
-#pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      const int kt = kt0 + s;
-      ring[s].load(p, m0, n0, kof(kt + PF), tid);
-      __syncthreads();
-      compute(kt & 1);
-      ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
-    }
+// Workgroup -> (N tile, M tile).  Workgroups are dispatched in id order (x fastest) and
+// dealt round-robin to the 8 XCDs, each with its own L2.  When the weights are the larger
+// operand (N > M) and there are several M tiles, the ids are remapped so that each XCD runs
+// a contiguous stretch of an M-fastest order: the M tiles of one N tile, which read the same
+// weight tile, run together on one XCD and share its L2, instead of each weight tile
+// streaming from HBM once per M tile (a bijection on the first 8 * floor(total / 8) ids,
+// identity on the rest).  Otherwise the launch order is kept: with the activations the
+// larger operand, N tiles fastest across the XCDs measured best.
+__device__ __forceinline__ void tile_of_block(int M, int N, int& nt_idx, int& mt_idx) {
+  const int nt = gridDim.x, mt = gridDim.y;
+  if (mt == 1 || N <= M) {
+    nt_idx = blockIdx.x;
+    mt_idx = blockIdx.y;
+    return;
   }
-#pragma unroll
-  for (int s = 0; s < 2 * PF; ++s) {
-    const int kt = kt0 + s;
-    if (kt < nk) {
-      if (kt + PF < nk) ring[s % PF].load(p, m0, n0, kof(kt + PF), tid);
-      __syncthreads();
-      compute(kt & 1);
-      if (kt + 1 < nk) ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
-    }
-  }
+  const int total = nt * mt;
+  const int id = blockIdx.y * nt + blockIdx.x;
+  const int t8 = total / 8;
+  const int rid = id < t8 * 8 ? (id % 8) * t8 + id / 8 : id;
+  mt_idx = rid % mt;
+  nt_idx = rid / mt;
+}
 
-  // Accumulator layout: lane holds column (lane & 15) and rows 4*(lane >> 4) + e.
+// The output stage shared by the LDS kernels: split-K partial planes, SiLU(gate) * up, or a
+// plain store, plus each 256-column tile's row maxima when asked for.  Accumulator layout:
+// lane holds column (lane & 15) and rows 4 * (lane >> 4) + e of each 16 x 16 block.
+template <int BM, int WN, int TM, int TN, int NT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (&acc)[TM][TN], int m0, int n0,
+                                              int wm, int wn, int lane, int tid) {
   const int mrow = m0 + wm * (TM * 16) + (lane >> 4) * 4;
   const int ncol = n0 + wn * (TN * 16) + (lane & 15);
   if (p.splits > 1) {
@@ -369,10 +307,105 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
         float v = rmax[0][r];
 #pragma unroll
         for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
-        p.tile_max[(size_t)m * gridDim.x + blockIdx.x] = v;
+        p.tile_max[(size_t)m * ((p.N + kGemmTileN - 1) / kGemmTileN) + n0 / kGemmTileN] = v;
       }
     }
   }
+}
+
+template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED, bool Q4 = false>
+__global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM / 16;
+  constexpr int TN = BN / WN / 16;
+  constexpr int LDS_STRIDE = BKS + 8;  // +16 bytes: 16-byte reads of 16 rows hit distinct banks
+  using Loader = std::conditional_t<Q4, TileLoaderQ4<BM, BN, BKS, NT, TILED>, TileLoader<BM, BN, BKS, NT, TILED>>;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * LDS_STRIDE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+  int ntile, mtile;
+  tile_of_block(p.M, p.N, ntile, mtile);
+  const int n0 = ntile * BN;
+  const int m0 = mtile * BM;
+  const int kbeg = blockIdx.z * p.k_per_split;
+  const int kend = min(p.K, kbeg + p.k_per_split);
+  const int nk = (kend - kbeg) / BKS;
+  // Step kt reads K block (kt + rot) mod nk: workgroups start their K loops at different
+  // blocks, so at any moment they read weights spread over the HBM channels instead of all
+  // at the same offset of their (equally sized, aligned) weight slabs.
+  const int rot = nk > 0 ? static_cast<int>((ntile * kKRotate) % static_cast<unsigned>(nk)) : 0;
+  auto kof = [&](int kt) {
+    const int q = kt + rot;
+    return kbeg + (q >= nk ? q - nk : q) * BKS;
+  };
+
+  Loader ring[PF];
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+    if (s < nk) ring[s].load(p, m0, n0, kof(s), tid);
+  if (nk > 0) ring[0].store(sA[0], sB[0], tid);
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < BKS / 32; ++ks) {
+      const int kk = ks * 32 + (lane >> 4) * 8;
+      bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * (TM * 16) + i * 16 + (lane & 15);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][row * LDS_STRIDE + kk]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn * (TN * 16) + j * 16 + (lane & 15);
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][col * LDS_STRIDE + kk]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Iteration kt: refill ring slot kt%PF with step kt+PF, compute step kt from LDS buffer
+  // kt%2, then move step kt+1 (ring slot (kt+1)%PF) into LDS buffer (kt+1)%2.  The main
+  // loop runs while every refill is in range and is unrolled PF times so every ring index
+  // is a compile-time constant; the last steps run in a guarded tail without refills.
+  int kt0 = 0;
+  for (; kt0 + 2 * PF <= nk; kt0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int kt = kt0 + s;
+      ring[s].load(p, m0, n0, kof(kt + PF), tid);
+      __syncthreads();
+      compute(kt & 1);
+      ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 2 * PF; ++s) {
+    const int kt = kt0 + s;
+    if (kt < nk) {
+      if (kt + PF < nk) ring[s % PF].load(p, m0, n0, kof(kt + PF), tid);
+      __syncthreads();
+      compute(kt & 1);
+      if (kt + 1 < nk) ring[(s + 1) % PF].store(sA[(kt + 1) & 1], sB[(kt + 1) & 1], tid);
+    }
+  }
+
+  gemm_epilogue<BM, WN, TM, TN, NT>(p, acc, m0, n0, wm, wn, lane, tid);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -491,6 +524,143 @@ __device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
 template <int N>
 __device__ __forceinline__ void lds_wait(bf16x8_t& v) {
   asm volatile("s_waitcnt lgkmcnt(%1) ; waits for %0" : "+v"(v) : "i"(N));
+}
+// lds_wait with the count given by a value the unrolled loop makes a constant (0..15).
+__device__ __forceinline__ void lds_wait_n(bf16x8_t& v, int n) {
+  switch (n) {
+    case 0: lds_wait<0>(v); break;
+    case 1: lds_wait<1>(v); break;
+    case 2: lds_wait<2>(v); break;
+    case 3: lds_wait<3>(v); break;
+    case 4: lds_wait<4>(v); break;
+    case 5: lds_wait<5>(v); break;
+    case 6: lds_wait<6>(v); break;
+    default: lds_wait<7>(v); break;
+  }
+}
+
+// 256 x 256 workgroup tiles for projections with enough rows to be bound by the matrix
+// cores.  Both operands go from global memory straight into LDS (global_load_lds, 16 bytes
+// a lane, no registers) through a ring of kDmaStages buffers; a buffer holds one 32-deep K
+// half of both tiles in MFMA fragment order: fragment f (16 rows x 32 K) is 1 KB with lane
+// l's 16 bytes (row l % 16, K offset 8 (l / 16)) at 16 l, so every fragment read is one
+// contiguous, conflict-free 1 KB per wavefront.  Tile-contiguous weights are already in
+// that order (each load is 1 KB contiguous); activations and row-major weights are read
+// as 16 row segments of 64 bytes.  Step kt + 3's loads are issued while step kt is
+// computed.  Eight wavefronts of 128 x 64 outputs (8 x 4 MFMA blocks).
+//
+// Waits: a wavefront's copies complete in issue order, so before step kt it waits until
+// at most the eight copies of steps kt + 1 and kt + 2 are outstanding; the barrier then
+// makes every wavefront's step-kt copies visible and tells it that all wavefronts are done
+// reading the buffer that step kt + 3 refills.  LDS reads are inline assembly (the
+// compiler's alias tracking would make them wait for every copy in flight), each value
+// tied to the lgkmcnt wait that covers it.
+constexpr int kDmaStages = 4;
+
+template <bool TILED>
+__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
+  constexpr int BN = kGemmTileN, WN = 4, TM = 8, TN = 4, NT = 512;
+  constexpr int FR = 512;         // bf16 per fragment
+  constexpr int STAGE = 16 * FR;  // one operand's K half of a 256-row tile
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kDmaStages][STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kDmaStages][STAGE];
+  static_assert(BN == 256, "fragment-order weight blocks are 256 rows");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  int ntile, mtile;
+  tile_of_block(p.M, p.N, ntile, mtile);
+  const int n0 = ntile * BN;
+  const int m0 = mtile * 256;
+  const int nkb = p.K / 64;  // 64-deep K blocks (one split)
+  const int nst = 2 * nkb;   // K halves
+  const int rot = nkb > 0 ? static_cast<int>((ntile * kKRotate) % static_cast<unsigned>(nkb)) : 0;
+  // wavefront w copies fragments 2w and 2w + 1 of both tiles every step
+  const int fa = 2 * wave;
+  const int fk = (lane >> 4) * 8;
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    arow[i] = p.A + (size_t)min(m0 + 16 * (fa + i) + (lane & 15), p.M - 1) * p.lda + fk;
+    brow[i] = TILED ? p.W + (size_t)(n0 / BN) * nkb * (BN * 64) + (size_t)(2 * (fa + i)) * FR + lane * 8
+                    : p.W + (size_t)min(n0 + 16 * (fa + i) + (lane & 15), p.N - 1) * p.K + fk;
+  }
+  // step st's copies into buffer slot (steps past the last re-read the last one, so every
+  // iteration issues and awaits the same number of copies)
+  auto issue = [&](int st, int slot) {
+    const int s = min(st, nst - 1);
+    const int h = s & 1;
+    int kb = (s >> 1) + rot;
+    kb = kb >= nkb ? kb - nkb : kb;
+    const int k0 = kb * 64 + h * 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + k0, &sA[slot][(fa + i) * FR], 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t* src = TILED ? brow[i] + (size_t)kb * (BN * 64) + h * FR : brow[i] + k0;
+      __builtin_amdgcn_global_load_lds(src, &sB[slot][(fa + i) * FR], 16, 0, 0);
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t sa0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0])) + (wm * TM * FR + lane * 8) * 2;
+  const uint32_t sb0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sB[0][0])) + (wn * TN * FR + lane * 8) * 2;
+  // Fragments are double-buffered in registers: step kt + 1's are read from LDS while step
+  // kt's MFMAs run, and awaited (every value tied to a wait) after them.
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  auto read = [&](int slot, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+    const uint32_t oa = sa0 + slot * (STAGE * 2), ob = sb0 + slot * (STAGE * 2);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = lds_read_b128(ob + j * (FR * 2));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = lds_read_b128(oa + i * (FR * 2));
+  };
+  auto await = [&](bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) lds_wait<0>(b[j]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) lds_wait<0>(a[i]);
+  };
+  auto mfma = [&](const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // iteration kt: step kt + 1's copies are in (only step kt + 2's four are outstanding),
+  // the barrier publishes them and frees step kt - 1's buffer, which step kt + 3 refills
+  auto step = [&](int kt, const bf16x8_t (&ca)[TM], const bf16x8_t (&cb)[TN], bf16x8_t (&na)[TM],
+                  bf16x8_t (&nb)[TN]) {
+    wait_vmcnt<4>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3, (kt + 3) & (kDmaStages - 1));
+    read((kt + 1) & (kDmaStages - 1), na, nb);  // past the last step: a re-read copy, unused
+    mfma(ca, cb);
+    await(na, nb);
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  wait_vmcnt<8>();
+  __builtin_amdgcn_s_barrier();
+  read(0, fa0, fb0);
+  await(fa0, fb0);
+  for (int kt = 0; kt < nst; kt += 2) {  // nst is even
+    step(kt, fa0, fb0, fa1, fb1);
+    step(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  wait_vmcnt<0>();  // the re-read copies past the last step land before the LDS is reused
+  gemm_epilogue<256, WN, TM, TN, NT>(p, acc, m0, n0, wm, wn, lane, tid);
 }
 
 // NW wavefronts per workgroup, 32 weight rows each, two wavefronts per SIMD (256 registers
@@ -910,9 +1080,9 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
         gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, false, true><<<grid, 512, 0, stream>>>(p);
     } else {
       if (W.tiled)
-        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, true><<<grid, 512, 0, stream>>>(p);
+        gemm_dma_kernel<true><<<grid, 512, 0, stream>>>(p);
       else
-        gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, false><<<grid, 512, 0, stream>>>(p);
+        gemm_dma_kernel<false><<<grid, 512, 0, stream>>>(p);
     }
     return hipGetLastError();
   }

@@ -1,6 +1,6 @@
-"""The hand-issued loads of the weight-streaming GEMM and of the attention chunks' K/V ring,
-checked on the compiled gfx950 assembly (host only: hipcc cross-compiles).  See
-tests/asm_waits.py for the rule."""
+"""The hand-issued loads of the weight-streaming GEMM, of the 256 x 256 DMA GEMM and of the
+attention chunks' K/V ring, checked on the compiled gfx950 assembly (host only: hipcc
+cross-compiles).  See tests/asm_waits.py for the rule."""
 import os
 import shutil
 import subprocess
@@ -57,5 +57,14 @@ def test_attention_ring_waits_cover_every_use(tmp_path):
     asm = _device_assembly(tmp_path, "attention.hip")
     result = check_assembly(asm, r"_ZN3dfl12_GLOBAL__N_117attn_chunk_kernel")
     assert len(result) == 4, "attention chunk kernel instances (D = 64, 128; rings of 1 and 4) not found"
+    bad = {k: v[:3] for k, v in result.items() if v}
+    assert not bad, bad
+
+
+@needs_hipcc
+def test_dma_gemm_fragment_reads_are_awaited(tmp_path):
+    # the 256 x 256 tile kernel's LDS fragment reads are inline assembly, each tied to a wait
+    result = check_assembly(_device_assembly(tmp_path, "gemm.hip"), r"_ZN3dfl12_GLOBAL__N_115gemm_dma_kernel")
+    assert len(result) == 2, "DMA kernel instances (tiled and row-major weights) not found"
     bad = {k: v[:3] for k, v in result.items() if v}
     assert not bad, bad
