@@ -573,8 +573,9 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   tile_of_block(p.M, p.N, ntile, mtile);
   const int n0 = ntile * BN;
   const int m0 = mtile * 256;
-  const int nkb = p.K / 64;  // 64-deep K blocks (one split)
-  const int nst = 2 * nkb;   // K halves
+  const int kb0 = blockIdx.z * (p.k_per_split / 64);               // first 64-deep K block of this split
+  const int nkb = (min(p.K, (blockIdx.z + 1) * p.k_per_split) - blockIdx.z * p.k_per_split) / 64;
+  const int nst = 2 * nkb;  // K halves
   const int rot = nkb > 0 ? static_cast<int>((ntile * kKRotate) % static_cast<unsigned>(nkb)) : 0;
   // wavefront w copies fragments 2w and 2w + 1 of both tiles every step
   const int fa = 2 * wave;
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     arow[i] = p.A + (size_t)min(m0 + 16 * (fa + i) + (lane & 15), p.M - 1) * p.lda + fk;
-    brow[i] = TILED ? p.W + (size_t)(n0 / BN) * nkb * (BN * 64) + (size_t)(2 * (fa + i)) * FR + lane * 8
+    brow[i] = TILED ? p.W + ((size_t)(n0 / BN) * (p.K / 64) + kb0) * (BN * 64) + (size_t)(2 * (fa + i)) * FR + lane * 8
                     : p.W + (size_t)min(n0 + 16 * (fa + i) + (lane & 15), p.N - 1) * p.K + fk;
   }
   // step st's copies into buffer slot (steps past the last re-read the last one, so every
@@ -592,9 +593,9 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   auto issue = [&](int st, int slot) {
     const int s = min(st, nst - 1);
     const int h = s & 1;
-    int kb = (s >> 1) + rot;
+    int kb = (s >> 1) + rot;  // K block within the split
     kb = kb >= nkb ? kb - nkb : kb;
-    const int k0 = kb * 64 + h * 32;
+    const int k0 = (kb0 + kb) * 64 + h * 32;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_global_load_lds(arow[i] + k0, &sA[slot][(fa + i) * FR], 16, 0, 0);
@@ -860,6 +861,7 @@ constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // flop per LDS byte instead of 32 and LDS bandwidth stops bounding the matrix units as early.
 // One weight stage in flight keeps the 128 accumulators within 256 registers.
 constexpr int kBigBM = 256;
+constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;  // big tiles with split K from these sizes
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
 // Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
 // workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
@@ -984,6 +986,21 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
     pl.k_per_split = K;
     return pl;
   }
+  // Enough rows for 256 x 256 tiles but too few tiles for a round (the layer projections of a
+  // 64-request block: o and down give 80 tiles, q|k|v 96): split K until they fill it.  The
+  // 128-row tiles would need half as many splits but move twice the operand bytes per flop.
+  if (M >= kBigSplitMinM && N >= kBigSplitMinN && K % BK == 0) {
+    const int bt = ((M + kBigBM - 1) / kBigBM) * ((N + kBN - 1) / kBN);
+    const int nkb = K / BK;
+    int s = std::max(1, std::min(kMaxSplits, kTargetWorkgroups / bt));
+    while (s > 1 && nkb / s < 4) --s;
+    const int per = (nkb + s - 1) / s;
+    pl.bm = kBigBM;
+    pl.k_per_split = per * BK;
+    pl.splits = (nkb + per - 1) / per;
+    pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+    return pl;
+  }
   const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
   const int nk = K / BK;
   // Narrow projections whose partial planes stay small (the kernel projection: 0.66 MB a
@@ -1071,8 +1088,8 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
     return launch_stream(p, pl, W, stream);
   }
   if (pl.bm == kBigBM) {
-    if (pl.splits != 1) return hipErrorInvalidValue;
-    const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBigBM - 1) / kBigBM, 1);
+    if (pl.k_per_split % BK != 0) return hipErrorInvalidValue;
+    const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBigBM - 1) / kBigBM, pl.splits);
     if (W.q) {
       if (W.tiled)
         gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, true, true><<<grid, 512, 0, stream>>>(p);

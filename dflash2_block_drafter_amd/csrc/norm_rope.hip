@@ -23,13 +23,20 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restric
   const int rin = (r / out_per_grp) * in_per_grp + skip + r % out_per_grp;
   const uint16_t* xr = x + (size_t)rin * ldx;
   const int chunks = H >> 3;
-  u32x4_t v[kMaxChunks];
+  u32x4_t v[kMaxChunks], gv[kMaxChunks];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = lane + i * 64;
-    if (c < chunks) {
+    if (c < chunks) {  // the gains load with the row: one round trip for both
       v[i] = *reinterpret_cast<const u32x4_t*>(xr + c * 8);
+      gv[i] = *reinterpret_cast<const u32x4_t*>(gamma + c * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * 64;
+    if (c < chunks) {
       float f[8];
       unpack8(v[i], f);
 #pragma unroll
@@ -45,7 +52,7 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(const uint16_t* __restric
     if (c < chunks) {
       float f[8], g[8];
       unpack8(v[i], f);
-      unpack8(*reinterpret_cast<const u32x4_t*>(gamma + c * 8), g);
+      unpack8(gv[i], g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = f[e] * inv * g[e];
       *reinterpret_cast<u32x4_t*>(yr + c * 8) = pack8(f);

@@ -41,6 +41,9 @@ def h(t):
     # 256 x 256 workgroup tiles once they fill a round of 256 workgroups
     (512, 32768, 256, False),
     (300, 32868, 320, True),    # ragged M and N
+    # 256 x 256 tiles with split K when they do not fill a round (o / down at 64 requests)
+    (600, 4096, 1024, True),
+    (520, 5000, 2048, False),   # ragged M and N, bf16 out through the split-K reduce
 ])
 def test_linear(M, N, K, out_f32):
     x = bf((M, K), 11)
