@@ -984,6 +984,26 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
   if (M > kBM && (size_t)((M + kBigBM - 1) / kBigBM) * ((N + kBN - 1) / kBN) >= (size_t)kTargetWorkgroups) {
     pl.bm = kBigBM;
     pl.k_per_split = K;
+    // A last round of workgroups at most half full (gate/up at M = 1024: 544 tiles, 32 in the
+    // third round) would take a whole tile's time on a few CUs: the weight rows of that round
+    // run as a second launch whose tiles split K over the whole chip.  Weight-major shapes
+    // only (N > M), whose full rounds are whole N tiles once the M tiles are grouped.
+    const int mt = (M + kBigBM - 1) / kBigBM, nt = (N + kBN - 1) / kBN;
+    const int full = (mt * nt / kTargetWorkgroups) * kTargetWorkgroups;
+    const int rest = mt * nt - full;
+    if (N > M && rest > 0 && 2 * rest <= kTargetWorkgroups && full % mt == 0 && K % BK == 0) {
+      const int nt_tail = nt - full / mt;
+      const int nkb = K / BK;
+      int sp = std::max(1, std::min(kMaxSplits, kTargetWorkgroups / (mt * nt_tail)));
+      while (sp > 1 && nkb / sp < 4) --sp;
+      if (sp > 1) {
+        const int per = (nkb + sp - 1) / sp;
+        pl.tail_n = (full / mt) * kBN;
+        pl.tail_k_per_split = per * BK;
+        pl.tail_splits = (nkb + per - 1) / per;
+        pl.partial_bytes = (size_t)pl.tail_splits * M * (N - pl.tail_n) * sizeof(float);
+      }
+    }
     return pl;
   }
   // Enough rows for 256 x 256 tiles but too few tiles for a round (the layer projections of a
@@ -1138,6 +1158,30 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
   // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup)
   if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0)) return hipErrorInvalidValue;
   if (W.q && K % BK != 0) return hipErrorInvalidValue;
+  if (pl.tail_n > 0 && pl.splits == 1 && !tile_max && !W.q && !out1 && pl.tail_n < N) {
+    // the full rounds: weight rows [0, tail_n) into the matching output columns
+    GemmPlan pm = pl;
+    pm.tail_n = 0;
+    const GemmArgs pa = make_args(pm, A, lda, W, M, pl.tail_n, K, epi, out0, ld0, nullptr, 0, pl.tail_n, partial,
+                                  nullptr);
+    hipError_t e = launch_main(pa, pm, W, stream);
+    if (e != hipSuccess) return e;
+    // the rest with split K: weights from row tail_n (a whole tile-contiguous tile boundary),
+    // outputs from the matching column (half of it for SiLU(gate) * up)
+    WeightRef wt = W;
+    wt.w = W.tiled ? W.w + (size_t)(pl.tail_n / kBN) * (K / BK) * (kBN * BK) : W.w + (size_t)pl.tail_n * K;
+    const int nt = N - pl.tail_n;
+    void* o = epi == EPI_SILU_MUL ? static_cast<void*>(static_cast<uint16_t*>(out0) + pl.tail_n / 2)
+            : epi == EPI_BF16     ? static_cast<void*>(static_cast<uint16_t*>(out0) + pl.tail_n)
+                                  : static_cast<void*>(static_cast<float*>(out0) + pl.tail_n);
+    GemmPlan pt = pm;
+    pt.splits = pl.tail_splits;
+    pt.k_per_split = pl.tail_k_per_split;
+    const GemmArgs pb = make_args(pt, A, lda, wt, M, nt, K, epi, o, ld0, nullptr, 0, nt, partial, nullptr);
+    e = launch_main(pb, pt, wt, stream);
+    if (e != hipSuccess) return e;
+    return launch_reduce(pb, stream);
+  }
   const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max);
   hipError_t e = launch_main(p, pl, W, stream);
   if (e != hipSuccess || pl.splits == 1) return e;

@@ -25,6 +25,9 @@ struct GemmPlan {
   int k_per_split = 0;
   size_t partial_bytes = 0;  // split-K scratch (fp32 [splits, M, N])
   int stream_waves = 0;      // > 0: the weight-streaming kernel (M <= 128), waves per workgroup
+  // 256 x 256 tiles whose last round of workgroups would be less than half full: weight rows
+  // from tail_n on run as a second launch with tail_splits K splits (0: no tail launch)
+  int tail_n = 0, tail_splits = 1, tail_k_per_split = 0;
 };
 
 // tile_max: the caller will ask launch_gemm for tile maxima (one split, 256-column workgroups).

@@ -44,6 +44,9 @@ def h(t):
     # 256 x 256 tiles with split K when they do not fill a round (o / down at 64 requests)
     (600, 4096, 1024, True),
     (520, 5000, 2048, False),   # ragged M and N, bf16 out through the split-K reduce
+    # a last round of 256 x 256 tiles at most half full: its weight rows run split K
+    (512, 33024, 1024, True),
+    (300, 65792, 1024, False),
 ])
 def test_linear(M, N, K, out_f32):
     x = bf((M, K), 11)
