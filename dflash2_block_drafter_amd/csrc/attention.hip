@@ -138,8 +138,8 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < ROWS_PER; ++i) {
       const uint32_t off = static_cast<uint32_t>(min(r0 + kg * ROWS_PER + i, rlast)) * stride + dg * 16;
-      kr[i] = vm_load16(kp, off);
-      vr[i] = vm_load16(vp, off);
+      kr[i] = vm_load16_nt(kp, off);
+      vr[i] = vm_load16_nt(vp, off);
     }
   };
   // every load but the newest n tiles' is in

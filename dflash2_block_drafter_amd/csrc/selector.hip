@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restric
     for (int j = 0; j < TQ; ++j) {
       const int col = t * kGemmTileN + j * 64 + l16 * 4;
       if (vec && col + 4 <= V) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + col);
+        // read once: non-temporal, so the stream does not evict what later kernels reuse
+        const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + col));
         acc = fmaxf(acc, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
       } else {
 #pragma unroll
@@ -149,6 +150,86 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
   }
   __syncthreads();
   const float theta = theta_s;
+
+  // Fast path (one round of tile maxima): every value >= theta is a candidate, usually K to
+  // 2K of them, so they are gathered into LDS (ballot + one LDS atomic per wavefront step)
+  // and sorted once by wavefront 0.  More than 64 of them (ties at theta across many tiles,
+  // constant rows, rows mostly -inf) falls through to the merging scan below.
+  __shared__ float cand_v[64];
+  __shared__ int cand_i[64];
+  __shared__ int ccount;
+  if (ntiles <= CH) {
+    if (wave == 0) {
+      float t[kTmPerLane];
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) {
+        const int i = j * 64 + lane;
+        t[j] = i < ntiles ? tm[i] : -INFINITY;
+      }
+      int cnt = 0;
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) {
+        const int i = j * 64 + lane;
+        const bool q = i < ntiles && t[j] >= theta;
+        const uint64_t mask = __ballot(q);
+        if (q) tl[cnt + __popcll(mask & below)] = i;
+        cnt += __popcll(mask);
+      }
+      if (lane == 0) {
+        tcount = cnt;
+        ccount = 0;
+      }
+    }
+    __syncthreads();
+    const int cnt = tcount;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int b0 = wave * kTilesInFlight; b0 < cnt; b0 += 4 * kTilesInFlight) {
+      const int n = min(kTilesInFlight, cnt - b0);
+      int tile[kTilesInFlight];
+      float x[kTilesInFlight][TPL];
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q) tile[q] = tl[b0 + min(q, n - 1)];
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q)
+#pragma unroll
+        for (int e = 0; e < TPL; ++e) {
+          const int col = tile[q] * TW + e * 64 + lane;
+          x[q][e] = col < V ? src[col] : -INFINITY;
+        }
+#pragma unroll
+      for (int q = 0; q < kTilesInFlight; ++q)
+#pragma unroll
+        for (int e = 0; e < TPL; ++e) {
+          const int col = tile[q] * TW + e * 64 + lane;
+          const bool take = q < n && col < V && x[q][e] >= theta;
+          const uint64_t mask = __ballot(take);
+          if (mask) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&ccount, __popcll(mask));
+            base = __shfl(base, 0, 64);
+            const int slot = base + __popcll(mask & below);
+            if (take && slot < 64) {
+              cand_v[slot] = x[q][e];
+              cand_i[slot] = col;
+            }
+          }
+        }
+    }
+    __syncthreads();
+    const int total = ccount;
+    if (total <= 64) {
+      if (wave != 0) return;
+      float v = lane < total ? cand_v[lane] : -INFINITY;
+      int id = lane < total ? cand_i[lane] : kNoId;
+      wave_bitonic_sort(v, id, lane);
+      if (lane < K) {
+        ids[(size_t)row * K + lane] = id_map && id >= 0 && id < V ? id_map[id] : id;
+        vals[(size_t)row * K + lane] = v;
+      }
+      return;
+    }
+  }
 
   // scan the qualifying tiles: per round wavefront 0 lists them in LDS, then wavefront w
   // takes list entries [w*F, w*F + F), [w*F + 4F, ...), F = kTilesInFlight at a time

@@ -36,6 +36,13 @@ __device__ __forceinline__ u32x4_t vm_load16(const void* sbase, uint32_t voff) {
   return v;
 }
 
+// The same, non-temporal: for streams read once (the context K/V of a draft block).
+__device__ __forceinline__ u32x4_t vm_load16_nt(const void* sbase, uint32_t voff) {
+  u32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, %2 nt" : "=v"(v) : "v"(voff), "s"(sbase));
+  return v;
+}
+
 // s_waitcnt vmcnt(N) that also passes v through, so no use of v is scheduled before it (the
 // comment names v's registers in the assembly).  Vector loads complete in issue order for
 // this count, so vmcnt(N) means every load but the N most recent is in.
