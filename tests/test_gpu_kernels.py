@@ -235,6 +235,8 @@ def test_conv_block_boundary_on_gpu():
     (4, 248320, 16, "hot_tile"),   # every candidate inside one 256-column tile
     (3, 10000, 16, "hot_last"),    # maxima in the ragged last tile
     (3, 5000, 16, "neg_inf"),      # most of each row -inf: fewer finite tiles than K
+    (2, 20000, 16, "theta_64"),    # exactly 64 values at or above theta: the gathered sort
+    (2, 20000, 16, "theta_65"),    # 65 of them: the merging scan
 ])
 def test_compute_candidates_bitexact(N, V, K, kind):
     g = torch.Generator(device=DEV).manual_seed(71)
@@ -254,6 +256,18 @@ def test_compute_candidates_bitexact(N, V, K, kind):
         logits = torch.full((N, V), float("-inf"), device=DEV)
         logits[:, 300:310] = torch.randn((N, 10), generator=g, device=DEV)
         logits[:, 4000:4003] = 1.5
+    elif kind.startswith("theta_"):
+        # 16 tiles whose maximum is 10 (theta = 10, ties at theta inside them, ordered by
+        # column), every other value below 1
+        total = int(kind.split("_")[1])
+        logits = torch.rand((N, V), generator=g, device=DEV)
+        tiles = [3 + 4 * i for i in range(16)]
+        for r in range(N):
+            extra = total - 16
+            for i, t in enumerate(tiles):
+                n_here = 1 + extra // 16 + (1 if i < extra % 16 else 0)
+                cols = t * 256 + (torch.arange(n_here, device=DEV) * 7 + 5 * r) % 256
+                logits[r, cols] = 10.0
     else:
         logits = torch.full((N, V), 0.25, device=DEV)
     ids = torch.empty((N, K), dtype=torch.int32, device=DEV)
