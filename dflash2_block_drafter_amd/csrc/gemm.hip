@@ -79,7 +79,9 @@ __device__ __forceinline__ void frag_chunk_pos(int c, int& row, int& k) {
 // a single contiguous BN*BKS*2-byte block; otherwise W is row-major [N, K].
 template <int BM, int BN, int BKS, int NT, bool TILED>
 struct TileLoader {
-  static_assert(!TILED || (BN == 256 && BKS == 64), "tiled weights come in 256 x 64 blocks");
+  // tiled weights come in 256 x 64 blocks; a BN-row slice (BN dividing 256) of a block is
+  // BN / 16 consecutive row groups, i.e. one contiguous run in fragment order
+  static_assert(!TILED || (256 % BN == 0 && BKS == 64), "tiled weights come in 256 x 64 blocks");
   static constexpr int CPR = BKS / 8;  // 16-byte chunks per tile row
   static constexpr int A_PER = BM * CPR / NT;
   static constexpr int B_PER = BN * CPR / NT;
@@ -99,7 +101,8 @@ struct TileLoader {
       a[i] = *reinterpret_cast<const u32x4_t*>(p.A + (size_t)gm * p.lda + k0 + (c % CPR) * 8);
     }
     if (TILED) {
-      const uint16_t* tile = p.W + ((size_t)(n0 / BN) * (p.K / BKS) + k0 / BKS) * (BN * BKS);
+      const uint16_t* tile =
+          p.W + ((size_t)(n0 / 256) * (p.K / BKS) + k0 / BKS) * (256 * BKS) + (size_t)(n0 % 256) * BKS;
 #pragma unroll
       for (int i = 0; i < B_PER; ++i)
         b[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(tile + (tid + i * NT) * 8));
@@ -861,7 +864,8 @@ constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // flop per LDS byte instead of 32 and LDS bandwidth stops bounding the matrix units as early.
 // One weight stage in flight keeps the 128 accumulators within 256 registers.
 constexpr int kBigBM = 256;
-constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;  // big tiles with split K from these sizes
+constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;
+constexpr int kNarrowBN = 64, kNarrowMaxN = 2048;  // 64-column workgroups for narrow projections  // big tiles with split K from these sizes
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
 // Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
 // workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
@@ -1021,8 +1025,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
     pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
     return pl;
   }
-  const int tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  // Narrow projections at M <= 128 (the kernel projection, N = 1280; the selector's, N = 64):
+  // 64-column workgroups of two wavefronts, two per CU, so that 20 column tiles x 16 K splits
+  // spread over the chip instead of 5 x 16 (each workgroup's short K loop is the time)
+  const bool narrow = M <= kBM && !tile_max && N <= kNarrowMaxN;
+  if (narrow) pl.bn = kNarrowBN;
+  const int tiles = ((M + kBM - 1) / kBM) * ((N + pl.bn - 1) / pl.bn);
   const int nk = K / BK;
+  const int target = narrow ? 2 * kTargetWorkgroups : kTargetWorkgroups;
   // Narrow projections whose partial planes stay small (the kernel projection: 0.66 MB a
   // plane) split deeper: with few tiles each workgroup's serial K loop is the time, and the
   // consumers read the extra planes in batches.
@@ -1031,7 +1041,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
   const int max_splits = small ? kMaxSplitsSmall : kMaxSplits;
   const int min_steps = small ? 4 : 6;
   int s = 1;
-  while (s < max_splits && tiles * (s + 1) <= kTargetWorkgroups && nk / (s + 1) >= min_steps) ++s;
+  while (s < max_splits && tiles * (s + 1) <= target && nk / (s + 1) >= min_steps) ++s;
   int per = (nk + s - 1) / s;
   pl.k_per_split = per * BK;
   pl.splits = (nk + per - 1) / per;
@@ -1123,6 +1133,15 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
     }
     return hipGetLastError();
   }
+  if (pl.bn == kNarrowBN && !W.q) {
+    const dim3 grid((p.N + kNarrowBN - 1) / kNarrowBN, (p.M + kBM - 1) / kBM, pl.splits);
+    if (W.tiled)
+      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 2, true><<<grid, 128, 0, stream>>>(p);
+    else
+      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 2, false><<<grid, 128, 0, stream>>>(p);
+    return hipGetLastError();
+  }
+  // (4-bit weights keep 256-column workgroups under a narrow plan: the same K splits)
   const dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM, pl.splits);
   if (W.q) {
     if (W.tiled)
