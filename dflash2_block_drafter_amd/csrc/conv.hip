@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Pl
 // per row next to its inputs, so there is no LDS staging and no barrier, and the only wait
 // is the one round trip for all of a thread's loads.  R rows of a block per thread, as in
 // conv_kernel; kConvCh / 8 threads cover kConvCh channels.
-template <int R>
+template <int R, bool NTS>
 __global__ __launch_bounds__(kConvCh / 8) void conv_plane_kernel(const uint16_t* __restrict__ y,
                                                                  const float* __restrict__ coef, int ld,
                                                                  const uint16_t* __restrict__ base, int side,
@@ -190,7 +190,11 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_plane_kernel(const uint16_t*
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = rr[e] + o[e];
     }
-    *reinterpret_cast<u32x4_t*>(out + (size_t)(t0 + r) * H + c0) = pack8(o);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + (size_t)(t0 + r) * H + c0);
+    if (NTS)
+      __builtin_nontemporal_store(pack8(o), dst);
+    else
+      *dst = pack8(o);
   }
 }
 
@@ -298,15 +302,27 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
   }
   const dim3 grid(chunks, T / R);
   if (coef.S == 1 && !coef_next) {
-    switch (R) {
-      case 4:
-        conv_plane_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+    // an output larger than an XCD's 4 MB L2 would not stay there for its reader anyway:
+    // stream it out with non-temporal stores
+    const bool nts = (size_t)T * H * sizeof(uint16_t) > (size_t(8) << 20);
+    switch (R * 2 + (nts ? 1 : 0)) {
+      case 9:
+        conv_plane_kernel<4, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
-      case 2:
-        conv_plane_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+      case 8:
+        conv_plane_kernel<4, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        break;
+      case 5:
+        conv_plane_kernel<2, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        break;
+      case 4:
+        conv_plane_kernel<2, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        break;
+      case 3:
+        conv_plane_kernel<1, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       default:
-        conv_plane_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<1, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
     }
     return hipGetLastError();
   }
