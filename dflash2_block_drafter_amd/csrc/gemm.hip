@@ -865,7 +865,7 @@ constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // One weight stage in flight keeps the 128 accumulators within 256 registers.
 constexpr int kBigBM = 256;
 constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;
-constexpr int kNarrowBN = 64, kNarrowMaxN = 2048;  // 64-column workgroups for narrow projections  // big tiles with split K from these sizes
+constexpr int kNarrowBN = 64, kNarrowMaxN = 2048, kNarrowAnyM = 256;  // 64-column workgroups for narrow projections  // big tiles with split K from these sizes
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
 // Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
 // workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
@@ -1028,7 +1028,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
   // Narrow projections at M <= 128 (the kernel projection, N = 1280; the selector's, N = 64):
   // 64-column workgroups of two wavefronts, two per CU, so that 20 column tiles x 16 K splits
   // spread over the chip instead of 5 x 16 (each workgroup's short K loop is the time)
-  const bool narrow = M <= kBM && !tile_max && N <= kNarrowMaxN;
+  // (at any M when N <= 256: one 256-column tile would load mostly clamped duplicate rows)
+  const bool narrow = !tile_max && ((M <= kBM && N <= kNarrowMaxN) || N <= kNarrowAnyM);
   if (narrow) pl.bn = kNarrowBN;
   const int tiles = ((M + kBM - 1) / kBM) * ((N + pl.bn - 1) / pl.bn);
   const int nk = K / BK;

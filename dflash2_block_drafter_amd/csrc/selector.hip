@@ -417,34 +417,19 @@ __global__ __launch_bounds__(256) void score_edges_kernel(const int32_t* __restr
   }
 }
 
-// One greedy step on the current predecessor row (K scores in LDS): the argmax with the
-// lowest candidate on ties.  Every lane agrees for finite scores; lane 0's winner is taken
-// so that a NaN can never send a lane past the K candidates.
-__device__ __forceinline__ int walk_step(const float* row, int K, int lane) {
-  float v = lane < K ? row[lane] : -INFINITY;
-  int c = lane < K ? lane : kNoId;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oc = __shfl_xor(c, o, 64);
-    if (before(ov, oc, v, c)) {
-      v = ov;
-      c = oc;
-    }
-  }
-  const int j = __shfl(c, 0, 64);
-  return (j >= 0 && j < K) ? j : 0;
-}
-
 // Greedy walk over given scores: one wavefront per request.  Chunks of slots are copied into
-// LDS with coalesced loads (every load of a chunk in flight at once), then walked there.
+// LDS with coalesced loads (every load of a chunk in flight at once); the argmax of each
+// (slot, predecessor) row is found for all rows at once, and the walk then follows them
+// (the argmax takes the lowest candidate on ties; every lane's scan agrees for finite
+// scores, and the index stays in [0, K) whatever the values).
 constexpr int kWalkLdsFloats = 4096;
 
 __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict__ scores,
                                                          const int32_t* __restrict__ cand, int S, int K,
                                                          int32_t* __restrict__ tokens) {
   __shared__ __attribute__((aligned(16))) float sc[kWalkLdsFloats];
-  __shared__ int ids[kWalkLdsFloats];  // the chunk's candidate ids (n * K <= kWalkLdsFloats / K)
+  __shared__ int ids[kWalkLdsFloats];   // the chunk's candidate ids (n * K <= kWalkLdsFloats / K)
+  __shared__ int best[kWalkLdsFloats];  // argmax of each (slot, predecessor) row of the chunk
   const int lane = threadIdx.x;
   const int b = blockIdx.x;
   const int KK = K * K;
@@ -498,10 +483,25 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
       }
     }
     __syncthreads();
-    for (int w = 0; w < n; ++w) {
-      const size_t bl = (size_t)b * S + l0 + w;
-      j = walk_step(sc + (size_t)w * KK + (size_t)j * K, K, lane);
-      if (lane == 0) tokens[bl] = ids[w * K + j];
+    // the argmax of every (slot, predecessor) row of the chunk does not depend on the path:
+    // all of them in parallel (lowest candidate on ties), then the walk is a chain of lookups
+    for (int r = lane; r < n * K; r += 64) {
+      const float* row = sc + (size_t)r * K;
+      float bv = row[0];
+      int bc = 0;
+      for (int c = 1; c < K; ++c)
+        if (before(row[c], c, bv, bc)) {
+          bv = row[c];
+          bc = c;
+        }
+      best[r] = bc;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      for (int w = 0; w < n; ++w) {
+        j = best[w * K + j];
+        tokens[(size_t)b * S + l0 + w] = ids[w * K + j];
+      }
     }
     __syncthreads();
   }
