@@ -18,6 +18,15 @@
 //   * the drafter's own weights are stored tile-contiguous, [N/256][K/64][256][64], so a K
 //     step of a tile is one contiguous 32 KB block; the target's head stays row-major.
 //
+//   * narrow projections (N <= 2048 at M <= 128, or N <= 256 at any M) take 64-column
+//     workgroups of two wavefronts reading 64-row slices of those blocks.
+//
+// With more rows (a 64-request block, the context projection) the projections approach
+// the matrix cores' bound and take 256 x 256 tiles whose operands are copied global -> LDS
+// directly (gemm_dma_kernel); weight-major grids run the M tiles of an N tile together on
+// one XCD, split K when the tiles alone do not fill a round of workgroups, and run a last,
+// mostly empty round's weight rows as a separate split-K launch.
+//
 // Split-K: grid.z slices K; slices write fp32 partials and a separate kernel sums them
 // in slice order (deterministic, no float atomics) and applies the epilogue, or the
 // partials are left for the consuming kernel, which sums them in the same order.

@@ -5,10 +5,11 @@
 // which the head projection writes with its logits (a separate pass computes them for
 // logits from elsewhere).  theta, the K-th largest tile maximum, is reached by K distinct
 // logits, so every top-K logit is >= theta and sits in a tile whose maximum is >= theta;
-// only those tiles are read (usually K of a row's V/256).  Their values are merged into a
-// running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes K..63
-// take new candidates).  Ties are ordered by id, so the result is exact and unique for any
-// input, including constant rows (where every tile qualifies).
+// only those tiles are read (usually K of a row's V/256).  Their values >= theta (usually K
+// to 2K) are gathered and sorted once when there are at most 64; otherwise they are merged
+// into a running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes
+// K..63 take new candidates).  Ties are ordered by id, so the result is exact and unique for
+// any input, including constant rows (where every tile qualifies).
 #include <algorithm>
 
 #include "common.hpp"
@@ -72,8 +73,10 @@ __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restric
 // tiles (ties included) are scanned.  One workgroup of four wavefronts per row.  Tile
 // maxima are read 64 * kTmPerLane at a time into registers (one round of loads); the four
 // wavefronts each merge a quarter of them and wavefront 0 merges the four lists into theta;
-// then the qualifying tiles are listed in LDS, each wavefront loads kTilesInFlight of them
-// at once into its own list, and wavefront 0 merges the four candidate lists.
+// then the qualifying tiles are listed in LDS and each wavefront loads kTilesInFlight of
+// them at once.  With one round of tile maxima, their values >= theta are gathered into LDS
+// and, when at most 64, sorted once by wavefront 0; otherwise (and for longer rows) each
+// wavefront merges its tiles into its own list and wavefront 0 merges the four lists.
 constexpr int kTmPerLane = 16;
 constexpr int kTilesInFlight = 4;
 
@@ -419,9 +422,9 @@ __global__ __launch_bounds__(256) void score_edges_kernel(const int32_t* __restr
 
 // Greedy walk over given scores: one wavefront per request.  Chunks of slots are copied into
 // LDS with coalesced loads (every load of a chunk in flight at once); the argmax of each
-// (slot, predecessor) row is found for all rows at once, and the walk then follows them
-// (the argmax takes the lowest candidate on ties; every lane's scan agrees for finite
-// scores, and the index stays in [0, K) whatever the values).
+// (slot, predecessor) row is found for all rows at once, one row per lane, and the walk then
+// follows them (the argmax takes the lowest candidate on ties and stays in [0, K) whatever
+// the values).
 constexpr int kWalkLdsFloats = 4096;
 
 __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict__ scores,
