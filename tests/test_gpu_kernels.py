@@ -130,6 +130,8 @@ def test_block_attention(D, NH, NKV, G, ctx):
     (30, 520, 2048, True),      # two 16-row fragments, split K
     (50, 256, 640, False),      # four 16-row fragments
     (300, 32768, 256, True),    # 256 x 256 workgroup tiles, ragged M
+    (600, 4096, 1024, False),   # 256 x 256 tiles with split K (too few tiles for a round)
+    (512, 33024, 1024, True),   # a last round at most half full: 4-bit weights keep one launch
 ])
 def test_linear_q4(M, N, K, out_f32):
     x = bf((M, K), 61)
