@@ -128,6 +128,13 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
   constexpr int EPL = D / 64;
   const int r = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  // the row's D/2 rotary (cos, sin) pairs, computed once for the workgroup's four heads
+  __shared__ float rc[D / 2], rs[D / 2];
+  if (r < rows && threadIdx.x < D / 2) {
+    const int pos = pos0[r / rows_per_req] + r % rows_per_req + pos_offset;
+    rope_cs(pos, threadIdx.x, D, log_theta, &rc[threadIdx.x], &rs[threadIdx.x]);
+  }
+  __syncthreads();
   if (r >= rows || h >= heads) return;
   const int lane = threadIdx.x & 63;
   const int half_lane = lane & 31;
@@ -148,14 +155,12 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / static_cast<float>(D) + eps);
   const uint16_t* g = h < split ? gamma : gamma2;
-  const int pos = pos0[r / rows_per_req] + r % rows_per_req + pos_offset;
   const bool first = lane < 32;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const float x = v[e] * inv * bf16_to_f32(g[e0 + e]);
     const float partner = __shfl_xor(x, 32, 64);
-    float c, s;
-    rope_cs(pos, half_lane * EPL + e, D, log_theta, &c, &s);
+    const float c = rc[half_lane * EPL + e], s = rs[half_lane * EPL + e];
     // rotate_half: first half x1 c - x2 s, second half x2 c + x1 s
     out[e] = f32_to_bf16(first ? x * c - partner * s : x * c + partner * s);
   }
