@@ -866,7 +866,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 
 constexpr int kBM = 128, kBN = kGemmTileN, kMaxSplits = 8;
 constexpr int kTargetWorkgroups = 256;  // one 128 x 256 workgroup per CU (110 KB of LDS)
-constexpr int kMaxSplitsSmall = 16;     // K splits when all partial planes fit kSmallPartialBytes
+constexpr int kMaxSplitsSmall = 12;     // K splits when all partial planes fit kSmallPartialBytes
 constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // Wide-M projections with at least a round of 256 x 256 tiles take those (one workgroup per
 // CU, 148 KB of LDS): each wavefront then computes a 128 x 64 block, so a K step reads 43
@@ -1035,7 +1035,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
     return pl;
   }
   // Narrow projections at M <= 128 (the kernel projection, N = 1280; the selector's, N = 64):
-  // 64-column workgroups of two wavefronts, two per CU, so that 20 column tiles x 16 K splits
+  // 64-column workgroups of two wavefronts, two per CU, so that 20 column tiles x 12 K splits
   // spread over the chip instead of 5 x 16 (each workgroup's short K loop is the time)
   // (at any M when N <= 256: one 256-column tile would load mostly clamped duplicate rows)
   const bool narrow = !tile_max && ((M <= kBM && N <= kNarrowMaxN) || N <= kNarrowAnyM);
