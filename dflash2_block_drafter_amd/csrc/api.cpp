@@ -254,7 +254,8 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) =
 // n = RMSNorm(x_out; next_gamma), the next layer's normed input.
 int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, int G, const uint16_t* Kl,
               const uint16_t* Vl, int Lcap, int Lmax, const int32_t* ctx_len, const int32_t* pos0, char* W,
-              const DraftLayout& lay, bool n_ready, const uint16_t* next_gamma, hipStream_t stream) {
+              const DraftLayout& lay, bool n_ready, const uint16_t* next_gamma, hipStream_t stream,
+              uint16_t* head_rows = nullptr) {
   const dfl_config& c = d->cfg;
   const LayerBuf& L = d->layers[li];
   const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
@@ -331,9 +332,11 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
                             stream);
   }));
   if (next_gamma) {
+    // the next layer's input norm, or (head_rows set) the final norm of rows 1..G-1, packed
+    // for the head
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
       return dfl::launch_conv_residual_norm(u, coef1, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
-                                            c.rms_eps, n, stream);
+                                            c.rms_eps, head_rows ? head_rows : n, stream, head_rows != nullptr);
     }));
   } else {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
@@ -787,14 +790,13 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   for (int li = 0; li < c.layers; ++li) {
     const uint16_t* Kl = Lmax > 0 ? K[li] : nullptr;
     const uint16_t* Vl = Lmax > 0 ? V[li] : nullptr;
-    const uint16_t* next_gamma = li + 1 < c.layers ? d->layers[li + 1].in_norm : nullptr;
-    DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, li > 0, next_gamma, stream));
+    const bool last = li + 1 == c.layers;
+    // the last layer's finish applies the final norm to rows 1..G-1, packed into h for the head
+    const uint16_t* next_gamma = last ? d->norm : d->layers[li + 1].in_norm;
+    DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, li > 0, next_gamma, stream,
+                      last ? h : nullptr));
     xin = x;
   }
-  // rows 1..G-1 of every block -> final norm -> head, selector
-  DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * N * H, stream, [&] {
-    return dfl::launch_rms_norm(xin, H, N, H, d->norm, c.rms_eps, h, H, S, G, 1, stream);
-  }));
   // An unsplit head also writes every 256-column tile's row maxima, which lets the top-K
   // read only the few tiles that can hold a candidate; a split head leaves them to a pass
   // over the logits.

@@ -206,7 +206,7 @@ template <int MAXC>
 __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
     const uint16_t* y, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
     const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
-    uint16_t* __restrict__ n_out) {
+    uint16_t* __restrict__ n_out, int skip_anchor) {
   __shared__ float red[4];
   __shared__ float cs[2 * MAXC * 256];  // the row's groups: H / grp <= H / 8 <= MAXC * 256
   const int t = blockIdx.x;
@@ -248,6 +248,9 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = rsqrtf(tot / static_cast<float>(H) + eps);
+  // with skip_anchor the normed rows are packed without each block's row 0
+  if (skip_anchor && t % G == 0) return;
+  const size_t nrow = skip_anchor ? (size_t)(t / G) * (G - 1) + t % G - 1 : (size_t)t;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int ch = tid + i * 256;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
       unpack8(gv[i], gm);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = xv[i][e] * inv * gm[e];
-      *reinterpret_cast<u32x4_t*>(n_out + (size_t)t * H + ch * 8) = pack8(o);
+      *reinterpret_cast<u32x4_t*>(n_out + nrow * H + ch * 8) = pack8(o);
     }
   }
 }
@@ -265,21 +268,23 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
 
 hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
-                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream) {
+                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
+                                     bool skip_anchor) {
   if (T <= 0) return hipSuccess;
   const int per = (H / 8 + 255) / 256;  // chunks of 8 channels per thread
+  const int sk = skip_anchor ? 1 : 0;
   switch (per) {
     case 1:
-      conv_residual_norm_kernel<1><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      conv_residual_norm_kernel<1><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
       break;
     case 2:
-      conv_residual_norm_kernel<2><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      conv_residual_norm_kernel<2><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
       break;
     case 3:
-      conv_residual_norm_kernel<3><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      conv_residual_norm_kernel<3><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
       break;
     case 4:
-      conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out);
+      conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
       break;
     default:
       return hipErrorInvalidValue;  // H > 8192

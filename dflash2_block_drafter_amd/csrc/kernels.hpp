@@ -130,9 +130,12 @@ hipError_t launch_context_kv_store_ragged(const uint16_t* kv, int rows, int B, i
 // Side-1 conv + residual, then RMSNorm of the new residual row: x_out = residual +
 // conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias
 // residual; H <= 8192.
+// skip_anchor: n_out holds only rows t % G != 0, packed (row (t / G) * (G - 1) + t % G - 1),
+// as the head reads them after the last layer.
 hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
-                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream);
+                                     const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
+                                     bool skip_anchor = false);
 
 // Grouped dynamic conv; side selects base[side]; residual may be null.  coef_next (side 0
 // only; coef then holds both sides, side 1 at column 2 * ng): also write side 1's summed
