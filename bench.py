@@ -43,9 +43,11 @@ def parse():
     return p.parse_args()
 
 
-def pmc_traffic(kernel_class: str, workload: str):
+def pmc_traffic(kernel_class: str, workload: str, weights: str = "bf16"):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken
-    on the current kernel sources (null otherwise)."""
+    on the current kernel sources with the same (bf16) weights (null otherwise)."""
+    if weights != "bf16":
+        return None
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel_class}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -164,13 +166,13 @@ def main():
         achieved = flops / (launch_ms * 1e-3) / 1e12
         roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
+                    "traffic": pmc_traffic(dominant, w.name, args.weights), "avg_launch_us": round(launch_ms * 1e3, 2),
                     "algorithmic_flops_per_launch": int(flops), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
     else:
         achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": pmc_traffic(dominant, w.name), "avg_launch_us": round(launch_ms * 1e3, 2),
+                    "traffic": pmc_traffic(dominant, w.name, args.weights), "avg_launch_us": round(launch_ms * 1e3, 2),
                     "algorithmic_bytes_per_launch": int(bytes_per_launch)}
 
     def frac(cls):
