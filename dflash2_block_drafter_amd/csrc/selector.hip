@@ -442,6 +442,16 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
     const int n = min(chunk, S - l0);
     const float* src = scores + ((size_t)b * S + l0) * KK;
     const int m = n * KK;
+    // the chunk's candidate ids (so that no step of the walk waits on a global load): the
+    // first 1024 are loaded before the scores are stored, in the same round trip
+    const int32_t* csrc = cand + ((size_t)b * S + l0) * K;
+    const int nk = n * K;
+    int idv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = lane + 64 * i;
+      if (q < nk) idv[i] = csrc[q];
+    }
     if (((reinterpret_cast<uintptr_t>(src) & 15) | (m & 3)) == 0) {
       // the chunk as float4: at most kWalkLdsFloats / 4 / 64 = 16 loads a lane, all in flight
       f32x4_t v[kWalkLdsFloats / 256];
@@ -470,19 +480,22 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
         }
       }
     }
-    // the chunk's candidate ids, so that no step of the walk waits on a global load
-    const int32_t* csrc = cand + ((size_t)b * S + l0) * K;
-    for (int i0 = 0; i0 < n * K; i0 += 64 * 16) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = lane + 64 * i;
+      if (q < nk) ids[q] = idv[i];
+    }
+    for (int i0 = 64 * 16; i0 < nk; i0 += 64 * 16) {
       int v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int q = i0 + lane + 64 * i;
-        if (q < n * K) v[i] = csrc[q];
+        if (q < nk) v[i] = csrc[q];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int q = i0 + lane + 64 * i;
-        if (q < n * K) ids[q] = v[i];
+        if (q < nk) ids[q] = v[i];
       }
     }
     __syncthreads();
