@@ -255,3 +255,39 @@ def test_ragged_context_append():
             assert_composed_close(K[i][b:b + 1, s:s + n], ks[i], f"request {b} K layer {i}")
             assert_composed_close(V[i][b:b + 1, s:s + n], vs[i], f"request {b} V layer {i}")
     dr.close()
+
+
+def test_tiny_ragged_context_lengths_end_to_end():
+    # requests with their own context lengths (a full one, an empty one, one ending inside
+    # the first 64-key tile, one just past it) over one 200-row K/V; rows past a request's
+    # length are materialised but must not be attended; each block starts at its request's
+    # own position
+    from dataclasses import replace
+    w = replace(configs.with_batch(configs.TINY, 4), ctx_len=200)
+    d = w.dims
+    lens = torch.tensor([200, 0, 37, 70], dtype=torch.int32)
+    weights_cpu = synth.drafter_weights(w)
+    tgt_cpu = synth.target_inputs(w)
+    tgt_cpu["ctx_len"] = lens.clone()
+    tgt_cpu["pos0"] = lens.clone()
+    weights = {k: v.to(DEV) for k, v in weights_cpu.items()}
+    tgt = {k: v.to(DEV) for k, v in tgt_cpu.items()}
+    dr = Drafter(d, weights, tap_layer_ids=list(range(d.n_taps)))
+    K, V = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(tgt["taps"], K, V)
+    tokens, logits = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"],
+                              tgt["lm_head"], want_logits=True)
+    torch.cuda.synchronize()
+    wh, th = _host(weights_cpu), _host(tgt_cpu)
+    ks, vs = O.materialize_context(th["taps"], wh, d, bf16_points=True)
+    ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
+                        bf16_points=True, return_all=True)
+    assert_composed_close(logits, ref["logits"], "head logits, ragged contexts")
+    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    # the bound tells these lengths apart: attending every materialised row would fail it
+    wrong = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, np.full(4, 200, np.int32),
+                          th["pos0"], d, bf16_points=True, return_all=True)["logits"]
+    for b in (1, 2, 3):
+        with pytest.raises(AssertionError):
+            assert_composed_close(wrong[b], ref["logits"][b])
+    dr.close()
