@@ -103,8 +103,8 @@ typedef struct {
   const dfl_bf16* biases;
 } dfl_q4_weight;
 
-/* The projections [P2] quantizes (the drafter's load: "projections only"; convs, norms and
- * codebooks stay bf16). */
+/* The projections [P2] quantizes (the drafter's constructor quantizes the linear projections
+ * alone; the convs, the norms and the codebooks keep bf16). */
 typedef struct {
   dfl_q4_weight q_proj, k_proj, v_proj, o_proj, gate_proj, up_proj, down_proj;
 } dfl_q4_layer;

@@ -8,8 +8,8 @@ Every step is computed in float64 from the bf16 inputs (bf16 bit patterns are
 widened exactly).  Where the pages fix a precision for a decision, the decision
 is taken in that precision: candidate selection runs on float32 logits and the
 walk on float32 scores (dflash2.ts diff on the @mlx-bun/inference page,
-`#select`: "fp32 scores"; MAX dflash2_qwen3_5 page, `compute_candidates`:
-float32 logits).
+`#select`, casts the scores to fp32; MAX dflash2_qwen3_5 page, `compute_candidates`,
+takes float32 logits).
 
 Sources, cited by page title and section:
   [P1] codehub.bot function listing of the mirror-sd project: the neox RoPE and
@@ -135,9 +135,10 @@ def silu(x: np.ndarray) -> np.ndarray:
 
 
 def kernel_projection(n: np.ndarray, w_kp: np.ndarray) -> np.ndarray:
-    """D = n . W_kp^T viewed as [T, side, tap, group] ([P2] header: "D =
-    kernel_projection(n) -> [stage, tap, group]"; [P3] `DFlash2GroupedConv`:
-    output width 2 * taps * num_groups, both sides at once)."""
+    """D = n . W_kp^T viewed as [T, side, tap, group] ([P2] header comment: one
+    projection of the normed rows gives a delta per conv side, tap and channel group;
+    [P3] `DFlash2GroupedConv`: its width is two sides times taps times groups, so both
+    sides come from the one projection)."""
     T = n.shape[0]
     d = linear(n, w_kp)
     return d.reshape(T, 2, 2, -1)
@@ -191,8 +192,8 @@ def conv_finish(y: np.ndarray, deltas1: np.ndarray, base: np.ndarray, block: int
 def attention(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray, k_blk: np.ndarray,
               v_blk: np.ndarray, ctx_len: np.ndarray, pos0=None, window: int = 0) -> np.ndarray:
     """Bidirectional block attention over the request's context prefix plus the
-    block's own rows ([P2] header: "bidirectional within the block"; `#block` passes
-    the block's k/v to `context.attend` with scale 1/sqrt(D)).
+    block's own rows ([P2] header comment: no causal mask inside the block; `#block`
+    hands the block's k/v to the context's attend call with scale 1/sqrt(D)).
 
     window > 0 is a sliding-attention layer ([P3] `DFlash2Qwen3_5` `layer_types`;
     [P3] `construct_kv_params`: the drafter's mask reaches back at most the window):
@@ -254,9 +255,9 @@ def mlp(i: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
 
 def project_context(taps: np.ndarray, w_fc: np.ndarray, hidden_norm: np.ndarray, eps: float,
                     bf16_points=False):
-    """c = RMSNorm(fc(concat of the target taps)) ([P2] header "context c =
-    hidden_norm(fc(concat(target layers)))" and `projectContext`, whose bf16 fc
-    output and norm output are what `bf16_points` rounds).
+    """c = RMSNorm(fc(concat of the target taps)) with the hidden_norm gain ([P2] header
+    comment and `projectContext`: the taps are concatenated, projected by fc and
+    normalised; the bf16 fc output and norm output there are what `bf16_points` rounds).
 
     taps: [B, L, n_taps*H] with the taps concatenated on the feature axis.
     """
