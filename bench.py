@@ -210,7 +210,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # 4-bit weights are dequantized to bf16 for the matrix units: u4 storage, bf16 arithmetic
+        "dtype": "bf16" if args.weights == "bf16" else "u4-weights/bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/embeddings)",
         "config": {"workload": f"{w.name}: {d.layers}-layer drafter H={d.hidden} NH/NKV/D="
                                f"{d.heads}/{d.kv_heads}/{d.head_dim} F={d.intermediate} V={d.vocab}, "

@@ -62,6 +62,21 @@ class dfl_weights(C.Structure):
                [("layers", C.POINTER(dfl_layer_weights)), ("q4_layers", C.POINTER(dfl_q4_layer))]
 
 
+TRACE_FIELDS = ("x_in", "n", "coef", "a", "coef1", "qkv", "attn", "u", "x_mid", "m", "coef_mlp", "i",
+                "coef1_mlp", "p", "f", "x_out", "n_next", "h", "tile_max", "cand", "unary", "z", "scores")
+
+
+class dfl_trace(C.Structure):
+    _fields_ = [("layer", C.c_int32)] + [(n, C.c_void_p) for n in TRACE_FIELDS]
+
+
+CONTEXT_TRACE_FIELDS = ("fc_out", "c", "kv")
+
+
+class dfl_context_trace(C.Structure):
+    _fields_ = [("layer", C.c_int32)] + [(n, C.c_void_p) for n in CONTEXT_TRACE_FIELDS]
+
+
 _P, _I, _F, _Z = C.c_void_p, C.c_int, C.c_float, C.c_size_t
 _SIGS = {
     "dfl_last_error": (C.c_char_p, []),
@@ -72,6 +87,11 @@ _SIGS = {
     "dfl_draft_workspace_bytes": (_Z, [_P, _I, _I, _I]),
     "dfl_draft_block": (_I, [_P, _P, _P, _I, _I, C.POINTER(_P), C.POINTER(_P), _I, _I, _P, _P, _P,
                              _P, _P, _P, _Z, _P]),
+    "dfl_draft_block_traced": (_I, [_P, _P, _P, _I, _I, C.POINTER(_P), C.POINTER(_P), _I, _I, _P, _P, _P,
+                                    _P, _P, _P, _Z, C.POINTER(dfl_trace), _P]),
+    "dfl_context_materialize_traced": (_I, [_P, _P, _I, _I, _I, _I, C.POINTER(_P), C.POINTER(_P), _P, _Z,
+                                            C.POINTER(dfl_context_trace), _P]),
+    "dfl_context_append_traced": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P, _Z, C.POINTER(dfl_context_trace), _P]),
     "dfl_block_layer": (_I, [_P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _P, _P, _P, _Z, _P]),
     "dfl_rms_norm": (_I, [_P, _I, _I, _I, _P, _F, _P, _I, _P]),
     "dfl_linear_workspace_bytes": (_Z, [_I, _I, _I]),
@@ -261,6 +281,44 @@ def dfl_draft_block(handle, embeds, anchors, B, G, K: list, V: list, Lcap, Lmax,
     _check(lib().dfl_draft_block(handle, _bf(embeds), _i32(anchors), B, G, kp, vp, Lcap, Lmax,
                                  _i32(ctx_len), _i32(pos0), _bf(lm_head), _i32(tokens),
                                  _f32(logits_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dfl_draft_block_traced(handle, embeds, anchors, B, G, K: list, V: list, Lcap, Lmax, ctx_len, pos0,
+                           lm_head, tokens, logits_out, ws, layer: int, stages: dict, stream=None):
+    """dfl_draft_block that also copies the stages named in `stages` (dfl_trace field name ->
+    device tensor of that stage's shape and dtype) of layer `layer` and of the tail."""
+    unknown = set(stages) - set(TRACE_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown trace stages {sorted(unknown)}")
+    tr = dfl_trace(int(layer), *[_ptr(stages.get(n)) for n in TRACE_FIELDS])
+    kp = _ptr_array(K) if K else None
+    vp = _ptr_array(V) if V else None
+    _check(lib().dfl_draft_block_traced(handle, _bf(embeds), _i32(anchors), B, G, kp, vp, Lcap, Lmax,
+                                        _i32(ctx_len), _i32(pos0), _bf(lm_head), _i32(tokens),
+                                        _f32(logits_out), _ptr(ws), ws.numel(), C.byref(tr), _stream(stream)))
+
+
+def dfl_context_materialize_traced(handle, taps, B, L, row_offset, Lcap, K: list, V: list, ws, layer: int,
+                                   stages: dict, stream=None):
+    unknown = set(stages) - set(CONTEXT_TRACE_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown context trace stages {sorted(unknown)}")
+    tr = dfl_context_trace(int(layer), *[_ptr(stages.get(n)) for n in CONTEXT_TRACE_FIELDS])
+    _check(lib().dfl_context_materialize_traced(handle, _bf(taps), B, L, row_offset, Lcap, _ptr_array(K),
+                                                _ptr_array(V), _ptr(ws), ws.numel(), C.byref(tr), _stream(stream)))
+
+
+def dfl_context_append_traced(handle, taps, row_offsets, starts, B, Lcap, K: list, V: list, ws, layer: int,
+                              stages: dict, stream=None):
+    unknown = set(stages) - set(CONTEXT_TRACE_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown context trace stages {sorted(unknown)}")
+    tr = dfl_context_trace(int(layer), *[_ptr(stages.get(n)) for n in CONTEXT_TRACE_FIELDS])
+    offs = (C.c_int32 * (B + 1))(*[int(x) for x in row_offsets])
+    st = (C.c_int32 * B)(*[int(x) for x in starts])
+    _check(lib().dfl_context_append_traced(handle, _bf(taps), C.cast(offs, C.c_void_p), C.cast(st, C.c_void_p), B,
+                                           Lcap, _ptr_array(K), _ptr_array(V), _ptr(ws), ws.numel(), C.byref(tr),
+                                           _stream(stream)))
 
 
 def dfl_block_layer(handle, layer, x_in, x_out, B, G, K, V, Lcap, Lmax, ctx_len, pos0, ws, stream=None):

@@ -139,6 +139,22 @@ int timed(dfl_drafter* d, int k, double bytes, hipStream_t s, F&& f) {
     if (rc_ != DFL_OK) return rc_; \
   } while (0)
 
+// Stage snapshot for dfl_*_traced: a stream-ordered device copy into the caller's buffer
+// (skipped when the buffer is NULL).
+int snap(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (!dst || bytes == 0) return DFL_OK;
+  DFL_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s));
+  return DFL_OK;
+}
+
+// Snapshot of a projection's fp32 split-K planes as their sum (in plane order, the order
+// every consumer of the planes adds them).
+int snap_planes(float* dst, const dfl::Planes& pl, int M, int N, hipStream_t s) {
+  if (!dst) return DFL_OK;
+  DFL_HIP(dfl::launch_planes_sum(pl, M, N, dst, s));
+  return DFL_OK;
+}
+
 // Algorithmic bytes of y = A . W^T: A and the output once, the weight at 2 bytes per
 // element, or (q4) at half a byte plus a bf16 scale and bias per 64.
 double gemm_bytes(int M, int N, int K, int epi, bool q4 = false) {
@@ -255,7 +271,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) =
 int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, int G, const uint16_t* Kl,
               const uint16_t* Vl, int Lcap, int Lmax, const int32_t* ctx_len, const int32_t* pos0, char* W,
               const DraftLayout& lay, bool n_ready, const uint16_t* next_gamma, hipStream_t stream,
-              uint16_t* head_rows = nullptr) {
+              uint16_t* head_rows = nullptr, const dfl_trace* trace = nullptr) {
   const dfl_config& c = d->cfg;
   const LayerBuf& L = d->layers[li];
   const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
@@ -280,18 +296,27 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
   coef1.plane = (size_t)T * 2 * ng;
   const double conv_bytes = 2.0 * T * H * 2 + 4.0 * T * 2 * ng;  // y in, out, one side's deltas
   const double norm_bytes = 4.0 * T * H;
+  const dfl_trace* tr = trace && trace->layer == li ? trace : nullptr;
+  const size_t rowsH = (size_t)T * H * sizeof(uint16_t);
   // attention half
+  if (tr) DFL_TRY(snap(tr->x_in, xin, rowsH, stream));
   if (!n_ready) {
     DFL_TRY(timed(d, DFL_K_RMSNORM, norm_bytes, stream, [&] {
       return dfl::launch_rms_norm(xin, H, T, H, L.in_norm, c.rms_eps, n, H, 1, 1, 0, stream);
     }));
   }
+  if (tr) DFL_TRY(snap(tr->n, n, rowsH, stream));
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm_partials(p_kp, n, H, L.attn_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
+  if (tr) DFL_TRY(snap_planes(tr->coef, coef0, T, 4 * ng, stream));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
     return dfl::launch_conv(n, coef0, L.attn_base, 0, T, H, G, c.conv_group, nullptr, a, stream, c1);
   }));
+  if (tr) {
+    DFL_TRY(snap(tr->a, a, rowsH, stream));
+    DFL_TRY(snap(tr->coef1, c1, (size_t)T * 2 * ng * sizeof(float), stream));
+  }
   DFL_TRY(timed(d, DFL_K_GEMM_QKV, gemm_bytes(T, qkvw, H, dfl::EPI_F32, d->q4), stream, [&] {
     return dfl::launch_gemm_partials(p_qkv, a, H, wref(L.qkv, L.qkv_q4), T, qkvw, H, part, stream);
   }));
@@ -300,37 +325,51 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
                                              NKV * D, L.q_norm, L.k_norm, c.rms_eps, c.rope_theta, pos0, G, 0,
                                              stream);
   }));
+  if (tr) DFL_TRY(snap(tr->qkv, qkv, (size_t)T * qkvw * sizeof(uint16_t), stream));
   const double attn_bytes = 4.0 * (double)B * Lmax * NKV * D + 2.0 * T * qkvw + 2.0 * T * NH * D;
   DFL_TRY(timed(d, DFL_K_ATTENTION, attn_bytes, stream, [&] {
     return dfl::launch_attention(apl, qkv, qkvw, qkv + NH * D, qkv + (NH + NKV) * D, qkvw, Kl, Vl, Lcap, ctx_len,
                                  pos0, d->window[li], B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
   }));
+  if (tr) DFL_TRY(snap(tr->attn, ao, (size_t)T * NH * D * sizeof(uint16_t), stream));
   // o and down keep a separate split-K reduce: their consumer, the residual conv + norm,
   // runs one workgroup per row and reads bf16 rows far faster than it could sum planes
   DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16, d->q4), stream, [&] {
     return dfl::launch_gemm(p_o, ao, NH * D, wref(L.o, L.o_q4), T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0,
                             part, stream);
   }));
+  if (tr) DFL_TRY(snap(tr->u, u, rowsH, stream));
   // x = x_in + conv1(u), fused with the MLP half's input norm
   DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
     return dfl::launch_conv_residual_norm(u, coef1, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
                                           c.rms_eps, n, stream);
   }));
+  if (tr) {
+    DFL_TRY(snap(tr->x_mid, x, rowsH, stream));
+    DFL_TRY(snap(tr->m, n, rowsH, stream));
+  }
   // MLP half
   DFL_TRY(timed(d, DFL_K_GEMM_KPROJ, gemm_bytes(T, 4 * ng, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm_partials(p_kp, n, H, L.mlp_kproj, true, T, 4 * ng, H, kpart, stream);
   }));
+  if (tr) DFL_TRY(snap_planes(tr->coef_mlp, coef0, T, 4 * ng, stream));
   DFL_TRY(timed(d, DFL_K_CONV_PREPARE, conv_bytes, stream, [&] {
     return dfl::launch_conv(n, coef0, L.mlp_base, 0, T, H, G, c.conv_group, nullptr, a, stream, c1);
   }));
+  if (tr) {
+    DFL_TRY(snap(tr->i, a, rowsH, stream));
+    DFL_TRY(snap(tr->coef1_mlp, c1, (size_t)T * 2 * ng * sizeof(float), stream));
+  }
   DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL, d->q4), stream, [&] {
     return dfl::launch_gemm(p_gu, a, H, wref(L.gateup, L.gateup_q4), T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr,
                             0, 0, part, stream);
   }));
+  if (tr) DFL_TRY(snap(tr->p, p, (size_t)T * F * sizeof(uint16_t), stream));
   DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16, d->q4), stream, [&] {
     return dfl::launch_gemm(p_dn, p, F, wref(L.down, L.down_q4), T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part,
                             stream);
   }));
+  if (tr) DFL_TRY(snap(tr->f, u, rowsH, stream));
   if (next_gamma) {
     // the next layer's input norm, or (head_rows set) the final norm of rows 1..G-1, packed
     // for the head
@@ -342,6 +381,10 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
       return dfl::launch_conv(u, coef1, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);
     }));
+  }
+  if (tr) {
+    DFL_TRY(snap(tr->x_out, x, rowsH, stream));
+    if (next_gamma && !head_rows) DFL_TRY(snap(tr->n_next, n, rowsH, stream));
   }
   return DFL_OK;
 }
@@ -643,6 +686,12 @@ size_t dfl_context_workspace_bytes(const dfl_drafter* d, int B, int L) {
 int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, int row_offset,
                             int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
                             size_t ws_bytes, hipStream_t stream) {
+  return dfl_context_materialize_traced(d, taps, B, L, row_offset, Lcap, K, V, ws, ws_bytes, nullptr, stream);
+}
+
+int dfl_context_materialize_traced(dfl_drafter* d, const dfl_bf16* taps, int B, int L, int row_offset,
+                                   int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
+                                   size_t ws_bytes, const dfl_context_trace* trace, hipStream_t stream) {
   DFL_REQUIRE(d && taps && K && V && ws, DFL_E_INVALID, "NULL argument");
   DFL_REQUIRE(B > 0 && L > 0 && row_offset >= 0 && Lcap > 0, DFL_E_INVALID, "B, L, Lcap must be positive");
   DFL_REQUIRE((int64_t)row_offset + L <= Lcap, DFL_E_SHAPE, "row_offset %d + L %d exceeds Lcap %d", row_offset, L,
@@ -664,9 +713,11 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
     return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, true, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
                             0, 0, part, stream);
   }));
+  if (trace) DFL_TRY(snap(trace->fc_out, craw, (size_t)M * H * sizeof(uint16_t), stream));
   DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * M * H, stream, [&] {
     return dfl::launch_rms_norm(craw, H, M, H, d->hidden_norm, c.rms_eps, cc, H, 1, 1, 0, stream);
   }));
+  if (trace) DFL_TRY(snap(trace->c, cc, (size_t)M * H * sizeof(uint16_t), stream));
   const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
   for (int i = 0; i < c.layers; ++i) {
     const LayerBuf& Lb = d->layers[i];
@@ -674,6 +725,7 @@ int dfl_context_materialize(dfl_drafter* d, const dfl_bf16* taps, int B, int L, 
       return dfl::launch_gemm(pkv, cc, H, wref(Lb.kv_ctx, Lb.kv_ctx_q4), M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr,
                               0, 0, part, stream);
     }));
+    if (trace && trace->layer == i) DFL_TRY(snap(trace->kv, kv, (size_t)M * kvw * sizeof(uint16_t), stream));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
       return dfl::launch_context_kv_store(kv, B, L, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,
                                           row_offset, Lcap, K[i], V[i], stream);
@@ -690,6 +742,12 @@ size_t dfl_context_append_workspace_bytes(const dfl_drafter* d, int B, int rows)
 int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_offsets, const int32_t* starts,
                        int B, int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
+  return dfl_context_append_traced(d, taps, row_offsets, starts, B, Lcap, K, V, ws, ws_bytes, nullptr, stream);
+}
+
+int dfl_context_append_traced(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_offsets,
+                              const int32_t* starts, int B, int Lcap, dfl_bf16* const* K, dfl_bf16* const* V,
+                              void* ws, size_t ws_bytes, const dfl_context_trace* trace, hipStream_t stream) {
   DFL_REQUIRE(d && taps && row_offsets && starts && K && V && ws, DFL_E_INVALID, "NULL argument");
   DFL_REQUIRE(B > 0 && Lcap > 0, DFL_E_INVALID, "B and Lcap must be positive");
   DFL_REQUIRE(row_offsets[0] == 0, DFL_E_SHAPE, "row_offsets[0] must be 0");
@@ -724,9 +782,11 @@ int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_
     return dfl::launch_gemm(pfc, taps, c.n_taps * H, d->fc, true, M, H, c.n_taps * H, dfl::EPI_BF16, craw, H, nullptr,
                             0, 0, part, stream);
   }));
+  if (trace) DFL_TRY(snap(trace->fc_out, craw, (size_t)M * H * sizeof(uint16_t), stream));
   DFL_TRY(timed(d, DFL_K_RMSNORM, 4.0 * M * H, stream, [&] {
     return dfl::launch_rms_norm(craw, H, M, H, d->hidden_norm, c.rms_eps, cc, H, 1, 1, 0, stream);
   }));
+  if (trace) DFL_TRY(snap(trace->c, cc, (size_t)M * H * sizeof(uint16_t), stream));
   const dfl::GemmPlan pkv = dfl::plan_gemm(M, kvw, H);
   for (int i = 0; i < c.layers; ++i) {
     const LayerBuf& Lb = d->layers[i];
@@ -734,6 +794,7 @@ int dfl_context_append(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_
       return dfl::launch_gemm(pkv, cc, H, wref(Lb.kv_ctx, Lb.kv_ctx_q4), M, kvw, H, dfl::EPI_BF16, kv, kvw, nullptr,
                               0, 0, part, stream);
     }));
+    if (trace && trace->layer == i) DFL_TRY(snap(trace->kv, kv, (size_t)M * kvw * sizeof(uint16_t), stream));
     DFL_TRY(timed(d, DFL_K_ROPE, 4.0 * M * kvw, stream, [&] {
       return dfl::launch_context_kv_store_ragged(kv, M, B, c.kv_heads, c.head_dim, Lb.k_norm, c.rms_eps, c.rope_theta,
                                                  offs_d, starts_d, Lcap, K[i], V[i], stream);
@@ -752,6 +813,15 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
                     const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
                     int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
+  return dfl_draft_block_traced(d, embeds, anchors, B, G, K, V, Lcap, Lmax, ctx_len, pos0, lm_head, tokens,
+                                logits_out, ws, ws_bytes, nullptr, stream);
+}
+
+int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
+                           const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,
+                           const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
+                           int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
+                           const dfl_trace* trace, hipStream_t stream) {
   DFL_REQUIRE(d && embeds && anchors && ctx_len && pos0 && tokens && ws, DFL_E_INVALID, "NULL argument");
   DFL_REQUIRE(lm_head || d->head, DFL_E_INVALID, "lm_head is NULL and no target head is bound");
   // the bound (tile-contiguous) copy serves a NULL head or the pointer it was bound from
@@ -794,9 +864,10 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
     // the last layer's finish applies the final norm to rows 1..G-1, packed into h for the head
     const uint16_t* next_gamma = last ? d->norm : d->layers[li + 1].in_norm;
     DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, li > 0, next_gamma, stream,
-                      last ? h : nullptr));
+                      last ? h : nullptr, trace));
     xin = x;
   }
+  if (trace) DFL_TRY(snap(trace->h, h, (size_t)N * H * sizeof(uint16_t), stream));
   // An unsplit head also writes every 256-column tile's row maxima, which lets the top-K
   // read only the few tiles that can hold a candidate; a split head leaves them to a pass
   // over the logits.
@@ -810,15 +881,23 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
   DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
   }));
+  if (trace) DFL_TRY(snap(trace->z, z, (size_t)N * R * sizeof(float), stream));
   DFL_TRY(timed(d, DFL_K_TOPK, tiles_fused ? 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) : 4.0 * N * V_,
                 stream, [&] {
     return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map)
                        : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream, id_map);
   }));
+  if (trace) {
+    DFL_TRY(snap(trace->tile_max, tmax, (size_t)N * ((V_ + dfl::kGemmTileN - 1) / dfl::kGemmTileN) * sizeof(float),
+                 stream));
+    DFL_TRY(snap(trace->cand, cand, (size_t)N * Kc * sizeof(int32_t), stream));
+    DFL_TRY(snap(trace->unary, unary, (size_t)N * Kc * sizeof(float), stream));
+  }
   DFL_TRY(timed(d, DFL_K_SCORE_EDGES, 4.0 * N * Kc * (2 * R + Kc + 2) + 4.0 * N * R, stream, [&] {
     return dfl::launch_score_edges(cand, unary, z, anchors, B, S, Kc, R, d->pred, d->succ, c.vocab, scores,
                                    stream);
   }));
+  if (trace) DFL_TRY(snap(trace->scores, scores, (size_t)N * Kc * Kc * sizeof(float), stream));
   DFL_TRY(timed(d, DFL_K_SELECT_PATH, 4.0 * N * Kc * (Kc + 1), stream, [&] {
     return dfl::launch_select_path(scores, cand, B, S, Kc, tokens, stream);
   }));

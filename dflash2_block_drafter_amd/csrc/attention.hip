@@ -1,7 +1,9 @@
-// Bidirectional block attention over a context K/V prefix (dflash2.ts diff: header, "no
-// sliding window", and `#block`, which hands the block's own k/v to `context.attend` with
-// scale 1/sqrt(D)).  Every query row of a request attends to all ctx_len[b] context rows
-// and all G block rows; query head h reads KV head h / (NH/NKV).
+// Bidirectional block attention over a context K/V prefix (dflash2.ts diff: the header
+// comment, under which the drafter attends every context row, and `#block`, which hands the
+// block's own k/v to the context's attend call with scale 1/sqrt(D)).  Every query row of a
+// request attends to its ctx_len[b] context rows (in a sliding-window layer, the ones inside
+// its window: see the last paragraph) and all G block rows; query head h reads KV head
+// h / (NH/NKV).
 //
 // Work split: one workgroup per (request b, KV head g, key chunk).  The Q tile is the
 // G x NH/NKV query rows that share KV head g (<= 64 rows, 16 per wavefront), so every

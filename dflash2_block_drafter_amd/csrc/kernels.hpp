@@ -78,6 +78,9 @@ inline Planes gemm_planes(const GemmPlan& pl, const float* partial, int M, int N
   p.plane = (size_t)M * N;
   return p;
 }
+// Sum of S fp32 planes [M, N] (src.ld = N) into one plane `out` [M, N], added in plane order.
+hipError_t launch_planes_sum(const Planes& src, int M, int N, float* out, hipStream_t stream);
+
 // Tile-contiguous copy of a row-major [N, K] weight: one block per (256-row tile, 64-wide K
 // step), [ceil(N/256)][K/64][block], rows past N zero.  Inside a block the order is the
 // matrix-core operand order: 32 fragments of 16 rows x 32 K (row group outer, K half inner),

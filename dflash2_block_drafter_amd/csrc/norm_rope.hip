@@ -116,8 +116,8 @@ __global__ __launch_bounds__(256) void head_norm_rope_kernel(uint16_t* x, int ld
 }
 
 // q|k|v projection finish from its fp32 split-K planes, one wavefront per (row, head):
-// the head's columns become bf16(sum over planes); heads [0, rope_heads) then get RMSNorm
-// + RoPE (q_norm below `split`, k_norm above); later heads (v) are stored as rounded.
+// heads [0, rope_heads) get RMSNorm + RoPE of the fp32 sum over planes (q_norm below
+// `split`, k_norm above), rounded once to bf16; later heads (v) are the sum, rounded.
 // Lane l holds EPL = D/64 adjacent values; for l < 32 they are first-half elements, their
 // rotary partners sit in lane l ^ 32.
 template <int D>
@@ -141,8 +141,6 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
   const int e0 = (lane >> 5) * (D / 2) + half_lane * EPL;  // this lane's first element
   float v[EPL];
   planes_sum<EPL>(src, (size_t)r * src.ld + h * D + e0, v);
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) v[e] = round_bf16(v[e]);
   uint16_t* out = dst + (size_t)r * ldd + h * D + e0;
   if (h >= rope_heads) {
 #pragma unroll

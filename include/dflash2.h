@@ -201,6 +201,69 @@ int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* ancho
                     int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* ---- stage snapshots, for parity tests ----
+ *
+ * dfl_draft_block_traced runs exactly the launch sequence of dfl_draft_block (the same
+ * kernels, plans and workspace) and, after the kernel that produces each stage below,
+ * copies that stage's output into the caller's buffer (device memory, caller-owned; a NULL
+ * pointer skips the stage).  The copies are ordinary stream-ordered device copies and
+ * change no result.  The stages follow [P3] `DFlash2TransformerBlock` and
+ * `DFlash2GroupedConv` and [P2] `#block` / `#select`; T = B*G, N = B*(G-1), ng = H/grp,
+ * qkvw = (NH + 2*NKV)*D, ntiles = ceil(V'/256) with V' the head's columns.
+ * Layer stages are taken from layer `layer` only. */
+typedef struct {
+  int32_t layer;        /* which layer's stages to copy (any value outside [0, layers): none) */
+  dfl_bf16* x_in;       /* [T, H]    the layer's input rows */
+  dfl_bf16* n;          /* [T, H]    RMSNorm(x_in; input_layernorm) */
+  float* coef;          /* [T, 4*ng] attention conv's kernel projection D = n . W^T (fp32,
+                                     columns [side][tap][group]) */
+  dfl_bf16* a;          /* [T, H]    conv side 0 of n (prepare's output) */
+  float* coef1;         /* [T, 2*ng] side-1 deltas as prepare hands them to finish */
+  dfl_bf16* qkv;        /* [T, qkvw] q|k after per-head norm and RoPE, v as projected */
+  dfl_bf16* attn;       /* [T, NH*D] attention output */
+  dfl_bf16* u;          /* [T, H]    o projection */
+  dfl_bf16* x_mid;      /* [T, H]    x_in + conv side 1 of u (the attention half's residual) */
+  dfl_bf16* m;          /* [T, H]    RMSNorm(x_mid; post_attention_layernorm) */
+  float* coef_mlp;      /* [T, 4*ng] MLP conv's kernel projection of m */
+  dfl_bf16* i;          /* [T, H]    MLP conv side 0 of m */
+  float* coef1_mlp;     /* [T, 2*ng] its side-1 deltas */
+  dfl_bf16* p;          /* [T, F]    silu(gate) * up */
+  dfl_bf16* f;          /* [T, H]    down projection */
+  dfl_bf16* x_out;      /* [T, H]    x_mid + MLP conv side 1 of f (the layer's output) */
+  dfl_bf16* n_next;     /* [T, H]    RMSNorm(x_out; next layer's input_layernorm); not written
+                                     for the last layer, whose normed rows are `h` */
+  dfl_bf16* h;          /* [N, H]    final-normed rows 1..G-1 of every block, packed */
+  float* tile_max;      /* [N, ntiles] row maxima of every 256-column tile of the logits */
+  int32_t* cand;        /* [N, K]    candidate ids */
+  float* unary;         /* [N, K]    their logits */
+  float* z;             /* [N, R]    selector projection */
+  float* scores;        /* [N, K, K] edge scores */
+} dfl_trace;
+
+int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
+                           const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,
+                           const int32_t* ctx_len, const int32_t* pos0, const dfl_bf16* lm_head,
+                           int32_t* tokens, float* logits_out, void* ws, size_t ws_bytes,
+                           const dfl_trace* trace, hipStream_t stream);
+
+/* The same for dfl_context_materialize: the fc output, the context rows, and one layer's
+ * k|v projection rows before the K store's norm and RoPE.  M = B*L. */
+typedef struct {
+  int32_t layer;        /* which layer's k|v rows to copy */
+  dfl_bf16* fc_out;     /* [M, H]           taps . fc^T */
+  dfl_bf16* c;          /* [M, H]           RMSNorm(fc_out; hidden_norm) */
+  dfl_bf16* kv;         /* [M, 2*NKV*D]     [c . k_proj^T | c . v_proj^T] of layer `layer` */
+} dfl_context_trace;
+
+/* The same for dfl_context_append (M = the appended rows, packed as in `taps`). */
+int dfl_context_append_traced(dfl_drafter* d, const dfl_bf16* taps, const int32_t* row_offsets,
+                              const int32_t* starts, int B, int Lcap, dfl_bf16* const* K, dfl_bf16* const* V,
+                              void* ws, size_t ws_bytes, const dfl_context_trace* trace, hipStream_t stream);
+
+int dfl_context_materialize_traced(dfl_drafter* d, const dfl_bf16* taps, int B, int L, int row_offset,
+                                   int Lcap, dfl_bf16* const* K, dfl_bf16* const* V, void* ws,
+                                   size_t ws_bytes, const dfl_context_trace* trace, hipStream_t stream);
+
 /* One drafter layer on a block ([P3] `DFlash2TransformerBlock`: r = x; h = conv.prepare(norm r);
  * h = attn(h); r += conv.finish(h), then the same for the MLP; [P2] `#block`, the body of the
  * layer loop).  x_in, x_out: [B*G, H] bf16, block rows of request b at b*G..b*G+G-1; x_out may

@@ -7,7 +7,7 @@ import torch
 from dflash2_block_drafter_amd import configs, synth
 from dflash2_block_drafter_amd.drafter import Drafter
 from oracle import dflash2 as O
-from tests.helpers import COMPOSED_REL, assert_composed_close, compare_tokens
+from tests.helpers import COMPOSED_REL, assert_bf16_close, assert_composed_close, compare_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -43,9 +43,30 @@ def test_tiny_drafter_end_to_end(batch):
         assert_composed_close(V[i][:, :w.ctx_len], vs[i], f"context V layer {i}")
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
-    assert_composed_close(logits, ref["logits"], "head logits")
-    n_eq = compare_tokens(tokens.cpu().numpy(), ref)
-    assert n_eq >= 1
+    # the head logits after the whole chain meet the spec bar against the oracle at P2's
+    # bf16 rounding points, element by element
+    assert_bf16_close(logits, ref["logits"], "head logits")
+    compare_tokens(tokens.cpu().numpy(), ref)
+    # the context K after fc, norm, projection, k_norm and RoPE does not, at a few elements: a
+    # value rounded one ulp apart before the rotation keeps that absolute error when the
+    # rotation cancels it to near zero (the K store alone meets the bar, given its input:
+    # test_gpu_stages).  The elementwise bar over the composed chain is reported here:
+    ks64, vs64 = O.materialize_context(th["taps"], wh, d)
+    ref64 = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks64, vs64, th["ctx_len"], th["pos0"], d,
+                          return_all=True)
+    for what, got, want in (("context K layer 0 vs cast points", K[0][:, :w.ctx_len], ks[0]),
+                            ("context K layer 0 vs float64", K[0][:, :w.ctx_len], ks64[0]),
+                            ("logits vs cast points", logits, ref["logits"]),
+                            ("logits vs float64", logits, ref64["logits"])):
+        g = got.float().cpu().numpy().astype(np.float64)
+        err = np.abs(g - want)
+        bad = err > 2e-3 + 2e-2 * np.abs(want)
+        rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True)) * np.ones_like(want)
+        worst = np.argsort(-(err - 2e-3 - 2e-2 * np.abs(want)).reshape(-1))[:3]
+        rows = [(np.unravel_index(i, want.shape), float(want.reshape(-1)[i]), float(err.reshape(-1)[i]),
+                 float(rms.reshape(-1)[i])) for i in worst if bad.reshape(-1)[i]]
+        print(f"[north-star bar] B={batch} {what}: {int(bad.sum())} of {bad.size} outside; "
+              f"worst (index, o, |g-o|, row rms) {rows}", flush=True)
     dr.close()
 
 
@@ -91,7 +112,7 @@ def test_wide_head_on_big_tiles():
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
     assert_composed_close(logits, ref["logits"], "head logits")
-    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    compare_tokens(tokens.cpu().numpy(), ref)
     tgt = {k: v.to(DEV) for k, v in synth.target_inputs(w).items()}
     dr.bind_target(tgt["lm_head"])
     t2, l2 = dr.draft(tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], None,
@@ -150,7 +171,7 @@ def _tiny_parity(w, G=None, q4=False, rel=COMPOSED_REL):
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
     assert_composed_close(logits, ref["logits"], "head logits", rel=rel)
-    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    compare_tokens(tokens.cpu().numpy(), ref)
     dr.close()
     return ref
 
@@ -216,7 +237,7 @@ def test_tiny_draft_vocabulary(order):
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True, vocab_ids=ids)
     assert_composed_close(logits, ref["logits"], "draft-vocabulary logits")
-    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    compare_tokens(tokens.cpu().numpy(), ref)
     assert np.isin(tokens.cpu().numpy(), ids).all()
     dr.close()
 
@@ -283,7 +304,7 @@ def test_tiny_ragged_context_lengths_end_to_end():
     ref = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, th["ctx_len"], th["pos0"], d,
                         bf16_points=True, return_all=True)
     assert_composed_close(logits, ref["logits"], "head logits, ragged contexts")
-    assert compare_tokens(tokens.cpu().numpy(), ref) >= 1
+    compare_tokens(tokens.cpu().numpy(), ref)
     # the bound tells these lengths apart: attending every materialised row would fail it
     wrong = O.draft_block(th["embeds"], wh, th["lm_head"], th["anchors"], ks, vs, np.full(4, 200, np.int32),
                           th["pos0"], d, bf16_points=True, return_all=True)["logits"]
