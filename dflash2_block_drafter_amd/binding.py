@@ -105,6 +105,7 @@ _SIGS = {
     "dfl_conv_finish": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "dfl_candidates_workspace_bytes": (_Z, [_I, _I, _I]),
     "dfl_compute_candidates": (_I, [_P, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "dfl_compute_candidates_static": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "dfl_selector_project_workspace_bytes": (_Z, [_I, _I, _I]),
     "dfl_selector_project": (_I, [_P, _I, _I, _P, _I, _P, _P, _Z, _P]),
     "dfl_score_edges": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
@@ -385,6 +386,13 @@ def dfl_candidates_workspace_bytes(N, V, K) -> int:
 def dfl_compute_candidates(logits, N, V, K, ids, unary, ws, stream=None):
     _check(lib().dfl_compute_candidates(_f32(logits), N, V, K, _i32(ids), _f32(unary), _ptr(ws), ws.numel(),
                                         _stream(stream)))
+
+
+CANDIDATES_STATIC_MAX_TILES = 1 << 20
+
+
+def dfl_compute_candidates_static(logits, N, V, K, ids, unary, stream=None):
+    _check(lib().dfl_compute_candidates_static(_f32(logits), N, V, K, _i32(ids), _f32(unary), _stream(stream)))
 
 
 def dfl_selector_project_workspace_bytes(N, H, R) -> int:

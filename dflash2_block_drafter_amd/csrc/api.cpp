@@ -1093,6 +1093,22 @@ int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* id
   return DFL_OK;
 }
 
+int dfl_compute_candidates_static(const float* logits, int N, int V, int K, int32_t* ids, float* unary,
+                                  hipStream_t stream) {
+  DFL_REQUIRE(logits && ids && unary, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(N > 0 && V > 0 && K > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= 32 && K <= V, DFL_E_UNSUPPORTED, "K=%d must be <= 32 and <= V", K);
+  const size_t need = dfl::topk_ws_bytes(N, V) / sizeof(float);
+  DFL_REQUIRE(need <= (size_t)DFL_CANDIDATES_STATIC_MAX_TILES && need <= dfl::topk_static_scratch_floats(),
+              DFL_E_WORKSPACE, "N * ceil(V / 256) = %zu tile maxima exceed the static scratch of %d", need,
+              DFL_CANDIDATES_STATIC_MAX_TILES);
+  float* scratch = nullptr;
+  DFL_HIP(dfl::topk_static_scratch(stream, &scratch));
+  hipError_t e = dfl::launch_topk(logits, N, V, K, ids, unary, scratch, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
 size_t dfl_selector_project_workspace_bytes(int N, int H, int R) { return dfl_linear_workspace_bytes(N, R, H); }
 
 int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z, void* ws,

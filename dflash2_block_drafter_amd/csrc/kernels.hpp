@@ -175,6 +175,12 @@ size_t topk_ws_bytes(int N, int V);
 hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, float* vals, void* ws,
                        hipStream_t stream, const int32_t* id_map = nullptr);
 
+// The library's static tile-maxima scratch (a file-scope device array of
+// topk_static_scratch_floats() floats): its device address on the GPU of `stream` (the
+// current device for the null stream), looked up on first use per device.
+size_t topk_static_scratch_floats();
+hipError_t topk_static_scratch(hipStream_t stream, float** out);
+
 hipError_t launch_score_edges(const int32_t* cand, const float* unary, const float* z,
                               const int32_t* anchors, int B, int S, int K, int R,
                               const uint16_t* pred, const uint16_t* succ, int V, float* scores,

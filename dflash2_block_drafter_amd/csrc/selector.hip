@@ -11,6 +11,7 @@
 // K..63 take new candidates).  Ties are ordered by id, so the result is exact and unique for
 // any input, including constant rows (where every tile qualifies).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -19,6 +20,14 @@
 namespace dfl {
 
 namespace {
+
+// The tile maxima of dfl_compute_candidates_static live here instead of in a caller
+// workspace: one copy of this array per GPU the library runs on, held until the process
+// ends.  On the host the name is only a stand-in for the device symbol; host code passes the
+// address topk_static_scratch() looked up, never the name, to a kernel.
+constexpr size_t kStaticScratchFloats = size_t(1) << 20;  // 4 MiB
+__device__ __align__(256) float scratch[kStaticScratchFloats];
+constexpr int kMaxDevices = 64;
 
 // Row maxima of every kGemmTileN-column tile of fp32 logits (the values the head projection
 // writes alongside its logits).  A quarter-wavefront (16 lanes, 4 x float4 each) covers one
@@ -524,6 +533,41 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
 }
 
 }  // namespace
+
+size_t topk_static_scratch_floats() { return kStaticScratchFloats; }
+
+hipError_t topk_static_scratch(hipStream_t stream, float** out) {
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // each GPU holds its own copy of the array at its own address: look it up with that
+    // device current, once
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 size_t topk_ws_bytes(int N, int V) {
   return (size_t)N * ((V + kGemmTileN - 1) / kGemmTileN) * sizeof(float);

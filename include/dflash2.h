@@ -345,6 +345,18 @@ size_t dfl_candidates_workspace_bytes(int N, int V, int K);
 int dfl_compute_candidates(const float* logits, int N, int V, int K, int32_t* ids, float* unary,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dfl_compute_candidates without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * tile maxima go to a static device array owned by the library, DFL_CANDIDATES_STATIC_MAX_TILES
+ * floats (4 MiB) on each GPU it runs on, held until the process ends.  The call allocates
+ * nothing.  N * ceil(V / 256) above that limit -> DFL_E_WORKSPACE (checked before anything is
+ * enqueued).  Every call on one GPU shares that GPU's array (each call writes all the tile
+ * maxima it reads before reading them), so calls that overlap on one GPU, on different
+ * streams or threads, race.  Other arguments, outputs and errors as dfl_compute_candidates. */
+#define DFL_CANDIDATES_STATIC_MAX_TILES (1 << 20)
+int dfl_compute_candidates_static(const float* logits, int N, int V, int K, int32_t* ids,
+                                  float* unary, hipStream_t stream);
+
 /* Selector projection z = h . proj^T kept in fp32 ([P2] `#block`: z = hidden_projection(h)).
  * h [N, H] bf16, proj [R, H] bf16, z [N, R] fp32. */
 size_t dfl_selector_project_workspace_bytes(int N, int H, int R);

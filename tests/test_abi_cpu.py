@@ -61,6 +61,11 @@ def test_validation_errors_before_any_launch():
     assert _err(L.dfl_compute_candidates(P, 4, 100, 40, P, P, P, 1 << 20, None))[0] == B.DFL_E_UNSUPPORTED
     # workspace too small
     assert L.dfl_compute_candidates(P, 4, 248320, 16, P, P, P, 16, None) == B.DFL_E_WORKSPACE
+    # the allocation-free variant: more tile maxima than its static scratch holds (1082 rows
+    # x 970 tiles > 2^20), or a bad K, are refused before any device call
+    assert L.dfl_compute_candidates_static(P, 1082, 248320, 16, P, P, None) == B.DFL_E_WORKSPACE
+    assert L.dfl_compute_candidates_static(P, 4, 100, 40, P, P, None) == B.DFL_E_UNSUPPORTED
+    assert L.dfl_compute_candidates_static(None, 4, 100, 4, P, P, None) == B.DFL_E_INVALID
     # null pointers
     assert L.dfl_select_path(None, P, 1, 1, 4, P, None) == B.DFL_E_INVALID
     # K not a multiple of 64
