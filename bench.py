@@ -38,6 +38,8 @@ def parse():
                    help="layer projection weights: bf16, or 4-bit affine (groups of 64); the q4 line "
                         "reports no cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="full workload: skip the embedded conv, selector and long-workload measurements")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB copy (counter calibration) and exit")
     return p.parse_args()
@@ -71,25 +73,51 @@ def main():
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
-
     if args.workload in ("conv", "selector"):
-        (bench_conv if args.workload == "conv" else bench_selector)(args)
+        rec = (bench_conv if args.workload == "conv" else bench_selector)(args.steps, args.warmup)
+        print(json.dumps(rec), flush=True)
         return
 
-    import numpy as np
+    from dflash2_block_drafter_amd import configs
+    w = configs.WORKLOADS[args.workload]
+    out = bench_draft(w, args.steps, args.warmup, args.weights, cpu=not args.no_cpu_baseline and args.weights == "bf16")
+    if args.workload == "full" and args.weights == "bf16" and not args.no_extras:
+        # The metric's second half, "conv+walk % HBM peak", as the grouped-conv microbenchmark
+        # (T = 1024 rows) and the candidate-selector chain (B = 32) measure it, each from cold
+        # HBM; and the long-context workload (B = 64, L = 8192), where the projections are
+        # bound by the matrix cores.
+        print("# conv microbenchmark", file=sys.stderr, flush=True)
+        out["conv_cfg2"] = _embedded(bench_conv(max(args.steps, 48), args.warmup))
+        print("# selector microbenchmark", file=sys.stderr, flush=True)
+        out["walk_cfg3"] = _embedded(bench_selector(max(args.steps, 40), args.warmup))
+        print("# long workload", file=sys.stderr, flush=True)
+        out["long"] = _embedded(bench_draft(configs.LONG, 10, 3, "bf16", cpu=False,
+                                            classes=["gemm_head", "gemm_gateup", "attention"]))
+    print(json.dumps(out), flush=True)
+
+
+def _embedded(rec: dict) -> dict:
+    """A sub-benchmark's record as embedded in the headline line (without the headline keys)."""
+    drop = {"metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "cpu_baseline"}
+    return {k: v for k, v in rec.items() if k not in drop}
+
+
+def bench_draft(w, steps: int, warmup: int, weight_kind: str = "bf16", cpu: bool = True, classes=None) -> dict:
+    """draft_block on workload w: `warmup` untimed steps, a per-kernel-class breakdown (one step
+    per class, that class's launches bracketed by HIP events on the launch stream), then
+    `steps` timed steps with the dominant class bracketed the same way (its roofline)."""
     import torch
 
     from dflash2_block_drafter_amd import binding as B_
-    from dflash2_block_drafter_amd import configs, synth
+    from dflash2_block_drafter_amd import synth
     from dflash2_block_drafter_amd.drafter import Drafter
 
-    w = configs.WORKLOADS[args.workload]
     d = w.dims
     dev = "cuda"
     torch.cuda.set_device(0)
     t0 = time.time()
     weights = synth.drafter_weights(w, device=dev)
-    q4 = synth.drafter_q4_weights(w, device=dev) if args.weights == "q4" else None
+    q4 = synth.drafter_q4_weights(w, device=dev) if weight_kind == "q4" else None
     if q4 is not None:
         for name in q4:
             del weights[name + ".weight"]
@@ -106,7 +134,7 @@ def main():
         ctx_ms = None
     else:
         K, V = dr.alloc_kv(Bq, L)
-        dr.materialize(tgt["taps"], K, V)          # compile-free warm call
+        dr.materialize(tgt["taps"], K, V)          # warm call
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
@@ -115,7 +143,7 @@ def main():
         torch.cuda.synchronize()
         ctx_ms = s.elapsed_time(e)
         del tgt["taps"]
-    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(f"# {w.name}: inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     ws = dr.workspace(Bq, G, L)
     tokens = torch.empty((Bq, G - 1), dtype=torch.int32, device=dev)
@@ -127,13 +155,15 @@ def main():
         dr.draft(tgt["embeds"], tgt["anchors"], K, V, L, tgt["ctx_len"], tgt["pos0"], tgt["lm_head"],
                  tokens=tokens, ws=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # per-kernel-class breakdown: one step per class with that class bracketed by events
+    # (each bracket adds the event's own cost, so short kernels read long here; the kernel
+    # trace in profiles/ has their true durations)
     breakdown = {}
-    for k in B_.KERNEL_CLASSES:
+    for k in (classes or B_.KERNEL_CLASSES):
         B_.dfl_set_timed_kernel(dr.handle, k)
         step()
         torch.cuda.synchronize()
@@ -142,90 +172,87 @@ def main():
             breakdown[k] = {"ms": round(ms, 4), "launches": n, "GBps": round(by / (ms * 1e-3) / 1e9, 1)}
     B_.dfl_set_timed_kernel(dr.handle, -1)
     dominant = max(breakdown, key=lambda k: breakdown[k]["ms"])
-    print(f"# breakdown {json.dumps(breakdown)}", file=sys.stderr, flush=True)
+    print(f"# {w.name} breakdown {json.dumps(breakdown)}", file=sys.stderr, flush=True)
 
     # timed region: the dominant class bracketed on the launch stream
     B_.dfl_set_timed_kernel(dr.handle, dominant)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_dom, n_dom, by_dom = B_.dfl_read_kernel_time(dr.handle)
     B_.dfl_set_timed_kernel(dr.handle, -1)
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = Bq * G / (elapsed / args.steps)
+    ms_per_step = elapsed * 1e3 / steps
+    value = Bq * G / (elapsed / steps)
+    roofline = _roofline(dominant, d, Bq, G, ms_dom / n_dom, by_dom / n_dom, w.name, weight_kind)
+    mfma = {}
+    for k in ("gemm_head", "gemm_gateup"):
+        # the projections as a fraction of the matrix cores' peak (the bound at large B)
+        b = breakdown.get(k)
+        fl = gemm_flops(k, d, Bq, G)
+        if b and fl:
+            mfma[k] = round(fl * b["launches"] / (b["ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
 
-    launch_ms = ms_dom / n_dom
-    bytes_per_launch = by_dom / n_dom
-    flops = gemm_flops(dominant, d, Bq, G)
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
-    if flops is not None and flops / bytes_per_launch > ridge:
-        # a projection with more flops per byte than the ridge is bounded by the matrix cores
-        achieved = flops / (launch_ms * 1e-3) / 1e12
-        roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": pmc_traffic(dominant, w.name, args.weights), "avg_launch_us": round(launch_ms * 1e3, 2),
-                    "algorithmic_flops_per_launch": int(flops), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
-    else:
-        achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": pmc_traffic(dominant, w.name, args.weights), "avg_launch_us": round(launch_ms * 1e3, 2),
-                    "algorithmic_bytes_per_launch": int(bytes_per_launch)}
-
-    def frac(cls):
-        b = breakdown.get(cls)
-        return None if b is None else round(b["GBps"] / HBM_PEAK_GBS, 4)
-
-    # The candidate walk (top-k, score_edges, select_path) against the bytes it cannot avoid:
-    # the head's tile maxima, K logit tiles of 256 per row (at least one per candidate when the
-    # tile maxima guide the top-k), the candidates' predecessor and successor codebook rows
-    # (bf16), and the edge scores written and read back.  A lower bound on what it moves, so
-    # the fraction is too; at these sizes the walk is a latency chain (15 dependent slots).
-    walk_cls = ["topk", "score_edges", "select_path"]
-    walk_ms = sum(breakdown[c]["ms"] for c in walk_cls if c in breakdown)
-    N = Bq * (G - 1)
-    K_, R_ = d.top_k, d.rank
-    walk_bytes = (4.0 * N * ((d.vocab + 255) // 256) + 4.0 * N * K_ * 256 + 2.0 * 2 * N * K_ * R_
-                  + 2 * 4.0 * N * K_ * K_)
-    hbm = {"conv_prepare": frac("conv_prepare"), "conv_finish": frac("conv_finish"),
-           "walk": round(walk_bytes / (walk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if walk_ms else None,
-           "walk_us": round(walk_ms * 1e3, 1) if walk_ms else None}
-
-    cpu = None
-    if not args.no_cpu_baseline and args.weights == "bf16":
+    cpu_rec = None
+    if cpu:
         print("# cpu baseline (oracle sample)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, weights, tgt)
+        cpu_rec = cpu_baseline(w, weights, tgt)
 
     out = {
         "metric": "drafted block tokens/sec (B×G) on 5-layer DFlash2; conv+walk % HBM peak",
         "value": round(value, 1),
         "unit": "block tok/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         # 4-bit weights are dequantized to bf16 for the matrix units: u4 storage, bf16 arithmetic
-        "dtype": "bf16" if args.weights == "bf16" else "u4-weights/bf16",
+        "dtype": "bf16" if weight_kind == "bf16" else "u4-weights/bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) taps/embeddings)",
         "config": {"workload": f"{w.name}: {d.layers}-layer drafter H={d.hidden} NH/NKV/D="
                                f"{d.heads}/{d.kv_heads}/{d.head_dim} F={d.intermediate} V={d.vocab}, "
-                               f"B={Bq} G={G} L={L}" + (", 4-bit affine layer projections" if args.weights == "q4"
+                               f"B={Bq} G={G} L={L}" + (", 4-bit affine layer projections" if weight_kind == "q4"
                                                         else ""),
-                   "B": Bq, "G": G, "L": L, "weights": args.weights},
+                   "B": Bq, "G": G, "L": L, "weights": weight_kind},
         "roofline": roofline,
-        "hbm_frac": hbm,
-        "breakdown_ms": {k: v["ms"] for k, v in breakdown.items()},
+        "mfma_frac": mfma,
+        "event_breakdown_ms": {k: v["ms"] for k, v in breakdown.items()},
         "context_materialize_ms": None if ctx_ms is None else round(ctx_ms, 3),
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_rec,
     }
-    print(json.dumps(out), flush=True)
+    if ctx_ms is not None:
+        # fc + hidden norm + five k|v projections and K/V stores over B*L context rows
+        T_ctx = Bq * L
+        kvw = 2 * d.kv_heads * d.head_dim
+        ctx_flops = 2.0 * T_ctx * d.hidden * (d.n_taps * d.hidden + d.layers * kvw)
+        out["context_materialize_mfma_frac"] = round(ctx_flops / (ctx_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     dr.close()
+    del weights, tgt, K, V, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def _roofline(cls, d, Bq, G, launch_ms, bytes_per_launch, workload, weight_kind):
+    flops = gemm_flops(cls, d, Bq, G)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte
+    if flops is not None and flops / bytes_per_launch > ridge:
+        # a projection with more flops per byte than the ridge is bounded by the matrix cores
+        achieved = flops / (launch_ms * 1e-3) / 1e12
+        return {"kernel": cls, "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": pmc_traffic(cls, workload, weight_kind), "avg_launch_us": round(launch_ms * 1e3, 2),
+                "algorithmic_flops_per_launch": int(flops), "algorithmic_bytes_per_launch": int(bytes_per_launch)}
+    achieved = bytes_per_launch / (launch_ms * 1e-3) / 1e9
+    return {"kernel": cls, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": pmc_traffic(cls, workload, weight_kind), "avg_launch_us": round(launch_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(bytes_per_launch)}
 
 
 def gemm_flops(cls: str, d, Bq: int, G: int):
@@ -285,7 +312,7 @@ def _time_graph(calls, replays: int, warmup: int) -> float:
     return a.elapsed_time(b) / (replays * len(calls))
 
 
-def bench_conv(args):
+def bench_conv(steps: int, warmup: int) -> dict:
     """Grouped conv microbenchmark: T = 64 blocks of 16 rows, H = 5120, groups of 16.
     Timed: one conv application (dfl_conv_finish: the conv kernel alone, side-1 deltas
     given), the kernel projection GEMM (dfl_linear, fp32 out) and a whole dfl_conv_prepare.
@@ -312,7 +339,7 @@ def bench_conv(args):
     torch.cuda.synchronize()
     finish = [lambda st=st: B_.dfl_conv_finish(st["a"], st["coef1"], st["base"], T, H, G, grp, None, st["y"])
               for st in sets]
-    reps = max(1, args.steps // nsets)
+    reps = max(1, steps // nsets)
     conv_ms = _time_graph(finish, reps, 2)
     # the replayed graph computes what an eager call computes
     last = sets[-1]
@@ -327,10 +354,13 @@ def bench_conv(args):
     conv_bytes = 2.0 * T * H + 4.0 * T * 2 * ng + 2.0 * 2 * H + 2.0 * T * H  # y, deltas, base side, out
     gemm_flop = 2.0 * T * 4 * ng * H
     achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
-    print(json.dumps({
+    del sets, ws, eager, last
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
         "metric": "grouped conv application time (T=1024 rows in 16-row blocks, H=5120, groups of 16)",
         "value": round(conv_ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * nsets,
-        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "warmup": warmup, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "conv: T=1024 H=5120 G=16 grp=16, kernel projection 5120 -> 1280; "
                                f"{nsets} input sets rotated (cold HBM), graph-replayed launches"},
         "roofline": {"kernel": "conv_plane_kernel", "bound": "hbm", "achieved": round(achieved, 1),
@@ -341,10 +371,10 @@ def bench_conv(args):
                                    "weight_GBps": round(2.0 * 4 * ng * H / (gemm_ms * 1e-3) / 1e9, 1)},
         "conv_prepare_us": round(prep_ms * 1e3, 2),
         "cpu_baseline": None,
-    }), flush=True)
+    }
 
 
-def bench_selector(args):
+def bench_selector(steps: int, warmup: int) -> dict:
     """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
     Timed: compute_candidates + selector_project + score_edges + select_path, the four C-ABI
     calls in order, over two input sets (0.95 GB of logits, more than the 256 MB Infinity
@@ -375,7 +405,7 @@ def bench_selector(args):
                            st["scores"])
         B_.dfl_select_path(st["scores"], st["ids"], Bq, S, K, st["tokens"])
 
-    reps = max(1, args.steps // 2)
+    reps = max(1, steps // 2)
     ms = _time_graph([lambda st=st: chain(st) for st in sets], reps, 2)
     got = sets[-1]["tokens"].clone()
     chain(sets[-1])
@@ -385,9 +415,12 @@ def bench_selector(args):
                            for st in sets], reps, 2)
     total_bytes = 4.0 * N * V + 2.0 * N * H + 2.0 * R * H + 4.0 * N * R + 2.0 * 2 * N * K * R + 4.0 * N * K * K
     achieved = total_bytes / (ms * 1e-3) / 1e9
-    print(json.dumps({
+    del sets, ws_c, ws_p, got
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {
         "metric": "candidate selector time (B=32, S=15, V=248320, K=16, R=64): top-k + projection + edges + walk",
-        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": args.warmup,
+        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": warmup,
         "higher_is_better": False, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16; "
                                "2 input sets rotated, graph-replayed chain"},
@@ -396,7 +429,7 @@ def bench_selector(args):
                      "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},
         "compute_candidates_us": round(topk_ms * 1e3, 2),
         "cpu_baseline": None,
-    }), flush=True)
+    }
 
 
 def cpu_baseline(w, weights, tgt, budget_s: float = 10.0):
@@ -430,6 +463,7 @@ def cpu_baseline(w, weights, tgt, budget_s: float = 10.0):
     threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
                   default=1)
     return {"value": round(done * d.block_size / spent, 4), "unit": "block tok/s", "cores": threads,
+            "host_cpus": os.cpu_count(),
             "kind": "oracle", "seconds": round(spent, 2),
             "sample": f"whole oracle draft blocks of requests 0..{done - 1} of {w.batch} (G={d.block_size}, "
                       f"all {d.layers} layers, full V={d.vocab} head), one request per call, context K/V "
