@@ -447,6 +447,9 @@ struct StreamW<TILED, false> {
   u32x4_t v[4];  // fragment (j, half) at j * 2 + half
   __device__ __forceinline__ void load(const GemmArgs& p, int nw0, int k0, int lane) {
     if (TILED) {
+      // a wave whose rows start past the last tile (the grid's last workgroup) re-reads the
+      // last 32 rows instead; its outputs are not stored
+      nw0 = min(nw0, (p.N + kGemmTileN - 1) / kGemmTileN * kGemmTileN - 32);
       const uint16_t* blk = p.W + ((size_t)(nw0 / kGemmTileN) * (p.K / BK) + k0 / BK) * (kGemmTileN * BK) +
                             (nw0 % kGemmTileN) / 16 * 2 * 512 + lane * 8;
 #pragma unroll
@@ -480,6 +483,7 @@ struct StreamW<true, true> {
   u32x4_t sb;  // scale | bias << 16 of the group's row sets 0..3
   int half = 0;
   __device__ __forceinline__ void load(const GemmArgs& p, int nw0, int k0, int lane) {
+    nw0 = min(nw0, (p.N + kGemmTileN - 1) / kGemmTileN * kGemmTileN - 32);
     const uint32_t* grp = p.Wq + ((size_t)(nw0 / kGemmTileN) * (p.K / BK) + k0 / BK) * (kGemmTileN * 9) +
                           (nw0 % kGemmTileN) / 64 * 576;
     half = (nw0 % 64) / 32;
@@ -876,13 +880,14 @@ constexpr int kBigBM = 256;
 constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;
 constexpr int kNarrowBN = 64, kNarrowMaxN = 2048, kNarrowAnyM = 256;  // 64-column workgroups for narrow projections  // big tiles with split K from these sizes
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
-// Wavefronts of 32 weight rows, two per SIMD, eight per workgroup (256 weight rows): every
-// workgroup re-reads the activation slab, and wider workgroups re-read it less (the vector
-// memory path delivers about 7 TB/s in all, cache hits included).  Used for wide
-// projections (at least kStreamMinN outputs and kStreamMinWeights weights), which keep the
-// grid wide without splitting K; deep, narrow ones keep the LDS kernel's split plan.
-constexpr int kStreamWaves = 8;
+// Wavefronts of 32 weight rows, at most two per SIMD.  Every workgroup re-reads the activation
+// slab of its K range, so fewer, wider workgroups re-read less, while more workgroups bring
+// more CUs' memory pipelines to bear (one CU sustains roughly 30 GB/s of weight reads): five
+// wavefronts (160 rows) balance the two for the wide and deep projections (plan_gemm).
+constexpr int kStreamWavesWide = 5;
 constexpr int kStreamStages = 8, kStreamStagesQ4 = 10;
+constexpr size_t kStreamMidMinWeights = size_t(16) << 20;
+constexpr int kStreamMidMinN = 4096;
 constexpr size_t kStreamMinWeights = size_t(64) << 20;
 constexpr int kStreamMinN = 16384;
 constexpr size_t kStreamMaxWaves = 2048;  // two wavefronts per SIMD on 256 CUs
@@ -988,10 +993,49 @@ GemmPlan plan_stream(int M, int N, int K, bool tile_max, int nw) {
   return pl;
 }
 
+// Streaming plan with nw wavefronts per workgroup and K split s ways.
+GemmPlan plan_stream_split(int M, int N, int K, int nw, int s) {
+  GemmPlan pl;
+  const int nk = K / BK;
+  const int per = (nk + s - 1) / s;
+  pl.bm = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  pl.bn = nw * 32;
+  pl.stream_waves = nw;
+  pl.k_per_split = per * BK;
+  pl.splits = (nk + per - 1) / per;
+  pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
+  return pl;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
   GemmPlan pl;
-  if (M <= kStreamMaxM && !tile_max && N >= kStreamMinN && (size_t)N * K >= kStreamMinWeights)
-    return plan_stream(M, N, K, false, kStreamWaves);
+  if (M <= kStreamMaxM && !tile_max && K % BK == 0) {
+    // Weight-streaming plans at M <= 128, sized so that about one round of workgroups covers
+    // the chip.  Wide projections (gate/up): five wavefronts (160 weight rows) per workgroup,
+    // 218 workgroups for N = 34816, no split.  Deep ones (down, N = 5120, K = 17408): the same
+    // workgroups with K split over 8 (256 workgroups).  Mid-size (o, N = 5120, K = 4096):
+    // two-wavefront workgroups, K split to fill a round (80 x 3).  Each measured faster than
+    // the 8-wavefront streaming plan and the 128 x 256 LDS kernel's split plan on these shapes.
+    const size_t weights = (size_t)N * K;
+    if (N >= kStreamMinN && weights >= kStreamMinWeights) {
+      // more than a round of 160-row workgroups (the head's 248320 rows): 256-row ones, which
+      // re-read the activations less
+      const bool one_round = (N + kStreamWavesWide * 32 - 1) / (kStreamWavesWide * 32) <= kTargetWorkgroups;
+      return plan_stream(M, N, K, false, one_round ? kStreamWavesWide : 8);
+    }
+    const int nk = K / BK;
+    if (weights >= kStreamMinWeights) {
+      const int tiles = (N + kStreamWavesWide * 32 - 1) / (kStreamWavesWide * 32);
+      int s = std::max(1, std::min(kMaxSplits, kTargetWorkgroups / tiles));
+      while (s > 1 && nk / s < 4) --s;
+      return plan_stream_split(M, N, K, kStreamWavesWide, s);
+    }
+    if (N >= kStreamMidMinN && weights >= kStreamMidMinWeights) {
+      const int tiles = (N + 63) / 64;
+      const int s = kTargetWorkgroups / tiles;
+      if (s >= 2 && tiles * s >= kTargetWorkgroups * 7 / 8 && nk / s >= 4) return plan_stream_split(M, N, K, 2, s);
+    }
+  }
   pl.bm = kBM;
   pl.bn = kBN;
   if (M > kBM && (size_t)((M + kBigBM - 1) / kBigBM) * ((N + kBN - 1) / kBN) >= (size_t)kTargetWorkgroups) {
@@ -1115,8 +1159,12 @@ hipError_t launch_stream_nw(const GemmArgs& p, const GemmPlan& pl, const WeightR
 }
 
 hipError_t launch_stream(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {
-  if (pl.stream_waves == kStreamWaves) return launch_stream_nw<kStreamWaves>(p, pl, W, stream);
-  return hipErrorInvalidValue;
+  switch (pl.stream_waves) {
+    case 8: return launch_stream_nw<8>(p, pl, W, stream);
+    case 5: return launch_stream_nw<5>(p, pl, W, stream);
+    case 2: return launch_stream_nw<2>(p, pl, W, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W, hipStream_t stream) {

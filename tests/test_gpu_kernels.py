@@ -38,6 +38,13 @@ def h(t):
     (30, 16640, 4096, True),    # N not a multiple of the 256-column workgroup
     (50, 32768, 2048, False),
     (128, 16384, 4096, True),
+    (100, 16500, 4096, False),  # the last 160-row workgroup partly past N
+    # deep projections at M <= 128: five wavefronts, K split 8 (the down projection's plan)
+    (128, 5120, 17408, False),
+    (70, 4960, 12800, True),    # N not a multiple of 160, ragged M
+    # mid-size projections at M <= 128: two wavefronts, K split to fill a round (o's plan)
+    (128, 5120, 4096, False),
+    (120, 4950, 4096, True),    # N not a multiple of 64
     # 256 x 256 workgroup tiles once they fill a round of 256 workgroups
     (512, 32768, 256, False),
     (300, 32868, 320, True),    # ragged M and N
