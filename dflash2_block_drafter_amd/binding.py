@@ -19,7 +19,7 @@ DFL_E_WORKSPACE, DFL_E_NOMEM, DFL_E_DEVICE = -4, -5, -6
 
 KERNEL_CLASSES = ["gemm_head", "gemm_gateup", "gemm_down", "gemm_qkv", "gemm_o", "gemm_kproj",
                   "gemm_selproj", "gemm_context", "attention", "conv_prepare", "conv_finish",
-                  "rmsnorm", "rope", "topk", "score_edges", "select_path"]
+                  "rmsnorm", "rope", "topk", "score_edges", "select_path", "select"]
 
 
 class DflError(RuntimeError):
@@ -110,6 +110,8 @@ _SIGS = {
     "dfl_selector_project": (_I, [_P, _I, _I, _P, _I, _P, _P, _Z, _P]),
     "dfl_score_edges": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dfl_tile_maxima": (_I, [_P, _I, _I, _P, _P]),
+    "dfl_select_tokens": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dfl_bind_target": (_I, [_P, _P, _P, _I, _P]),
     "dfl_context_append_workspace_bytes": (_Z, [_P, _I, _I]),
     "dfl_linear_q4": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _I, _P, _Z, _P]),
@@ -411,6 +413,16 @@ def dfl_score_edges(cand, unary, z, anchors, B, S, K, R, pred, succ, V, scores, 
 
 def dfl_select_path(scores, cand, B, S, K, tokens, stream=None):
     _check(lib().dfl_select_path(_f32(scores), _i32(cand), B, S, K, _i32(tokens), _stream(stream)))
+
+
+def dfl_tile_maxima(logits, N, V, tile_max, stream=None):
+    _check(lib().dfl_tile_maxima(_f32(logits), N, V, _f32(tile_max), _stream(stream)))
+
+
+def dfl_select_tokens(logits, tile_max, B, S, V, K, z, R, anchors, pred, succ, cand, unary, scores, tokens,
+                      stream=None):
+    _check(lib().dfl_select_tokens(_f32(logits), _f32(tile_max), B, S, V, K, _f32(z), R, _i32(anchors), _bf(pred),
+                                   _bf(succ), _i32(cand), _f32(unary), _f32(scores), _i32(tokens), _stream(stream)))
 
 
 def dfl_bind_target(handle, lm_head, vocab_ids=None, stream=None):

@@ -882,6 +882,25 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
     return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
   }));
   if (trace) DFL_TRY(snap(trace->z, z, (size_t)N * R * sizeof(float), stream));
+  // with the tile maxima in hand, the selection (top-k, edge scores, walk) is one launch when
+  // its per-request state fits one workgroup's LDS
+  const bool fused_select = tiles_fused && dfl::select_tokens_fits(S, Kc, R);
+  if (fused_select) {
+    DFL_TRY(timed(d, DFL_K_SELECT, 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) + 4.0 * N * R +
+                                       2.0 * 2 * N * Kc * R + 4.0 * N * Kc * (Kc + 2),
+                  stream, [&] {
+      return dfl::launch_select_tokens(logits, tmax, B, S, V_, Kc, id_map, z, R, anchors, d->pred, d->succ, c.vocab,
+                                       cand, unary, scores, tokens, stream);
+    }));
+    if (trace) {
+      DFL_TRY(snap(trace->tile_max, tmax, (size_t)N * ((V_ + dfl::kGemmTileN - 1) / dfl::kGemmTileN) * sizeof(float),
+                   stream));
+      DFL_TRY(snap(trace->cand, cand, (size_t)N * Kc * sizeof(int32_t), stream));
+      DFL_TRY(snap(trace->unary, unary, (size_t)N * Kc * sizeof(float), stream));
+      DFL_TRY(snap(trace->scores, scores, (size_t)N * Kc * Kc * sizeof(float), stream));
+    }
+    return DFL_OK;
+  }
   DFL_TRY(timed(d, DFL_K_TOPK, tiles_fused ? 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) : 4.0 * N * V_,
                 stream, [&] {
     return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map)
@@ -1123,6 +1142,29 @@ int dfl_score_edges(const int32_t* cand, const float* unary, const float* z, con
   DFL_REQUIRE(B > 0 && S > 0 && K > 0 && R > 0 && V > 0, DFL_E_INVALID, "sizes must be positive");
   DFL_REQUIRE(K <= 32 && R <= 128, DFL_E_UNSUPPORTED, "K <= 32 and R <= 128 required");
   hipError_t e = dfl::launch_score_edges(cand, unary, z, anchors, B, S, K, R, pred, succ, V, scores, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStream_t stream) {
+  DFL_REQUIRE(logits && tile_max, DFL_E_INVALID, "NULL argument");
+  DFL_REQUIRE(N > 0 && V > 0, DFL_E_INVALID, "sizes must be positive");
+  hipError_t e = dfl::launch_tile_maxima(logits, N, V, tile_max, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K, const float* z, int R,
+                      const int32_t* anchors, const dfl_bf16* pred, const dfl_bf16* succ, int32_t* cand,
+                      float* unary, float* scores, int32_t* tokens, hipStream_t stream) {
+  DFL_REQUIRE(logits && tile_max && z && anchors && pred && succ && cand && unary && tokens, DFL_E_INVALID,
+              "NULL argument");
+  DFL_REQUIRE(B > 0 && S > 0 && V > 0 && K > 0 && R > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= V, DFL_E_UNSUPPORTED, "K=%d exceeds V=%d", K, V);
+  DFL_REQUIRE(dfl::select_tokens_fits(S, K, R), DFL_E_UNSUPPORTED,
+              "S=%d, K=%d, R=%d: this call needs S <= 64, K <= 16 and R a multiple of 4 in [4, 64]", S, K, R);
+  hipError_t e = dfl::launch_select_tokens(logits, tile_max, B, S, V, K, nullptr, z, R, anchors, pred, succ, V, cand,
+                                           unary, scores, tokens, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

@@ -169,6 +169,8 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
 // id_map (device, optional): the reported id of column c is id_map[c] (a draft vocabulary).
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
                              int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map = nullptr);
+// Row maxima of every kGemmTileN-column tile of fp32 logits [N, V] -> [N, ceil(V / kGemmTileN)].
+hipError_t launch_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStream_t stream);
 // Exact top-K of each fp32 row (value descending, id ascending): tile maxima into ws
 // (topk_ws_bytes), then launch_topk_tiles.
 size_t topk_ws_bytes(int N, int V);
@@ -185,6 +187,16 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
                               const int32_t* anchors, int B, int S, int K, int R,
                               const uint16_t* pred, const uint16_t* succ, int V, float* scores,
                               hipStream_t stream);
+// Top-K from tile maxima (topk_tiles_kernel), then score_edges and the greedy walk of B
+// requests of S slots in one more launch (one workgroup per request, the scores on the matrix
+// cores): logits [B*S, V] with tile maxima [B*S, ceil(V/256)], z [B*S, R]; cand/unary
+// [B*S, K] and tokens [B, S] out, scores [B*S, K, K] out when not NULL.  Requires
+// select_tokens_fits(S, K, R): S <= 64, K <= 16, R a multiple of 4 in [4, 64].
+bool select_tokens_fits(int S, int K, int R);
+hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
+                                const int32_t* id_map, const float* z, int R, const int32_t* anchors,
+                                const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,
+                                float* scores, int32_t* tokens, hipStream_t stream);
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
                               int32_t* tokens, hipStream_t stream);
 

@@ -532,6 +532,163 @@ __global__ __launch_bounds__(64) void select_path_kernel(const float* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Edge scores of one slot on the matrix cores: S[p][c] = unary[c] + sum_r (pred[pid_p][r] *
+// z[r]) * succ[cid_c][r] for p, c < K <= 16 is a [16 x R] . [R x 16] product in fp32
+// (v_mfma_f32_16x16x4_f32, R/4 steps).  Lane l supplies row / column l % 16 for the R/4
+// consecutive r from (R/4) (l / 16), one per step (the order in which the products of a
+// sum are added is free), so its codebook and z values are contiguous runs: 16-byte loads
+// when R = 64 and the codebooks are 16-byte aligned.  pred * z is rounded to fp32 as one
+// product, as in the row-by-row form.  The lane ends with S[4 (l / 16) + e][l % 16], e =
+// 0..3.  Every lane of the wavefront takes part; ids are clamped into [0, V) by the caller.
+constexpr int kMfmaMaxK = 16;
+constexpr int kMfmaMaxR = 64;
+
+__device__ __forceinline__ f32x4_t slot_scores_mfma(const uint16_t* __restrict__ pred,
+                                                    const uint16_t* __restrict__ succ, int pid, int cid,
+                                                    const float* __restrict__ zrow, int K, int R, int lane) {
+  constexpr int QM = kMfmaMaxR / 4;
+  const int i = lane & 15, kq = lane >> 4;
+  const bool live = i < K;
+  const int pi = __shfl(pid, i, 64), ci = __shfl(cid, i, 64);
+  const int RQ = R / 4, r0 = kq * RQ;
+  float a[QM], bv[QM];
+  const uint16_t* prow = pred + (size_t)pi * R + r0;
+  const uint16_t* srow = succ + (size_t)ci * R + r0;
+  const float* zr = zrow + r0;
+  const bool vec = R == kMfmaMaxR &&
+                   ((reinterpret_cast<uintptr_t>(pred) | reinterpret_cast<uintptr_t>(succ) |
+                     reinterpret_cast<uintptr_t>(zrow)) & 15) == 0;
+  if (vec) {
+    u32x4_t pv[2], sv[2];
+    f32x4_t zv[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pv[h] = *reinterpret_cast<const u32x4_t*>(prow + 8 * h);
+      sv[h] = *reinterpret_cast<const u32x4_t*>(srow + 8 * h);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) zv[h] = *reinterpret_cast<const f32x4_t*>(zr + 4 * h);
+    float pf[QM], sf[QM];
+    unpack8(pv[0], pf);
+    unpack8(pv[1], pf + 8);
+    unpack8(sv[0], sf);
+    unpack8(sv[1], sf + 8);
+#pragma unroll
+    for (int q = 0; q < QM; ++q) {
+      a[q] = live ? pf[q] * zv[q >> 2][q & 3] : 0.f;
+      bv[q] = live ? sf[q] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < QM; ++q)
+      if (q < RQ) {
+        a[q] = live ? bf16_to_f32(prow[q]) * zr[q] : 0.f;
+        bv[q] = live ? bf16_to_f32(srow[q]) : 0.f;
+      }
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < QM; ++q)
+    if (q < RQ) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q], bv[q], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ bool mfma_scores_fit(int K, int R) {
+  return K >= 1 && K <= kMfmaMaxK && R >= 4 && R <= kMfmaMaxR && R % 4 == 0;
+}
+
+// The edge scores and the walk of B requests in one launch: one workgroup per request, one
+// wavefront per slot (slots l = wave, wave + kSelWaves, ...).  Each wavefront scores its slot
+// on the matrix cores and keeps, for every predecessor p, the lowest candidate c of maximum
+// score; after a barrier one lane walks those argmaxima from predecessor 0.  Candidates come
+// from the top-k (their ids index the codebooks), scores are also written out when asked.
+constexpr int kSelWaves = 16;
+constexpr int kSelMaxS = 64;
+
+__global__ __launch_bounds__(kSelWaves * 64) void edges_walk_kernel(
+    const int32_t* __restrict__ cand, const float* __restrict__ unary, const float* __restrict__ z, int R,
+    const int32_t* __restrict__ anchors, int S, int K, const uint16_t* __restrict__ pred,
+    const uint16_t* __restrict__ succ, int V, float* __restrict__ scores_out, int32_t* __restrict__ tokens) {
+  __shared__ int best_s[kSelMaxS][kMfmaMaxK];
+  __shared__ int cand_s[kSelMaxS][kMfmaMaxK];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  auto clampv = [V](int t) { return t < 0 ? 0 : (t >= V ? V - 1 : t); };
+  for (int l = wave; l < S; l += kSelWaves) {
+    const size_t row = (size_t)b * S + l;
+    int cid = 0, pid = 0, craw = 0;
+    float u = 0.f;
+    if (lane < K) {
+      craw = cand[row * K + lane];
+      cid = clampv(craw);
+      pid = clampv(l == 0 ? anchors[b] : cand[(row - 1) * K + lane]);
+      u = unary[row * K + lane];
+    }
+    const f32x4_t acc = slot_scores_mfma(pred, succ, pid, cid, z + row * R, K, R, lane);
+    const int c = lane & 15;
+    const float uc = __shfl(u, c, 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * (lane >> 4) + e;
+      const float sc = uc + acc[e];
+      if (scores_out && p < K && c < K) scores_out[row * K * K + p * K + c] = sc;
+      // argmax over the 16 lanes of this row of the tile (lowest c on ties; c >= K never wins)
+      float bv = c < K ? sc : -INFINITY;
+      int bc = c;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oc = __shfl_xor(bc, off, 64);
+        if (before(ov, oc, bv, bc)) {
+          bv = ov;
+          bc = oc;
+        }
+      }
+      if (c == 0 && p < K) best_s[l][p] = bc;
+    }
+    if (lane < K) cand_s[l][lane] = craw;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int j = 0;
+    for (int l = 0; l < S; ++l) {
+      j = best_s[l][j];
+      tokens[(size_t)b * S + l] = cand_s[l][j];
+    }
+  }
+}
+
+// score_edges on the matrix cores, one wavefront per (b, l) slot, four slots per workgroup:
+// the same arithmetic as edges_walk_kernel's scores.
+__global__ __launch_bounds__(256) void score_edges_mfma_kernel(
+    const int32_t* __restrict__ cand, const float* __restrict__ unary, const float* __restrict__ z,
+    const int32_t* __restrict__ anchors, int S, int K, int R, const uint16_t* __restrict__ pred,
+    const uint16_t* __restrict__ succ, int V, float* __restrict__ scores) {
+  const int lane = threadIdx.x & 63;
+  const int l = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (l >= S) return;
+  auto clampv = [V](int t) { return t < 0 ? 0 : (t >= V ? V - 1 : t); };
+  const size_t row = (size_t)b * S + l;
+  int cid = 0, pid = 0;
+  float u = 0.f;
+  if (lane < K) {
+    cid = clampv(cand[row * K + lane]);
+    pid = clampv(l == 0 ? anchors[b] : cand[(row - 1) * K + lane]);
+    u = unary[row * K + lane];
+  }
+  const f32x4_t acc = slot_scores_mfma(pred, succ, pid, cid, z + row * R, K, R, lane);
+  const int c = lane & 15;
+  const float uc = __shfl(u, c, 64);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int p = 4 * (lane >> 4) + e;
+    if (p < K && c < K) scores[row * K * K + p * K + c] = uc + acc[e];
+  }
+}
+
 }  // namespace
 
 size_t topk_static_scratch_floats() { return kStaticScratchFloats; }
@@ -585,6 +742,14 @@ hipError_t launch_topk(const float* logits, int N, int V, int K, int32_t* ids, f
   return launch_topk_tiles(logits, N, V, K, tmax, ids, vals, stream, id_map);
 }
 
+hipError_t launch_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
+  const int waves = (ntiles + kRowmaxTiles - 1) / kRowmaxTiles;
+  tile_rowmax_kernel<<<dim3((waves + 3) / 4, N), 256, 0, stream>>>(logits, V, ntiles, tile_max);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
                              int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map) {
   if (N <= 0) return hipSuccess;
@@ -599,6 +764,11 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
                               hipStream_t stream) {
   if (B <= 0 || S <= 0) return hipSuccess;
   if (K > 32 || R > 128) return hipErrorInvalidValue;
+  if (K <= kMfmaMaxK && R >= 4 && R <= kMfmaMaxR && R % 4 == 0) {
+    score_edges_mfma_kernel<<<dim3((S + 3) / 4, B), 256, 0, stream>>>(cand, unary, z, anchors, S, K, R, pred, succ, V,
+                                                                      scores);
+    return hipGetLastError();
+  }
   // wavefronts per workgroup: up to 4 slots, within 64 KB of LDS
   const size_t per_wave = (2 * (size_t)K * (R + 1) + R) * sizeof(float);
   const int nw = (int)std::max<size_t>(1, std::min<size_t>(4, (64 << 10) / per_wave));
@@ -611,6 +781,30 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
     score_edges_kernel<false><<<grid, 64 * nw, per_wave * nw, stream>>>(cand, unary, z, anchors, S, K, R, pred, succ,
                                                                         V, scores);
   return hipGetLastError();
+}
+
+bool select_tokens_fits(int S, int K, int R) {
+  return S >= 1 && S <= kSelMaxS && K >= 1 && K <= kMfmaMaxK && R >= 4 && R <= kMfmaMaxR && R % 4 == 0;
+}
+
+hipError_t launch_edges_walk(const int32_t* cand, const float* unary, const float* z, int R, const int32_t* anchors,
+                             int B, int S, int K, const uint16_t* pred, const uint16_t* succ, int V, float* scores,
+                             int32_t* tokens, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  if (!select_tokens_fits(S, K, R)) return hipErrorInvalidValue;
+  edges_walk_kernel<<<B, kSelWaves * 64, 0, stream>>>(cand, unary, z, R, anchors, S, K, pred, succ, V, scores, tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
+                                const int32_t* id_map, const float* z, int R, const int32_t* anchors,
+                                const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,
+                                float* scores, int32_t* tokens, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  if (!select_tokens_fits(S, K, R)) return hipErrorInvalidValue;
+  hipError_t e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map);
+  if (e != hipSuccess) return e;
+  return launch_edges_walk(cand, unary, z, R, anchors, B, S, K, pred, succ, Vcb, scores, tokens, stream);
 }
 
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,

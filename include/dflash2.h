@@ -377,6 +377,24 @@ int dfl_score_edges(const int32_t* cand, const float* unary, const float* z,
 int dfl_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
                     int32_t* tokens, hipStream_t stream);
 
+/* The selection of B requests in one launch ([P3] `compute_candidates`, `score_edges` and
+ * `select_path`; [P2] `#select`): for each request's S slots the top-K of the logits (value
+ * descending, id ascending), the edge scores and the greedy walk, with the same results as
+ * dfl_compute_candidates, dfl_score_edges and dfl_select_path called in turn.
+ *   logits:   [B*S, V] fp32;  tile_max: [B*S, ceil(V/256)] fp32, each row's maximum over every
+ *             256-column tile (dfl_tile_maxima);  z: [B*S, R] fp32 (dfl_selector_project);
+ *   anchors:  [B] int32;  pred, succ: [V, R] bf16;
+ *   cand, unary: [B*S, K] out;  scores: [B*S, K, K] out, or NULL;  tokens: [B, S] out.
+ * Requires S <= 64, K <= 16 and R a multiple of 4 in [4, 64] (DFL_E_UNSUPPORTED otherwise:
+ * the three calls above cover every size).  Ids outside [0, V) are clamped for the codebook
+ * reads, as in dfl_score_edges.  Two launches: the top-k, then the edge scores (fp32 on the
+ * matrix cores, as dfl_score_edges computes them for these sizes) and the walk. */
+int dfl_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStream_t stream);
+int dfl_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
+                      const float* z, int R, const int32_t* anchors, const dfl_bf16* pred,
+                      const dfl_bf16* succ, int32_t* cand, float* unary, float* scores,
+                      int32_t* tokens, hipStream_t stream);
+
 /* ---- measurement ---- */
 
 /* Kernel classes whose launches can be bracketed with HIP events. */
@@ -385,7 +403,7 @@ enum dfl_kernel_class {
   DFL_K_GEMM_HEAD = 0, DFL_K_GEMM_GATEUP, DFL_K_GEMM_DOWN, DFL_K_GEMM_QKV, DFL_K_GEMM_O,
   DFL_K_GEMM_KPROJ, DFL_K_GEMM_SELPROJ, DFL_K_GEMM_CONTEXT, DFL_K_ATTENTION, DFL_K_CONV_PREPARE,
   DFL_K_CONV_FINISH, DFL_K_RMSNORM, DFL_K_ROPE, DFL_K_TOPK, DFL_K_SCORE_EDGES,
-  DFL_K_SELECT_PATH, DFL_K_COUNT
+  DFL_K_SELECT_PATH, DFL_K_SELECT, DFL_K_COUNT
 };
 
 /* Bracket every later launch of class `k` made through `d` with a pair of HIP events on

@@ -66,6 +66,13 @@ def test_validation_errors_before_any_launch():
     assert L.dfl_compute_candidates_static(P, 1082, 248320, 16, P, P, None) == B.DFL_E_WORKSPACE
     assert L.dfl_compute_candidates_static(P, 4, 100, 40, P, P, None) == B.DFL_E_UNSUPPORTED
     assert L.dfl_compute_candidates_static(None, 4, 100, 4, P, P, None) == B.DFL_E_INVALID
+    # the fused selection: K above 16, R not a multiple of 4 or above 64, more than 64 slots
+    sel = lambda S, K, R, pred=P: L.dfl_select_tokens(P, P, 2, S, 1000, K, P, R, P, pred, P, P, P, None, P, None)
+    assert sel(15, 32, 64) == B.DFL_E_UNSUPPORTED
+    assert sel(15, 16, 62) == B.DFL_E_UNSUPPORTED
+    assert sel(15, 16, 128) == B.DFL_E_UNSUPPORTED
+    assert sel(65, 16, 64) == B.DFL_E_UNSUPPORTED
+    assert sel(15, 16, 64, pred=None) == B.DFL_E_INVALID
     # null pointers
     assert L.dfl_select_path(None, P, 1, 1, 4, P, None) == B.DFL_E_INVALID
     # K not a multiple of 64
