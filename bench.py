@@ -376,9 +376,8 @@ def bench_conv(steps: int, warmup: int) -> dict:
 
 def bench_selector(steps: int, warmup: int) -> dict:
     """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
-    Timed: the tile maxima of the logits (dfl_tile_maxima) with the selector projection
-    (dfl_selector_project) forked onto a second stream beside it, then dfl_select_tokens (top-k,
-    edge scores and walk), over two input sets (0.95 GB of logits, more than the 256 MB
+    Timed: the selector projection (dfl_selector_project), the tile maxima of the logits
+    (dfl_tile_maxima), then dfl_select_tokens (top-k, edge scores and walk), over two input sets (0.95 GB of logits, more than the 256 MB
     Infinity Cache), captured into a HIP graph and replayed.  Also timed the same way: the
     single-step chain (compute_candidates, selector_project, score_edges, select_path in turn)."""
     import torch
@@ -399,16 +398,12 @@ def bench_selector(steps: int, warmup: int) -> dict:
                      "tokens": torch.empty((Bq, S), dtype=torch.int32, device="cuda")})
     ws_c = B_.workspace(B_.dfl_candidates_workspace_bytes(N, V, K))
     ws_p = B_.workspace(B_.dfl_selector_project_workspace_bytes(N, H, R))
-    side = torch.cuda.Stream()
-
     def fused(st):
+        # (forking the projection onto a second stream beside the tile pass measured slower:
+        # the cross-queue fork and join cost about 20 us a chain, more than the overlap buys)
         inp = st["inp"]
-        main = torch.cuda.current_stream()
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            B_.dfl_selector_project(st["hidden"], N, H, inp["proj"], R, st["z"], ws_p)
+        B_.dfl_selector_project(st["hidden"], N, H, inp["proj"], R, st["z"], ws_p)
         B_.dfl_tile_maxima(st["logits"], N, V, st["tmax"])
-        main.wait_stream(side)
         B_.dfl_select_tokens(st["logits"], st["tmax"], Bq, S, V, K, st["z"], R, inp["anchors"], inp["pred"],
                              inp["succ"], st["ids"], st["unary"], st["scores"], st["tokens"])
 
@@ -439,8 +434,8 @@ def bench_selector(steps: int, warmup: int) -> dict:
         "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": warmup,
         "higher_is_better": False, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16; "
-                               "2 input sets rotated, graph-replayed chain (tile maxima with the projection on a "
-                               "forked stream, then the one-call selection)"},
+                               "2 input sets rotated, graph-replayed chain (projection, tile maxima, then the "
+                               "two-launch selection)"},
         "roofline": {"kernel": "selector chain", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},
