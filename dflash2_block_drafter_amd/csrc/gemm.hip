@@ -325,6 +325,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
   }
 }
 
+// MINB is the minimum number of wavefronts per SIMD the registers must allow (the second
+// launch bound); the 128 x 64 instance takes 1, since its LDS admits two 2-wavefront
+// workgroups per CU, one wavefront per SIMD.
 template <int BM, int BN, int BKS, int WM, int WN, int PF, int MINB, bool TILED, bool Q4 = false>
 __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NT = WM * WN * 64;
@@ -426,14 +429,14 @@ __global__ __launch_bounds__(WM* WN * 64, MINB) void gemm_bf16_kernel(GemmArgs p
 // At these row counts a projection reads each weight once, at 128 flop per bf16 weight
 // byte, so it should run at HBM speed; what costs time in the LDS kernel above is staging
 // the weight tile through LDS (a write and four reads of every weight) and, for the wide
-// projections, having fewer 128 x 256 tiles than CUs.  Here each wavefront owns 64 weight
+// projections, having fewer 128 x 256 tiles than CUs.  Here each wavefront owns 32 weight
 // rows and all M rows of the output: its weight fragments go from HBM straight into MFMA
 // operand registers (the tile-contiguous layout is the operand order, so each load is 1 KB
 // contiguous per wavefront) and only the activations, shared by the NW wavefronts of a
-// workgroup, pass through LDS.  A stage (one 64-wide K step of the activations and of the
-// wave's weights) is loaded PF - 1 steps ahead into a register ring; one barrier per step.
-// Workgroups of NW = 2 wavefronts, at one wavefront per SIMD, let two workgroups share a CU
-// on separate SIMDs, so a grid of up to 512 workgroups is resident at once.
+// workgroup, pass through LDS.  A weight stage (one 64-wide K step of the wave's rows) is
+// loaded PF steps ahead into a register ring and the activations AD steps ahead into LDS;
+// one barrier per step.  The plan picks NW (8, 5 or 2 wavefronts) and the K split so that
+// the grid fills about one round of CUs; two wavefronts share a SIMD (256 registers each).
 
 // A wavefront's weights for one K step: 32 weight rows = 2 fragments of 16 rows x 2 K
 // halves.  LOADS is the number of vector-memory instructions load() issues.
@@ -681,9 +684,10 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
 }
 
 // NW wavefronts per workgroup, 32 weight rows each, two wavefronts per SIMD (256 registers
-// each), so while one waits the other computes.
+// each), so while one waits the other computes.  A 2-wavefront workgroup's LDS admits two
+// per CU, one wavefront per SIMD, so that instance asks for one.
 template <int MT, int NW, int PF, int AD, bool TILED, bool Q4>
-__global__ __launch_bounds__(NW * 64, 2) void gemm_stream_kernel(GemmArgs p) {
+__global__ __launch_bounds__(NW * 64, NW >= 4 ? 2 : 1) void gemm_stream_kernel(GemmArgs p) {
   constexpr int MR = MT * 16;
   // AD: activation steps in flight ahead of the one being computed (AD + 1 LDS buffers)
   __shared__ __attribute__((aligned(16))) uint16_t sA[AD + 1][MR * 64];
@@ -1197,9 +1201,9 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
   if (pl.bn == kNarrowBN && !W.q) {
     const dim3 grid((p.N + kNarrowBN - 1) / kNarrowBN, (p.M + kBM - 1) / kBM, pl.splits);
     if (W.tiled)
-      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 2, true><<<grid, 128, 0, stream>>>(p);
+      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 1, true><<<grid, 128, 0, stream>>>(p);
     else
-      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 2, false><<<grid, 128, 0, stream>>>(p);
+      gemm_bf16_kernel<kBM, kNarrowBN, BK, 2, 1, 2, 1, false><<<grid, 128, 0, stream>>>(p);
     return hipGetLastError();
   }
   // (4-bit weights keep 256-column workgroups under a narrow plan: the same K splits)
