@@ -595,7 +595,10 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   const int kb0 = blockIdx.z * (p.k_per_split / 64);               // first 64-deep K block of this split
   const int nkb = (min(p.K, (blockIdx.z + 1) * p.k_per_split) - blockIdx.z * p.k_per_split) / 64;
   const int nst = 2 * nkb;  // K halves
-  const int rot = nkb > 0 ? static_cast<int>((ntile * kKRotate) % static_cast<unsigned>(nkb)) : 0;
+  // No staggered start here (unlike the 128-row kernels): with every workgroup of an XCD at
+  // the same K block, the activation block they share stays in that XCD's L2; staggered,
+  // the whole activation slab (up to 10 MB) is read from the Infinity Cache instead, and every
+  // projection measured 4-5% slower.
   // wavefront w copies fragments 2w and 2w + 1 of both tiles every step
   const int fa = 2 * wave;
   const int fk = (lane >> 4) * 8;
@@ -612,8 +615,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   auto issue = [&](int st, int slot) {
     const int s = min(st, nst - 1);
     const int h = s & 1;
-    int kb = (s >> 1) + rot;  // K block within the split
-    kb = kb >= nkb ? kb - nkb : kb;
+    const int kb = s >> 1;  // K block within the split
     const int k0 = (kb0 + kb) * 64 + h * 32;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
