@@ -332,18 +332,29 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
                                  pos0, d->window[li], B, G, NH, NKV, D, Lmax, ao, NH * D, W + lay.attn, stream);
   }));
   if (tr) DFL_TRY(snap(tr->attn, ao, (size_t)T * NH * D * sizeof(uint16_t), stream));
-  // o and down keep a separate split-K reduce: their consumer, the residual conv + norm,
-  // runs one workgroup per row and reads bf16 rows far faster than it could sum planes
+  // A split o or down projection leaves its fp32 planes to the residual conv + norm, which
+  // sums each row's planes itself (and rounds the sum to bf16 as the reduce would), so the
+  // split-K reduce launch goes away; the bf16 output u is then only written under tracing.
+  const bool o_planes = p_o.splits > 1 && H <= dfl::kCrnPlanesMaxH;
   DFL_TRY(timed(d, DFL_K_GEMM_O, gemm_bytes(T, H, NH * D, dfl::EPI_BF16, d->q4), stream, [&] {
-    return dfl::launch_gemm(p_o, ao, NH * D, wref(L.o, L.o_q4), T, H, NH * D, dfl::EPI_BF16, u, H, nullptr, 0, 0,
-                            part, stream);
+    return o_planes ? dfl::launch_gemm_partials(p_o, ao, NH * D, wref(L.o, L.o_q4), T, H, NH * D, part, stream)
+                    : dfl::launch_gemm(p_o, ao, NH * D, wref(L.o, L.o_q4), T, H, NH * D, dfl::EPI_BF16, u, H,
+                                       nullptr, 0, 0, part, stream);
   }));
-  if (tr) DFL_TRY(snap(tr->u, u, rowsH, stream));
+  const dfl::Planes o_pl{part, p_o.splits, H, (size_t)T * H};
+  if (tr) {
+    if (o_planes) DFL_HIP(dfl::launch_planes_sum_bf16(o_pl, T, H, u, stream));
+    DFL_TRY(snap(tr->u, u, rowsH, stream));
+  }
   // x = x_in + conv1(u), fused with the MLP half's input norm
-  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-    return dfl::launch_conv_residual_norm(u, coef1, L.attn_base, T, H, G, c.conv_group, xin, x, L.post_norm,
-                                          c.rms_eps, n, stream);
-  }));
+  DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H + (o_planes ? 4.0 * T * H * p_o.splits : 0.0), stream,
+                [&] {
+                  return o_planes ? dfl::launch_conv_residual_norm_planes(o_pl, coef1, L.attn_base, T, H, G,
+                                                                          c.conv_group, xin, x, L.post_norm,
+                                                                          c.rms_eps, n, stream)
+                                  : dfl::launch_conv_residual_norm(u, coef1, L.attn_base, T, H, G, c.conv_group,
+                                                                   xin, x, L.post_norm, c.rms_eps, n, stream);
+                }));
   if (tr) {
     DFL_TRY(snap(tr->x_mid, x, rowsH, stream));
     DFL_TRY(snap(tr->m, n, rowsH, stream));
@@ -365,18 +376,31 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
                             0, 0, part, stream);
   }));
   if (tr) DFL_TRY(snap(tr->p, p, (size_t)T * F * sizeof(uint16_t), stream));
+  const bool d_planes = p_dn.splits > 1 && next_gamma && H <= dfl::kCrnPlanesMaxH;
   DFL_TRY(timed(d, DFL_K_GEMM_DOWN, gemm_bytes(T, H, F, dfl::EPI_BF16, d->q4), stream, [&] {
-    return dfl::launch_gemm(p_dn, p, F, wref(L.down, L.down_q4), T, H, F, dfl::EPI_BF16, u, H, nullptr, 0, 0, part,
-                            stream);
+    return d_planes ? dfl::launch_gemm_partials(p_dn, p, F, wref(L.down, L.down_q4), T, H, F, part, stream)
+                    : dfl::launch_gemm(p_dn, p, F, wref(L.down, L.down_q4), T, H, F, dfl::EPI_BF16, u, H, nullptr,
+                                       0, 0, part, stream);
   }));
-  if (tr) DFL_TRY(snap(tr->f, u, rowsH, stream));
+  const dfl::Planes d_pl{part, p_dn.splits, H, (size_t)T * H};
+  if (tr) {
+    if (d_planes) DFL_HIP(dfl::launch_planes_sum_bf16(d_pl, T, H, u, stream));
+    DFL_TRY(snap(tr->f, u, rowsH, stream));
+  }
   if (next_gamma) {
     // the next layer's input norm, or (head_rows set) the final norm of rows 1..G-1, packed
     // for the head
-    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H, stream, [&] {
-      return dfl::launch_conv_residual_norm(u, coef1, L.mlp_base, T, H, G, c.conv_group, x, x, next_gamma,
-                                            c.rms_eps, head_rows ? head_rows : n, stream, head_rows != nullptr);
-    }));
+    uint16_t* nrows = head_rows ? head_rows : n;
+    const bool pack = head_rows != nullptr;
+    DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H + (d_planes ? 4.0 * T * H * p_dn.splits : 0.0),
+                  stream, [&] {
+                    return d_planes ? dfl::launch_conv_residual_norm_planes(d_pl, coef1, L.mlp_base, T, H, G,
+                                                                            c.conv_group, x, x, next_gamma,
+                                                                            c.rms_eps, nrows, stream, pack)
+                                    : dfl::launch_conv_residual_norm(u, coef1, L.mlp_base, T, H, G, c.conv_group,
+                                                                     x, x, next_gamma, c.rms_eps, nrows, stream,
+                                                                     pack);
+                  }));
   } else {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
       return dfl::launch_conv(u, coef1, L.mlp_base, 1, T, H, G, c.conv_group, x, x, stream);

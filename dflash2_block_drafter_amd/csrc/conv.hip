@@ -264,6 +264,136 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
   }
 }
 
+// Sums of 8 channels at two element offsets over the planes, in plane order (the order the
+// split-K reduce adds them).  With the plane count S a compile-time constant every load is
+// issued before the first add (one round trip); S = 0 takes the count from pl.S, a batch of
+// eight planes at a time.
+template <int S>
+__device__ __forceinline__ void planes_sum8_pair(const Planes& pl, size_t off0, size_t off1, float* s0, float* s1) {
+  const float* q = pl.p;
+  if constexpr (S > 0) {
+    f32x4_t v[S][4];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const size_t po = (size_t)i * pl.plane;
+      v[i][0] = *reinterpret_cast<const f32x4_t*>(q + po + off0);
+      v[i][1] = *reinterpret_cast<const f32x4_t*>(q + po + off0 + 4);
+      v[i][2] = *reinterpret_cast<const f32x4_t*>(q + po + off1);
+      v[i][3] = *reinterpret_cast<const f32x4_t*>(q + po + off1 + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s0[e] = v[0][0][e];
+      s0[4 + e] = v[0][1][e];
+      s1[e] = v[0][2][e];
+      s1[4 + e] = v[0][3][e];
+    }
+#pragma unroll
+    for (int i = 1; i < S; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s0[e] += v[i][0][e];
+        s0[4 + e] += v[i][1][e];
+        s1[e] += v[i][2][e];
+        s1[4 + e] += v[i][3][e];
+      }
+  } else {
+    for (int b = 0; b < pl.S; b += 8) {
+      f32x4_t v[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const size_t po = (size_t)min(b + i, pl.S - 1) * pl.plane;
+        v[i][0] = *reinterpret_cast<const f32x4_t*>(q + po + off0);
+        v[i][1] = *reinterpret_cast<const f32x4_t*>(q + po + off0 + 4);
+        v[i][2] = *reinterpret_cast<const f32x4_t*>(q + po + off1);
+        v[i][3] = *reinterpret_cast<const f32x4_t*>(q + po + off1 + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (b + i >= pl.S) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s0[e] = b + i == 0 ? v[i][0][e] : s0[e] + v[i][0][e];
+          s0[4 + e] = b + i == 0 ? v[i][1][e] : s0[4 + e] + v[i][1][e];
+          s1[e] = b + i == 0 ? v[i][2][e] : s1[e] + v[i][2][e];
+          s1[4 + e] = b + i == 0 ? v[i][3][e] : s1[4 + e] + v[i][3][e];
+        }
+      }
+    }
+  }
+}
+
+// At most 640 threads (H <= 5120): three wavefronts per SIMD leave a thread the registers
+// for eight planes' loads of both rows in flight at once.
+constexpr int kCrnPlanesMaxThreads = kCrnPlanesMaxH / 8;
+
+// conv_residual_norm_kernel with the sublayer output y given as its projection's split-K
+// planes (o or down) instead of the reduced bf16 rows: each thread sums its 8 channels of
+// rows t and t - 1 over the planes and rounds them to bf16, which is exactly what the
+// split-K reduce would have stored, so no separate reduce launch is needed.  One thread per
+// 8 channels (H / 8 threads, rounded up to whole wavefronts), so a thread's plane loads for
+// both rows go out as one round per batch of eight planes.
+template <int S>
+__global__ __launch_bounds__(kCrnPlanesMaxThreads) void conv_residual_norm_planes_kernel(
+    Planes y, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
+    const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
+    uint16_t* __restrict__ n_out, int skip_anchor) {
+  __shared__ float red[kCrnPlanesMaxThreads / 64];
+  __shared__ float cs[2 * kCrnPlanesMaxThreads];  // the row's groups: H / grp <= H / 8
+  // Workgroups are dealt to the 8 XCDs in turn; rows are mapped so that each XCD gets a
+  // contiguous run of them, and row t's read of row t - 1's planes finds them in that XCD's
+  // L2 behind row t - 1's own reader.
+  const int T = gridDim.x;
+  const int t = T % 8 == 0 ? (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int tid = threadIdx.x;
+  const int chunks = H >> 3;
+  const int ng = H / grp;
+  const bool live = tid < chunks;
+  const int c0 = min(tid, chunks - 1) * 8;  // clamped: every load unconditional
+  const bool has_prev = t % G != 0;
+  const u32x4_t rv = *reinterpret_cast<const u32x4_t*>(residual + (size_t)t * H + c0);
+  const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(gamma + c0);
+  ConvIn in;
+  in.b0 = *reinterpret_cast<const u32x4_t*>(base + (size_t)2 * H + c0);
+  in.b1 = *reinterpret_cast<const u32x4_t*>(base + (size_t)3 * H + c0);
+  {
+    float cur[8], prev[8];
+    planes_sum8_pair<S>(y, (size_t)t * y.ld + c0, (size_t)(has_prev ? t - 1 : t) * y.ld + c0, cur, prev);
+    in.cur = pack8(cur);
+    in.prev = has_prev ? pack8(prev) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  stage_coef(coef, t, ng, 0, ng, cs);
+  float xv[8];
+  float ss = 0.f;
+  if (live) {
+    const int g = c0 / grp;
+    float o[8], r[8];
+    conv8(in, cs[g], cs[ng + g], o);
+    unpack8(rv, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = r[e] + o[e];
+    const u32x4_t packed = pack8(o);
+    *reinterpret_cast<u32x4_t*>(x_out + (size_t)t * H + c0) = packed;
+    unpack8(packed, xv);  // the norm reads the rounded residual, as a separate norm would
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += xv[e] * xv[e];
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  const int waves = (int)(blockDim.x >> 6);
+  for (int w = 0; w < waves; ++w) tot += red[w];
+  const float inv = rsqrtf(tot / static_cast<float>(H) + eps);
+  if (!live || (skip_anchor && t % G == 0)) return;
+  const size_t nrow = skip_anchor ? (size_t)(t / G) * (G - 1) + t % G - 1 : (size_t)t;
+  float gm[8], o[8];
+  unpack8(gv, gm);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = xv[e] * inv * gm[e];
+  *reinterpret_cast<u32x4_t*>(n_out + nrow * H + c0) = pack8(o);
+}
+
 }  // namespace
 
 hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
@@ -289,6 +419,32 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
     default:
       return hipErrorInvalidValue;  // H > 8192
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_residual_norm_planes(const Planes& y, const Planes& coef, const uint16_t* base, int T, int H,
+                                            int G, int grp, const uint16_t* residual, uint16_t* x_out,
+                                            const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
+                                            bool skip_anchor) {
+  if (T <= 0) return hipSuccess;
+  if (H % 8 != 0 || H > 8 * kCrnPlanesMaxThreads || y.S < 1 || y.ld != H || y.plane < (size_t)T * H)
+    return hipErrorInvalidValue;
+  const int threads = (H / 8 + 63) / 64 * 64;
+  const int sk = skip_anchor ? 1 : 0;
+#define DFL_CRN_PLANES(S_)                                                                              \
+  conv_residual_norm_planes_kernel<S_><<<T, threads, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, \
+                                                                  gamma, eps, n_out, sk)
+  switch (y.S) {
+    case 2: DFL_CRN_PLANES(2); break;
+    case 3: DFL_CRN_PLANES(3); break;
+    case 4: DFL_CRN_PLANES(4); break;
+    case 5: DFL_CRN_PLANES(5); break;
+    case 6: DFL_CRN_PLANES(6); break;
+    case 7: DFL_CRN_PLANES(7); break;
+    case 8: DFL_CRN_PLANES(8); break;
+    default: DFL_CRN_PLANES(0);
+  }
+#undef DFL_CRN_PLANES
   return hipGetLastError();
 }
 

@@ -1290,19 +1290,29 @@ hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, 
   return launch_main(p, pl, W, stream);
 }
 
-hipError_t launch_planes_sum(const Planes& src, int M, int N, float* out, hipStream_t stream) {
+namespace {
+hipError_t planes_sum_as(const Planes& src, int M, int N, int epi, void* out, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (src.ld != N || src.plane != (size_t)M * N || src.S < 1) return hipErrorInvalidValue;
   GemmArgs p = {};
   p.M = M;
   p.N = N;
-  p.epi = EPI_F32;
+  p.epi = epi;
   p.out0 = out;
   p.ld0 = N;
   p.nsplit = N;
   p.partial = const_cast<float*>(src.p);
   p.splits = src.S;
   return launch_reduce(p, stream);
+}
+}  // namespace
+
+hipError_t launch_planes_sum(const Planes& src, int M, int N, float* out, hipStream_t stream) {
+  return planes_sum_as(src, M, N, EPI_F32, out, stream);
+}
+
+hipError_t launch_planes_sum_bf16(const Planes& src, int M, int N, uint16_t* out, hipStream_t stream) {
+  return planes_sum_as(src, M, N, EPI_BF16, out, stream);
 }
 
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,

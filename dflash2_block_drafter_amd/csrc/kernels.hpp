@@ -80,6 +80,8 @@ inline Planes gemm_planes(const GemmPlan& pl, const float* partial, int M, int N
 }
 // Sum of S fp32 planes [M, N] (src.ld = N) into one plane `out` [M, N], added in plane order.
 hipError_t launch_planes_sum(const Planes& src, int M, int N, float* out, hipStream_t stream);
+// The same sum rounded to bf16 (what a split-K projection with bf16 output stores).
+hipError_t launch_planes_sum_bf16(const Planes& src, int M, int N, uint16_t* out, hipStream_t stream);
 
 // Tile-contiguous copy of a row-major [N, K] weight: one block per (256-row tile, 64-wide K
 // step), [ceil(N/256)][K/64][block], rows past N zero.  Inside a block the order is the
@@ -139,6 +141,16 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
                                      bool skip_anchor = false);
+
+// The same with y given as the fp32 split-K planes of its projection ([y.S][T][H], plane
+// stride y.plane >= T * H): each row's sum over the planes, in plane order, is rounded to
+// bf16 as the split-K reduce would store it, so the result equals reduce + the call above.
+// H <= kCrnPlanesMaxH.
+constexpr int kCrnPlanesMaxH = 5120;
+hipError_t launch_conv_residual_norm_planes(const Planes& y, const Planes& coef, const uint16_t* base, int T, int H,
+                                            int G, int grp, const uint16_t* residual, uint16_t* x_out,
+                                            const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
+                                            bool skip_anchor = false);
 
 // Grouped dynamic conv; side selects base[side]; residual may be null.  coef_next (side 0
 // only; coef then holds both sides, side 1 at column 2 * ng): also write side 1's summed
