@@ -94,6 +94,7 @@ struct dfl_drafter {
   const void* head_src = nullptr;    // the caller pointer it was copied from
   int head_cols = 0;                 // its rows: the vocabulary, or the listed draft vocabulary
   int32_t* head_ids = nullptr;       // device [head_cols] token ids of a draft vocabulary, else NULL
+  bool head_sel = false;             // the bound head also holds sel_proj's rows, one tile after its own
   int timed_class = DFL_K_NONE;
   std::vector<TimedLaunch> timed;
   std::vector<hipEvent_t> pool;
@@ -678,7 +679,12 @@ int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* voca
   }
   void* buf = nullptr;
   void* ids = nullptr;
-  const size_t bytes = dfl::tiled_weight_elems(cols, H) * sizeof(uint16_t);
+  // When the head's rows fill whole 256-row tiles, the selector projection's (already tiled)
+  // rows follow as one more tile, so a single launch writes the logits and z.
+  const bool with_sel = cols % dfl::kGemmTileN == 0;
+  const size_t head_bytes = dfl::tiled_weight_elems(cols, H) * sizeof(uint16_t);
+  const size_t sel_bytes = with_sel ? dfl::tiled_weight_elems(d->cfg.rank, H) * sizeof(uint16_t) : 0;
+  const size_t bytes = head_bytes + sel_bytes;
   if (hipMalloc(&buf, bytes) != hipSuccess ||
       (vocab_ids && hipMalloc(&ids, (size_t)cols * sizeof(int32_t)) != hipSuccess)) {
     (void)hipGetLastError();
@@ -689,6 +695,8 @@ int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* voca
   if (ids) e = hipMemcpyAsync(ids, vocab_ids, (size_t)cols * sizeof(int32_t), hipMemcpyHostToDevice, stream);
   if (e == hipSuccess)
     e = dfl::launch_tile_weights(lm_head, cols, H, static_cast<uint16_t*>(buf), stream, static_cast<int32_t*>(ids));
+  if (e == hipSuccess && with_sel)
+    e = hipMemcpyAsync(static_cast<char*>(buf) + head_bytes, d->sel_proj, sel_bytes, hipMemcpyDeviceToDevice, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     (void)hipFree(buf);
@@ -698,6 +706,7 @@ int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* voca
   d->head = static_cast<uint16_t*>(buf);
   d->head_src = lm_head;
   d->head_cols = cols;
+  d->head_sel = with_sel;
   d->head_ids = static_cast<int32_t*>(ids);
   return DFL_OK;
 }
@@ -878,7 +887,11 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
   float* logits = logits_out ? logits_out : f32(lay.logits);
   int32_t* cand = reinterpret_cast<int32_t*>(W + lay.cand);
   float* part = f32(lay.partial);
-  const dfl::GemmPlan p_head = dfl::plan_gemm(N, V_, H, true), p_sel = dfl::plan_gemm(N, R, H);
+  // A bound head holding the selector projection's rows after its own computes z in the same
+  // launch: columns [0, V_) go to the logits, the R after them to z.
+  const bool head_sel = bound_head && d->head_sel;
+  const int NHd = V_ + (head_sel ? R : 0);
+  const dfl::GemmPlan p_head = dfl::plan_gemm(N, NHd, H, true), p_sel = dfl::plan_gemm(N, R, H);
 
   const uint16_t* xin = embeds;
   for (int li = 0; li < c.layers; ++li) {
@@ -897,14 +910,16 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
   // over the logits.
   const bool tiles_fused = p_head.splits == 1;
   float* tmax = f32(lay.tmax);
-  DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, V_, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_head, h, H, bound_head ? d->head : lm_head, bound_head, N, V_, H, dfl::EPI_F32, logits,
-                            V_, nullptr, 0, 0, part, stream,
-                            tiles_fused ? tmax : nullptr);
+  DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, NHd, H, dfl::EPI_F32), stream, [&] {
+    return dfl::launch_gemm(p_head, h, H, bound_head ? d->head : lm_head, bound_head, N, NHd, H, dfl::EPI_F32, logits,
+                            V_, head_sel ? z : nullptr, R, V_, part, stream, tiles_fused ? tmax : nullptr);
   }));
-  DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part, stream);
-  }));
+  if (!head_sel) {
+    DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
+      return dfl::launch_gemm(p_sel, h, H, d->sel_proj, true, N, R, H, dfl::EPI_F32, z, R, nullptr, 0, 0, part,
+                              stream);
+    }));
+  }
   if (trace) DFL_TRY(snap(trace->z, z, (size_t)N * R * sizeof(float), stream));
   // with the tile maxima in hand, the selection (top-k, edge scores, walk) is one launch when
   // its per-request state fits one workgroup's LDS

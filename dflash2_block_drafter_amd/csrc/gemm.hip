@@ -56,7 +56,7 @@ struct GemmArgs {
   int nsplit;
   float* partial;
   int splits;
-  float* tile_max;  // EPI_F32, one split: [M, ceil(N / 256)] row maxima of each 256-column tile
+  float* tile_max;  // EPI_F32, one split: [M, ceil(nsplit / 256)] row maxima of each 256-column tile of out0
   // 4-bit affine weights (used instead of W): row-major packed [N, K/8] words with scales and
   // biases [N, K/64] bf16, or tile-contiguous blocks (q4_tiled_words)
   const uint32_t* Wq;
@@ -295,8 +295,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         const int n = ncol + j * 16;
         if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
       }
-  if (p.tile_max) {
-    // Row maxima of this tile over its columns < N: within a lane over its TN columns, then
+  if (p.tile_max && n0 < p.nsplit) {
+    // Row maxima of this tile over its first output's columns (< nsplit, which is N unless
+    // a second output takes the columns after it): within a lane over its TN columns, then
     // over the 16 lanes that share a row, then over the WN wavefronts through LDS.  fmaxf
     // skips NaN, so a tile's maximum is NaN only when all of its values are.
     __shared__ float rmax[WN][BM];
@@ -307,7 +308,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         float v = -INFINITY;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          if (ncol + j * 16 < p.N) v = fmaxf(v, acc[i][j][e]);
+          if (ncol + j * 16 < p.nsplit) v = fmaxf(v, acc[i][j][e]);
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
         if ((lane & 15) == 0) rmax[wn][wm * (TM * 16) + i * 16 + (lane >> 4) * 4 + e] = v;
@@ -319,7 +320,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         float v = rmax[0][r];
 #pragma unroll
         for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
-        p.tile_max[(size_t)m * ((p.N + kGemmTileN - 1) / kGemmTileN) + n0 / kGemmTileN] = v;
+        p.tile_max[(size_t)m * ((p.nsplit + kGemmTileN - 1) / kGemmTileN) + n0 / kGemmTileN] = v;
       }
     }
   }
@@ -883,8 +884,9 @@ constexpr size_t kSmallPartialBytes = size_t(16) << 20;
 // flop per LDS byte instead of 32 and LDS bandwidth stops bounding the matrix units as early.
 // One weight stage in flight keeps the 128 accumulators within 256 registers.
 constexpr int kBigBM = 256;
-constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;
-constexpr int kNarrowBN = 64, kNarrowMaxN = 2048, kNarrowAnyM = 256;  // 64-column workgroups for narrow projections  // big tiles with split K from these sizes
+constexpr int kBigSplitMinM = 512, kBigSplitMinN = 4096;  // big tiles with split K from these sizes
+// 64-column workgroups (LDS or streaming) for narrow projections
+constexpr int kNarrowBN = 64, kNarrowMaxN = 2048, kNarrowAnyM = 256, kNarrowStreamMinN = 512;
 constexpr int kStreamMaxM = 128, kStreamMaxSplits = 16;
 // Wavefronts of 32 weight rows, at most two per SIMD.  Every workgroup re-reads the activation
 // slab of its K range, so fewer, wider workgroups re-read less, while more workgroups bring
@@ -1084,10 +1086,21 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
     pl.partial_bytes = pl.splits > 1 ? (size_t)pl.splits * M * N * sizeof(float) : 0;
     return pl;
   }
-  // Narrow projections at M <= 128 (the kernel projection, N = 1280; the selector's, N = 64):
-  // 64-column workgroups of two wavefronts, two per CU, so that 20 column tiles x 12 K splits
-  // spread over the chip instead of 5 x 16 (each workgroup's short K loop is the time)
-  // (at any M when N <= 256: one 256-column tile would load mostly clamped duplicate rows)
+  // The kernel projection at M <= 128 (N = 1280): two-wavefront streaming workgroups of 64
+  // weight rows with K split to about three quarters of a round (20 x 10 = 200 workgroups).
+  // Measured in the draft block against the 128 x 64 LDS kernel with 12 splits: 1.691 ->
+  // 1.680 ms a step (8 splits: 1.686, 12: 1.688); fewer planes also shorten the conv that
+  // sums them.
+  if (!tile_max && M <= kBM && N >= kNarrowStreamMinN && N <= kNarrowMaxN && K % BK == 0) {
+    const int tiles = (N + 63) / 64;
+    int s = std::max(1, std::min(kMaxSplitsSmall, (kTargetWorkgroups * 3 / 4 + tiles - 1) / tiles));
+    while (s > 1 && K / BK / s < 4) --s;
+    return plan_stream_split(M, N, K, 2, s);
+  }
+  // Narrow projections at M <= 128 below that (the selector's, N = 64): 64-column
+  // workgroups of two wavefronts, two per CU, K split deep (each workgroup's short K loop is
+  // the time) (at any M when N <= 256: one 256-column tile would load mostly clamped
+  // duplicate rows)
   const bool narrow = !tile_max && ((M <= kBM && N <= kNarrowMaxN) || N <= kNarrowAnyM);
   if (narrow) pl.bn = kNarrowBN;
   const int tiles = ((M + kBM - 1) / kBM) * ((N + pl.bn - 1) / pl.bn);
@@ -1241,8 +1254,11 @@ hipError_t launch_reduce(const GemmArgs& p, hipStream_t stream) {
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
                        hipStream_t stream, float* tile_max) {
-  // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup)
-  if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0)) return hipErrorInvalidValue;
+  // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup); a
+  // tile may not straddle the two outputs
+  if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0 ||
+                   (out1 && nsplit % kGemmTileN != 0)))
+    return hipErrorInvalidValue;
   if (W.q && K % BK != 0) return hipErrorInvalidValue;
   if (pl.tail_n > 0 && pl.splits == 1 && !tile_max && !W.q && !out1 && pl.tail_n < N) {
     // the full rounds: weight rows [0, tail_n) into the matching output columns

@@ -61,7 +61,8 @@ hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint1
 // to out0 (ld0), the rest to out1 (ld1) when out1 != nullptr.  EPI_SILU_MUL: W rows
 // interleaved per 16 as [gate|up]; out0 bf16 [M, N/2] = silu(gate) * up.
 // tile_max (EPI_F32 with an unsplit plan only): also write the row maxima of every
-// kGemmTileN-column tile, [M, ceil(N / kGemmTileN)].
+// kGemmTileN-column tile of out0's columns, [M, ceil(nsplit / kGemmTileN)] (nsplit = N
+// without out1; with out1, nsplit must be a multiple of kGemmTileN).
 constexpr int kGemmTileN = 256;
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,

@@ -124,7 +124,9 @@ def test_wide_head_on_big_tiles():
 
 def test_bound_head_matches_borrowed_head():
     # binding the target's head (a tile-contiguous copy) changes how the head projection
-    # reads it, not what it computes: tokens and logits are identical bit for bit
+    # reads it, not what it computes: the logits are identical bit for bit.  The bound copy
+    # also carries the selector projection's rows, so z then comes out of the head's launch
+    # (the same sums in another fp32 order); the tokens agree on these seeded inputs.
     from dflash2_block_drafter_amd import binding as B_
     w = configs.with_batch(configs.TINY, 3)
     dr, _, _, K, V, tokens, logits = _run_tiny(w)
