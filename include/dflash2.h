@@ -173,7 +173,10 @@ size_t dfl_draft_workspace_bytes(const dfl_drafter* d, int B, int G, int Lmax);
  * `DraftProjection.vocabulary`), n_vocab distinct token ids in [0, V), top_k <= n_vocab: only
  * those rows are copied, drafts that use the bound head project onto them (logits_out then
  * has n_vocab columns, in list order) and their candidates are the listed ids.  NULL: the
- * whole vocabulary.  Synchronises `stream`.  Errors: a second call with another pointer or
+ * whole vocabulary.  When the copied rows fill whole 256-row tiles, the copy also holds the
+ * drafter's selector projection after them, so drafts with the bound head compute z in the
+ * head's launch (the same products, summed in another fp32 order than the separate
+ * projection).  Synchronises `stream`.  Errors: a second call with another pointer or
  * vocabulary -> DFL_E_INVALID (the same binding again is a no-op); bad ids -> DFL_E_INVALID;
  * n_vocab out of range -> DFL_E_SHAPE; allocation -> DFL_E_NOMEM; HIP failure ->
  * DFL_E_DEVICE. */
