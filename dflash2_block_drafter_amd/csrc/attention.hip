@@ -152,6 +152,12 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       vm_wait<(R - 1) * LOADS>(vr[i]);
     }
   };
+  // V^T row r (dim r) holds the tile's 64 keys as 32 dwords with the key pairs rotated by
+  // 2 * (r / 16) dwords: the 16 lanes of one store instruction write the same key slot of
+  // dims 8 apart, which without the rotation fall on two bank pairs (rows 8 apart are 272
+  // dwords apart); the fragment reads of rows 16 dt .. 16 dt + 15 share one rotation, so they
+  // keep their conflict-free row stride.
+  auto vt_dw = [](int r, int key_dw) { return r * (VS / 2) + ((key_dw + 2 * (r >> 4)) & 31); };
   auto tile_store = [&](const u32x4_t (&kr)[ROWS_PER], const u32x4_t (&vr)[ROWS_PER]) {
 #pragma unroll
     for (int i = 0; i < ROWS_PER; ++i)
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       uint32_t h[ROWS_PER];
 #pragma unroll
       for (int i = 0; i < ROWS_PER; ++i) h[i] = (vr[i][e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      uint16_t* dst = &Vt[(dg * 8 + e) * VS + kg * ROWS_PER];
+      uint16_t* dst = &Vt[2 * vt_dw(dg * 8 + e, kg * ROWS_PER / 2)];
       if constexpr (ROWS_PER == 4) {
         *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
       } else {
@@ -240,9 +246,9 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vrow = &Vt[(dt * 16 + (lane & 15)) * VS + ks * 32 + lg * 4];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+        const int r = dt * 16 + (lane & 15);
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(&Vt[2 * vt_dw(r, ks * 16 + lg * 2)]);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(&Vt[2 * vt_dw(r, ks * 16 + 8 + lg * 2)]);
         const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
                                                         o[dt], 0, 0, 0);
