@@ -376,9 +376,10 @@ def bench_conv(steps: int, warmup: int) -> dict:
 
 def bench_selector(steps: int, warmup: int) -> dict:
     """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
-    Timed: the selector projection (dfl_selector_project), the tile maxima of the logits
-    (dfl_tile_maxima), then dfl_select_tokens (top-k, edge scores and walk), over two input sets (0.95 GB of logits, more than the 256 MB
-    Infinity Cache), captured into a HIP graph and replayed.  Also timed the same way: the
+    Timed: the selector projection (dfl_selector_project), then dfl_select_tokens without tile
+    maxima (each row's workgroup scans its logits and takes its top-k; then edge scores and
+    walk), over two input sets (0.95 GB of logits, more than the 256 MB Infinity Cache),
+    captured into a HIP graph and replayed.  Also timed the same way: the
     single-step chain (compute_candidates, selector_project, score_edges, select_path in turn)."""
     import torch
     from dflash2_block_drafter_amd import binding as B_
@@ -390,7 +391,6 @@ def bench_selector(steps: int, warmup: int) -> dict:
     for i in range(2):
         inp = synth.selector_inputs(Bq, S, H, K, V, R, c["seed"] + i, device="cuda")
         sets.append({"inp": inp, "logits": inp["logits"].reshape(N, V), "hidden": inp["hidden"].reshape(N, H),
-                     "tmax": torch.empty((N, (V + 255) // 256), dtype=torch.float32, device="cuda"),
                      "ids": torch.empty((N, K), dtype=torch.int32, device="cuda"),
                      "unary": torch.empty((N, K), dtype=torch.float32, device="cuda"),
                      "z": torch.empty((N, R), dtype=torch.float32, device="cuda"),
@@ -399,12 +399,12 @@ def bench_selector(steps: int, warmup: int) -> dict:
     ws_c = B_.workspace(B_.dfl_candidates_workspace_bytes(N, V, K))
     ws_p = B_.workspace(B_.dfl_selector_project_workspace_bytes(N, H, R))
     def fused(st):
-        # (forking the projection onto a second stream beside the tile pass measured slower:
-        # the cross-queue fork and join cost about 20 us a chain, more than the overlap buys)
+        # (forking the projection onto a second stream beside the scan measured slower: the
+        # cross-queue fork and join cost about 20 us a chain, more than the overlap buys)
         inp = st["inp"]
         B_.dfl_selector_project(st["hidden"], N, H, inp["proj"], R, st["z"], ws_p)
-        B_.dfl_tile_maxima(st["logits"], N, V, st["tmax"])
-        B_.dfl_select_tokens(st["logits"], st["tmax"], Bq, S, V, K, st["z"], R, inp["anchors"], inp["pred"],
+        # no tile maxima: each row's workgroup scans its logits and takes its top-k at once
+        B_.dfl_select_tokens(st["logits"], None, Bq, S, V, K, st["z"], R, inp["anchors"], inp["pred"],
                              inp["succ"], st["ids"], st["unary"], st["scores"], st["tokens"])
 
     def steps_chain(st):
@@ -434,8 +434,8 @@ def bench_selector(steps: int, warmup: int) -> dict:
         "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": warmup,
         "higher_is_better": False, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16; "
-                               "2 input sets rotated, graph-replayed chain (projection, tile maxima, then the "
-                               "two-launch selection)"},
+                               "2 input sets rotated, graph-replayed chain (projection, then the two-launch "
+                               "selection: per-row scan + top-k, edge scores + walk)"},
         "roofline": {"kernel": "selector chain", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},

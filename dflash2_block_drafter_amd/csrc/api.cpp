@@ -1196,12 +1196,14 @@ int dfl_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStrea
 int dfl_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K, const float* z, int R,
                       const int32_t* anchors, const dfl_bf16* pred, const dfl_bf16* succ, int32_t* cand,
                       float* unary, float* scores, int32_t* tokens, hipStream_t stream) {
-  DFL_REQUIRE(logits && tile_max && z && anchors && pred && succ && cand && unary && tokens, DFL_E_INVALID,
-              "NULL argument");
+  DFL_REQUIRE(logits && z && anchors && pred && succ && cand && unary && tokens, DFL_E_INVALID, "NULL argument");
   DFL_REQUIRE(B > 0 && S > 0 && V > 0 && K > 0 && R > 0, DFL_E_INVALID, "sizes must be positive");
   DFL_REQUIRE(K <= V, DFL_E_UNSUPPORTED, "K=%d exceeds V=%d", K, V);
   DFL_REQUIRE(dfl::select_tokens_fits(S, K, R), DFL_E_UNSUPPORTED,
               "S=%d, K=%d, R=%d: this call needs S <= 64, K <= 16 and R a multiple of 4 in [4, 64]", S, K, R);
+  DFL_REQUIRE(tile_max || (V + dfl::kGemmTileN - 1) / dfl::kGemmTileN <= dfl::kSelectScanMaxTiles, DFL_E_UNSUPPORTED,
+              "without tile maxima V=%d needs at most %d tiles of %d columns", V, dfl::kSelectScanMaxTiles,
+              dfl::kGemmTileN);
   hipError_t e = dfl::launch_select_tokens(logits, tile_max, B, S, V, K, nullptr, z, R, anchors, pred, succ, V, cand,
                                            unary, scores, tokens, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));

@@ -206,6 +206,9 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
 // [B*S, K] and tokens [B, S] out, scores [B*S, K, K] out when not NULL.  Requires
 // select_tokens_fits(S, K, R): S <= 64, K <= 16, R a multiple of 4 in [4, 64].
 bool select_tokens_fits(int S, int K, int R);
+// launch_select_tokens without tile maxima (tile_max = nullptr): each row's workgroup scans
+// its logits, keeping the row's tile maxima in LDS, so ceil(V / 256) <= kSelectScanMaxTiles.
+constexpr int kSelectScanMaxTiles = 4096;
 hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
                                 const int32_t* id_map, const float* z, int R, const int32_t* anchors,
                                 const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,

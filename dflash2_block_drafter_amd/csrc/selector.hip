@@ -103,11 +103,11 @@ __device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*l
   mg.flush();
 }
 
-__global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict__ logits, int V,
-                                                         const float* __restrict__ tile_max, int ntiles,
-                                                         int K, int32_t* __restrict__ ids,
-                                                         float* __restrict__ vals,
-                                                         const int32_t* __restrict__ id_map) {
+// The top-K of one row given its tile maxima tm (in global memory, or in LDS), for one
+// 256-thread workgroup: the body of topk_tiles_kernel and of topk_scan_kernel.
+__device__ __forceinline__ void topk_row(const float* tm, const float* __restrict__ src, int V, int ntiles, int K,
+                                         int row, int32_t* __restrict__ ids, float* __restrict__ vals,
+                                         const int32_t* __restrict__ id_map) {
   constexpr int TW = kGemmTileN;
   constexpr int TPL = TW / 64;                 // values of a tile per lane
   constexpr int CH = 64 * kTmPerLane;          // tile maxima per round
@@ -120,9 +120,6 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
   __shared__ int tcount;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int row = blockIdx.x;
-  const float* tm = tile_max + (size_t)row * ntiles;
-  const float* src = logits + (size_t)row * V;
   TopkMerger mg;
 
   // theta: the K-th largest tile maximum; wavefront w merges slots w, w+4, w+8, ... of a round
@@ -308,6 +305,100 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
     ids[(size_t)row * K + lane] = id_map && col >= 0 && col < V ? id_map[col] : col;
     vals[(size_t)row * K + lane] = mg.v;
   }
+}
+
+__global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict__ logits, int V,
+                                                         const float* __restrict__ tile_max, int ntiles,
+                                                         int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ vals,
+                                                         const int32_t* __restrict__ id_map) {
+  const int row = blockIdx.x;
+  topk_row(tile_max + (size_t)row * ntiles, logits + (size_t)row * V, V, ntiles, K, row, ids, vals, id_map);
+}
+
+// Maximum over each aligned group of 16 lanes, left in every lane of the group, with DPP
+// lane moves inside the registers (no LDS round trip): the row's mirror, the half-row's
+// mirror, then the two quad permutations that swap neighbours and pairs.
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  return v;
+}
+
+// Top-K of each row straight from the logits: one 256-thread workgroup per row scans the
+// whole row once (each round, 4 wavefronts x 16 tiles of 256 columns, 16 lanes a tile; the
+// next round's loads are issued before this round's reduction), keeps the row's tile maxima
+// in LDS and then runs topk_row on them.  Every row's top-K thus runs as soon as its own
+// scan ends, beside the other rows' scans, instead of in a launch after all of them.
+constexpr int kScanMaxTiles = kSelectScanMaxTiles;
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void topk_scan_kernel(const float* __restrict__ logits, int V, int ntiles, int K,
+                                                        int32_t* __restrict__ ids, float* __restrict__ vals,
+                                                        const int32_t* __restrict__ id_map) {
+  constexpr int TQ = kGemmTileN / 64;  // float4 per lane per tile
+  constexpr int PASS = 4;              // tiles per 16-lane group per round
+  constexpr int ROUND = 4 * 4 * PASS;  // tiles per round: 4 wavefronts x 4 groups x PASS
+  __shared__ float tms[kScanMaxTiles];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const int row = blockIdx.x;
+  const float* src = logits + (size_t)row * V;
+  // tile of (round c, pass p) for this lane's group
+  auto tile_of = [&](int c, int p) { return c * ROUND + (wave * PASS + p) * 4 + q; };
+  // Every load is unconditional, at an address clamped into the row (tiles past the last and
+  // columns past V re-read valid ones), so no branch separates a round's loads and the next
+  // round's stay in flight while this one is reduced; the clamped values are replaced by
+  // -inf after the wait.
+  auto load_round = [&](int c, f32x4_t (&v)[PASS][TQ]) {
+#pragma unroll
+    for (int p = 0; p < PASS; ++p) {
+      const int t = min(tile_of(c, p), ntiles - 1);
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        const int col = t * kGemmTileN + j * 64 + l16 * 4;
+        if constexpr (VEC) {
+          // read once: non-temporal, so the stream does not evict what later kernels reuse
+          v[p][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + min(col, V - 4)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[p][j][e] = src[min(col + e, V - 1)];
+        }
+      }
+    }
+  };
+  auto reduce_round = [&](int c, const f32x4_t (&v)[PASS][TQ]) {
+#pragma unroll
+    for (int p = 0; p < PASS; ++p) {
+      const int t = tile_of(c, p);
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < TQ; ++j) {
+        const int col = t * kGemmTileN + j * 64 + l16 * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, t < ntiles && col + e < V ? v[p][j][e] : -INFINITY);
+      }
+      m = max16(m);
+      if (l16 == 0 && t < ntiles) tms[t] = m;
+    }
+  };
+  // two rounds in flight: the next round's loads go out (clamped past the end) before this
+  // round is reduced
+  const int rounds = (ntiles + ROUND - 1) / ROUND;
+  f32x4_t va[PASS][TQ], vb[PASS][TQ];
+  load_round(0, va);
+  for (int c = 0; c < rounds; c += 2) {
+    load_round(c + 1, vb);
+    reduce_round(c, va);
+    load_round(c + 2, va);
+    reduce_round(c + 1, vb);
+  }
+  __syncthreads();
+  topk_row(tms, src, V, ntiles, K, row, ids, vals, id_map);
 }
 
 // score_edges, one wavefront per (b, l) slot, NW wavefronts per workgroup.  Three memory
@@ -802,7 +893,19 @@ hipError_t launch_select_tokens(const float* logits, const float* tile_max, int 
                                 float* scores, int32_t* tokens, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
   if (!select_tokens_fits(S, K, R)) return hipErrorInvalidValue;
-  hipError_t e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map);
+  hipError_t e;
+  if (tile_max) {
+    e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map);
+  } else {
+    // no tile maxima given: each row's workgroup scans its logits and then takes its top-K
+    const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
+    if (ntiles > kScanMaxTiles) return hipErrorInvalidValue;
+    if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
+      topk_scan_kernel<true><<<B * S, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map);
+    else
+      topk_scan_kernel<false><<<B * S, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   return launch_edges_walk(cand, unary, z, R, anchors, B, S, K, pred, succ, Vcb, scores, tokens, stream);
 }

@@ -385,7 +385,10 @@ int dfl_select_path(const float* scores, const int32_t* cand, int B, int S, int 
  * descending, id ascending), the edge scores and the greedy walk, with the same results as
  * dfl_compute_candidates, dfl_score_edges and dfl_select_path called in turn.
  *   logits:   [B*S, V] fp32;  tile_max: [B*S, ceil(V/256)] fp32, each row's maximum over every
- *             256-column tile (dfl_tile_maxima);  z: [B*S, R] fp32 (dfl_selector_project);
+ *             256-column tile (dfl_tile_maxima), or NULL: then one workgroup per row scans that
+ *             row's logits, keeps its tile maxima on chip and takes its top-k as soon as its
+ *             scan ends (ceil(V/256) <= 4096, else DFL_E_UNSUPPORTED);
+ *             z: [B*S, R] fp32 (dfl_selector_project);
  *   anchors:  [B] int32;  pred, succ: [V, R] bf16;
  *   cand, unary: [B*S, K] out;  scores: [B*S, K, K] out, or NULL;  tokens: [B, S] out.
  * Requires S <= 64, K <= 16 and R a multiple of 4 in [4, 64] (DFL_E_UNSUPPORTED otherwise:

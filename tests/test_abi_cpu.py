@@ -73,6 +73,9 @@ def test_validation_errors_before_any_launch():
     assert sel(15, 16, 128) == B.DFL_E_UNSUPPORTED
     assert sel(65, 16, 64) == B.DFL_E_UNSUPPORTED
     assert sel(15, 16, 64, pred=None) == B.DFL_E_INVALID
+    # without tile maxima the row's scan keeps them on chip: at most 4096 tiles (V <= 2^20)
+    assert L.dfl_select_tokens(P, None, 2, 15, 4096 * 256 + 1, 16, P, 64, P, P, P, P, P, None, P,
+                               None) == B.DFL_E_UNSUPPORTED
     # null pointers
     assert L.dfl_select_path(None, P, 1, 1, 4, P, None) == B.DFL_E_INVALID
     # K not a multiple of 64

@@ -1,6 +1,7 @@
-"""The one-launch selection (top-k from tile maxima, score_edges and the walk) against the
-three single-step calls and against the oracle: candidates and their logits bit for bit,
-scores at the fp32 bar, tokens bit for bit given the scores."""
+"""The two-launch selection (top-k from tile maxima or from its own scan of the logits, then
+score_edges and the walk) against the three single-step calls and against the oracle:
+candidates and their logits bit for bit, scores at the fp32 bar, tokens bit for bit given
+the scores."""
 import numpy as np
 import pytest
 import torch
@@ -60,10 +61,18 @@ def test_select_tokens_matches_steps_and_oracle(Bq, S, V, K, R, kind):
     B.dfl_score_edges(c2, u2, z, anchors, Bq, S, K, R, pred, succ, V, s2)
     t2 = torch.empty_like(tokens)
     B.dfl_select_path(s2, c2, Bq, S, K, t2)
+    # without tile maxima: one workgroup per row scans its logits, then takes its top-k
+    c3 = torch.full_like(cand, -1)
+    u3 = torch.full_like(unary, float("nan"))
+    s3 = torch.full_like(scores, float("nan"))
+    t3 = torch.full_like(tokens, -1)
+    B.dfl_select_tokens(logits, None, Bq, S, V, K, z, R, anchors, pred, succ, c3, u3, s3, t3)
     torch.cuda.synchronize()
     assert torch.equal(cand, c2) and torch.equal(unary, u2)
     assert torch.equal(scores, s2), "edge scores differ from dfl_score_edges"
     assert torch.equal(tokens, t2)
+    assert torch.equal(cand, c3) and torch.equal(unary, u3), "the scanning top-k differs"
+    assert torch.equal(scores, s3) and torch.equal(tokens, t3)
     # the oracle
     lg = logits.cpu().numpy()
     rows = np.arange(N) if N <= 96 else np.linspace(0, N - 1, 96).astype(int)
