@@ -186,7 +186,8 @@ def test_block_attention_sliding_window(D, NH, NKV, G, ctx, pos, window):
     assert_bf16_close(out.reshape(Bq, G, NH, D), want, "sliding-window attention")
 
 
-@pytest.mark.parametrize("T,H,G,grp", [(64, 512, 16, 16), (1024, 5120, 16, 16), (24, 256, 8, 16)])
+@pytest.mark.parametrize("T,H,G,grp", [(64, 512, 16, 16), (1024, 5120, 16, 16), (1024, 5120, 8, 16),
+                                        (24, 256, 8, 16)])  # 1024 rows: 8-row workgroups, blocks of 16 and 8
 def test_conv_prepare_finish(T, H, G, grp):
     x = bf((T, H), 51)
     kp = bf((4 * H // grp, H), 52, std=0.02)
