@@ -3,10 +3,11 @@
 //
 // Top-k (value descending, id ascending) is guided by the row maxima of 256-column tiles,
 // which the head projection writes with its logits (a separate pass computes them for
-// logits from elsewhere).  theta, the K-th largest tile maximum, is reached by K distinct
-// logits, so every top-K logit is >= theta and sits in a tile whose maximum is >= theta;
-// only those tiles are read (usually K of a row's V/256).  Their values >= theta (usually K
-// to 2K) are gathered and sorted once when there are at most 64; otherwise they are merged
+// logits from elsewhere).  theta, the K-th largest maximum over K disjoint groups of tiles,
+// is reached by K distinct logits, so every top-K logit is >= theta and sits in a tile whose
+// maximum is >= theta; only those tiles are read (usually K to 2K of a row's V/256).  Their
+// values >= theta (usually K to 2K) are gathered and sorted once when there are at most
+// 64; otherwise they are merged
 // into a running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes
 // K..63 take new candidates).  Ties are ordered by id, so the result is exact and unique for
 // any input, including constant rows (where every tile qualifies).
@@ -76,18 +77,27 @@ __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restric
   }
 }
 
-// Top-K of a row from its tile maxima (tiles of kGemmTileN columns).  theta, the K-th
-// largest tile maximum in candidate order, is a value that K distinct logits reach, so
-// every top-K logit is >= theta and lies in a tile whose maximum is >= theta: only those
-// tiles (ties included) are scanned.  One workgroup of four wavefronts per row.  Tile
-// maxima are read 64 * kTmPerLane at a time into registers (one round of loads); the four
-// wavefronts each merge a quarter of them and wavefront 0 merges the four lists into theta;
-// then the qualifying tiles are listed in LDS and each wavefront loads kTilesInFlight of
-// them at once.  With one round of tile maxima, their values >= theta are gathered into LDS
+// Top-K of a row from its tile maxima (tiles of kGemmTileN columns).  theta is a value that
+// K distinct logits reach, so every top-K logit is >= theta and lies in a tile whose maximum
+// is >= theta: only those tiles (ties included) are scanned.  One workgroup of four
+// wavefronts per row.  Wavefront 0 reads the tile maxima 64 * kTmPerLane at a time (one
+// round of loads) into 256 group maxima and takes their K-th largest as theta by ballots
+// (no sorting); then the qualifying tiles are listed in LDS and each wavefront loads
+// kTilesInFlight of them at once.  With one round of tile maxima, their values >= theta are gathered into LDS
 // and, when at most 64, sorted once by wavefront 0; otherwise (and for longer rows) each
 // wavefront merges its tiles into its own list and wavefront 0 merges the four lists.
 constexpr int kTmPerLane = 16;
 constexpr int kTilesInFlight = 4;
+
+// Order-preserving map of a float to an unsigned integer (NaN excluded by the callers), and
+// back.
+__device__ __forceinline__ uint32_t float_order(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b & 0x80000000u ? ~b : b | 0x80000000u;
+}
+__device__ __forceinline__ float order_float(uint32_t u) {
+  return __uint_as_float(u & 0x80000000u ? u & 0x7FFFFFFFu : ~u);
+}
 
 // Merge lanes 0..K-1 of the other three wavefronts' lists (lv/li) into wavefront 0's list.
 __device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*lv)[64], const int (*li)[64],
@@ -122,40 +132,43 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
   const int wave = threadIdx.x >> 6;
   TopkMerger mg;
 
-  // theta: the K-th largest tile maximum; wavefront w merges slots w, w+4, w+8, ... of a round
-  mg.init(K, lane, sv[wave], si[wave]);
-  for (int c0 = 0; c0 < ntiles; c0 += CH) {
-    float t[kTmPerLane / 4];
-#pragma unroll
-    for (int j = 0; j < kTmPerLane / 4; ++j) {
-      const int i = c0 + (j * 4 + wave) * 64 + lane;
-      t[j] = i < ntiles ? tm[i] : -INFINITY;
-    }
-    // floor: the K-th largest lane maximum, reached by K of this round's values, so only
-    // values >= it are offered (a handful, instead of a whole first batch)
-    float lm = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kTmPerLane / 4; ++j) lm = fmaxf(lm, t[j]);
-    int lid = lane;
-    wave_bitonic_sort(lm, lid, lane);
-    const float floor_v = __shfl(lm, K - 1, 64);
-#pragma unroll
-    for (int j = 0; j < kTmPerLane / 4; ++j) {
-      const int i = c0 + (j * 4 + wave) * 64 + lane;
-      const float kth = __shfl(mg.v, K - 1, 64);
-      const int kthi = __shfl(mg.id, K - 1, 64);
-      const bool take = i < ntiles && t[j] >= floor_v && before(t[j], i, kth, kthi);
-      if (__ballot(take)) mg.offer(take, t[j], i);
-    }
-  }
-  mg.flush();
-  lv[wave][lane] = mg.v;
-  li[wave][lane] = mg.id;
-  __syncthreads();
+  // theta: a value that K distinct logits reach, as large as cheaply found.  Wavefront 0's
+  // lane L keeps four group maxima, group (L, i) holding the tiles L + 64 (i + 4k); the K-th
+  // largest of the 256 group maxima is reached by K distinct logits (one in each of K
+  // disjoint groups), so every top-K logit is >= it, and with <= 256 tiles it is the K-th
+  // largest tile maximum itself.  It is found bit by bit in an order-preserving integer map
+  // of the floats (the largest u with at least K group maxima >= u): ballots, no sorting.
+  // -inf with fewer than K groups (every tile then qualifies).
   if (wave == 0) {
-    merge_wave_lists(mg, lv, li, K, lane);
-    const float th = __shfl(mg.v, K - 1, 64);  // -inf when fewer than K tiles
-    if (lane == 0) theta_s = th;              // (the shuffle itself runs on every lane)
+    float g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g[i] = __builtin_nanf("");  // NaN: empty (fmaxf skips NaN)
+    for (int c0 = 0; c0 < ntiles; c0 += CH) {
+      float t[kTmPerLane];
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) {
+        const int i = c0 + j * 64 + lane;
+        t[j] = i < ntiles ? tm[i] : __builtin_nanf("");
+      }
+#pragma unroll
+      for (int j = 0; j < kTmPerLane; ++j) g[j & 3] = fmaxf(g[j & 3], t[j]);
+    }
+    uint32_t u[4];
+    int groups = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u[i] = g[i] == g[i] ? float_order(g[i]) : 0u;
+      groups += __popcll(__ballot(g[i] == g[i]));
+    }
+    uint32_t cu = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t tryu = cu | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n += __popcll(__ballot(g[i] == g[i] && u[i] >= tryu));
+      if (n >= K) cu = tryu;
+    }
+    if (lane == 0) theta_s = groups >= K ? order_float(cu) : -INFINITY;
   }
   __syncthreads();
   const float theta = theta_s;

@@ -24,6 +24,14 @@ def _inputs(Bq, S, V, K, R, kind, seed):
     elif kind == "few_hot":       # K hot values in one tile, the rest low
         logits[:] = -5.0
         logits[:, 300:300 + K] = torch.arange(K, device=DEV, dtype=torch.float32)
+    elif kind == "hot_ties":      # 80 equal maxima in 80 tiles: more than 64 values reach theta
+        logits[:, 1000:1000 + 3001 * 80:3001] = 20.0
+    elif kind == "negative":      # every logit far below zero, tile maxima not integers
+        logits -= 50.0
+    elif kind == "neg_inf":       # mostly -inf, a finite value every 997 columns
+        finite = logits[:, ::997].clone()
+        logits[:] = float("-inf")
+        logits[:, ::997] = finite
     z = synth.normal((Bq * S, R), 0.0, 1.0, seed=seed + 1, device=DEV, dtype=torch.float32)
     pred = synth.normal((V, R), 0.0, 0.5, seed=seed + 2, device=DEV)
     succ = synth.normal((V, R), 0.0, 0.5, seed=seed + 3, device=DEV)
@@ -40,6 +48,9 @@ def _inputs(Bq, S, V, K, R, kind, seed):
     (3, 4, 20000, 16, 64, "few_hot"),
     (4, 1, 3000, 2, 8, "normal"),         # one slot
     (1, 63, 4096, 16, 64, "normal"),      # more slots than wavefronts
+    (2, 3, 248320, 16, 64, "hot_ties"),
+    (2, 5, 70000, 16, 64, "neg_inf"),
+    (4, 15, 248320, 16, 64, "negative"),
 ])
 def test_select_tokens_matches_steps_and_oracle(Bq, S, V, K, R, kind):
     print(f"[select] B={Bq} S={S} V={V} K={K} R={R} {kind}", flush=True)
