@@ -376,10 +376,10 @@ def bench_conv(steps: int, warmup: int) -> dict:
 
 def bench_selector(steps: int, warmup: int) -> dict:
     """Candidate-selector microbenchmark: B=32 requests, S=15 slots, V=248320, K=16, R=64.
-    Timed: the selector projection (dfl_selector_project), then dfl_select_tokens without tile
-    maxima (each row's workgroup scans its logits and takes its top-k; then edge scores and
-    walk), over two input sets (0.95 GB of logits, more than the 256 MB Infinity Cache),
-    captured into a HIP graph and replayed.  Also timed the same way: the
+    Timed: dfl_select_tokens_projected (the selector projection in extra workgroups of the
+    launch in which each row's workgroup scans its logits and takes its top-k; then edge
+    scores and walk), over two input sets (0.95 GB of logits, more than the 256 MB Infinity
+    Cache), captured into a HIP graph and replayed.  Also timed the same way: the
     single-step chain (compute_candidates, selector_project, score_edges, select_path in turn)."""
     import torch
     from dflash2_block_drafter_amd import binding as B_
@@ -399,13 +399,12 @@ def bench_selector(steps: int, warmup: int) -> dict:
     ws_c = B_.workspace(B_.dfl_candidates_workspace_bytes(N, V, K))
     ws_p = B_.workspace(B_.dfl_selector_project_workspace_bytes(N, H, R))
     def fused(st):
-        # (forking the projection onto a second stream beside the scan measured slower: the
-        # cross-queue fork and join cost about 20 us a chain, more than the overlap buys)
+        # the projection's workgroups run in the scan's launch (forking it onto a second
+        # stream measured slower: the cross-queue fork and join cost about 20 us a chain)
         inp = st["inp"]
-        B_.dfl_selector_project(st["hidden"], N, H, inp["proj"], R, st["z"], ws_p)
-        # no tile maxima: each row's workgroup scans its logits and takes its top-k at once
-        B_.dfl_select_tokens(st["logits"], None, Bq, S, V, K, st["z"], R, inp["anchors"], inp["pred"],
-                             inp["succ"], st["ids"], st["unary"], st["scores"], st["tokens"])
+        B_.dfl_select_tokens_projected(st["logits"], Bq, S, V, K, st["hidden"], H, inp["proj"], R, st["z"],
+                                       inp["anchors"], inp["pred"], inp["succ"], st["ids"], st["unary"],
+                                       st["scores"], st["tokens"])
 
     def steps_chain(st):
         inp = st["inp"]
@@ -434,8 +433,8 @@ def bench_selector(steps: int, warmup: int) -> dict:
         "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": reps * 2, "warmup": warmup,
         "higher_is_better": False, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "selector: logits [32,15,248320] fp32 N(0,3), codebooks [248320,64] bf16; "
-                               "2 input sets rotated, graph-replayed chain (projection, then the two-launch "
-                               "selection: per-row scan + top-k, edge scores + walk)"},
+                               "2 input sets rotated, graph-replayed chain (two launches: per-row scan + "
+                               "top-k with the projection beside it, then edge scores + walk)"},
         "roofline": {"kernel": "selector chain", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes_per_launch": int(total_bytes)},

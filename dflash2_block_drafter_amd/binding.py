@@ -112,6 +112,7 @@ _SIGS = {
     "dfl_select_path": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dfl_tile_maxima": (_I, [_P, _I, _I, _P, _P]),
     "dfl_select_tokens": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dfl_select_tokens_projected": (_I, [_P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dfl_bind_target": (_I, [_P, _P, _P, _I, _P]),
     "dfl_context_append_workspace_bytes": (_Z, [_P, _I, _I]),
     "dfl_linear_q4": (_I, [_P, _I, _I, _I, _P, _P, _P, _I, _P, _I, _I, _P, _Z, _P]),
@@ -423,6 +424,13 @@ def dfl_select_tokens(logits, tile_max, B, S, V, K, z, R, anchors, pred, succ, c
                       stream=None):
     _check(lib().dfl_select_tokens(_f32(logits), _f32(tile_max), B, S, V, K, _f32(z), R, _i32(anchors), _bf(pred),
                                    _bf(succ), _i32(cand), _f32(unary), _f32(scores), _i32(tokens), _stream(stream)))
+
+
+def dfl_select_tokens_projected(logits, B, S, V, K, h, H, proj, R, z, anchors, pred, succ, cand, unary, scores,
+                                tokens, stream=None):
+    _check(lib().dfl_select_tokens_projected(_f32(logits), B, S, V, K, _bf(h), H, _bf(proj), R, _f32(z),
+                                             _i32(anchors), _bf(pred), _bf(succ), _i32(cand), _f32(unary),
+                                             _f32(scores), _i32(tokens), _stream(stream)))
 
 
 def dfl_bind_target(handle, lm_head, vocab_ids=None, stream=None):

@@ -1171,6 +1171,12 @@ size_t dfl_selector_project_workspace_bytes(int N, int H, int R) { return dfl_li
 
 int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
+  if (h && proj && z && N > 0 && dfl::selproj_fits(H, R, h, proj)) {
+    // the kernel dfl_select_tokens_projected runs beside its scan: the same z bit for bit
+    hipError_t e = dfl::launch_selector_project(h, N, H, proj, R, z, stream);
+    DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+    return DFL_OK;
+  }
   return dfl_linear(h, N, H, H, proj, R, z, R, 1, ws, ws_bytes, stream);
 }
 
@@ -1206,6 +1212,26 @@ int dfl_select_tokens(const float* logits, const float* tile_max, int B, int S, 
               dfl::kGemmTileN);
   hipError_t e = dfl::launch_select_tokens(logits, tile_max, B, S, V, K, nullptr, z, R, anchors, pred, succ, V, cand,
                                            unary, scores, tokens, stream);
+  DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
+  return DFL_OK;
+}
+
+int dfl_select_tokens_projected(const float* logits, int B, int S, int V, int K, const dfl_bf16* h, int H,
+                                const dfl_bf16* proj, int R, float* z, const int32_t* anchors, const dfl_bf16* pred,
+                                const dfl_bf16* succ, int32_t* cand, float* unary, float* scores, int32_t* tokens,
+                                hipStream_t stream) {
+  DFL_REQUIRE(logits && h && proj && z && anchors && pred && succ && cand && unary && tokens, DFL_E_INVALID,
+              "NULL argument");
+  DFL_REQUIRE(B > 0 && S > 0 && V > 0 && K > 0 && R > 0 && H > 0, DFL_E_INVALID, "sizes must be positive");
+  DFL_REQUIRE(K <= V, DFL_E_UNSUPPORTED, "K=%d exceeds V=%d", K, V);
+  DFL_REQUIRE(dfl::select_tokens_fits(S, K, R), DFL_E_UNSUPPORTED,
+              "S=%d, K=%d, R=%d: this call needs S <= 64, K <= 16 and R a multiple of 4 in [4, 64]", S, K, R);
+  DFL_REQUIRE((V + dfl::kGemmTileN - 1) / dfl::kGemmTileN <= dfl::kSelectScanMaxTiles, DFL_E_UNSUPPORTED,
+              "V=%d needs at most %d tiles of %d columns", V, dfl::kSelectScanMaxTiles, dfl::kGemmTileN);
+  DFL_REQUIRE(dfl::selproj_fits(H, R, h, proj), DFL_E_UNSUPPORTED,
+              "H=%d must be a multiple of 128 and h, proj 16-byte aligned", H);
+  hipError_t e = dfl::launch_select_tokens_projected(logits, B, S, V, K, h, H, proj, R, z, anchors, pred, succ,
+                                                     cand, unary, scores, tokens, stream);
   DFL_REQUIRE(e == hipSuccess, DFL_E_DEVICE, "launch: %s", hipGetErrorString(e));
   return DFL_OK;
 }

@@ -215,6 +215,19 @@ hipError_t launch_select_tokens(const float* logits, const float* tile_max, int 
                                 float* scores, int32_t* tokens, hipStream_t stream);
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
                               int32_t* tokens, hipStream_t stream);
+// Selector projection z = h . proj^T, fp32 [N, R], 16 rows per workgroup on the matrix cores
+// (K in quarters per wavefront, summed in a fixed order): h [N, H] and proj [R, H] bf16,
+// 16-byte aligned, H a multiple of 128, R <= 64 (selproj_fits).
+bool selproj_fits(int H, int R, const void* h, const void* proj);
+hipError_t launch_selector_project(const uint16_t* h, int N, int H, const uint16_t* proj, int R, float* z,
+                                   hipStream_t stream);
+// launch_select_tokens without tile maxima, with z computed by the same kernel as
+// launch_selector_project in extra workgroups of the scanning top-k's launch (z is written,
+// then read by the edge scores).
+hipError_t launch_select_tokens_projected(const float* logits, int B, int S, int V, int K, const uint16_t* h, int H,
+                                          const uint16_t* proj, int R, float* z, const int32_t* anchors,
+                                          const uint16_t* pred, const uint16_t* succ, int32_t* cand, float* unary,
+                                          float* scores, int32_t* tokens, hipStream_t stream);
 
 
 }  // namespace dfl

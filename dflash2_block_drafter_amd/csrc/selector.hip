@@ -340,6 +340,72 @@ __device__ __forceinline__ float max16(float v) {
   return v;
 }
 
+// The selector projection z = h . proj^T (fp32) of kProjRows rows per 256-thread
+// workgroup, on the matrix cores: the four wavefronts take a quarter of K each (H a multiple
+// of 128, so each quarter is whole 32-deep steps) and every wavefront computes all R <= 64
+// columns (16x16x32 bf16 MFMA blocks); the four partial products are summed through LDS in
+// wavefront order, so the result does not depend on timing.  Lane l supplies row / column
+// l % 16 at K offset 8 (l / 16) of a step, 16 bytes straight from global memory.  Rows past
+// N and columns past R read the last valid one and are not written.
+constexpr int kProjRows = 16;
+constexpr int kProjMaxR = 64;
+// U: K steps whose loads are issued together (the order of the MFMAs, and so the result, is
+// the same for every U).
+template <int U>
+__device__ __forceinline__ void selproj_block(const uint16_t* __restrict__ h, int N, int H,
+                                              const uint16_t* __restrict__ proj, int R, float* __restrict__ z,
+                                              int blk) {
+  __shared__ float part[4][kProjRows][kProjMaxR + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r0 = blk * kProjRows;
+  const int kq = H / 4;
+  const int nsteps = kq / 32;
+  const int koff = wave * kq + 8 * (lane >> 4);
+  const uint16_t* ap = h + (size_t)min(r0 + (lane & 15), N - 1) * H + koff;
+  const uint16_t* bp[kProjMaxR / 16];
+#pragma unroll
+  for (int cb = 0; cb < kProjMaxR / 16; ++cb) bp[cb] = proj + (size_t)min(cb * 16 + (lane & 15), R - 1) * H + koff;
+  const int nb = (R + 15) / 16;
+  f32x4_t acc[kProjMaxR / 16];
+#pragma unroll
+  for (int cb = 0; cb < kProjMaxR / 16; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsteps; s0 += U) {
+    // every load is issued (steps past the last re-read it) before the first MFMA
+    bf16x8_t a[U], b[U][kProjMaxR / 16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = min(s0 + u, nsteps - 1) * 32;
+      a[u] = *reinterpret_cast<const bf16x8_t*>(ap + k);
+#pragma unroll
+      for (int cb = 0; cb < kProjMaxR / 16; ++cb) b[u][cb] = *reinterpret_cast<const bf16x8_t*>(bp[cb] + k);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < nsteps) {
+#pragma unroll
+        for (int cb = 0; cb < kProjMaxR / 16; ++cb)
+          if (cb < nb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][cb], acc[cb], 0, 0, 0);
+      }
+  }
+  // lane holds column cb * 16 + lane % 16, rows 4 (lane / 16) + e
+#pragma unroll
+  for (int cb = 0; cb < kProjMaxR / 16; ++cb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[wave][4 * (lane >> 4) + e][cb * 16 + (lane & 15)] = acc[cb][e];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kProjRows * R; i += 256) {
+    const int r = i / R, c = i % R;
+    if (r0 + r < N) z[(size_t)(r0 + r) * R + c] = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
+  }
+}
+
+__global__ __launch_bounds__(256) void selproj_kernel(const uint16_t* __restrict__ h, int N, int H,
+                                                      const uint16_t* __restrict__ proj, int R,
+                                                      float* __restrict__ z) {
+  selproj_block<4>(h, N, H, proj, R, z, blockIdx.x);
+}
+
 // Top-K of each row straight from the logits: one 256-thread workgroup per row scans the
 // whole row once (each round, 4 wavefronts x 16 tiles of 256 columns, 16 lanes a tile; the
 // next round's loads are issued before this round's reduction), keeps the row's tile maxima
@@ -347,10 +413,20 @@ __device__ __forceinline__ float max16(float v) {
 // scan ends, beside the other rows' scans, instead of in a launch after all of them.
 constexpr int kScanMaxTiles = kSelectScanMaxTiles;
 
+//
+// Workgroups past the N rows' (launched when h is given) compute the selector projection
+// (selproj_block, kProjRows rows each) beside the scans.
 template <bool VEC>
 __global__ __launch_bounds__(256) void topk_scan_kernel(const float* __restrict__ logits, int V, int ntiles, int K,
                                                         int32_t* __restrict__ ids, float* __restrict__ vals,
-                                                        const int32_t* __restrict__ id_map) {
+                                                        const int32_t* __restrict__ id_map,
+                                                        const uint16_t* __restrict__ h, int N, int H,
+                                                        const uint16_t* __restrict__ proj, int R,
+                                                        float* __restrict__ z) {
+  if ((int)blockIdx.x >= N) {
+    selproj_block<2>(h, N, H, proj, R, z, blockIdx.x - N);  // (2: within the scan's registers)
+    return;
+  }
   constexpr int TQ = kGemmTileN / 64;  // float4 per lane per tile
   constexpr int PASS = 4;              // tiles per 16-lane group per round
   constexpr int ROUND = 4 * 4 * PASS;  // tiles per round: 4 wavefronts x 4 groups x PASS
@@ -900,6 +976,24 @@ hipError_t launch_edges_walk(const int32_t* cand, const float* unary, const floa
   return hipGetLastError();
 }
 
+// The scanning top-k of N rows, with the selector projection's workgroups first when h is
+// given (selproj_fits checked by the caller).
+hipError_t launch_topk_scan(const float* logits, int N, int V, int K, int32_t* cand, float* unary,
+                            const int32_t* id_map, const uint16_t* h, int H, const uint16_t* proj, int R, float* z,
+                            hipStream_t stream) {
+  const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
+  if (ntiles > kScanMaxTiles) return hipErrorInvalidValue;
+  const int nproj = h ? (N + kProjRows - 1) / kProjRows : 0;
+  const dim3 grid(nproj + N);
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
+    topk_scan_kernel<true><<<grid, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map, h, N, H, proj, R,
+                                                     z);
+  else
+    topk_scan_kernel<false><<<grid, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map, h, N, H, proj,
+                                                      R, z);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
                                 const int32_t* id_map, const float* z, int R, const int32_t* anchors,
                                 const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,
@@ -911,16 +1005,34 @@ hipError_t launch_select_tokens(const float* logits, const float* tile_max, int 
     e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map);
   } else {
     // no tile maxima given: each row's workgroup scans its logits and then takes its top-K
-    const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
-    if (ntiles > kScanMaxTiles) return hipErrorInvalidValue;
-    if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0)
-      topk_scan_kernel<true><<<B * S, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map);
-    else
-      topk_scan_kernel<false><<<B * S, 256, 0, stream>>>(logits, V, ntiles, K, cand, unary, id_map);
-    e = hipGetLastError();
+    e = launch_topk_scan(logits, B * S, V, K, cand, unary, id_map, nullptr, 0, nullptr, 0, nullptr, stream);
   }
   if (e != hipSuccess) return e;
   return launch_edges_walk(cand, unary, z, R, anchors, B, S, K, pred, succ, Vcb, scores, tokens, stream);
+}
+
+bool selproj_fits(int H, int R, const void* h, const void* proj) {
+  return H > 0 && H % 128 == 0 && R >= 1 && R <= kProjMaxR &&
+         ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(proj)) & 15) == 0;
+}
+
+hipError_t launch_selector_project(const uint16_t* h, int N, int H, const uint16_t* proj, int R, float* z,
+                                   hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  if (!selproj_fits(H, R, h, proj)) return hipErrorInvalidValue;
+  selproj_kernel<<<(N + kProjRows - 1) / kProjRows, 256, 0, stream>>>(h, N, H, proj, R, z);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_tokens_projected(const float* logits, int B, int S, int V, int K, const uint16_t* h, int H,
+                                          const uint16_t* proj, int R, float* z, const int32_t* anchors,
+                                          const uint16_t* pred, const uint16_t* succ, int32_t* cand, float* unary,
+                                          float* scores, int32_t* tokens, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  if (!select_tokens_fits(S, K, R) || !selproj_fits(H, R, h, proj)) return hipErrorInvalidValue;
+  hipError_t e = launch_topk_scan(logits, B * S, V, K, cand, unary, nullptr, h, H, proj, R, z, stream);
+  if (e != hipSuccess) return e;
+  return launch_edges_walk(cand, unary, z, R, anchors, B, S, K, pred, succ, V, scores, tokens, stream);
 }
 
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,

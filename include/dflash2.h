@@ -361,7 +361,9 @@ int dfl_compute_candidates_static(const float* logits, int N, int V, int K, int3
                                   float* unary, hipStream_t stream);
 
 /* Selector projection z = h . proj^T kept in fp32 ([P2] `#block`: z = hidden_projection(h)).
- * h [N, H] bf16, proj [R, H] bf16, z [N, R] fp32. */
+ * h [N, H] bf16, proj [R, H] bf16, z [N, R] fp32.  With H a multiple of 128, R <= 64 and h,
+ * proj 16-byte aligned it runs the kernel dfl_select_tokens_projected runs (the same z bit
+ * for bit) and uses no workspace; otherwise the split-K GEMM of dfl_linear. */
 size_t dfl_selector_project_workspace_bytes(int N, int H, int R);
 int dfl_selector_project(const dfl_bf16* h, int N, int H, const dfl_bf16* proj, int R, float* z,
                          void* ws, size_t ws_bytes, hipStream_t stream);
@@ -400,6 +402,20 @@ int dfl_select_tokens(const float* logits, const float* tile_max, int B, int S, 
                       const float* z, int R, const int32_t* anchors, const dfl_bf16* pred,
                       const dfl_bf16* succ, int32_t* cand, float* unary, float* scores,
                       int32_t* tokens, hipStream_t stream);
+
+/* The selection with its projection ([P2] `#block`: z = hidden_projection(h), then
+ * `#select`; [P3] `compute_candidates`, `score_edges`, `select_path`): z = h . proj^T is
+ * computed by extra workgroups of the scanning top-k's launch (dfl_select_tokens with
+ * tile_max NULL), beside the scans, and written to z; then the edge scores and the walk read
+ * it.  The results equal dfl_selector_project followed by dfl_select_tokens(tile_max NULL).
+ *   h: [B*S, H] bf16; proj: [R, H] bf16; z: [B*S, R] fp32 out;
+ *   other arguments as dfl_select_tokens.
+ * Requires H a multiple of 128, h and proj 16-byte aligned, and dfl_select_tokens's limits
+ * (DFL_E_UNSUPPORTED otherwise).  Two launches. */
+int dfl_select_tokens_projected(const float* logits, int B, int S, int V, int K, const dfl_bf16* h, int H,
+                                const dfl_bf16* proj, int R, float* z, const int32_t* anchors,
+                                const dfl_bf16* pred, const dfl_bf16* succ, int32_t* cand, float* unary,
+                                float* scores, int32_t* tokens, hipStream_t stream);
 
 /* ---- measurement ---- */
 

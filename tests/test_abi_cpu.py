@@ -76,6 +76,12 @@ def test_validation_errors_before_any_launch():
     # without tile maxima the row's scan keeps them on chip: at most 4096 tiles (V <= 2^20)
     assert L.dfl_select_tokens(P, None, 2, 15, 4096 * 256 + 1, 16, P, 64, P, P, P, P, P, None, P,
                                None) == B.DFL_E_UNSUPPORTED
+    # the selection with its projection: H not a multiple of 128, R above 64, a NULL input
+    selp = lambda H, R, h=P: L.dfl_select_tokens_projected(P, 2, 15, 1000, 16, h, H, P, R, P, P, P, P, P, P, None,
+                                                           P, None)
+    assert selp(200, 64) == B.DFL_E_UNSUPPORTED
+    assert selp(256, 128) == B.DFL_E_UNSUPPORTED
+    assert selp(256, 64, h=None) == B.DFL_E_INVALID
     # null pointers
     assert L.dfl_select_path(None, P, 1, 1, 4, P, None) == B.DFL_E_INVALID
     # K not a multiple of 64

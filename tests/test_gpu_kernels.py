@@ -331,8 +331,13 @@ def test_select_path_bitexact(Bq, S, K):
     assert np.array_equal(tokens.cpu().numpy(), want)
 
 
-def test_selector_project():
-    N, H, R = 120, 5120, 64
+@pytest.mark.parametrize("N,H,R", [
+    (120, 5120, 64),   # the full drafter's selector rows
+    (37, 384, 20),     # ragged rows and columns; three K steps a quarter
+    (5, 192, 8),       # H not a multiple of 128: the split-K GEMM
+])
+def test_selector_project(N, H, R):
+    print(f"[selector_project] N={N} H={H} R={R}", flush=True)
     hh = bf((N, H), 101)
     proj = bf((R, H), 102, std=0.02)
     z = torch.empty((N, R), dtype=torch.float32, device=DEV)

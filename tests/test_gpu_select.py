@@ -84,6 +84,24 @@ def test_select_tokens_matches_steps_and_oracle(Bq, S, V, K, R, kind):
     assert torch.equal(tokens, t2)
     assert torch.equal(cand, c3) and torch.equal(unary, u3), "the scanning top-k differs"
     assert torch.equal(scores, s3) and torch.equal(tokens, t3)
+    # with the projection in the scan's launch: the same z as dfl_selector_project, and the
+    # same selection as dfl_select_tokens given that z
+    H = 5120 if V > 100000 else 256
+    hid = synth.normal((N, H), 0.0, 1.0, seed=950 + V % 89, device=DEV)
+    proj = synth.normal((R, H), 0.0, 0.02, seed=951 + V % 89, device=DEV)
+    zp = torch.full((N, R), float("nan"), dtype=torch.float32, device=DEV)
+    c4, u4, s4, t4 = (torch.full_like(cand, -1), torch.full_like(unary, float("nan")),
+                      torch.full_like(scores, float("nan")), torch.full_like(tokens, -1))
+    B.dfl_select_tokens_projected(logits, Bq, S, V, K, hid, H, proj, R, zp, anchors, pred, succ, c4, u4, s4, t4)
+    zr = torch.empty_like(zp)
+    B.dfl_selector_project(hid, N, H, proj, R, zr, None)
+    c5, u5, s5, t5 = (torch.empty_like(cand), torch.empty_like(unary), torch.empty_like(scores),
+                      torch.empty_like(tokens))
+    B.dfl_select_tokens(logits, None, Bq, S, V, K, zr, R, anchors, pred, succ, c5, u5, s5, t5)
+    torch.cuda.synchronize()
+    assert torch.equal(zp, zr), "the projection in the scan's launch differs from dfl_selector_project"
+    assert torch.equal(c4, cand) and torch.equal(u4, unary)
+    assert torch.equal(s4, s5) and torch.equal(t4, t5)
     # the oracle
     lg = logits.cpu().numpy()
     rows = np.arange(N) if N <= 96 else np.linspace(0, N - 1, 96).astype(int)
