@@ -342,19 +342,21 @@ __device__ __forceinline__ float max16(float v) {
 
 // The selector projection z = h . proj^T (fp32) of kProjRows rows per 256-thread
 // workgroup, on the matrix cores: the four wavefronts take a quarter of K each (H a multiple
-// of 128, so each quarter is whole 32-deep steps) and every wavefront computes all R <= 64
-// columns (16x16x32 bf16 MFMA blocks); the four partial products are summed through LDS in
-// wavefront order, so the result does not depend on timing.  Lane l supplies row / column
-// l % 16 at K offset 8 (l / 16) of a step, 16 bytes straight from global memory.  Rows past
-// N and columns past R read the last valid one and are not written.
+// of 128, so each quarter is whole 32-deep steps) over NCB 16-column blocks from cb0 (16x16x32
+// bf16 MFMA blocks); the four partial products are summed through LDS in wavefront order, so
+// an output's value depends neither on timing nor on how many column blocks a workgroup
+// takes.  Lane l supplies row / column l % 16 at K offset 8 (l / 16) of a step, 16 bytes
+// straight from global memory.  Rows past N and columns past R read the last valid one and
+// are not written.
 constexpr int kProjRows = 16;
 constexpr int kProjMaxR = 64;
+
 // U: K steps whose loads are issued together (the order of the MFMAs, and so the result, is
 // the same for every U).
-template <int U>
+template <int U, int NCB>
 __device__ __forceinline__ void selproj_block(const uint16_t* __restrict__ h, int N, int H,
                                               const uint16_t* __restrict__ proj, int R, float* __restrict__ z,
-                                              int blk) {
+                                              int blk, int cb0) {
   __shared__ float part[4][kProjRows][kProjMaxR + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -363,47 +365,51 @@ __device__ __forceinline__ void selproj_block(const uint16_t* __restrict__ h, in
   const int nsteps = kq / 32;
   const int koff = wave * kq + 8 * (lane >> 4);
   const uint16_t* ap = h + (size_t)min(r0 + (lane & 15), N - 1) * H + koff;
-  const uint16_t* bp[kProjMaxR / 16];
+  const uint16_t* bp[NCB];
 #pragma unroll
-  for (int cb = 0; cb < kProjMaxR / 16; ++cb) bp[cb] = proj + (size_t)min(cb * 16 + (lane & 15), R - 1) * H + koff;
-  const int nb = (R + 15) / 16;
-  f32x4_t acc[kProjMaxR / 16];
+  for (int c = 0; c < NCB; ++c) bp[c] = proj + (size_t)min((cb0 + c) * 16 + (lane & 15), R - 1) * H + koff;
+  const int nb = min(NCB, (R + 15) / 16 - cb0);  // column blocks with columns < R
+  f32x4_t acc[NCB];
 #pragma unroll
-  for (int cb = 0; cb < kProjMaxR / 16; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NCB; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nsteps; s0 += U) {
     // every load is issued (steps past the last re-read it) before the first MFMA
-    bf16x8_t a[U], b[U][kProjMaxR / 16];
+    bf16x8_t a[U], b[U][NCB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = min(s0 + u, nsteps - 1) * 32;
       a[u] = *reinterpret_cast<const bf16x8_t*>(ap + k);
 #pragma unroll
-      for (int cb = 0; cb < kProjMaxR / 16; ++cb) b[u][cb] = *reinterpret_cast<const bf16x8_t*>(bp[cb] + k);
+      for (int c = 0; c < NCB; ++c) b[u][c] = *reinterpret_cast<const bf16x8_t*>(bp[c] + k);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (s0 + u < nsteps) {
 #pragma unroll
-        for (int cb = 0; cb < kProjMaxR / 16; ++cb)
-          if (cb < nb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][cb], acc[cb], 0, 0, 0);
+        for (int c = 0; c < NCB; ++c)
+          if (c < nb) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][c], acc[c], 0, 0, 0);
       }
   }
-  // lane holds column cb * 16 + lane % 16, rows 4 (lane / 16) + e
+  // lane holds column (cb0 + c) * 16 + lane % 16, rows 4 (lane / 16) + e
 #pragma unroll
-  for (int cb = 0; cb < kProjMaxR / 16; ++cb)
+  for (int c = 0; c < NCB; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part[wave][4 * (lane >> 4) + e][cb * 16 + (lane & 15)] = acc[cb][e];
+    for (int e = 0; e < 4; ++e) part[wave][4 * (lane >> 4) + e][c * 16 + (lane & 15)] = acc[c][e];
   __syncthreads();
-  for (int i = threadIdx.x; i < kProjRows * R; i += 256) {
-    const int r = i / R, c = i % R;
-    if (r0 + r < N) z[(size_t)(r0 + r) * R + c] = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
+  const int cols = min(NCB * 16, R - cb0 * 16);
+  for (int i = threadIdx.x; i < kProjRows * cols; i += 256) {
+    const int r = i / cols, c = i % cols;
+    if (r0 + r < N)
+      z[(size_t)(r0 + r) * R + cb0 * 16 + c] = ((part[0][r][c] + part[1][r][c]) + part[2][r][c]) + part[3][r][c];
   }
 }
 
+// One 16-column block of 16 rows a workgroup (blockIdx.x: rows, blockIdx.y: columns): four
+// times the workgroups of the all-columns form, each with a quarter of the weight rows.
 __global__ __launch_bounds__(256) void selproj_kernel(const uint16_t* __restrict__ h, int N, int H,
                                                       const uint16_t* __restrict__ proj, int R,
                                                       float* __restrict__ z) {
-  selproj_block<4>(h, N, H, proj, R, z, blockIdx.x);
+  selproj_block<8, 1>(h, N, H, proj, R, z, blockIdx.x, blockIdx.y);
 }
 
 // Top-K of each row straight from the logits: one 256-thread workgroup per row scans the
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(256) void topk_scan_kernel(const float* __restrict_
                                                         const uint16_t* __restrict__ proj, int R,
                                                         float* __restrict__ z) {
   if ((int)blockIdx.x >= N) {
-    selproj_block<2>(h, N, H, proj, R, z, blockIdx.x - N);  // (2: within the scan's registers)
+    selproj_block<2, kProjMaxR / 16>(h, N, H, proj, R, z, blockIdx.x - N, 0);  // (2: within the scan's registers)
     return;
   }
   constexpr int TQ = kGemmTileN / 64;  // float4 per lane per tile
@@ -1020,7 +1026,7 @@ hipError_t launch_selector_project(const uint16_t* h, int N, int H, const uint16
                                    hipStream_t stream) {
   if (N <= 0) return hipSuccess;
   if (!selproj_fits(H, R, h, proj)) return hipErrorInvalidValue;
-  selproj_kernel<<<(N + kProjRows - 1) / kProjRows, 256, 0, stream>>>(h, N, H, proj, R, z);
+  selproj_kernel<<<dim3((N + kProjRows - 1) / kProjRows, (R + 15) / 16), 256, 0, stream>>>(h, N, H, proj, R, z);
   return hipGetLastError();
 }
 
