@@ -138,13 +138,18 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
   // disjoint groups), so every top-K logit is >= it, and with <= 256 tiles it is the K-th
   // largest tile maximum itself.  It is found bit by bit in an order-preserving integer map
   // of the floats (the largest u with at least K group maxima >= u): ballots, no sorting.
-  // -inf with fewer than K groups (every tile then qualifies).
+  // -inf with fewer than K groups (every tile then qualifies).  With one round of tile
+  // maxima wavefront 0 still holds them and lists the qualifying tiles at once.
+  __shared__ float cand_v[64];
+  __shared__ int cand_i[64];
+  __shared__ int ccount;
+  const bool one_round = ntiles <= CH;
   if (wave == 0) {
     float g[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) g[i] = __builtin_nanf("");  // NaN: empty (fmaxf skips NaN)
+    float t[kTmPerLane];
     for (int c0 = 0; c0 < ntiles; c0 += CH) {
-      float t[kTmPerLane];
 #pragma unroll
       for (int j = 0; j < kTmPerLane; ++j) {
         const int i = c0 + j * 64 + lane;
@@ -168,32 +173,15 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
       for (int i = 0; i < 4; ++i) n += __popcll(__ballot(g[i] == g[i] && u[i] >= tryu));
       if (n >= K) cu = tryu;
     }
-    if (lane == 0) theta_s = groups >= K ? order_float(cu) : -INFINITY;
-  }
-  __syncthreads();
-  const float theta = theta_s;
-
-  // Fast path (one round of tile maxima): every value >= theta is a candidate, usually K to
-  // 2K of them, so they are gathered into LDS (ballot + one LDS atomic per wavefront step)
-  // and sorted once by wavefront 0.  More than 64 of them (ties at theta across many tiles,
-  // constant rows, rows mostly -inf) falls through to the merging scan below.
-  __shared__ float cand_v[64];
-  __shared__ int cand_i[64];
-  __shared__ int ccount;
-  if (ntiles <= CH) {
-    if (wave == 0) {
-      float t[kTmPerLane];
-#pragma unroll
-      for (int j = 0; j < kTmPerLane; ++j) {
-        const int i = j * 64 + lane;
-        t[j] = i < ntiles ? tm[i] : -INFINITY;
-      }
+    const float th = groups >= K ? order_float(cu) : -INFINITY;  // the same in every lane
+    if (lane == 0) theta_s = th;
+    if (one_round) {
       int cnt = 0;
       const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
       for (int j = 0; j < kTmPerLane; ++j) {
         const int i = j * 64 + lane;
-        const bool q = i < ntiles && t[j] >= theta;
+        const bool q = i < ntiles && t[j] >= th;
         const uint64_t mask = __ballot(q);
         if (q) tl[cnt + __popcll(mask & below)] = i;
         cnt += __popcll(mask);
@@ -203,7 +191,15 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
         ccount = 0;
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const float theta = theta_s;
+
+  // Fast path (one round of tile maxima): every value >= theta is a candidate, usually K to
+  // 2K of them, so they are gathered into LDS (ballot + one LDS atomic per wavefront step)
+  // and sorted once by wavefront 0.  More than 64 of them (ties at theta across many tiles,
+  // constant rows, rows mostly -inf) falls through to the merging scan below.
+  if (one_round) {
     const int cnt = tcount;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     for (int b0 = wave * kTilesInFlight; b0 < cnt; b0 += 4 * kTilesInFlight) {
