@@ -6,7 +6,7 @@
 // logits from elsewhere).  theta, the K-th largest maximum over K disjoint groups of tiles,
 // is reached by K distinct logits, so every top-K logit is >= theta and sits in a tile whose
 // maximum is >= theta; only those tiles are read (usually K to 2K of a row's V/256).  Their
-// values >= theta (usually K to 2K) are gathered and sorted once when there are at most
+// values >= theta (usually K to 2K) are gathered and ranked once when there are at most
 // 64; otherwise they are merged
 // into a running top-K list with a 64-lane bitonic sort (lanes 0..K-1 keep the list, lanes
 // K..63 take new candidates).  Ties are ordered by id, so the result is exact and unique for
@@ -83,11 +83,14 @@ __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restric
 // wavefronts per row.  Wavefront 0 reads the tile maxima 64 * kTmPerLane at a time (one
 // round of loads) into 256 group maxima and takes their K-th largest as theta by ballots
 // (no sorting); then the qualifying tiles are listed in LDS and each wavefront loads
-// kTilesInFlight of them at once.  With one round of tile maxima, their values >= theta are gathered into LDS
-// and, when at most 64, sorted once by wavefront 0; otherwise (and for longer rows) each
-// wavefront merges its tiles into its own list and wavefront 0 merges the four lists.
+// kFastTilesInFlight of them at once.  With one round of tile maxima, their values >= theta
+// are gathered into LDS and, when at most 64, ranked once by wavefront 0 (each lane counts
+// the candidates that precede its own); otherwise (and for longer rows) each wavefront
+// merges its tiles, kTilesInFlight at a time, into its own list and wavefront 0 merges the
+// four lists.
 constexpr int kTmPerLane = 16;
 constexpr int kTilesInFlight = 4;
+constexpr int kFastTilesInFlight = 8;  // the fast path's loads: usually every qualifying tile at once
 
 // Order-preserving map of a float to an unsigned integer (NaN excluded by the callers), and
 // back.
@@ -140,8 +143,8 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
   // of the floats (the largest u with at least K group maxima >= u): ballots, no sorting.
   // -inf with fewer than K groups (every tile then qualifies).  With one round of tile
   // maxima wavefront 0 still holds them and lists the qualifying tiles at once.
-  __shared__ float cand_v[64];
-  __shared__ int cand_i[64];
+  __shared__ __attribute__((aligned(16))) float cand_v[64];
+  __shared__ __attribute__((aligned(16))) int cand_i[64];
   __shared__ int ccount;
   const bool one_round = ntiles <= CH;
   if (wave == 0) {
@@ -197,26 +200,27 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
 
   // Fast path (one round of tile maxima): every value >= theta is a candidate, usually K to
   // 2K of them, so they are gathered into LDS (ballot + one LDS atomic per wavefront step)
-  // and sorted once by wavefront 0.  More than 64 of them (ties at theta across many tiles,
+  // and ranked once by wavefront 0.  More than 64 of them (ties at theta across many tiles,
   // constant rows, rows mostly -inf) falls through to the merging scan below.
   if (one_round) {
+    constexpr int F = kFastTilesInFlight;
     const int cnt = tcount;
     const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    for (int b0 = wave * kTilesInFlight; b0 < cnt; b0 += 4 * kTilesInFlight) {
-      const int n = min(kTilesInFlight, cnt - b0);
-      int tile[kTilesInFlight];
-      float x[kTilesInFlight][TPL];
+    for (int b0 = wave * F; b0 < cnt; b0 += 4 * F) {
+      const int n = min(F, cnt - b0);
+      int tile[F];
+      float x[F][TPL];
 #pragma unroll
-      for (int q = 0; q < kTilesInFlight; ++q) tile[q] = tl[b0 + min(q, n - 1)];
+      for (int q = 0; q < F; ++q) tile[q] = tl[b0 + min(q, n - 1)];
 #pragma unroll
-      for (int q = 0; q < kTilesInFlight; ++q)
+      for (int q = 0; q < F; ++q)
 #pragma unroll
         for (int e = 0; e < TPL; ++e) {
           const int col = tile[q] * TW + e * 64 + lane;
           x[q][e] = col < V ? src[col] : -INFINITY;
         }
 #pragma unroll
-      for (int q = 0; q < kTilesInFlight; ++q)
+      for (int q = 0; q < F; ++q)
 #pragma unroll
         for (int e = 0; e < TPL; ++e) {
           const int col = tile[q] * TW + e * 64 + lane;
@@ -238,12 +242,22 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
     const int total = ccount;
     if (total <= 64) {
       if (wave != 0) return;
-      float v = lane < total ? cand_v[lane] : -INFINITY;
-      int id = lane < total ? cand_i[lane] : kNoId;
-      wave_bitonic_sort(v, id, lane);
-      if (lane < K) {
-        ids[(size_t)row * K + lane] = id_map && id >= 0 && id < V ? id_map[id] : id;
-        vals[(size_t)row * K + lane] = v;
+      // the first K in candidate order by rank: each lane counts the candidates that precede
+      // its own (read four at a time, every lane the same address); ids are distinct, so the
+      // ranks are 0 .. total - 1.  With fewer than K candidates the rest are (-inf, kNoId).
+      const float v = lane < total ? cand_v[lane] : -INFINITY;
+      const int id = lane < total ? cand_i[lane] : kNoId;
+      int rank = 0;
+      for (int j = 0; j < total; j += 4) {
+        const f32x4_t cv = *reinterpret_cast<const f32x4_t*>(&cand_v[j]);
+        const u32x4_t ci = *reinterpret_cast<const u32x4_t*>(&cand_i[j]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rank += j + t < total && before(cv[t], (int)ci[t], v, id);
+      }
+      const int slot = lane < total ? rank : lane;
+      if (slot < K) {
+        ids[(size_t)row * K + slot] = id_map && id >= 0 && id < V ? id_map[id] : id;
+        vals[(size_t)row * K + slot] = v;
       }
       return;
     }
