@@ -794,6 +794,26 @@ __device__ __forceinline__ bool mfma_scores_fit(int K, int R) {
   return K >= 1 && K <= kMfmaMaxK && R >= 4 && R <= kMfmaMaxR && R % 4 == 0;
 }
 
+// The first of each aligned group of 16 lanes in candidate order (value descending, then
+// id ascending), left in every lane of the group: the same DPP lane moves as max16, moving
+// the value and its id together (the order is total, so any reduction order gives the same
+// winner).
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& id) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oid = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
+  if (before(ov, oid, v, id)) {
+    v = ov;
+    id = oid;
+  }
+}
+__device__ __forceinline__ void argmax16(float& v, int& id) {
+  argmax_step<0x140>(v, id);  // row_mirror
+  argmax_step<0x141>(v, id);  // row_half_mirror
+  argmax_step<0x4E>(v, id);   // quad_perm 2,3,0,1
+  argmax_step<0xB1>(v, id);   // quad_perm 1,0,3,2
+}
+
 // The edge scores and the walk of B requests in one launch: one workgroup per request, one
 // wavefront per slot (slots l = wave, wave + kSelWaves, ...).  Each wavefront scores its slot
 // on the matrix cores and keeps, for every predecessor p, the lowest candidate c of maximum
@@ -833,15 +853,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void edges_walk_kernel(
       // argmax over the 16 lanes of this row of the tile (lowest c on ties; c >= K never wins)
       float bv = c < K ? sc : -INFINITY;
       int bc = c;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oc = __shfl_xor(bc, off, 64);
-        if (before(ov, oc, bv, bc)) {
-          bv = ov;
-          bc = oc;
-        }
-      }
+      argmax16(bv, bc);
       if (c == 0 && p < K) best_s[l][p] = bc;
     }
     if (lane < K) cand_s[l][lane] = craw;
