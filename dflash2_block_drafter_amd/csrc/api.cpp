@@ -200,7 +200,7 @@ int check_config(const dfl_config* c) {
 }
 
 struct DraftLayout {
-  size_t x, n, a, qkv, ao, u, p, h, logits, tmax, z, cand, unary, scores, attn, kpart, coef1, partial;
+  size_t x, n, a, qkv, ao, u, p, h, logits, tmax, tbound, z, cand, unary, scores, attn, kpart, coef1, partial;
   size_t total;
 };
 
@@ -220,6 +220,7 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
   L.h = cv.off; cv.take<uint16_t>((size_t)N * H);
   L.logits = cv.off; cv.take<float>((size_t)N * c.vocab);
   L.tmax = cv.off; cv.take<float>((size_t)N * ((c.vocab + dfl::kGemmTileN - 1) / dfl::kGemmTileN));
+  L.tbound = cv.off; cv.take<uint32_t>((size_t)N * dfl::kTileBoundSlots);
   L.z = cv.off; cv.take<float>((size_t)N * c.rank);
   L.cand = cv.off; cv.take<int32_t>((size_t)N * c.top_k);
   L.unary = cv.off; cv.take<float>((size_t)N * c.top_k);
@@ -272,7 +273,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) =
 int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, int G, const uint16_t* Kl,
               const uint16_t* Vl, int Lcap, int Lmax, const int32_t* ctx_len, const int32_t* pos0, char* W,
               const DraftLayout& lay, bool n_ready, const uint16_t* next_gamma, hipStream_t stream,
-              uint16_t* head_rows = nullptr, const dfl_trace* trace = nullptr) {
+              uint16_t* head_rows = nullptr, const dfl_trace* trace = nullptr, uint32_t* clear_bound = nullptr) {
   const dfl_config& c = d->cfg;
   const LayerBuf& L = d->layers[li];
   const int H = c.hidden, NH = c.heads, NKV = c.kv_heads, D = c.head_dim, F = c.intermediate;
@@ -395,12 +396,14 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     const bool pack = head_rows != nullptr;
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 4.0 * T * H + (d_planes ? 4.0 * T * H * p_dn.splits : 0.0),
                   stream, [&] {
+                    // with the packed rows it also clears the head's bound slots
+                    uint32_t* cb = pack ? clear_bound : nullptr;
                     return d_planes ? dfl::launch_conv_residual_norm_planes(d_pl, coef1, L.mlp_base, T, H, G,
                                                                             c.conv_group, x, x, next_gamma,
-                                                                            c.rms_eps, nrows, stream, pack)
+                                                                            c.rms_eps, nrows, stream, pack, cb)
                                     : dfl::launch_conv_residual_norm(u, coef1, L.mlp_base, T, H, G, c.conv_group,
                                                                      x, x, next_gamma, c.rms_eps, nrows, stream,
-                                                                     pack);
+                                                                     pack, cb);
                   }));
   } else {
     DFL_TRY(timed(d, DFL_K_CONV_FINISH, conv_bytes + 2.0 * T * H, stream, [&] {
@@ -892,6 +895,18 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
   const bool head_sel = bound_head && d->head_sel;
   const int NHd = V_ + (head_sel ? R : 0);
   const dfl::GemmPlan p_head = dfl::plan_gemm(N, NHd, H, true), p_sel = dfl::plan_gemm(N, R, H);
+  // An unsplit head also writes every 256-column tile's row maxima, which lets the top-K
+  // read only the few tiles that can hold a candidate; a split head leaves them to a pass
+  // over the logits.
+  const bool tiles_fused = p_head.splits == 1;
+  // When nobody else reads the logits, a head on 256-row tiles leaves out each row's tiles
+  // that cannot hold one of its top kTileBoundSlots (launch_gemm's tile_bound), and the top-K
+  // reads only tiles above the same bound; the last layer's finish clears the slots.  (On the
+  // 128-row tiles the bound's device-scope round trip per workgroup costs more than the
+  // stores it saves.)
+  uint32_t* tbound = tiles_fused && p_head.bm == 256 && !logits_out && !trace && Kc <= dfl::kTileBoundSlots
+                         ? reinterpret_cast<uint32_t*>(W + lay.tbound)
+                         : nullptr;
 
   const uint16_t* xin = embeds;
   for (int li = 0; li < c.layers; ++li) {
@@ -901,18 +916,15 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
     // the last layer's finish applies the final norm to rows 1..G-1, packed into h for the head
     const uint16_t* next_gamma = last ? d->norm : d->layers[li + 1].in_norm;
     DFL_TRY(run_layer(d, li, xin, x, B, G, Kl, Vl, Lcap, Lmax, ctx_len, pos0, W, lay, li > 0, next_gamma, stream,
-                      last ? h : nullptr, trace));
+                      last ? h : nullptr, trace, last ? tbound : nullptr));
     xin = x;
   }
   if (trace) DFL_TRY(snap(trace->h, h, (size_t)N * H * sizeof(uint16_t), stream));
-  // An unsplit head also writes every 256-column tile's row maxima, which lets the top-K
-  // read only the few tiles that can hold a candidate; a split head leaves them to a pass
-  // over the logits.
-  const bool tiles_fused = p_head.splits == 1;
   float* tmax = f32(lay.tmax);
   DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, NHd, H, dfl::EPI_F32), stream, [&] {
     return dfl::launch_gemm(p_head, h, H, bound_head ? d->head : lm_head, bound_head, N, NHd, H, dfl::EPI_F32, logits,
-                            V_, head_sel ? z : nullptr, R, V_, part, stream, tiles_fused ? tmax : nullptr);
+                            V_, head_sel ? z : nullptr, R, V_, part, stream, tiles_fused ? tmax : nullptr,
+                            tbound);
   }));
   if (!head_sel) {
     DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {
@@ -929,7 +941,7 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
                                        2.0 * 2 * N * Kc * R + 4.0 * N * Kc * (Kc + 2),
                   stream, [&] {
       return dfl::launch_select_tokens(logits, tmax, B, S, V_, Kc, id_map, z, R, anchors, d->pred, d->succ, c.vocab,
-                                       cand, unary, scores, tokens, stream);
+                                       cand, unary, scores, tokens, stream, tbound);
     }));
     if (trace) {
       DFL_TRY(snap(trace->tile_max, tmax, (size_t)N * ((V_ + dfl::kGemmTileN - 1) / dfl::kGemmTileN) * sizeof(float),
@@ -942,7 +954,7 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
   }
   DFL_TRY(timed(d, DFL_K_TOPK, tiles_fused ? 4.0 * N * (V_ / dfl::kGemmTileN + Kc * dfl::kGemmTileN) : 4.0 * N * V_,
                 stream, [&] {
-    return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map)
+    return tiles_fused ? dfl::launch_topk_tiles(logits, N, V_, Kc, tmax, cand, unary, stream, id_map, tbound)
                        : dfl::launch_topk(logits, N, V_, Kc, cand, unary, tmax, stream, id_map);
   }));
   if (trace) {

@@ -66,6 +66,16 @@ __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x));
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// Order-preserving map of a float to an unsigned integer (NaN excluded by the callers), and
+// back: a < b as floats implies float_order(a) < float_order(b) (-0 maps just below +0).
+__device__ __forceinline__ uint32_t float_order(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return b & 0x80000000u ? ~b : b | 0x80000000u;
+}
+__device__ __forceinline__ float order_float(uint32_t u) {
+  return __uint_as_float(u & 0x80000000u ? u & 0x7FFFFFFFu : ~u);
+}
+
 // Sum over the S planes of pl (fp32 split-K partials) of the VW values at element offset
 // `off` (VW = 1, 2, 4 or 8; off a multiple of min(VW, 4)), added in plane order 0, 1, 2, ...
 // as the split-K reduce adds them.  Planes are read eight at a time with the plane index

@@ -206,7 +206,7 @@ template <int MAXC>
 __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
     const uint16_t* y, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
     const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
-    uint16_t* __restrict__ n_out, int skip_anchor) {
+    uint16_t* __restrict__ n_out, int skip_anchor, uint32_t* __restrict__ clear_bound) {
   __shared__ float red[4];
   __shared__ float cs[2 * MAXC * 256];  // the row's groups: H / grp <= H / 8 <= MAXC * 256
   const int t = blockIdx.x;
@@ -251,6 +251,7 @@ __global__ __launch_bounds__(256) void conv_residual_norm_kernel(
   // with skip_anchor the normed rows are packed without each block's row 0
   if (skip_anchor && t % G == 0) return;
   const size_t nrow = skip_anchor ? (size_t)(t / G) * (G - 1) + t % G - 1 : (size_t)t;
+  if (skip_anchor && clear_bound && tid < kTileBoundSlots) clear_bound[nrow * kTileBoundSlots + tid] = 0u;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int ch = tid + i * 256;
@@ -337,7 +338,7 @@ template <int S>
 __global__ __launch_bounds__(kCrnPlanesMaxThreads) void conv_residual_norm_planes_kernel(
     Planes y, Planes coef, const uint16_t* __restrict__ base, int H, int G, int grp,
     const uint16_t* residual, uint16_t* x_out, const uint16_t* __restrict__ gamma, float eps,
-    uint16_t* __restrict__ n_out, int skip_anchor) {
+    uint16_t* __restrict__ n_out, int skip_anchor, uint32_t* __restrict__ clear_bound) {
   __shared__ float red[kCrnPlanesMaxThreads / 64];
   __shared__ float cs[2 * kCrnPlanesMaxThreads];  // the row's groups: H / grp <= H / 8
   // Workgroups are dealt to the 8 XCDs in turn; rows are mapped so that each XCD gets a
@@ -385,6 +386,9 @@ __global__ __launch_bounds__(kCrnPlanesMaxThreads) void conv_residual_norm_plane
   const int waves = (int)(blockDim.x >> 6);
   for (int w = 0; w < waves; ++w) tot += red[w];
   const float inv = rsqrtf(tot / static_cast<float>(H) + eps);
+  // (the workgroup has at least 64 threads, live or not)
+  if (skip_anchor && clear_bound && t % G != 0 && tid < kTileBoundSlots)
+    clear_bound[((size_t)(t / G) * (G - 1) + t % G - 1) * kTileBoundSlots + tid] = 0u;
   if (!live || (skip_anchor && t % G == 0)) return;
   const size_t nrow = skip_anchor ? (size_t)(t / G) * (G - 1) + t % G - 1 : (size_t)t;
   float gm[8], o[8];
@@ -399,22 +403,26 @@ __global__ __launch_bounds__(kCrnPlanesMaxThreads) void conv_residual_norm_plane
 hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
-                                     bool skip_anchor) {
+                                     bool skip_anchor, uint32_t* clear_bound) {
   if (T <= 0) return hipSuccess;
   const int per = (H / 8 + 255) / 256;  // chunks of 8 channels per thread
   const int sk = skip_anchor ? 1 : 0;
   switch (per) {
     case 1:
-      conv_residual_norm_kernel<1><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
+      conv_residual_norm_kernel<1><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk,
+                                                          clear_bound);
       break;
     case 2:
-      conv_residual_norm_kernel<2><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
+      conv_residual_norm_kernel<2><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk,
+                                                          clear_bound);
       break;
     case 3:
-      conv_residual_norm_kernel<3><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
+      conv_residual_norm_kernel<3><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk,
+                                                          clear_bound);
       break;
     case 4:
-      conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk);
+      conv_residual_norm_kernel<4><<<T, 256, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, gamma, eps, n_out, sk,
+                                                          clear_bound);
       break;
     default:
       return hipErrorInvalidValue;  // H > 8192
@@ -425,7 +433,7 @@ hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, cons
 hipError_t launch_conv_residual_norm_planes(const Planes& y, const Planes& coef, const uint16_t* base, int T, int H,
                                             int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                             const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
-                                            bool skip_anchor) {
+                                            bool skip_anchor, uint32_t* clear_bound) {
   if (T <= 0) return hipSuccess;
   if (H % 8 != 0 || H > 8 * kCrnPlanesMaxThreads || y.S < 1 || y.ld != H || y.plane < (size_t)T * H)
     return hipErrorInvalidValue;
@@ -433,7 +441,7 @@ hipError_t launch_conv_residual_norm_planes(const Planes& y, const Planes& coef,
   const int sk = skip_anchor ? 1 : 0;
 #define DFL_CRN_PLANES(S_)                                                                              \
   conv_residual_norm_planes_kernel<S_><<<T, threads, 0, stream>>>(y, coef, base, H, G, grp, residual, x_out, \
-                                                                  gamma, eps, n_out, sk)
+                                                                  gamma, eps, n_out, sk, clear_bound)
   switch (y.S) {
     case 2: DFL_CRN_PLANES(2); break;
     case 3: DFL_CRN_PLANES(3); break;

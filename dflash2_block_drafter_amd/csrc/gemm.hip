@@ -57,6 +57,7 @@ struct GemmArgs {
   float* partial;
   int splits;
   float* tile_max;  // EPI_F32, one split: [M, ceil(nsplit / 256)] row maxima of each 256-column tile of out0
+  uint32_t* tile_bound;  // with tile_max, optional: [M, kTileBoundSlots] (launch_gemm's declaration)
   // 4-bit affine weights (used instead of W): row-major packed [N, K/8] words with scales and
   // biases [N, K/64] bf16, or tile-contiguous blocks (q4_tiled_words)
   const uint32_t* Wq;
@@ -285,45 +286,96 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = mrow + i * 16 + e;
-        const int n = ncol + j * 16;
-        if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
-      }
-  if (p.tile_max && n0 < p.nsplit) {
-    // Row maxima of this tile over its first output's columns (< nsplit, which is N unless
-    // a second output takes the columns after it): within a lane over its TN columns, then
-    // over the 16 lanes that share a row, then over the WN wavefronts through LDS.  fmaxf
-    // skips NaN, so a tile's maximum is NaN only when all of its values are.
-    __shared__ float rmax[WN][BM];
+  if (!p.tile_max || n0 >= p.nsplit) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = -INFINITY;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          if (ncol + j * 16 < p.nsplit) v = fmaxf(v, acc[i][j][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int m = mrow + i * 16 + e;
+          const int n = ncol + j * 16;
+          if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
+        }
+    return;
+  }
+  // Row maxima of this tile over its first output's columns (< nsplit, which is N unless a
+  // second output takes the columns after it): within a lane over its TN columns, then over
+  // the 16 lanes that share a row, then over the WN wavefronts through LDS.  fmaxf skips NaN,
+  // so a tile's maximum is NaN only when all of its values are.
+  __shared__ float rmax[WN][BM];
+  __shared__ int rskip[BM];
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-        if ((lane & 15) == 0) rmax[wn][wm * (TM * 16) + i * 16 + (lane >> 4) * 4 + e] = v;
-      }
-    __syncthreads();
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if (ncol + j * 16 < p.nsplit) v = fmaxf(v, acc[i][j][e]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      if ((lane & 15) == 0) rmax[wn][wm * (TM * 16) + i * 16 + (lane >> 4) * 4 + e] = v;
+    }
+  __syncthreads();
+  const int tile = n0 / kGemmTileN;
+  const int ntl = (p.nsplit + kGemmTileN - 1) / kGemmTileN;
+  if (!p.tile_bound) {
     for (int r = tid; r < BM; r += NT) {
       const int m = m0 + r;
       if (m < p.M) {
         float v = rmax[0][r];
 #pragma unroll
         for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
-        p.tile_max[(size_t)m * ((p.nsplit + kGemmTileN - 1) / kGemmTileN) + n0 / kGemmTileN] = v;
+        p.tile_max[(size_t)m * ntl + tile] = v;
+      }
+      rskip[r] = 0;
+    }
+  } else {
+    // Four lanes per row read the row's slots (one 64-byte line) as other workgroups have
+    // filled them so far, with one device-scope load that bypasses this XCD's L2 (a stale
+    // slot is only smaller, so the bound stays valid); then the row's tile maximum goes into
+    // its own slot.
+    static_assert(BM * 4 % NT == 0 && kTileBoundSlots == 16, "four lanes of four slots per row, every lane");
+    for (int r4 = tid; r4 < BM * 4; r4 += NT) {
+      const int r = r4 >> 2, q = r4 & 3;
+      const int m = m0 + r;
+      float v = rmax[0][r];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
+      uint32_t lo = 0xFFFFFFFFu;
+      if (m < p.M) {
+        const uint32_t* slot = p.tile_bound + (size_t)m * kTileBoundSlots + q * 4;
+        u32x4_t s4;
+        asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(s4) : "v"(slot) : "memory");
+        lo = min(min(s4[0], s4[1]), min(s4[2], s4[3]));
+      }
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, 1, 64));
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, 2, 64));
+      if (q == 0) {
+        if (m < p.M) {
+          p.tile_max[(size_t)m * ntl + tile] = v;
+          if (v == v)
+            __hip_atomic_fetch_max(p.tile_bound + (size_t)m * kTileBoundSlots + tile % kTileBoundSlots,
+                                   float_order(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        rskip[r] = m < p.M && lo != 0u && v < order_float(lo);  // 0: a slot still empty
       }
     }
   }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = mrow + i * 16 + e;
+      if (m >= p.M || rskip[m - m0]) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = ncol + j * 16;
+        if (n < p.N) store_out(p, m, n, acc[i][j][e]);
+      }
+    }
 }
 
 // MINB is the minimum number of wavefronts per SIMD the registers must allow (the second
@@ -1125,7 +1177,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool tile_max) {
 namespace {
 
 GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K, int epi,
-                   void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial, float* tile_max) {
+                   void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial, float* tile_max,
+                   uint32_t* tile_bound = nullptr) {
   GemmArgs p;
   p.A = A;
   p.W = W.w;
@@ -1146,6 +1199,7 @@ GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightR
   p.partial = partial;
   p.splits = pl.splits;
   p.tile_max = tile_max;
+  p.tile_bound = tile_max ? tile_bound : nullptr;
   return p;
 }
 
@@ -1253,7 +1307,7 @@ hipError_t launch_reduce(const GemmArgs& p, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
-                       hipStream_t stream, float* tile_max) {
+                       hipStream_t stream, float* tile_max, uint32_t* tile_bound) {
   // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup); a
   // tile may not straddle the two outputs
   if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0 ||
@@ -1284,7 +1338,8 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
     if (e != hipSuccess) return e;
     return launch_reduce(pb, stream);
   }
-  const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max);
+  const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max,
+                               tile_bound);
   hipError_t e = launch_main(p, pl, W, stream);
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_reduce(p, stream);
@@ -1292,11 +1347,12 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
 
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
-                       float* partial, hipStream_t stream, float* tile_max) {
+                       float* partial, hipStream_t stream, float* tile_max, uint32_t* tile_bound) {
   WeightRef w;
   w.w = W;
   w.tiled = w_tiled;
-  return launch_gemm(pl, A, lda, w, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, stream, tile_max);
+  return launch_gemm(pl, A, lda, w, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, stream, tile_max,
+                     tile_bound);
 }
 
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,

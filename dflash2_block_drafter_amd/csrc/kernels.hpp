@@ -45,7 +45,7 @@ struct WeightRef {
 };
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
-                       hipStream_t stream, float* tile_max = nullptr);
+                       hipStream_t stream, float* tile_max = nullptr, uint32_t* tile_bound = nullptr);
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,
                                 int K, float* partial, hipStream_t stream);
 // Tile-contiguous 4-bit weights: per (256-row tile, 64-wide K step) four 64-row groups of
@@ -63,10 +63,19 @@ hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint1
 // tile_max (EPI_F32 with an unsplit plan only): also write the row maxima of every
 // kGemmTileN-column tile of out0's columns, [M, ceil(nsplit / kGemmTileN)] (nsplit = N
 // without out1; with out1, nsplit must be a multiple of kGemmTileN).
+// tile_bound (with tile_max; [M, kTileBoundSlots] uint32, zero before the launch): slot s of
+// row m collects, in float_order's map, the largest maximum of row m over the tiles t with
+// t % kTileBoundSlots == s.  Once every slot of a row is filled, their least value is reached
+// by kTileBoundSlots logits of distinct tiles, so it is at most the row's kTileBoundSlots-th
+// largest logit; a tile whose row maximum is below it (as floats) cannot hold any of the
+// row's top kTileBoundSlots, and its values of that row are not stored.  A top-K with K <=
+// kTileBoundSlots stays exact when it reads only tiles whose maximum reaches that bound.
 constexpr int kGemmTileN = 256;
+constexpr int kTileBoundSlots = 16;
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
-                       int nsplit, float* partial, hipStream_t stream, float* tile_max = nullptr);
+                       int nsplit, float* partial, hipStream_t stream, float* tile_max = nullptr,
+                       uint32_t* tile_bound = nullptr);
 // y = A . W^T left as fp32 planes for the consumer: pl.splits planes [M, N] at plane stride
 // M*N in `partial` (one plane, the plain result, when the plan does not split K).
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,
@@ -137,11 +146,12 @@ hipError_t launch_context_kv_store_ragged(const uint16_t* kv, int rows, int B, i
 // conv1(y); n_out = RMSNorm(x_out; gamma).  One workgroup per row; x_out may alias
 // residual; H <= 8192.
 // skip_anchor: n_out holds only rows t % G != 0, packed (row (t / G) * (G - 1) + t % G - 1),
-// as the head reads them after the last layer.
+// as the head reads them after the last layer; with skip_anchor, clear_bound (optional)
+// receives kTileBoundSlots zeros per packed row (the head's tile_bound slots).
 hipError_t launch_conv_residual_norm(const uint16_t* y, const Planes& coef, const uint16_t* base, int T, int H,
                                      int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                      const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
-                                     bool skip_anchor = false);
+                                     bool skip_anchor = false, uint32_t* clear_bound = nullptr);
 
 // The same with y given as the fp32 split-K planes of its projection ([y.S][T][H], plane
 // stride y.plane >= T * H): each row's sum over the planes, in plane order, is rounded to
@@ -151,7 +161,7 @@ constexpr int kCrnPlanesMaxH = 5120;
 hipError_t launch_conv_residual_norm_planes(const Planes& y, const Planes& coef, const uint16_t* base, int T, int H,
                                             int G, int grp, const uint16_t* residual, uint16_t* x_out,
                                             const uint16_t* gamma, float eps, uint16_t* n_out, hipStream_t stream,
-                                            bool skip_anchor = false);
+                                            bool skip_anchor = false, uint32_t* clear_bound = nullptr);
 
 // Grouped dynamic conv; side selects base[side]; residual may be null.  coef_next (side 0
 // only; coef then holds both sides, side 1 at column 2 * ng): also write side 1's summed
@@ -180,8 +190,12 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
 // tile_max writes them): only tiles whose maximum reaches the K-th largest tile maximum
 // are read.
 // id_map (device, optional): the reported id of column c is id_map[c] (a draft vocabulary).
+// tile_bound (optional, K <= kTileBoundSlots): the slots launch_gemm filled; when all of a
+// row's are filled, only tiles whose maximum also reaches their least value are read (the
+// logits of the others may never have been stored).
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
-                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map = nullptr);
+                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map = nullptr,
+                             const uint32_t* tile_bound = nullptr);
 // Row maxima of every kGemmTileN-column tile of fp32 logits [N, V] -> [N, ceil(V / kGemmTileN)].
 hipError_t launch_tile_maxima(const float* logits, int N, int V, float* tile_max, hipStream_t stream);
 // Exact top-K of each fp32 row (value descending, id ascending): tile maxima into ws
@@ -204,7 +218,8 @@ hipError_t launch_score_edges(const int32_t* cand, const float* unary, const flo
 // requests of S slots in one more launch (one workgroup per request, the scores on the matrix
 // cores): logits [B*S, V] with tile maxima [B*S, ceil(V/256)], z [B*S, R]; cand/unary
 // [B*S, K] and tokens [B, S] out, scores [B*S, K, K] out when not NULL.  Requires
-// select_tokens_fits(S, K, R): S <= 64, K <= 16, R a multiple of 4 in [4, 64].
+// select_tokens_fits(S, K, R): S <= 64, K <= 16, R a multiple of 4 in [4, 64].  tile_bound:
+// as for launch_topk_tiles.
 bool select_tokens_fits(int S, int K, int R);
 // launch_select_tokens without tile maxima (tile_max = nullptr): each row's workgroup scans
 // its logits, keeping the row's tile maxima in LDS, so ceil(V / 256) <= kSelectScanMaxTiles.
@@ -212,7 +227,8 @@ constexpr int kSelectScanMaxTiles = 4096;
 hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
                                 const int32_t* id_map, const float* z, int R, const int32_t* anchors,
                                 const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,
-                                float* scores, int32_t* tokens, hipStream_t stream);
+                                float* scores, int32_t* tokens, hipStream_t stream,
+                                const uint32_t* tile_bound = nullptr);
 hipError_t launch_select_path(const float* scores, const int32_t* cand, int B, int S, int K,
                               int32_t* tokens, hipStream_t stream);
 // Selector projection z = h . proj^T, fp32 [N, R], 16 rows per workgroup on the matrix cores

@@ -92,16 +92,6 @@ constexpr int kTmPerLane = 16;
 constexpr int kTilesInFlight = 4;
 constexpr int kFastTilesInFlight = 8;  // the fast path's loads: usually every qualifying tile at once
 
-// Order-preserving map of a float to an unsigned integer (NaN excluded by the callers), and
-// back.
-__device__ __forceinline__ uint32_t float_order(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return b & 0x80000000u ? ~b : b | 0x80000000u;
-}
-__device__ __forceinline__ float order_float(uint32_t u) {
-  return __uint_as_float(u & 0x80000000u ? u & 0x7FFFFFFFu : ~u);
-}
-
 // Merge lanes 0..K-1 of the other three wavefronts' lists (lv/li) into wavefront 0's list.
 __device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*lv)[64], const int (*li)[64],
                                                  int K, int lane) {
@@ -120,7 +110,8 @@ __device__ __forceinline__ void merge_wave_lists(TopkMerger& mg, const float (*l
 // 256-thread workgroup: the body of topk_tiles_kernel and of topk_scan_kernel.
 __device__ __forceinline__ void topk_row(const float* tm, const float* __restrict__ src, int V, int ntiles, int K,
                                          int row, int32_t* __restrict__ ids, float* __restrict__ vals,
-                                         const int32_t* __restrict__ id_map) {
+                                         const int32_t* __restrict__ id_map,
+                                         const uint32_t* __restrict__ bound = nullptr) {
   constexpr int TW = kGemmTileN;
   constexpr int TPL = TW / 64;                 // values of a tile per lane
   constexpr int CH = 64 * kTmPerLane;          // tile maxima per round
@@ -176,7 +167,17 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
       for (int i = 0; i < 4; ++i) n += __popcll(__ballot(g[i] == g[i] && u[i] >= tryu));
       if (n >= K) cu = tryu;
     }
-    const float th = groups >= K ? order_float(cu) : -INFINITY;  // the same in every lane
+    float th = groups >= K ? order_float(cu) : -INFINITY;  // the same in every lane
+    if (bound) {
+      // the head's bound slots (K <= kTileBoundSlots): once all are filled their least value
+      // is reached by kTileBoundSlots logits of distinct tiles, so it is a theta too, and the
+      // tiles below it may never have been stored
+      uint32_t b = lane < kTileBoundSlots ? bound[lane] : 0xFFFFFFFFu;
+#pragma unroll
+      for (int o = 1; o < kTileBoundSlots; o <<= 1) b = min(b, (uint32_t)__shfl_xor((int)b, o, 64));
+      b = (uint32_t)__shfl((int)b, 0, 64);
+      if (b != 0u) th = fmaxf(th, order_float(b));
+    }
     if (lane == 0) theta_s = th;
     if (one_round) {
       int cnt = 0;
@@ -334,9 +335,11 @@ __global__ __launch_bounds__(256) void topk_tiles_kernel(const float* __restrict
                                                          const float* __restrict__ tile_max, int ntiles,
                                                          int K, int32_t* __restrict__ ids,
                                                          float* __restrict__ vals,
-                                                         const int32_t* __restrict__ id_map) {
+                                                         const int32_t* __restrict__ id_map,
+                                                         const uint32_t* __restrict__ tile_bound) {
   const int row = blockIdx.x;
-  topk_row(tile_max + (size_t)row * ntiles, logits + (size_t)row * V, V, ntiles, K, row, ids, vals, id_map);
+  topk_row(tile_max + (size_t)row * ntiles, logits + (size_t)row * V, V, ntiles, K, row, ids, vals, id_map,
+           tile_bound ? tile_bound + (size_t)row * kTileBoundSlots : nullptr);
 }
 
 // Maximum over each aligned group of 16 lanes, left in every lane of the group, with DPP
@@ -959,10 +962,12 @@ hipError_t launch_tile_maxima(const float* logits, int N, int V, float* tile_max
 }
 
 hipError_t launch_topk_tiles(const float* logits, int N, int V, int K, const float* tile_max,
-                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map) {
+                             int32_t* ids, float* vals, hipStream_t stream, const int32_t* id_map,
+                             const uint32_t* tile_bound) {
   if (N <= 0) return hipSuccess;
+  if (tile_bound && K > kTileBoundSlots) return hipErrorInvalidValue;
   const int ntiles = (V + kGemmTileN - 1) / kGemmTileN;
-  topk_tiles_kernel<<<N, 256, 0, stream>>>(logits, V, tile_max, ntiles, K, ids, vals, id_map);
+  topk_tiles_kernel<<<N, 256, 0, stream>>>(logits, V, tile_max, ntiles, K, ids, vals, id_map, tile_bound);
   return hipGetLastError();
 }
 
@@ -1025,12 +1030,12 @@ hipError_t launch_topk_scan(const float* logits, int N, int V, int K, int32_t* c
 hipError_t launch_select_tokens(const float* logits, const float* tile_max, int B, int S, int V, int K,
                                 const int32_t* id_map, const float* z, int R, const int32_t* anchors,
                                 const uint16_t* pred, const uint16_t* succ, int Vcb, int32_t* cand, float* unary,
-                                float* scores, int32_t* tokens, hipStream_t stream) {
+                                float* scores, int32_t* tokens, hipStream_t stream, const uint32_t* tile_bound) {
   if (B <= 0) return hipSuccess;
   if (!select_tokens_fits(S, K, R)) return hipErrorInvalidValue;
   hipError_t e;
   if (tile_max) {
-    e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map);
+    e = launch_topk_tiles(logits, B * S, V, K, tile_max, cand, unary, stream, id_map, tile_bound);
   } else {
     // no tile maxima given: each row's workgroup scans its logits and then takes its top-K
     e = launch_topk_scan(logits, B * S, V, K, cand, unary, id_map, nullptr, 0, nullptr, 0, nullptr, stream);

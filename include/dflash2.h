@@ -196,7 +196,11 @@ int dfl_bind_target(dfl_drafter* d, const dfl_bf16* lm_head, const int32_t* voca
  *             dfl_bind_target, selects the bound copy.
  *   tokens:   [B, G-1] int32 device output ([P2] returns the proposals on the device).
  *   logits_out: NULL or [B, G-1, V] float32 device output of the head ([B, G-1, n_vocab]
- *             when a bound draft vocabulary is used).
+ *             when a bound draft vocabulary is used).  NULL: the logits stay in the
+ *             workspace; with more than 128 head rows (B*(G-1)) and top_k <= 16 the head
+ *             then stores only the 256-column tiles of a row whose maximum reaches a value
+ *             that 16 of the row's logits in distinct tiles reach (the others cannot hold a
+ *             candidate).  The tokens are the same either way.
  *   G must satisfy 2 <= G <= block_size ([P3] `supports_zero_draft_rows` is false). */
 int dfl_draft_block(dfl_drafter* d, const dfl_bf16* embeds, const int32_t* anchors, int B, int G,
                     const dfl_bf16* const* K, const dfl_bf16* const* V, int Lcap, int Lmax,

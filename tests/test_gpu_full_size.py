@@ -114,6 +114,34 @@ def test_full_drafter_end_to_end_properties():
     dr.close()
 
 
+@pytest.mark.parametrize("w", [configs.FULL, configs.LONG], ids=["full", "long"])
+def test_draft_without_logits_matches_with_logits(w):
+    """Without a logits output the head stores only the logit tiles that can hold one of a
+    row's top 16 (by the bound its workgroups build up) and the top-K reads only those; the
+    tokens must be the ones drafted when every logit is stored, and each among its slot's
+    top-K logits."""
+    d = w.dims
+    say(f"{w.name}: draft with and without logits, B={w.batch} L={w.ctx_len}")
+    weights = synth.drafter_weights(w, device=DEV)
+    tgt = synth.target_inputs(w, device=DEV, with_taps=not w.kv_given)
+    dr = Drafter(d, weights)
+    if w.kv_given:
+        K, V = map(list, zip(*(synth.given_kv(w, i, device=DEV) for i in range(d.layers))))
+    else:
+        K, V = dr.alloc_kv(w.batch, w.ctx_len)
+        dr.materialize(tgt["taps"], K, V)
+    dr.bind_target(tgt["lm_head"])
+    args = (tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], None)
+    t_full, lg = dr.draft(*args, want_logits=True)
+    t_a = dr.draft(*args).clone()
+    t_b = dr.draft(*args).clone()   # the workspace now holds the previous block's logits
+    torch.cuda.synchronize()
+    assert torch.equal(t_a, t_full), "tokens differ when the head skips tiles"
+    assert torch.equal(t_b, t_full)
+    _drafted_tokens_are_topk(t_full.cpu().numpy(), lg.cpu().numpy(), d.top_k)
+    dr.close()
+
+
 def test_head_projection_full_size_sampled_columns():
     """The head GEMM at its full size (M = B*(G-1) = 120, V = 248320, H = 5120), row-major
     weight as the target lends it; the oracle computes 512 sampled vocabulary columns."""
