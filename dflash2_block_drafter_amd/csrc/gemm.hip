@@ -286,7 +286,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         }
     return;
   }
-  if (!p.tile_max || n0 >= p.nsplit) {
+  // Without a bound every value is stored, first, so the stores drain while the tile maxima
+  // are reduced.
+  if (!p.tile_max || n0 >= p.nsplit || !p.tile_bound) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -297,7 +299,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
           const int n = ncol + j * 16;
           if (m < p.M && n < p.N) store_out(p, m, n, acc[i][j][e]);
         }
-    return;
+    if (!p.tile_max || n0 >= p.nsplit) return;
   }
   // Row maxima of this tile over its first output's columns (< nsplit, which is N unless a
   // second output takes the columns after it): within a lane over its TN columns, then over
@@ -329,38 +331,37 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
         for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
         p.tile_max[(size_t)m * ntl + tile] = v;
       }
-      rskip[r] = 0;
     }
-  } else {
-    // Four lanes per row read the row's slots (one 64-byte line) as other workgroups have
-    // filled them so far, with one device-scope load that bypasses this XCD's L2 (a stale
-    // slot is only smaller, so the bound stays valid); then the row's tile maximum goes into
-    // its own slot.
-    static_assert(BM * 4 % NT == 0 && kTileBoundSlots == 16, "four lanes of four slots per row, every lane");
-    for (int r4 = tid; r4 < BM * 4; r4 += NT) {
-      const int r = r4 >> 2, q = r4 & 3;
-      const int m = m0 + r;
-      float v = rmax[0][r];
+    return;
+  }
+  // Four lanes per row read the row's slots (one 64-byte line) as other workgroups have
+  // filled them so far, with one device-scope load that bypasses this XCD's L2 (a stale
+  // slot is only smaller, so the bound stays valid); then the row's tile maximum goes into
+  // its own slot.
+  static_assert(BM * 4 % NT == 0 && kTileBoundSlots == 16, "four lanes of four slots per row, every lane");
+  for (int r4 = tid; r4 < BM * 4; r4 += NT) {
+    const int r = r4 >> 2, q = r4 & 3;
+    const int m = m0 + r;
+    float v = rmax[0][r];
 #pragma unroll
-      for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
-      uint32_t lo = 0xFFFFFFFFu;
+    for (int w = 1; w < WN; ++w) v = fmaxf(v, rmax[w][r]);
+    uint32_t lo = 0xFFFFFFFFu;
+    if (m < p.M) {
+      const uint32_t* slot = p.tile_bound + (size_t)m * kTileBoundSlots + q * 4;
+      u32x4_t s4;
+      asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(s4) : "v"(slot) : "memory");
+      lo = min(min(s4[0], s4[1]), min(s4[2], s4[3]));
+    }
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, 1, 64));
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, 2, 64));
+    if (q == 0) {
       if (m < p.M) {
-        const uint32_t* slot = p.tile_bound + (size_t)m * kTileBoundSlots + q * 4;
-        u32x4_t s4;
-        asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(s4) : "v"(slot) : "memory");
-        lo = min(min(s4[0], s4[1]), min(s4[2], s4[3]));
+        p.tile_max[(size_t)m * ntl + tile] = v;
+        if (v == v)
+          __hip_atomic_fetch_max(p.tile_bound + (size_t)m * kTileBoundSlots + tile % kTileBoundSlots,
+                                 float_order(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, 1, 64));
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, 2, 64));
-      if (q == 0) {
-        if (m < p.M) {
-          p.tile_max[(size_t)m * ntl + tile] = v;
-          if (v == v)
-            __hip_atomic_fetch_max(p.tile_bound + (size_t)m * kTileBoundSlots + tile % kTileBoundSlots,
-                                   float_order(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        rskip[r] = m < p.M && lo != 0u && v < order_float(lo);  // 0: a slot still empty
-      }
+      rskip[r] = m < p.M && lo != 0u && v < order_float(lo);  // 0: a slot still empty
     }
   }
   __syncthreads();
