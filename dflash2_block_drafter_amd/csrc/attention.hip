@@ -127,9 +127,11 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   const int dg = tid % DG;
   const int kg = tid / DG;
   u32x4_t kreg[R][ROWS_PER], vreg[R][ROWS_PER];
-  // tile t of this workgroup (uniform); tiles past the last repeat it, rows past a tile's
-  // end repeat its last row
+  // tile t of this workgroup (uniform); rows past a tile's end repeat its last row.  Loads
+  // for tiles past the last (the ring's tail) all read the last tile's first 16 bytes, one
+  // line per instruction, so the ring costs no second read of a tile.
   auto tile_load = [&](u32x4_t (&kr)[ROWS_PER], u32x4_t (&vr)[ROWS_PER], int t) {
+    const bool live = t < ntiles;
     t = min(t, ntiles - 1);
     const bool blk = has_block && t == 0;
     const uint16_t* kp = blk ? kblk : kctx;
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
     const int rlast = blk ? a.G - 1 : kend - 1;
 #pragma unroll
     for (int i = 0; i < ROWS_PER; ++i) {
-      const uint32_t off = static_cast<uint32_t>(min(r0 + kg * ROWS_PER + i, rlast)) * stride + dg * 16;
+      const uint32_t off = live ? static_cast<uint32_t>(min(r0 + kg * ROWS_PER + i, rlast)) * stride + dg * 16
+                                : static_cast<uint32_t>(r0) * stride;
       kr[i] = vm_load16_nt(kp, off);
       vr[i] = vm_load16_nt(vp, off);
     }
