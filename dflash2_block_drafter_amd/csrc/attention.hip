@@ -212,8 +212,8 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < KT / 16; ++kt)
       tmax = fmaxf(tmax, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = bfly16(tmax, OpMax{});
+    tmax = bfly32(tmax, OpMax{});
     const float mnew = fmaxf(m, tmax * a.scale_log2);
     // a query whose keys so far are all masked (sliding window) keeps m = -inf, l = 0, o = 0:
     // msafe keeps the exponents finite so that every weight below is exactly 0
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
         s[kt][e] = p;
         psum += p;
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum = bfly16(psum, OpAdd{});
+    psum = bfly32(psum, OpAdd{});
     l = l * alpha + psum;
     m = mnew;
 #pragma unroll

@@ -50,17 +50,48 @@ __device__ __forceinline__ u32x4_t pack8(const float* f) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Butterfly steps of the wave reductions without an LDS round trip: gfx950's row-swap
+// permutes for the lane distances 32 and 16 (with v as both operands, the two results hold v
+// of the lower and of the upper lane of each pair), DPP moves within a row of 16 lanes.
+// op(lo, hi) gives both lanes of a pair the value op(v[lane], v[lane ^ d]) has (op
+// commutative), so a sum adds in exactly the order of the xor tree.
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+template <class Op>
+__device__ __forceinline__ float bfly32(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+template <class Op>
+__device__ __forceinline__ float bfly16(float v, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// CTRL: a DPP lane move within each row of 16 (row_ror:8 is xor 8; quad_perm 0x4E and 0xB1
+// are xor 2 and xor 1; row_ror:4 matches xor 4 once the values repeat every 8 lanes, i.e.
+// after the xor-8 step)
+template <int CTRL, class Op>
+__device__ __forceinline__ float bfly_dpp(float v, Op op) {
+  return op(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Reductions over the 64 lanes in the order of the xor tree 32, 16, 8, 4, 2, 1.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = bfly32(v, op);
+  v = bfly16(v, op);
+  v = bfly_dpp<kDppRor8>(v, op);
+  v = bfly_dpp<kDppRor4>(v, op);
+  v = bfly_dpp<kDppXor2>(v, op);
+  return bfly_dpp<kDppXor1>(v, op);
 }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd{}); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 

@@ -157,7 +157,10 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     const float x = v[e] * inv * bf16_to_f32(g[e0 + e]);
-    const float partner = __shfl_xor(x, 32, 64);
+    // lane ^ 32's value: the row-swap permute leaves it in the second result in the lower
+    // half of the wave and in the first in the upper half
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float partner = __uint_as_float(first ? sw[1] : sw[0]);
     const float c = rc[half_lane * EPL + e], s = rs[half_lane * EPL + e];
     // rotate_half: first half x1 c - x2 s, second half x2 c + x1 s
     out[e] = f32_to_bf16(first ? x * c - partner * s : x * c + partner * s);
