@@ -93,6 +93,24 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, OpAdd{}); }
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, OpMax{}); }
 
+// Maximum (fmaxf: NaN only if all are) over each row of 16 lanes, in every lane of the row;
+// any order gives the same maximum.
+__device__ __forceinline__ float row16_max(float v) {
+  v = bfly_dpp<kDppXor1>(v, OpMax{});
+  v = bfly_dpp<kDppXor2>(v, OpMax{});
+  v = bfly_dpp<kDppRor4>(v, OpMax{});
+  return bfly_dpp<kDppRor8>(v, OpMax{});
+}
+// Unsigned minimum over each row of 16 lanes (or, with QUAD, each quad), in every lane of it.
+template <bool QUAD = false>
+__device__ __forceinline__ uint32_t row16_umin(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor2, 0xF, 0xF, false));
+  if (QUAD) return v;
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRor4, 0xF, 0xF, false));
+  return min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRor8, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }

@@ -315,8 +315,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         if (ncol + j * 16 < p.nsplit) v = fmaxf(v, acc[i][j][e]);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      v = row16_max(v);
       if ((lane & 15) == 0) rmax[wn][wm * (TM * 16) + i * 16 + (lane >> 4) * 4 + e] = v;
     }
   __syncthreads();
@@ -352,8 +351,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x4_t (
       asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(s4) : "v"(slot) : "memory");
       lo = min(min(s4[0], s4[1]), min(s4[2], s4[3]));
     }
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, 1, 64));
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, 2, 64));
+    lo = row16_umin<true>(lo);
     if (q == 0) {
       if (m < p.M) {
         p.tile_max[(size_t)m * ntl + tile] = v;

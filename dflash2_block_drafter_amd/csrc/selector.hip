@@ -70,8 +70,7 @@ __global__ __launch_bounds__(256) void tile_rowmax_kernel(const float* __restric
   }
 #pragma unroll
   for (int p = 0; p < PASS; ++p) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m[p] = fmaxf(m[p], __shfl_xor(m[p], o, 64));
+    m[p] = row16_max(m[p]);
     const int t = t0 + p * 4 + q;
     if (l16 == 0 && t < ntiles) tile_max[(size_t)row * ntiles + t] = m[p];
   }
@@ -173,9 +172,8 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
       // is reached by kTileBoundSlots logits of distinct tiles, so it is a theta too, and the
       // tiles below it may never have been stored
       uint32_t b = lane < kTileBoundSlots ? bound[lane] : 0xFFFFFFFFu;
-#pragma unroll
-      for (int o = 1; o < kTileBoundSlots; o <<= 1) b = min(b, (uint32_t)__shfl_xor((int)b, o, 64));
-      b = (uint32_t)__shfl((int)b, 0, 64);
+      static_assert(kTileBoundSlots == 16, "one row of lanes");
+      b = (uint32_t)__builtin_amdgcn_readfirstlane((int)row16_umin(b));
       if (b != 0u) th = fmaxf(th, order_float(b));
     }
     if (lane == 0) theta_s = th;
