@@ -122,6 +122,41 @@ def test_wide_head_on_big_tiles():
     dr.close()
 
 
+def test_head_skip_keeps_ties_at_the_bound():
+    """Above 128 head rows, a draft with no logits output stores only the logit tiles that can
+    hold one of a row's top candidates.  With every head row present three times, 10922
+    columns apart (on the 256-row tiles every tile accumulates in one order, so the copies'
+    logits are equal bit for bit), a row's K-th value has tied copies in other tiles; the
+    tokens must equal those drafted with every tile stored."""
+    import dataclasses
+    w = configs.with_batch(configs.TINY, 37)
+    w = dataclasses.replace(w, name="tiny_tied_head", dims=dataclasses.replace(w.dims, vocab=32768))
+    d = w.dims
+    weights = {k: v.to(DEV) for k, v in synth.drafter_weights(w).items()}
+    tgt = {k: v.to(DEV) for k, v in synth.target_inputs(w).items()}
+    third = d.vocab // 3
+    head = tgt["lm_head"].clone()
+    head[third:2 * third] = head[:third]
+    head[2 * third:3 * third] = head[:third]
+    dr = Drafter(d, weights, tap_layer_ids=list(range(d.n_taps)))
+    K, V = dr.alloc_kv(w.batch, w.ctx_len)
+    dr.materialize(tgt["taps"], K, V)
+    dr.bind_target(head)
+    args = (tgt["embeds"], tgt["anchors"], K, V, w.ctx_len, tgt["ctx_len"], tgt["pos0"], None)
+    t_full, lg = dr.draft(*args, want_logits=True)
+    t_a = dr.draft(*args).clone()
+    t_b = dr.draft(*args).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(lg[..., :third], lg[..., third:2 * third])
+    assert torch.equal(lg[..., :third], lg[..., 2 * third:3 * third])
+    assert torch.equal(t_a, t_full) and torch.equal(t_b, t_full)
+    # each drafted token is among its slot's top-K logits
+    lgn, tk = lg.cpu().numpy().reshape(-1, d.vocab), t_full.cpu().numpy().reshape(-1)
+    kth = -np.partition(-lgn, d.top_k - 1, axis=1)[:, d.top_k - 1]
+    assert np.all(lgn[np.arange(lgn.shape[0]), tk] >= kth)
+    dr.close()
+
+
 def test_bound_head_matches_borrowed_head():
     # binding the target's head (a tile-contiguous copy) changes how the head projection
     # reads it, not what it computes: the logits are identical bit for bit.  The bound copy
