@@ -77,6 +77,30 @@ __device__ __forceinline__ void planes_sum_pair(const Planes& pl, size_t off0, s
   }
 }
 
+// The same with the plane count S a compile-time constant: all 2 S loads are issued before
+// the first add (one round trip), the adds in the same plane order; S = 0 takes pl.S.
+template <int S>
+__device__ __forceinline__ void planes_sum_pair_n(const Planes& pl, size_t off0, size_t off1, float& s0, float& s1) {
+  if constexpr (S == 0) {
+    planes_sum_pair(pl, off0, off1, s0, s1);
+  } else {
+    const float* q = pl.p;
+    float v0[S], v1[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      v0[i] = q[(size_t)i * pl.plane + off0];
+      v1[i] = q[(size_t)i * pl.plane + off1];
+    }
+    s0 = v0[0];
+    s1 = v1[0];
+#pragma unroll
+    for (int i = 1; i < S; ++i) {
+      s0 += v0[i];
+      s1 += v1[i];
+    }
+  }
+}
+
 // R consecutive rows of one block (R divides G) for kConvCh channels per workgroup of
 // kConvCh/8 threads: the R + 1 input rows are loaded once (row t-1 of the first row only
 // when it is in the block) and each later row reuses its predecessor from registers.
@@ -86,7 +110,7 @@ __device__ __forceinline__ void planes_sum_pair(const Planes& pl, size_t off0, s
 // plane instead of every split of the kernel projection.
 constexpr int kConvCh = 1024;
 
-template <int R>
+template <int R, int S>
 __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Planes coef,
                                                            const uint16_t* __restrict__ base, int side,
                                                            int H, int G, int grp,
@@ -118,7 +142,7 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Pl
       const int col = i < ngw ? g0 + i : ng + g0 + (i - ngw);
       if (coef_next) {
         float here, next;
-        planes_sum_pair(coef, crow + col, crow + 2 * ng + col, here, next);
+        planes_sum_pair_n<S>(coef, crow + col, crow + 2 * ng + col, here, next);
         cs[r][i] = here;
         coef_next[(size_t)(t0 + r) * 2 * ng + col] = next;
       } else {
@@ -505,16 +529,25 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
     }
     return hipGetLastError();
   }
-  switch (R) {
-    case 4:
-      conv_kernel<4><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
-      break;
-    case 2:
-      conv_kernel<2><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
-      break;
-    default:
-      conv_kernel<1><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, out, coef_next);
+  // the kernel projection's plane count as a compile-time constant where the plans put it
+  // (one round trip for all of a thread's plane loads), else read from coef
+#define DFL_CONV_S(R_)                                                                                        \
+  switch (coef.S) {                                                                                          \
+    case 8: conv_kernel<R_, 8><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual,   \
+                                                                 out, coef_next); break;                     \
+    case 10: conv_kernel<R_, 10><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, \
+                                                                   out, coef_next); break;                   \
+    case 12: conv_kernel<R_, 12><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual, \
+                                                                   out, coef_next); break;                   \
+    default: conv_kernel<R_, 0><<<grid, kConvCh / 8, 0, stream>>>(y, coef, base, side, H, G, grp, residual,  \
+                                                                  out, coef_next);                           \
   }
+  switch (R) {
+    case 4: DFL_CONV_S(4); break;
+    case 2: DFL_CONV_S(2); break;
+    default: DFL_CONV_S(1);
+  }
+#undef DFL_CONV_S
   return hipGetLastError();
 }
 
