@@ -126,8 +126,22 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
     const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ gamma2, float eps, double log_theta,
     const int32_t* __restrict__ pos0, int rows_per_req, int pos_offset) {
   constexpr int EPL = D / 64;
+  typedef float ev_t __attribute__((ext_vector_type(EPL)));
   const int r = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int half_lane = lane & 31;
+  const int e0 = (lane >> 5) * (D / 2) + half_lane * EPL;  // this lane's first element
+  // Up to eight planes: their loads go out first (row and head clamped in range), so they are
+  // in flight while the rotary pairs are computed.
+  const bool live = r < rows && h < heads;
+  const size_t off = (size_t)min(r, rows - 1) * src.ld + min(h, heads - 1) * D + e0;
+  ev_t raw[8];
+  if (src.S <= 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      raw[i] = *reinterpret_cast<const ev_t*>(src.p + (size_t)min(i, src.S - 1) * src.plane + off);
+  }
   // the row's D/2 rotary (cos, sin) pairs, computed once for the workgroup's four heads
   __shared__ float rc[D / 2], rs[D / 2];
   if (r < rows && threadIdx.x < D / 2) {
@@ -135,12 +149,19 @@ __global__ __launch_bounds__(256) void head_norm_rope_planes_kernel(
     rope_cs(pos, threadIdx.x, D, log_theta, &rc[threadIdx.x], &rs[threadIdx.x]);
   }
   __syncthreads();
-  if (r >= rows || h >= heads) return;
-  const int lane = threadIdx.x & 63;
-  const int half_lane = lane & 31;
-  const int e0 = (lane >> 5) * (D / 2) + half_lane * EPL;  // this lane's first element
+  if (!live) return;
   float v[EPL];
-  planes_sum<EPL>(src, (size_t)r * src.ld + h * D + e0, v);
+  if (src.S <= 8) {
+    // the planes in order 0, 1, 2, ..., as planes_sum adds them
+    ev_t acc = raw[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if (i < src.S) acc += raw[i];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = acc[e];
+  } else {
+    planes_sum<EPL>(src, off, v);
+  }
   uint16_t* out = dst + (size_t)r * ldd + h * D + e0;
   if (h >= rope_heads) {
 #pragma unroll
