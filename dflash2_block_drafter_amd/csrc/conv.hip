@@ -381,13 +381,30 @@ __global__ __launch_bounds__(kCrnPlanesMaxThreads) void conv_residual_norm_plane
   ConvIn in;
   in.b0 = *reinterpret_cast<const u32x4_t*>(base + (size_t)2 * H + c0);
   in.b1 = *reinterpret_cast<const u32x4_t*>(base + (size_t)3 * H + c0);
+  // With one coefficient plane (the side-1 deltas the prepare summed) this thread's share of
+  // the row's 2 * ng coefficients (at most two: grp >= 8) is loaded here too, so one round
+  // trip covers every input of the row; more planes are staged after the sums.
+  const bool one_plane = coef.S == 1;
+  const int nthr = static_cast<int>(blockDim.x);
+  float cv0 = 0.f, cv1 = 0.f;
+  if (one_plane) {
+    const float* crow = coef.p + (size_t)t * coef.ld;
+    if (tid < 2 * ng) cv0 = crow[tid];
+    if (tid + nthr < 2 * ng) cv1 = crow[tid + nthr];
+  }
   {
     float cur[8], prev[8];
     planes_sum8_pair<S>(y, (size_t)t * y.ld + c0, (size_t)(has_prev ? t - 1 : t) * y.ld + c0, cur, prev);
     in.cur = pack8(cur);
     in.prev = has_prev ? pack8(prev) : u32x4_t{0u, 0u, 0u, 0u};
   }
-  stage_coef(coef, t, ng, 0, ng, cs);
+  if (one_plane) {
+    if (tid < 2 * ng) cs[tid] = cv0;
+    if (tid + nthr < 2 * ng) cs[tid + nthr] = cv1;
+    __syncthreads();
+  } else {
+    stage_coef(coef, t, ng, 0, ng, cs);
+  }
   float xv[8];
   float ss = 0.f;
   if (live) {
