@@ -72,6 +72,23 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   const int hpg = a.NH / a.NKV;
   const int lg = lane >> 4;  // lane group
 
+  // this wavefront's 16 queries as MFMA B operands (column = query, k = d), loaded first: they
+  // do not depend on the request's context length, which the tile loads wait for
+  const int qi = wave * 16 + (lane & 15);
+  const bool qvalid = qi < a.qrows;
+  bf16x8_t qf[DK];
+  {
+    const int t = qi / hpg;
+    const int h = g * hpg + qi % hpg;
+    const uint16_t* qrow = a.q + ((size_t)b * a.G + t) * a.ldq + h * D;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4_t*>(qrow + ks * 32 + lg * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
   // context key range of this chunk; the last chunk also takes the block's own G keys as
   // one more tile, its first
   const bool has_block = chunk == a.nchunks - 1;
@@ -87,27 +104,11 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   const uint16_t* vblk = a.vb + (size_t)b * a.G * a.ldkv + g * D;
   const uint32_t ctx_stride = static_cast<uint32_t>(a.NKV * D);  // host checks Lcap*NKV*D < 2^31, so byte offsets fit 32 bits
 
-  // this wavefront's 16 queries as MFMA B operands (column = query, k = d)
-  const int qi = wave * 16 + (lane & 15);
-  const bool qvalid = qi < a.qrows;
   // sliding window: this lane's query (block row qi / hpg) sees context keys >= kmin; tiles
   // starting at or past kmin_hi (the largest kmin of the workgroup) need no mask
   const bool windowed = a.window > 0;
   const int kmin = windowed ? a.pos0[b] + qi / hpg - a.window + 1 : INT_MIN;
   const int kmin_hi = windowed ? a.pos0[b] + (a.G - 1) - a.window + 1 : INT_MIN;
-  bf16x8_t qf[DK];
-  {
-    const int t = qi / hpg;
-    const int h = g * hpg + qi % hpg;
-    const uint16_t* qrow = a.q + ((size_t)b * a.G + t) * a.ldq + h * D;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (qvalid) v = *reinterpret_cast<const u32x4_t*>(qrow + ks * 32 + lg * 8);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
-
   float m = -INFINITY, l = 0.f;
   f32x4_t o[DT];
 #pragma unroll

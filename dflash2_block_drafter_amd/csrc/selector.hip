@@ -138,6 +138,8 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
   __shared__ int ccount;
   const bool one_round = ntiles <= CH;
   if (wave == 0) {
+    // the head's bound slots, when given, load with the tile maxima
+    uint32_t b = bound && lane < kTileBoundSlots ? bound[lane] : 0xFFFFFFFFu;
     float g[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) g[i] = __builtin_nanf("");  // NaN: empty (fmaxf skips NaN)
@@ -171,7 +173,6 @@ __device__ __forceinline__ void topk_row(const float* tm, const float* __restric
       // the head's bound slots (K <= kTileBoundSlots): once all are filled their least value
       // is reached by kTileBoundSlots logits of distinct tiles, so it is a theta too, and the
       // tiles below it may never have been stored
-      uint32_t b = lane < kTileBoundSlots ? bound[lane] : 0xFFFFFFFFu;
       static_assert(kTileBoundSlots == 16, "one row of lanes");
       b = (uint32_t)__builtin_amdgcn_readfirstlane((int)row16_umin(b));
       if (b != 0u) th = fmaxf(th, order_float(b));
