@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
   // 8*dg .. +7, with dg running fastest, so each load instruction of a wavefront reads
   // whole key rows (DG lanes per row) and each V^T store is one 8-byte pack of ROWS_PER
   // keys per dim and lane.  The next R tiles are in flight in a register ring while
-  // one is computed (hand-issued loads, each awaited once by name); loads past the last
-  // tile or row repeat it, so that every load is unconditional.
+  // one is computed (hand-issued loads, each awaited once by name); loads past a tile's last
+  // row repeat that row and loads past the last tile read one line of it, so that every
+  // load is unconditional.
   constexpr int DG = D / 8;                  // 16-byte chunks per key row
   static_assert(KT * DG % 256 == 0, "tile must split over 256 threads");
   constexpr int ROWS_PER = (KT * DG) / 256;  // key rows per thread per tile (4 for D=128)
