@@ -176,16 +176,21 @@ __global__ __launch_bounds__(kConvCh / 8) void conv_kernel(const uint16_t* y, Pl
 // deltas, or a standalone prepare's): each thread loads its own group's two coefficients
 // per row next to its inputs, so there is no LDS staging and no barrier, and the only wait
 // is the one round trip for all of a thread's loads.  R rows of a block per thread, as in
-// conv_kernel; kConvCh / 8 threads cover kConvCh channels.
+// conv_kernel; kConvPlaneCh / 8 threads (one wavefront) cover kConvPlaneCh channels.  At
+// T = 1024, H = 5120 that is 1280 workgroups of 8 rows, five per CU: 5.8 us a conv against
+// 6.4 us for 1024 channels (2.5 workgroups per CU), 6.7 us for 256 and 6.6 us for 512 with
+// 4 rows.
+constexpr int kConvPlaneCh = 512;
+
 template <int R, bool NTS>
-__global__ __launch_bounds__(kConvCh / 8) void conv_plane_kernel(const uint16_t* __restrict__ y,
+__global__ __launch_bounds__(kConvPlaneCh / 8) void conv_plane_kernel(const uint16_t* __restrict__ y,
                                                                  const float* __restrict__ coef, int ld,
                                                                  const uint16_t* __restrict__ base, int side,
                                                                  int H, int G, int grp,
                                                                  const uint16_t* residual,
                                                                  uint16_t* out) {  // may be residual
   const int t0 = blockIdx.y * R;
-  const int c0 = blockIdx.x * kConvCh + threadIdx.x * 8;
+  const int c0 = blockIdx.x * kConvPlaneCh + threadIdx.x * 8;
   if (c0 >= H) return;
   const int g = c0 / grp;
   const int ng = H / grp;
@@ -502,10 +507,10 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
   if (T <= 0) return hipSuccess;
   if (coef_next && side != 0) return hipErrorInvalidValue;
   // rows per workgroup: the largest of 8 (one coefficient plane only), 4, 2, 1 dividing G that
-  // still leaves >= 512 workgroups (T = 1024, H = 5120: 8 rows, 640 workgroups, 6.75 -> 6.43
-  // us a conv against 4 rows; 16 rows: 7.9 us)
+  // still leaves >= 512 workgroups (with 1024 channels a workgroup at T = 1024, H = 5120: 8
+  // rows, 640 workgroups, 6.75 -> 6.43 us a conv against 4 rows; 16 rows: 7.9 us)
   const bool plane = coef.S == 1 && !coef_next;
-  const int chunks = (H + kConvCh - 1) / kConvCh;
+  const int chunks = (H + (plane ? kConvPlaneCh : kConvCh) - 1) / (plane ? kConvPlaneCh : kConvCh);
   int R = 1;
   for (int r : {8, 4, 2}) {
     if (r == 8 && !plane) continue;
@@ -521,28 +526,28 @@ hipError_t launch_conv(const uint16_t* y, const Planes& coef, const uint16_t* ba
     const bool nts = (size_t)T * H * sizeof(uint16_t) > (size_t(8) << 20);
     switch (R * 2 + (nts ? 1 : 0)) {
       case 17:
-        conv_plane_kernel<8, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<8, true><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 16:
-        conv_plane_kernel<8, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<8, false><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 9:
-        conv_plane_kernel<4, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<4, true><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 8:
-        conv_plane_kernel<4, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<4, false><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 5:
-        conv_plane_kernel<2, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<2, true><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 4:
-        conv_plane_kernel<2, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<2, false><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       case 3:
-        conv_plane_kernel<1, true><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<1, true><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
         break;
       default:
-        conv_plane_kernel<1, false><<<grid, kConvCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
+        conv_plane_kernel<1, false><<<grid, kConvPlaneCh / 8, 0, stream>>>(y, coef.p, coef.ld, base, side, H, G, grp, residual, out);
     }
     return hipGetLastError();
   }
