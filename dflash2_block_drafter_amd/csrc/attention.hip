@@ -10,9 +10,10 @@
 // K/V row read from HBM serves all of them.  The chunks split the context rows, and the
 // last one also takes the block's own G keys as one more tile (its first); each writes
 // (max, sum, unnormalised O) in fp32 and a combine kernel merges the chunks with their
-// log-sum-exp weights.  A workgroup keeps R tiles of K/V in flight: R = 4 for long chunks,
-// sized so that the whole grid is resident at once (two workgroups per CU); R = 1 for short
-// ones, where three workgroups per CU and more chunks hide more latency than a deep ring.
+// log-sum-exp weights.  A workgroup keeps R tiles of K/V in flight: R = 3 for long chunks,
+// sized so that the whole grid is resident at once (two workgroups per CU; R = 4 and R = 2
+// measured slower: more loads in flight only queue longer); R = 1 for short ones, where
+// three workgroups per CU and more chunks hide more latency than a deep ring.
 //
 // Per 64-key tile a wavefront computes S^T = K . Q^T (keys on rows, its 16 queries on
 // columns) with v_mfma_f32_16x16x32_bf16, so each lane holds one query's scores and the
@@ -376,7 +377,7 @@ AttnPlan plan_attention(int B, int G, int NH, int NKV, int D, int Lmax) {
     return std::max(c, 256);
   };
   pl.chunk = chunk_for(std::max(1, 512 / pairs));
-  pl.stages = 4;
+  pl.stages = 3;
   if (pl.chunk / KT < kDeepMinTiles) {
     pl.chunk = chunk_for(std::max(1, 2048 / pairs));
     pl.stages = 1;
@@ -421,14 +422,14 @@ hipError_t launch_attention(const AttnPlan& pl, const uint16_t* q, int ldq, cons
   const int rows = NKV * pl.qrows;  // per request
   dim3 cgrid((rows + 3) / 4, B);
   if (D == 128) {
-    if (pl.stages == 4)
-      attn_chunk_kernel<128, 4><<<grid, 256, 0, stream>>>(a);
+    if (pl.stages == 3)
+      attn_chunk_kernel<128, 3><<<grid, 256, 0, stream>>>(a);
     else
       attn_chunk_kernel<128, 1><<<grid, 256, 0, stream>>>(a);
     attn_combine_kernel<128><<<cgrid, 256, 0, stream>>>(a, out, ldo);
   } else {
-    if (pl.stages == 4)
-      attn_chunk_kernel<64, 4><<<grid, 256, 0, stream>>>(a);
+    if (pl.stages == 3)
+      attn_chunk_kernel<64, 3><<<grid, 256, 0, stream>>>(a);
     else
       attn_chunk_kernel<64, 1><<<grid, 256, 0, stream>>>(a);
     attn_combine_kernel<64><<<cgrid, 256, 0, stream>>>(a, out, ldo);

@@ -56,7 +56,7 @@ def test_streaming_gemm_waits_cover_every_use(tmp_path):
 def test_attention_ring_waits_cover_every_use(tmp_path):
     asm = _device_assembly(tmp_path, "attention.hip")
     result = check_assembly(asm, r"_ZN3dfl12_GLOBAL__N_117attn_chunk_kernel")
-    assert len(result) == 4, "attention chunk kernel instances (D = 64, 128; rings of 1 and 4) not found"
+    assert len(result) == 4, "attention chunk kernel instances (D = 64, 128; rings of 1 and 3) not found"
     bad = {k: v[:3] for k, v in result.items() if v}
     assert not bad, bad
 
