@@ -612,29 +612,44 @@ __device__ __forceinline__ void lds_wait_n(bf16x8_t& v, int n) {
 
 // 256 x 256 workgroup tiles for projections with enough rows to be bound by the matrix
 // cores.  Both operands go from global memory straight into LDS (global_load_lds, 16 bytes
-// a lane, no registers) through a ring of kDmaStages buffers; a buffer holds one 32-deep K
-// half of both tiles in MFMA fragment order: fragment f (16 rows x 32 K) is 1 KB with lane
-// l's 16 bytes (row l % 16, K offset 8 (l / 16)) at 16 l, so every fragment read is one
-// contiguous, conflict-free 1 KB per wavefront.  Tile-contiguous weights are already in
-// that order (each load is 1 KB contiguous); activations and row-major weights are read
-// as 16 row segments of 64 bytes.  Step kt + 3's loads are issued while step kt is
-// computed.  Eight wavefronts of 128 x 64 outputs (8 x 4 MFMA blocks).
+// a lane, no registers); eight wavefronts of 128 x 64 outputs (8 x 4 MFMA blocks) step
+// through K 32 deep.
 //
-// Waits: a wavefront's copies complete in issue order, so before step kt it waits until
-// at most the eight copies of steps kt + 1 and kt + 2 are outstanding; the barrier then
-// makes every wavefront's step-kt copies visible and tells it that all wavefronts are done
-// reading the buffer that step kt + 3 refills.  LDS reads are inline assembly (the
-// compiler's alias tracking would make them wait for every copy in flight), each value
-// tied to the lgkmcnt wait that covers it.
-constexpr int kDmaStages = 4;
+// Weights (B) go through a ring of three 32-deep buffers in MFMA fragment order: fragment
+// f (16 rows x 32 K) is 1 KB with lane l's 16 bytes (row l % 16, K offset 8 (l / 16)) at
+// 16 l, so every fragment read is one contiguous 1 KB a wavefront.  Tile-contiguous
+// weights are already in that order (each copy is 1 KB contiguous); row-major weights
+// are copied as 16 row segments of 64 bytes.
+//
+// Activations (A) are row-major, and a copy of 16 rows x 64 bytes uses half of each
+// 128-byte line it touches; a 64-deep block of 8 rows is 8 whole lines.  So A goes through
+// a ring of three 64-deep blocks (32 KB each): chunk q (rows 8q..8q+7) is 1 KB with row p
+// at 128 p and its 16-byte K chunk c in slot c ^ p ^ (q & 1).  A fragment read (rows 16F +
+// l % 16, K chunk 4h + l / 16 of the block) then meets every bank once per 16 lanes: rows
+// 0-7 and 8-15 of the fragment sit in chunks of opposite parity, whose slots interleave.
+//
+// Schedule, per 32-deep step kt (h = kt & 1 of block kt / 2): the fragments of step kt + 1
+// are read from LDS while step kt's MFMAs run (registers double-buffered).  Step kt
+// refills the buffers read during step kt - 1: B step kt + 3 into B's slot kt % 3 and, on
+// odd steps, A block (kt - 1) / 2 + 3 into its A buffer.  A wavefront's copies complete in
+// issue order (B before A within a step), and in every step the last six it issued (one
+// B step and one A block at most) are all that may still be outstanding when it waits,
+// which leaves B step kt + 1 and A block (kt + 1) / 2 landed; the barrier after the wait
+// publishes them and tells the wavefront that all others have awaited their reads of the
+// buffers it is about to refill.  LDS reads are inline assembly (the compiler's alias
+// tracking would make them wait for every copy in flight), each value tied to the lgkmcnt
+// wait that covers it.
+constexpr int kDmaStagesB = 3;
+constexpr int kDmaBlocksA = 3;
 
 template <bool TILED>
 __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   constexpr int BN = kGemmTileN, WN = 4, TM = 8, TN = 4, NT = 512;
-  constexpr int FR = 512;         // bf16 per fragment
-  constexpr int STAGE = 16 * FR;  // one operand's K half of a 256-row tile
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kDmaStages][STAGE];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kDmaStages][STAGE];
+  constexpr int FR = 512;          // bf16 per 1 KB fragment or chunk
+  constexpr int STAGE = 16 * FR;   // B: one 32-deep K half of a 256-row tile
+  constexpr int BLOCK = 32 * FR;   // A: one 64-deep K block of a 256-row tile
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kDmaBlocksA][BLOCK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kDmaStagesB][STAGE];
   static_assert(BN == 256, "fragment-order weight blocks are 256 rows");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -651,32 +666,40 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   // the same K block, the activation block they share stays in that XCD's L2; staggered,
   // the whole activation slab (up to 10 MB) is read from the Infinity Cache instead, and every
   // projection measured 4-5% slower.
-  // wavefront w copies fragments 2w and 2w + 1 of both tiles every step
+  // wavefront w copies A chunks 4w..4w+3 of every block and B fragments 2w, 2w + 1 of
+  // every step; lane i of an A copy brings row 8q + i / 8's K chunk (i % 8) ^ (i / 8) ^ (q & 1)
   const int fa = 2 * wave;
   const int fk = (lane >> 4) * 8;
-  const uint16_t* arow[2];
+  const uint16_t* arow[4];
   const uint16_t* brow[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    arow[i] = p.A + (size_t)min(m0 + 16 * (fa + i) + (lane & 15), p.M - 1) * p.lda + fk;
+  for (int u = 0; u < 4; ++u) {
+    const int q = 4 * wave + u;  // q & 1 == u & 1
+    const int c = (lane & 7) ^ (lane >> 3) ^ (u & 1);
+    arow[u] = p.A + (size_t)min(m0 + 8 * q + (lane >> 3), p.M - 1) * p.lda + kb0 * 64 + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
     brow[i] = TILED ? p.W + ((size_t)(n0 / BN) * (p.K / 64) + kb0) * (BN * 64) + (size_t)(2 * (fa + i)) * FR + lane * 8
                     : p.W + (size_t)min(n0 + 16 * (fa + i) + (lane & 15), p.N - 1) * p.K + fk;
-  }
-  // step st's copies into buffer slot (steps past the last re-read the last one, so every
-  // iteration issues and awaits the same number of copies)
-  auto issue = [&](int st, int slot) {
+  // copies past the last step or block re-read the last one, so every step issues and
+  // awaits the same number of copies
+  auto issue_b = [&](int st) {  // B step st into slot st % 3
     const int s = min(st, nst - 1);
     const int h = s & 1;
     const int kb = s >> 1;  // K block within the split
-    const int k0 = (kb0 + kb) * 64 + h * 32;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(arow[i] + k0, &sA[slot][(fa + i) * FR], 16, 0, 0);
+    uint16_t* dst = &sB[st % kDmaStagesB][0];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint16_t* src = TILED ? brow[i] + (size_t)kb * (BN * 64) + h * FR : brow[i] + k0;
-      __builtin_amdgcn_global_load_lds(src, &sB[slot][(fa + i) * FR], 16, 0, 0);
+      const uint16_t* src = TILED ? brow[i] + (size_t)kb * (BN * 64) + h * FR : brow[i] + (kb0 + kb) * 64 + h * 32;
+      __builtin_amdgcn_global_load_lds(src, dst + (fa + i) * FR, 16, 0, 0);
     }
+  };
+  auto issue_a = [&](int j) {  // A block j into buffer j % 3
+    const int jj = min(j, nkb - 1);
+    uint16_t* dst = &sA[j % kDmaBlocksA][0];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_amdgcn_global_load_lds(arow[u] + jj * 64, dst + (4 * wave + u) * FR, 16, 0, 0);
   };
 
   f32x4_t acc[TM][TN];
@@ -685,17 +708,24 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t sa0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0])) + (wm * TM * FR + lane * 8) * 2;
+  // A fragment i of this wavefront (tile rows 16 (8 wm + i) ..) lies in chunks 2 (8 wm + i)
+  // and + 1; lane l reads chunk 2 (8 wm + i) + (l % 16) / 8, row l % 8, slot (4h + l / 16) ^
+  // (l % 8) ^ ((l % 16) / 8)
+  const int slot0 = (lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1);
+  const uint32_t sa_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0])) + wm * TM * 2048 +
+                           ((lane >> 3) & 1) * 1024 + (lane & 7) * 128;
+  const uint32_t sa0 = sa_lane + slot0 * 16, sa1 = sa_lane + (slot0 ^ 4) * 16;
   const uint32_t sb0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sB[0][0])) + (wn * TN * FR + lane * 8) * 2;
   // Fragments are double-buffered in registers: step kt + 1's are read from LDS while step
   // kt's MFMAs run, and awaited (every value tied to a wait) after them.
   bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  auto read = [&](int slot, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
-    const uint32_t oa = sa0 + slot * (STAGE * 2), ob = sb0 + slot * (STAGE * 2);
+  auto read = [&](int st, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+    const uint32_t oa = ((st & 1) ? sa1 : sa0) + ((st >> 1) % kDmaBlocksA) * (BLOCK * 2);
+    const uint32_t ob = sb0 + (st % kDmaStagesB) * (STAGE * 2);
 #pragma unroll
     for (int j = 0; j < TN; ++j) b[j] = lds_read_b128(ob + j * (FR * 2));
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = lds_read_b128(oa + i * (FR * 2));
+    for (int i = 0; i < TM; ++i) a[i] = lds_read_b128(oa + i * 2048);
   };
   auto await = [&](bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
 #pragma unroll
@@ -710,30 +740,34 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
-  // iteration kt: step kt + 1's copies are in (only step kt + 2's four are outstanding),
-  // the barrier publishes them and frees step kt - 1's buffer, which step kt + 3 refills
-  auto step = [&](int kt, const bf16x8_t (&ca)[TM], const bf16x8_t (&cb)[TN], bf16x8_t (&na)[TM],
+  auto step = [&](int kt, bool odd, const bf16x8_t (&ca)[TM], const bf16x8_t (&cb)[TN], bf16x8_t (&na)[TM],
                   bf16x8_t (&nb)[TN]) {
-    wait_vmcnt<4>();
+    wait_vmcnt<6>();
     __builtin_amdgcn_s_barrier();
-    issue(kt + 3, (kt + 3) & (kDmaStages - 1));
-    read((kt + 1) & (kDmaStages - 1), na, nb);  // past the last step: a re-read copy, unused
+    issue_b(kt + 3);
+    if (odd) issue_a((kt - 1) / 2 + 3);
+    read(kt + 1, na, nb);  // past the last step: a re-read copy, unused
     mfma(ca, cb);
     await(na, nb);
   };
 
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  wait_vmcnt<8>();
+  // issue order A0 B0 B1 A1 B2 A2: the first wait leaves the last twelve (B1 onwards)
+  // outstanding, and step 0's wait for six leaves B2 and A2
+  issue_a(0);
+  issue_b(0);
+  issue_b(1);
+  issue_a(1);
+  issue_b(2);
+  issue_a(2);
+  wait_vmcnt<12>();
   __builtin_amdgcn_s_barrier();
   read(0, fa0, fb0);
   await(fa0, fb0);
   for (int kt = 0; kt < nst; kt += 2) {  // nst is even
-    step(kt, fa0, fb0, fa1, fb1);
-    step(kt + 1, fa1, fb1, fa0, fb0);
+    step(kt, false, fa0, fb0, fa1, fb1);
+    step(kt + 1, true, fa1, fb1, fa0, fb0);
   }
-  wait_vmcnt<0>();  // the re-read copies past the last step land before the LDS is reused
+  wait_vmcnt<0>();  // the re-read copies past the last step land before the workgroup ends
   gemm_epilogue<256, WN, TM, TN, NT>(p, acc, m0, n0, wm, wn, lane, tid);
 }
 
