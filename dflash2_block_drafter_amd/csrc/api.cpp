@@ -201,6 +201,7 @@ int check_config(const dfl_config* c) {
 
 struct DraftLayout {
   size_t x, n, a, qkv, ao, u, p, h, logits, tmax, tbound, z, cand, unary, scores, attn, kpart, coef1, partial;
+  size_t atile, atile_elems;
   size_t total;
 };
 
@@ -238,6 +239,13 @@ DraftLayout draft_layout(const dfl_config& c, int B, int G, int Lmax) {
                            {N, c.rank, H, 0}};
   for (auto& s : shapes) part = std::max(part, dfl::plan_gemm(s[0], s[1], s[2], s[3] != 0).partial_bytes);
   L.partial = cv.off; cv.take<char>(part);
+  // the fragment-order copy of gate/up's or the head's activations when they run on 256-row
+  // tiles (the 256 x 256 kernel then copies whole contiguous 1 KB fragments)
+  const bool wide = dfl::gemm_takes_tiled_a(dfl::plan_gemm(T, 2 * F, H), false) ||
+                    dfl::gemm_takes_tiled_a(dfl::plan_gemm(N, c.vocab + c.rank, H, true), false) ||
+                    dfl::gemm_takes_tiled_a(dfl::plan_gemm(N, c.vocab, H, true), false);
+  L.atile_elems = wide ? dfl::tiled_rows_elems(std::max(T, N), H) : 0;
+  L.atile = cv.off; cv.take<uint16_t>(L.atile_elems);
   L.total = cv.off;
   return L;
 }
@@ -373,9 +381,15 @@ int run_layer(dfl_drafter* d, int li, const uint16_t* xin, uint16_t* x, int B, i
     DFL_TRY(snap(tr->i, a, rowsH, stream));
     DFL_TRY(snap(tr->coef1_mlp, c1, (size_t)T * 2 * ng * sizeof(float), stream));
   }
+  // on 256-row tiles gate/up reads a fragment-order copy of a (counted with the projection)
+  const bool gu_tiled = dfl::gemm_takes_tiled_a(p_gu, d->q4) && lay.atile_elems >= dfl::tiled_rows_elems(T, H);
   DFL_TRY(timed(d, DFL_K_GEMM_GATEUP, gemm_bytes(T, 2 * F, H, dfl::EPI_SILU_MUL, d->q4), stream, [&] {
-    return dfl::launch_gemm(p_gu, a, H, wref(L.gateup, L.gateup_q4), T, 2 * F, H, dfl::EPI_SILU_MUL, p, F, nullptr,
-                            0, 0, part, stream);
+    if (gu_tiled) {
+      const hipError_t e = dfl::launch_tile_rows(a, H, T, H, u16(lay.atile), stream);
+      if (e != hipSuccess) return e;
+    }
+    return dfl::launch_gemm(p_gu, gu_tiled ? u16(lay.atile) : a, H, wref(L.gateup, L.gateup_q4), T, 2 * F, H,
+                            dfl::EPI_SILU_MUL, p, F, nullptr, 0, 0, part, stream, nullptr, nullptr, gu_tiled);
   }));
   if (tr) DFL_TRY(snap(tr->p, p, (size_t)T * F * sizeof(uint16_t), stream));
   const bool d_planes = p_dn.splits > 1 && next_gamma && H <= dfl::kCrnPlanesMaxH;
@@ -921,10 +935,17 @@ int dfl_draft_block_traced(dfl_drafter* d, const dfl_bf16* embeds, const int32_t
   }
   if (trace) DFL_TRY(snap(trace->h, h, (size_t)N * H * sizeof(uint16_t), stream));
   float* tmax = f32(lay.tmax);
+  // on 256-row tiles the head reads a fragment-order copy of h (counted with the projection)
+  const bool head_tiled = dfl::gemm_takes_tiled_a(p_head, false) && lay.atile_elems >= dfl::tiled_rows_elems(N, H);
+  uint16_t* htile = reinterpret_cast<uint16_t*>(W + lay.atile);
   DFL_TRY(timed(d, DFL_K_GEMM_HEAD, gemm_bytes(N, NHd, H, dfl::EPI_F32), stream, [&] {
-    return dfl::launch_gemm(p_head, h, H, bound_head ? d->head : lm_head, bound_head, N, NHd, H, dfl::EPI_F32, logits,
-                            V_, head_sel ? z : nullptr, R, V_, part, stream, tiles_fused ? tmax : nullptr,
-                            tbound);
+    if (head_tiled) {
+      const hipError_t e = dfl::launch_tile_rows(h, H, N, H, htile, stream);
+      if (e != hipSuccess) return e;
+    }
+    return dfl::launch_gemm(p_head, head_tiled ? htile : h, H, bound_head ? d->head : lm_head, bound_head, N, NHd,
+                            H, dfl::EPI_F32, logits, V_, head_sel ? z : nullptr, R, V_, part, stream,
+                            tiles_fused ? tmax : nullptr, tbound, head_tiled);
   }));
   if (!head_sel) {
     DFL_TRY(timed(d, DFL_K_GEMM_SELPROJ, gemm_bytes(N, R, H, dfl::EPI_F32), stream, [&] {

@@ -58,6 +58,7 @@ struct GemmArgs {
   int splits;
   float* tile_max;  // EPI_F32, one split: [M, ceil(nsplit / 256)] row maxima of each 256-column tile of out0
   uint32_t* tile_bound;  // with tile_max, optional: [M, kTileBoundSlots] (launch_gemm's declaration)
+  int a_tiled;           // A in fragment order (launch_tile_rows), 256 x 256 kernel only
   // 4-bit affine weights (used instead of W): row-major packed [N, K/8] words with scales and
   // biases [N, K/64] bf16, or tile-contiguous blocks (q4_tiled_words)
   const uint32_t* Wq;
@@ -771,6 +772,122 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   gemm_epilogue<256, WN, TM, TN, NT>(p, acc, m0, n0, wm, wn, lane, tid);
 }
 
+// The same 256 x 256 tiles for activations already in fragment order (launch_tile_rows):
+// both operands are then copied as contiguous 1 KB fragments, through a ring of four
+// buffers, each one 32-deep K half of both tiles in fragment order, and every fragment
+// read is one contiguous 1 KB a wavefront.  Step kt + 3's copies are issued while step kt
+// is computed.  Waits: a wavefront's copies complete in issue order, so before step kt it
+// waits until at most the eight copies of steps kt + 1 and kt + 2 are outstanding; the
+// barrier then makes every wavefront's step-kt copies visible and tells it that all
+// wavefronts are done reading the buffer that step kt + 3 refills.  (This ring measured
+// faster than the row-major kernel's for fragment-order activations.)
+constexpr int kDmaStages = 4;
+
+template <bool TILED>
+__global__ __launch_bounds__(512, 1) void gemm_dma_frag_kernel(GemmArgs p) {
+  constexpr int BN = kGemmTileN, WN = 4, TM = 8, TN = 4, NT = 512;
+  constexpr int FR = 512;         // bf16 per fragment
+  constexpr int STAGE = 16 * FR;  // one operand's K half of a 256-row tile
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kDmaStages][STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kDmaStages][STAGE];
+  static_assert(BN == 256, "fragment-order weight blocks are 256 rows");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  int ntile, mtile;
+  tile_of_block(p.M, p.N, ntile, mtile);
+  const int n0 = ntile * BN;
+  const int m0 = mtile * 256;
+  const int kb0 = blockIdx.z * (p.k_per_split / 64);               // first 64-deep K block of this split
+  const int nkb = (min(p.K, (blockIdx.z + 1) * p.k_per_split) - blockIdx.z * p.k_per_split) / 64;
+  const int nst = 2 * nkb;  // K halves
+  // wavefront w copies fragments 2w and 2w + 1 of both tiles every step
+  const int fa = 2 * wave;
+  const int fk = (lane >> 4) * 8;
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    arow[i] = p.A + ((size_t)min(m0 / 16 + fa + i, (p.M + 15) / 16 - 1) * (p.K / 32) + 2 * kb0) * FR + lane * 8;
+    brow[i] = TILED ? p.W + ((size_t)(n0 / BN) * (p.K / 64) + kb0) * (BN * 64) + (size_t)(2 * (fa + i)) * FR + lane * 8
+                    : p.W + (size_t)min(n0 + 16 * (fa + i) + (lane & 15), p.N - 1) * p.K + fk;
+  }
+  // step st's copies into buffer slot (steps past the last re-read the last one, so every
+  // iteration issues and awaits the same number of copies)
+  auto issue = [&](int st, int slot) {
+    const int s = min(st, nst - 1);
+    const int h = s & 1;
+    const int kb = s >> 1;  // K block within the split
+    const int k0 = (kb0 + kb) * 64 + h * 32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(arow[i] + (2 * kb + h) * FR, &sA[slot][(fa + i) * FR], 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint16_t* src = TILED ? brow[i] + (size_t)kb * (BN * 64) + h * FR : brow[i] + k0;
+      __builtin_amdgcn_global_load_lds(src, &sB[slot][(fa + i) * FR], 16, 0, 0);
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t sa0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0])) + (wm * TM * FR + lane * 8) * 2;
+  const uint32_t sb0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sB[0][0])) + (wn * TN * FR + lane * 8) * 2;
+  // Fragments are double-buffered in registers: step kt + 1's are read from LDS while step
+  // kt's MFMAs run, and awaited (every value tied to a wait) after them.
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  auto read = [&](int slot, bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+    const uint32_t oa = sa0 + slot * (STAGE * 2), ob = sb0 + slot * (STAGE * 2);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = lds_read_b128(ob + j * (FR * 2));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = lds_read_b128(oa + i * (FR * 2));
+  };
+  auto await = [&](bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) lds_wait<0>(b[j]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) lds_wait<0>(a[i]);
+  };
+  auto mfma = [&](const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  // iteration kt: step kt + 1's copies are in (only step kt + 2's four are outstanding),
+  // the barrier publishes them and frees step kt - 1's buffer, which step kt + 3 refills
+  auto step = [&](int kt, const bf16x8_t (&ca)[TM], const bf16x8_t (&cb)[TN], bf16x8_t (&na)[TM],
+                  bf16x8_t (&nb)[TN]) {
+    wait_vmcnt<4>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3, (kt + 3) & (kDmaStages - 1));
+    read((kt + 1) & (kDmaStages - 1), na, nb);  // past the last step: a re-read copy, unused
+    mfma(ca, cb);
+    await(na, nb);
+  };
+
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  wait_vmcnt<8>();
+  __builtin_amdgcn_s_barrier();
+  read(0, fa0, fb0);
+  await(fa0, fb0);
+  for (int kt = 0; kt < nst; kt += 2) {  // nst is even
+    step(kt, fa0, fb0, fa1, fb1);
+    step(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  wait_vmcnt<0>();  // the re-read copies past the last step land before the LDS is reused
+  gemm_epilogue<256, WN, TM, TN, NT>(p, acc, m0, n0, wm, wn, lane, tid);
+}
+
 // NW wavefronts per workgroup, 32 weight rows each, two wavefronts per SIMD (256 registers
 // each), so while one waits the other computes.  A 2-wavefront workgroup's LDS admits two
 // per CU, one wavefront per SIMD, so that instance asks for one.
@@ -1044,7 +1161,31 @@ __global__ __launch_bounds__(256) void tile_q4_kernel(const uint32_t* __restrict
   dst[w] = v;
 }
 
+// One thread per 16 bytes of the fragment-order copy: thread t fills lane t % 64 of fragment
+// t / 64 (row group g, K step ks) with row 16 g + lane % 16, K offsets 32 ks + 8 (lane / 16)..
+__global__ __launch_bounds__(256) void tile_rows_kernel(const uint16_t* __restrict__ A, int lda, int M, int K,
+                                                        uint16_t* __restrict__ dst, size_t chunks) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= chunks) return;
+  const size_t f = t / 64;
+  const int lane = static_cast<int>(t % 64);
+  const int ksteps = K / 32;
+  const int g = static_cast<int>(f / ksteps), ks = static_cast<int>(f % ksteps);
+  const int row = min(16 * g + (lane & 15), M - 1);
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(A + (size_t)row * lda + 32 * ks + 8 * (lane >> 4));
+  *reinterpret_cast<u32x4_t*>(dst + t * 8) = v;
+}
+
 }  // namespace
+
+size_t tiled_rows_elems(int M, int K) { return (size_t)((M + 15) / 16) * 16 * K; }
+
+hipError_t launch_tile_rows(const uint16_t* A, int lda, int M, int K, uint16_t* dst, hipStream_t stream) {
+  if (M <= 0 || K % 32 != 0 || lda % 8 != 0 || lda < K) return hipErrorInvalidValue;
+  const size_t chunks = tiled_rows_elems(M, K) / 8;
+  tile_rows_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(A, lda, M, K, dst, chunks);
+  return hipGetLastError();
+}
 
 size_t q4_tiled_words(int N, int K) { return (size_t)((N + kBN - 1) / kBN) * (K / BK) * kBN * 9; }
 
@@ -1211,7 +1352,7 @@ namespace {
 
 GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K, int epi,
                    void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial, float* tile_max,
-                   uint32_t* tile_bound = nullptr) {
+                   uint32_t* tile_bound = nullptr, bool a_tiled = false) {
   GemmArgs p;
   p.A = A;
   p.W = W.w;
@@ -1233,6 +1374,7 @@ GemmArgs make_args(const GemmPlan& pl, const uint16_t* A, int lda, const WeightR
   p.splits = pl.splits;
   p.tile_max = tile_max;
   p.tile_bound = tile_max ? tile_bound : nullptr;
+  p.a_tiled = a_tiled ? 1 : 0;
   return p;
 }
 
@@ -1293,10 +1435,16 @@ hipError_t launch_main(const GemmArgs& p, const GemmPlan& pl, const WeightRef& W
       else
         gemm_bf16_kernel<kBigBM, kBN, BK, 2, 4, 1, 1, false, true><<<grid, 512, 0, stream>>>(p);
     } else {
-      if (W.tiled)
+      if (p.a_tiled) {
+        if (W.tiled)
+          gemm_dma_frag_kernel<true><<<grid, 512, 0, stream>>>(p);
+        else
+          gemm_dma_frag_kernel<false><<<grid, 512, 0, stream>>>(p);
+      } else if (W.tiled) {
         gemm_dma_kernel<true><<<grid, 512, 0, stream>>>(p);
-      else
+      } else {
         gemm_dma_kernel<false><<<grid, 512, 0, stream>>>(p);
+      }
     }
     return hipGetLastError();
   }
@@ -1340,19 +1488,20 @@ hipError_t launch_reduce(const GemmArgs& p, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
-                       hipStream_t stream, float* tile_max, uint32_t* tile_bound) {
+                       hipStream_t stream, float* tile_max, uint32_t* tile_bound, bool a_tiled) {
   // tile maxima come from the LDS kernel's epilogue (one 256-column tile per workgroup); a
   // tile may not straddle the two outputs
   if (tile_max && (epi != EPI_F32 || pl.splits != 1 || pl.stream_waves > 0 ||
                    (out1 && nsplit % kGemmTileN != 0)))
     return hipErrorInvalidValue;
+  if (a_tiled && !gemm_takes_tiled_a(pl, W.q != nullptr)) return hipErrorInvalidValue;
   if (W.q && K % BK != 0) return hipErrorInvalidValue;
   if (pl.tail_n > 0 && pl.splits == 1 && !tile_max && !W.q && !out1 && pl.tail_n < N) {
     // the full rounds: weight rows [0, tail_n) into the matching output columns
     GemmPlan pm = pl;
     pm.tail_n = 0;
     const GemmArgs pa = make_args(pm, A, lda, W, M, pl.tail_n, K, epi, out0, ld0, nullptr, 0, pl.tail_n, partial,
-                                  nullptr);
+                                  nullptr, nullptr, a_tiled);
     hipError_t e = launch_main(pa, pm, W, stream);
     if (e != hipSuccess) return e;
     // the rest with split K: weights from row tail_n (a whole tile-contiguous tile boundary),
@@ -1366,13 +1515,14 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
     GemmPlan pt = pm;
     pt.splits = pl.tail_splits;
     pt.k_per_split = pl.tail_k_per_split;
-    const GemmArgs pb = make_args(pt, A, lda, wt, M, nt, K, epi, o, ld0, nullptr, 0, nt, partial, nullptr);
+    const GemmArgs pb = make_args(pt, A, lda, wt, M, nt, K, epi, o, ld0, nullptr, 0, nt, partial, nullptr, nullptr,
+                                  a_tiled);
     e = launch_main(pb, pt, wt, stream);
     if (e != hipSuccess) return e;
     return launch_reduce(pb, stream);
   }
   const GemmArgs p = make_args(pl, A, lda, W, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, tile_max,
-                               tile_bound);
+                               tile_bound, a_tiled);
   hipError_t e = launch_main(p, pl, W, stream);
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_reduce(p, stream);
@@ -1380,12 +1530,12 @@ hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const Wei
 
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1, int nsplit,
-                       float* partial, hipStream_t stream, float* tile_max, uint32_t* tile_bound) {
+                       float* partial, hipStream_t stream, float* tile_max, uint32_t* tile_bound, bool a_tiled) {
   WeightRef w;
   w.w = W;
   w.tiled = w_tiled;
   return launch_gemm(pl, A, lda, w, M, N, K, epi, out0, ld0, out1, ld1, nsplit, partial, stream, tile_max,
-                     tile_bound);
+                     tile_bound, a_tiled);
 }
 
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,

@@ -45,7 +45,8 @@ struct WeightRef {
 };
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N, int K,
                        int epi, void* out0, int ld0, void* out1, int ld1, int nsplit, float* partial,
-                       hipStream_t stream, float* tile_max = nullptr, uint32_t* tile_bound = nullptr);
+                       hipStream_t stream, float* tile_max = nullptr, uint32_t* tile_bound = nullptr,
+                       bool a_tiled = false);
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const WeightRef& W, int M, int N,
                                 int K, float* partial, hipStream_t stream);
 // Tile-contiguous 4-bit weights: per (256-row tile, 64-wide K step) four 64-row groups of
@@ -70,12 +71,22 @@ hipError_t launch_tile_q4(const uint32_t* q, const uint16_t* scales, const uint1
 // largest logit; a tile whose row maximum is below it (as floats) cannot hold any of the
 // row's top kTileBoundSlots, and its values of that row are not stored.  A top-K with K <=
 // kTileBoundSlots stays exact when it reads only tiles whose maximum reaches that bound.
+// a_tiled: A is not row-major but in fragment order as written by launch_tile_rows (lda is
+// then unused); only plans for which gemm_takes_tiled_a holds accept it.
 constexpr int kGemmTileN = 256;
 constexpr int kTileBoundSlots = 16;
 hipError_t launch_gemm(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W, bool w_tiled,
                        int M, int N, int K, int epi, void* out0, int ld0, void* out1, int ld1,
                        int nsplit, float* partial, hipStream_t stream, float* tile_max = nullptr,
-                       uint32_t* tile_bound = nullptr);
+                       uint32_t* tile_bound = nullptr, bool a_tiled = false);
+// The plan runs the 256 x 256 kernel, which can read A in fragment order.
+inline bool gemm_takes_tiled_a(const GemmPlan& pl, bool q4) { return pl.bm == 256 && pl.stream_waves == 0 && !q4; }
+// Fragment-order copy of row-major activations A [M, K] (lda; K % 32 == 0, lda % 8 == 0):
+// [ceil(M/16)][K/32] fragments of 16 rows x 32 K, each 64 lanes x 8 bf16 where lane l holds
+// row l % 16 and K offset 8 * (l / 16); rows past M repeat row M - 1.  tiled_rows_elems gives
+// the destination size in bf16 elements.
+size_t tiled_rows_elems(int M, int K);
+hipError_t launch_tile_rows(const uint16_t* A, int lda, int M, int K, uint16_t* dst, hipStream_t stream);
 // y = A . W^T left as fp32 planes for the consumer: pl.splits planes [M, N] at plane stride
 // M*N in `partial` (one plane, the plain result, when the plan does not split K).
 hipError_t launch_gemm_partials(const GemmPlan& pl, const uint16_t* A, int lda, const uint16_t* W,

@@ -64,7 +64,10 @@ def test_attention_ring_waits_cover_every_use(tmp_path):
 @needs_hipcc
 def test_dma_gemm_fragment_reads_are_awaited(tmp_path):
     # the 256 x 256 tile kernel's LDS fragment reads are inline assembly, each tied to a wait
-    result = check_assembly(_device_assembly(tmp_path, "gemm.hip"), r"_ZN3dfl12_GLOBAL__N_115gemm_dma_kernel")
+    asm = _device_assembly(tmp_path, "gemm.hip")
+    result = check_assembly(asm, r"_ZN3dfl12_GLOBAL__N_115gemm_dma_kernel")
     assert len(result) == 2, "DMA kernel instances (tiled and row-major weights) not found"
-    bad = {k: v[:3] for k, v in result.items() if v}
+    frag = check_assembly(asm, r"_ZN3dfl12_GLOBAL__N_120gemm_dma_frag_kernel")
+    assert len(frag) == 2, "fragment-order DMA kernel instances not found"
+    bad = {k: v[:3] for k, v in {**result, **frag}.items() if v}
     assert not bad, bad
