@@ -625,9 +625,11 @@ __device__ __forceinline__ void lds_wait_n(bf16x8_t& v, int n) {
 // Activations (A) are row-major, and a copy of 16 rows x 64 bytes uses half of each
 // 128-byte line it touches; a 64-deep block of 8 rows is 8 whole lines.  So A goes through
 // a ring of three 64-deep blocks (32 KB each): chunk q (rows 8q..8q+7) is 1 KB with row p
-// at 128 p and its 16-byte K chunk c in slot c ^ p ^ (q & 1).  A fragment read (rows 16F +
-// l % 16, K chunk 4h + l / 16 of the block) then meets every bank once per 16 lanes: rows
-// 0-7 and 8-15 of the fragment sit in chunks of opposite parity, whose slots interleave.
+// at 128 p and its 16-byte K chunk c in slot sw(c) ^ p ^ (q & 1), where sw swaps the two low
+// bits of c.  A fragment read (rows 16F + l % 16, K chunk 4h + l / 16 of the block) then
+// meets every bank once per 512 bytes read by 32 consecutive lanes (and per 256 by 16, per
+// 128 by 8): within 32 lanes the slot's bit 0 follows the row parity q & 1, bit 1 the low
+// bit of l / 16, bit 2 the row's bit 2.
 //
 // Schedule, per 32-deep step kt (h = kt & 1 of block kt / 2): the fragments of step kt + 1
 // are read from LDS while step kt's MFMAs run (registers double-buffered).  Step kt
@@ -668,7 +670,8 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
   // the whole activation slab (up to 10 MB) is read from the Infinity Cache instead, and every
   // projection measured 4-5% slower.
   // wavefront w copies A chunks 4w..4w+3 of every block and B fragments 2w, 2w + 1 of
-  // every step; lane i of an A copy brings row 8q + i / 8's K chunk (i % 8) ^ (i / 8) ^ (q & 1)
+  // every step; lane i of an A copy brings row 8q + i / 8's K chunk sw((i % 8) ^ (i / 8) ^ (q & 1))
+  auto sw = [](int c) { return (c & 4) | ((c & 1) << 1) | ((c >> 1) & 1); };
   const int fa = 2 * wave;
   const int fk = (lane >> 4) * 8;
   const uint16_t* arow[4];
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int q = 4 * wave + u;  // q & 1 == u & 1
-    const int c = (lane & 7) ^ (lane >> 3) ^ (u & 1);
+    const int c = sw((lane & 7) ^ (lane >> 3) ^ (u & 1));
     arow[u] = p.A + (size_t)min(m0 + 8 * q + (lane >> 3), p.M - 1) * p.lda + kb0 * 64 + c * 8;
   }
 #pragma unroll
@@ -710,9 +713,9 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs p) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // A fragment i of this wavefront (tile rows 16 (8 wm + i) ..) lies in chunks 2 (8 wm + i)
-  // and + 1; lane l reads chunk 2 (8 wm + i) + (l % 16) / 8, row l % 8, slot (4h + l / 16) ^
-  // (l % 8) ^ ((l % 16) / 8)
-  const int slot0 = (lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1);
+  // and + 1; lane l reads chunk 2 (8 wm + i) + (l % 16) / 8, row l % 8, slot sw(4h + l / 16) ^
+  // (l % 8) ^ ((l % 16) / 8), which is 4h ^ its value at h = 0
+  const int slot0 = sw(lane >> 4) ^ (lane & 7) ^ ((lane >> 3) & 1);
   const uint32_t sa_lane = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&sA[0][0])) + wm * TM * 2048 +
                            ((lane >> 3) & 1) * 1024 + (lane & 7) * 128;
   const uint32_t sa0 = sa_lane + slot0 * 16, sa1 = sa_lane + (slot0 ^ 4) * 16;
