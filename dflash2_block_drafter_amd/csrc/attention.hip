@@ -57,7 +57,10 @@ struct AttnArgs {
 
 template <int D, int R>
 __global__ __launch_bounds__(256, 2) void attn_chunk_kernel(AttnArgs a) {
-  constexpr int KS = D + 8;   // K tile row stride (bf16)
+  // K tile row stride (bf16): 2 (D / 16 + 1) 16-byte slots, twice an odd number, so a
+  // fragment read's 32 lanes (16 rows x 2 adjacent chunks, which gfx950's LDS serves
+  // together over 512 bytes) land on 32 distinct slots; D + 8 left one 2-way collision
+  constexpr int KS = D + 16;
   constexpr int VS = KT + 4;  // V^T tile row stride (bf16): 34 dwords, conflict-free reads
   constexpr int DT = D / 16;  // output d tiles
   constexpr int DK = D / 32;  // MFMA k steps over D
